@@ -1,0 +1,145 @@
+"""Pins of the oracle's cumulative-attention selection, block conversion and
+minimum-budget floor: brute force over all subsets, token-level masks and
+invariants (no GPU)."""
+import itertools
+
+import numpy as np
+import pytest
+
+import oracle as O
+
+F32 = np.float32
+
+
+def _fixed(values, gamma):
+    u = [int(round(float(x) * 2 ** 32)) for x in values]
+    U = sum(u)
+    G = int(round(float(F32(gamma)) * 2 ** 24))
+    T = -(-G * U // 2 ** 24)
+    return u, T
+
+
+def brute_force_select(values, gamma):
+    """All subsets: the minimal-cardinality subsets whose fixed-point mass
+    reaches T; among them the one whose (value desc, index asc) key sequence
+    is lexicographically first."""
+    n = len(values)
+    u, T = _fixed(values, gamma)
+    if T == 0:
+        return set()
+    for size in range(1, n + 1):
+        best = None
+        for sub in itertools.combinations(range(n), size):
+            if sum(u[i] for i in sub) >= T:
+                key = sorted((-float(values[i]), i) for i in sub)
+                if best is None or key < best[0]:
+                    best = (key, set(sub))
+        if best is not None:
+            return best[1]
+    raise AssertionError("threshold unreachable")
+
+
+@pytest.mark.parametrize("seed", range(60))
+def test_selection_equals_brute_force(seed):
+    rng = np.random.default_rng(seed)
+    n = int(rng.integers(1, 12))
+    if seed % 3 == 0:    # many exact ties
+        vals = rng.choice(np.array([0.0, 0.125, 0.25, 0.5], F32), size=n)
+        if vals.sum() == 0:
+            vals[0] = F32(0.5)
+    else:
+        vals = rng.dirichlet(np.ones(n)).astype(F32)
+    gamma = float(rng.choice([0.5, 0.8, 0.9, 0.95, 0.999, rng.uniform(0.01, 1.0)]))
+    sel = O.select_cumulative(vals, gamma)
+    assert set(np.nonzero(sel)[0].tolist()) == brute_force_select(vals, gamma)
+
+
+def test_selection_invariants_and_monotone_in_gamma():
+    rng = np.random.default_rng(11)
+    vals = (rng.pareto(1.2, 5000) + 1e-3).astype(F32)
+    vals /= vals.sum()
+    prev = None
+    for gamma in (0.5, 0.8, 0.9, 0.95, 0.99):
+        sel = O.select_cumulative(vals, gamma)
+        u, T = _fixed(vals, gamma)
+        u = np.array(u, dtype=object)
+        chosen = np.nonzero(sel)[0]
+        mass = sum(u[chosen])
+        assert mass >= T
+        # dropping the smallest chosen element falls below the threshold
+        smallest = min(chosen, key=lambda i: (float(vals[i]), -i))
+        assert mass - u[smallest] < T
+        # every chosen value >= every unchosen value
+        assert vals[sel].min() >= vals[~sel].max()
+        # float64 mass reaches gamma up to the fixed-point resolution
+        assert vals[sel].astype(np.float64).sum() >= gamma * vals.astype(np.float64).sum() - 1e-6
+        if prev is not None:
+            assert np.all(sel[prev])                 # S(g1) subset of S(g2)
+        prev = sel
+
+
+def test_selection_ties_prefer_lower_index():
+    vals = np.full(10, 0.1, F32)
+    sel = O.select_cumulative(vals, 0.35)
+    assert np.nonzero(sel)[0].tolist() == [0, 1, 2, 3]
+
+
+def test_gamma_one_selects_every_nonzero_entry():
+    vals = np.array([0.5, 0.0, 0.25, 0.25], F32)
+    assert O.select_cumulative(vals, 1.0).tolist() == [True, False, True, True]
+
+
+def token_level_vs_blocks(sel_cols, sel_diags, bs):
+    N = len(sel_cols)
+    i = np.arange(N)[:, None]
+    j = np.arange(N)[None, :]
+    tok = (j <= i) & (sel_cols[j] | sel_diags[np.clip(i - j, 0, N - 1)])
+    nb = N // bs
+    return tok.reshape(nb, bs, nb, bs).any(axis=(1, 3))
+
+
+@pytest.mark.parametrize("seed", range(25))
+def test_vs_block_mask_equals_token_level_any(seed):
+    rng = np.random.default_rng(100 + seed)
+    bs = int(rng.choice([4, 8, 16]))
+    nb = int(rng.integers(1, 10))
+    N = bs * nb
+    sel_cols = rng.random(N) < rng.uniform(0, 0.2)
+    sel_diags = rng.random(N) < rng.uniform(0, 0.2)
+    if seed == 0:
+        sel_diags[:] = False
+        sel_diags[bs] = True           # r = 0: exactly one block diagonal
+    got = O.vs_block_mask(sel_cols, sel_diags, bs)
+    assert np.array_equal(got, token_level_vs_blocks(sel_cols, sel_diags, bs))
+
+
+def test_floor_tops_up_nearest_first():
+    nb, bs = 12, 16
+    mask = np.zeros((nb, nb), bool)
+    mask[7, 0] = True
+    mask[9, [0, 2, 5, 9]] = True
+    out = O.apply_floor(mask, min_budget=3 * bs, bs=bs)
+    for qb in range(nb):
+        assert out[qb, : qb + 1].sum() >= min(qb + 1, 3)
+        assert not out[qb, qb + 1:].any()
+    assert np.nonzero(out[7])[0].tolist() == [0, 6, 7]
+    assert np.nonzero(out[9])[0].tolist() == [0, 2, 5, 9]      # already >= 3: unchanged
+    assert np.nonzero(out[1])[0].tolist() == [0, 1]
+    # min_budget 0 still keeps one block per row
+    out0 = O.apply_floor(np.zeros((nb, nb), bool), 0, bs)
+    assert np.array_equal(out0, np.eye(nb, dtype=bool))
+    # a budget that is not a multiple of the block rounds up
+    assert O.floor_blocks(1000, 128) == 8 and O.floor_blocks(1024, 128) == 8
+    assert O.floor_blocks(2048, 64) == 32 and O.floor_blocks(1, 64) == 1
+
+
+def test_qa_mask_maps_flattened_triangle():
+    nb = 6
+    sel = np.zeros(nb * (nb + 1) // 2, bool)
+    sel[0] = True           # (0, 0)
+    sel[4] = True           # (2, 1): 2*3/2 + 1
+    sel[20] = True          # (5, 5)
+    m = O.qa_block_mask(sel, nb)
+    assert sorted(zip(*np.nonzero(m))) == [(0, 0), (2, 1), (5, 5)]
+    A = np.arange(nb * nb, dtype=F32).reshape(nb, nb)
+    assert O.tri_values(A)[4] == A[2, 1]
