@@ -1,0 +1,182 @@
+/*
+ * fp_prefill.h -- C ABI of the MI355X (gfx950) FlexPrefill sparse pre-filling
+ * library, one attention layer's causal prefill on one GPU.
+ *
+ * Method (FlexPrefill, ICLR 2025 submission 1022): abstract on the OpenReview
+ * and codewithpapers pages, "Approach" paragraph and ablation table of the
+ * atlas.scime.ai summary page.  Per attention head:
+ *   1. query-aware sparse pattern determination -- the last query block's
+ *      exact attention over all keys, pooled per key block, is compared with
+ *      the softmax of block-pooled queries x block-pooled keys by the square
+ *      root of the Jensen-Shannon divergence; below tau the head is
+ *      query-aware, otherwise vertical-slash;
+ *   2. cumulative-attention index selection -- the smallest set of blocks
+ *      (query-aware: the flattened estimated block map) or lines (vertical:
+ *      key columns, slash: diagonals of the last block's attention) whose
+ *      normalised attention reaches gamma, plus a minimum budget;
+ *   3. causal attention restricted to the selected key blocks.
+ * Steps 1-2 are fp_prefill_plan, step 3 is fp_prefill_attend.  Selection runs
+ * in one fixed ("canonical") arithmetic, so plans are bit-reproducible.
+ *
+ * Conventions shared by every entry point
+ *   Layout: Q [B, Hq, N, d], K and V [B, Hkv, N, d], O [B, Hq, N, d]; dense,
+ *     row-major, device pointers.  Query head h reads key/value head
+ *     h / (Hq / Hkv) (grouped-query attention).  Q, K, V and O share one dtype.
+ *   Supported shapes: d = 128; block in {64, 128}; N a multiple of block,
+ *     1 <= N / block <= 4096; Hq a multiple of Hkv.  B, Hq or N equal to 0
+ *     is an empty problem: FP_OK, nothing is launched.
+ *   Streams: `stream` is a hipStream_t (NULL = the legacy default stream).
+ *     All device work is enqueued on it asynchronously; no call below blocks
+ *     the host unless its comment says "synchronizes".
+ *   Ownership: the caller owns q, k, v, o and keeps them alive until the
+ *     enqueued work completes.  The library owns every plan buffer.
+ *   Errors: every call returns an fp_status; nothing aborts or throws across
+ *     the ABI.  Arguments are validated on the host before any HIP call, so
+ *     validation errors need no GPU.  fp_last_error() describes the most
+ *     recent failure of the calling thread.  Faults of already-enqueued
+ *     kernels surface as FP_ERR_HIP from the next call that synchronizes.
+ */
+#ifndef FP_PREFILL_H
+#define FP_PREFILL_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum fp_status {
+    FP_OK = 0,
+    FP_ERR_INVALID_ARG = -1,   /* null pointer, gamma outside (0,1], tau < 0, ... */
+    FP_ERR_UNSUPPORTED = -2,   /* d != 128, block not 64/128, unknown dtype */
+    FP_ERR_SHAPE = -3,         /* N % block != 0, Hq % Hkv != 0, sizes too large */
+    FP_ERR_OOM = -4,           /* device allocation failed */
+    FP_ERR_HIP = -5            /* a HIP runtime call failed */
+} fp_status;
+
+typedef enum fp_dtype { FP_BF16 = 0, FP_FP32 = 1 } fp_dtype;
+
+/* Head pattern codes (fp_plan_copy_out `pattern`). */
+enum { FP_PATTERN_VERTICAL_SLASH = 0, FP_PATTERN_QUERY_AWARE = 1 };
+
+typedef struct fp_plan fp_plan;   /* opaque; device-resident block lists */
+
+typedef struct fp_plan_info {
+    int B, Hq, Hkv, N, d, block, nb;   /* nb = N / block */
+    fp_dtype dtype;
+    float gamma, tau;
+    int min_budget;
+    long long total_blocks;            /* selected (query-block, key-block) pairs, all heads */
+    long long dense_blocks;            /* B * Hq * nb (nb + 1) / 2 */
+    int query_aware_heads;             /* heads whose pattern is query-aware */
+} fp_plan_info;
+
+/*
+ * fp_prefill_plan -- steps 1 and 2 for every (batch, query head).
+ *   q, k: device pointers, layout above, dtype `dtype`.
+ *   gamma in (0, 1]: cumulative-attention threshold (pages: 0.95 default,
+ *     0.9 and 0.85 tested); gamma == 1 selects every causal block.
+ *   tau >= 0: divergence threshold; query-aware iff sqrt(JSD) < tau
+ *     (pages: 0.1 default, 0 disables query-aware, 0.3 tested).
+ *   min_budget >= 0 tokens: every query-block row keeps at least
+ *     min(row + 1, max(1, ceil(min_budget / block))) blocks, the missing ones
+ *     filled nearest-first from the diagonal (pages: 1024 default, 2048).
+ *   On FP_OK *out receives a new plan (released with fp_plan_destroy).  The
+ *   plan's buffers are allocated stream-ordered on `stream`; a transient
+ *   workspace of B*Hq*block*N*4 bytes is used and released within the call.
+ */
+fp_status fp_prefill_plan(const void* q, const void* k, fp_dtype dtype,
+                          int B, int Hq, int Hkv, int N, int d, int block,
+                          float gamma, float tau, int min_budget,
+                          void* stream, fp_plan** out);
+
+/*
+ * fp_prefill_attend -- step 3: O = causal softmax(Q K^T / sqrt(d)) V with
+ *   each query block attending only to the key blocks its plan selected.
+ *   q must be the tensor the plan was built from (the plan stores lists,
+ *   not values); k and v of the plan's shape.  o is written in full.
+ *   Uses a stream-ordered workspace of B*Hkv*N*d elements (V transposed).
+ */
+fp_status fp_prefill_attend(const fp_plan* plan, const void* q, const void* k,
+                            const void* v, void* o, void* stream);
+
+/*
+ * fp_dense_attend -- full causal attention with the same tile kernel (every
+ *   key block 0..row of every row); the baseline the sparse path is measured
+ *   against (the pages compare with FlashAttention).  Same layout and
+ *   support rules as above.
+ */
+fp_status fp_dense_attend(const void* q, const void* k, const void* v, void* o,
+                          fp_dtype dtype, int B, int Hq, int Hkv, int N, int d,
+                          int block, void* stream);
+
+/* Plan summary.  Synchronizes the plan's stream. */
+fp_status fp_plan_info_get(const fp_plan* plan, fp_plan_info* out);
+
+/*
+ * fp_plan_copy_out -- host copies of the plan (synchronizes `stream`).
+ *   pattern [B*Hq]          FP_PATTERN_* per head        (may be NULL)
+ *   djs     [B*Hq]          sqrt(JSD) per head            (may be NULL)
+ *   row_ptr [B*Hq*nb + 1]   CSR row offsets, rows ordered (b, h, row)
+ *   col_idx [total_blocks]  key-block indices, ascending within a row
+ *   row_ptr and col_idx may both be NULL; if one is given both must be.
+ */
+fp_status fp_plan_copy_out(const fp_plan* plan, unsigned char* pattern, double* djs,
+                           int* row_ptr, int* col_idx, void* stream);
+
+/*
+ * fp_plan_copy_debug -- host copy of an intermediate of steps 1-2
+ *   (synchronizes the plan's stream).  `bytes` must equal the item's size:
+ *   FP_DBG_QBAR   float [B*Hq][nb][d]      block means of Q
+ *   FP_DBG_KBAR   float [B*Hkv][nb][d]     block means of K
+ *   FP_DBG_ROWMAX float [B*Hq][block]      last-block row maxima (scaled scores)
+ *   FP_DBG_ROWSUM float [B*Hq][block]      last-block row sums of exp2
+ *   FP_DBG_COLSUM float [B*Hq][N]          vertical line scores
+ *   FP_DBG_DIAGSUM float [B*Hq][N]         slash line scores (offset i - j)
+ *   FP_DBG_ATRUE  float [B*Hq][nb]         block-pooled true distribution
+ *   FP_DBG_AHAT   float [B*Hq][nb(nb+1)/2] estimated map, causal triangle row-major
+ *   FP_DBG_COUNTS int   [B*Hq][nb]         selected blocks per row
+ */
+enum {
+    FP_DBG_QBAR = 0, FP_DBG_KBAR = 1, FP_DBG_ROWMAX = 2, FP_DBG_ROWSUM = 3,
+    FP_DBG_COLSUM = 4, FP_DBG_DIAGSUM = 5, FP_DBG_ATRUE = 6, FP_DBG_AHAT = 7,
+    FP_DBG_COUNTS = 8
+};
+fp_status fp_plan_copy_debug(const fp_plan* plan, int which, void* host_dst, size_t bytes);
+
+/* Releases the plan's buffers, stream-ordered on the stream the plan was
+ * created on; work using the plan on other streams must be complete. */
+void fp_plan_destroy(fp_plan* plan);
+
+const char* fp_status_str(fp_status s);
+const char* fp_last_error(void);
+
+/*
+ * Measurement hooks.  While enabled, fp_prefill_attend and fp_dense_attend
+ * record HIP events around their attention kernel on the call's stream;
+ * fp_profile_read synchronizes those events and returns the summed kernel
+ * time in ms and the number of launches since the last reset.
+ */
+fp_status fp_profile_enable(int on);
+fp_status fp_profile_read(double* sparse_ms, long long* sparse_launches,
+                          double* dense_ms, long long* dense_launches, int reset);
+
+/*
+ * Canonical-arithmetic probes (host only, no GPU): the constants the
+ * selection kernels use for head dim d -- exp2 Taylor coefficients e2[8]
+ * (fp32 nearest to (ln 2)^k / k!), artanh series coefficients lnc[11]
+ * (1 / (2k + 1)), ln 2, sqrt(1/2) and the score scale C = log2(e)/sqrt(d).
+ */
+fp_status fp_canonical_constants(int d, float* e2, double* lnc, double* ln2,
+                                 double* sqrt_half, float* score_scale);
+
+/* Device probes of the canonical exp2, ln and of the binary64 square root the
+ * divergence uses, on n elements (device pointers, enqueued on `stream`). */
+fp_status fp_probe_exp2(const float* x, float* y, long long n, void* stream);
+fp_status fp_probe_ln(const double* x, double* y, long long n, void* stream);
+fp_status fp_probe_sqrt(const double* x, double* y, long long n, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FP_PREFILL_H */

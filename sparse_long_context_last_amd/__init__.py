@@ -1,0 +1,206 @@
+"""FlexPrefill sparse pre-filling attention for one layer on an MI355X (gfx950).
+
+Thin Python binding over the C ABI of ``libfp_prefill.so`` (include/fp_prefill.h):
+torch tensors only provide device memory and the current HIP stream; every
+step of the method runs in the library's HIP kernels.
+
+    plan = plan(q, k, block=128, gamma=0.95, tau=0.1, min_budget=1024)
+    o = attend(plan, q, k, v)          # block-sparse causal attention
+    o_dense = dense_attend(q, k, v, block=128)
+"""
+from __future__ import annotations
+
+import ctypes as C
+from typing import Optional
+
+import numpy as np
+
+from . import _lib
+from ._lib import FpError, PlanInfo  # noqa: F401
+
+__all__ = ["Plan", "plan", "attend", "dense_attend", "profile_enable", "profile_read",
+           "canonical_constants", "FpError"]
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return _lib.FP_BF16
+    if t.dtype == torch.float32:
+        return _lib.FP_FP32
+    raise TypeError(f"unsupported dtype {t.dtype} (bfloat16 or float32)")
+
+
+def _check_tensor(t, name: str) -> None:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.dim() != 4:
+        raise ValueError(f"{name} must be [B, H, N, d]")
+
+
+def _stream_ptr(stream=None) -> int:
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+class Plan:
+    """Device-resident FlexPrefill plan (pattern per head, block lists)."""
+
+    def __init__(self, handle: C.c_void_p, shape, dtype_code: int, stream):
+        self._h = handle
+        self.B, self.Hq, self.Hkv, self.N, self.d, self.block = shape
+        self.nb = self.N // self.block if self.block else 0
+        self.dtype_code = dtype_code
+        self._stream = stream
+
+    @property
+    def handle(self):
+        if self._h is None:
+            raise RuntimeError("plan has been destroyed")
+        return self._h
+
+    def info(self) -> PlanInfo:
+        out = PlanInfo()
+        _lib.check(_lib.load().fp_plan_info_get(self.handle, C.byref(out)), "fp_plan_info_get")
+        return out
+
+    def copy_out(self):
+        """(pattern [B*Hq] uint8, djs [B*Hq] float64, row_ptr, col_idx) on the host."""
+        inf = self.info()
+        BH = self.B * self.Hq
+        pattern = np.zeros(BH, np.uint8)
+        djs = np.zeros(BH, np.float64)
+        row_ptr = np.zeros(BH * self.nb + 1, np.int32)
+        col_idx = np.zeros(max(inf.total_blocks, 1), np.int32)
+        _lib.check(_lib.load().fp_plan_copy_out(
+            self.handle, pattern.ctypes.data, djs.ctypes.data, row_ptr.ctypes.data,
+            col_idx.ctypes.data, _stream_ptr(self._stream)), "fp_plan_copy_out")
+        return pattern, djs, row_ptr, col_idx[: inf.total_blocks]
+
+    def lists(self):
+        """Per (b*Hq + h) a list of per-row int32 arrays of key-block indices."""
+        pattern, djs, row_ptr, col_idx = self.copy_out()
+        out = []
+        for bh in range(self.B * self.Hq):
+            rows = []
+            for r in range(self.nb):
+                i = bh * self.nb + r
+                rows.append(col_idx[row_ptr[i]: row_ptr[i + 1]].copy())
+            out.append(rows)
+        return out
+
+    def debug(self, item: str) -> np.ndarray:
+        BH, nb, bs, N = self.B * self.Hq, self.nb, self.block, self.N
+        shapes = {"qbar": ((BH, nb, self.d), np.float32),
+                  "kbar": ((self.B * self.Hkv, nb, self.d), np.float32),
+                  "rowmax": ((BH, bs), np.float32), "rowsum": ((BH, bs), np.float32),
+                  "colsum": ((BH, N), np.float32), "diagsum": ((BH, N), np.float32),
+                  "atrue": ((BH, nb), np.float32),
+                  "ahat": ((BH, nb * (nb + 1) // 2), np.float32),
+                  "counts": ((BH, nb), np.int32)}
+        shape, dt = shapes[item]
+        arr = np.zeros(shape, dt)
+        _lib.check(_lib.load().fp_plan_copy_debug(self.handle, _lib.DEBUG_ITEMS[item],
+                                                  arr.ctypes.data, arr.nbytes), "fp_plan_copy_debug")
+        return arr
+
+    def destroy(self) -> None:
+        if self._h is not None:
+            _lib.load().fp_plan_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.destroy()
+        except Exception:
+            pass
+
+
+def plan(q, k, block: int = 128, gamma: float = 0.95, tau: float = 0.1,
+         min_budget: int = 1024, stream=None) -> Plan:
+    """Pattern determination and index selection (fp_prefill_plan)."""
+    _check_tensor(q, "q")
+    _check_tensor(k, "k")
+    if q.dtype != k.dtype:
+        raise TypeError("q and k must share a dtype")
+    B, Hq, N, d = q.shape
+    Hkv = k.shape[1]
+    if tuple(k.shape) != (B, Hkv, N, d):
+        raise ValueError("k must be [B, Hkv, N, d] with q's B, N and d")
+    dt = _dtype_code(q)
+    h = C.c_void_p()
+    _lib.check(_lib.load().fp_prefill_plan(q.data_ptr(), k.data_ptr(), dt, B, Hq, Hkv, N, d, block,
+                                           float(gamma), float(tau), int(min_budget),
+                                           _stream_ptr(stream), C.byref(h)), "fp_prefill_plan")
+    return Plan(h, (B, Hq, Hkv, N, d, block), dt, stream)
+
+
+def attend(p: Plan, q, k, v, out=None, stream=None):
+    """Block-sparse causal attention over the plan's selection (fp_prefill_attend)."""
+    torch = _torch()
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _check_tensor(t, n)
+    if tuple(q.shape) != (p.B, p.Hq, p.N, p.d) or tuple(k.shape) != (p.B, p.Hkv, p.N, p.d) \
+            or k.shape != v.shape:
+        raise ValueError("q / k / v shapes do not match the plan")
+    if _dtype_code(q) != p.dtype_code or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k, v must have the plan's dtype")
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _check_tensor(out, "out")
+        if out.shape != q.shape or out.dtype != q.dtype:
+            raise ValueError("out must match q")
+    _lib.check(_lib.load().fp_prefill_attend(p.handle, q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                             out.data_ptr(), _stream_ptr(stream)), "fp_prefill_attend")
+    return out
+
+
+def dense_attend(q, k, v, block: int = 128, out=None, stream=None):
+    """Full causal attention with the same tile kernel (fp_dense_attend)."""
+    torch = _torch()
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _check_tensor(t, n)
+    B, Hq, N, d = q.shape
+    Hkv = k.shape[1]
+    if tuple(k.shape) != (B, Hkv, N, d) or k.shape != v.shape:
+        raise ValueError("k and v must be [B, Hkv, N, d]")
+    dt = _dtype_code(q)
+    if out is None:
+        out = torch.empty_like(q)
+    _lib.check(_lib.load().fp_dense_attend(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                           dt, B, Hq, Hkv, N, d, block, _stream_ptr(stream)),
+               "fp_dense_attend")
+    return out
+
+
+def profile_enable(on: bool = True) -> None:
+    _lib.check(_lib.load().fp_profile_enable(1 if on else 0), "fp_profile_enable")
+
+
+def profile_read(reset: bool = True):
+    """(sparse_ms, sparse_launches, dense_ms, dense_launches) of the attention kernel."""
+    sm, dm = C.c_double(), C.c_double()
+    sn, dn = C.c_longlong(), C.c_longlong()
+    _lib.check(_lib.load().fp_profile_read(C.byref(sm), C.byref(sn), C.byref(dm), C.byref(dn),
+                                           1 if reset else 0), "fp_profile_read")
+    return sm.value, sn.value, dm.value, dn.value
+
+
+def canonical_constants(d: int = 128) -> dict:
+    e2 = np.zeros(8, np.float32)
+    lnc = np.zeros(11, np.float64)
+    ln2, sh = C.c_double(), C.c_double()
+    cs = C.c_float()
+    _lib.check(_lib.load().fp_canonical_constants(d, e2.ctypes.data, lnc.ctypes.data, C.byref(ln2),
+                                                  C.byref(sh), C.byref(cs)), "fp_canonical_constants")
+    return {"e2": e2, "lnc": lnc, "ln2": ln2.value, "sqrt_half": sh.value,
+            "C": np.float32(cs.value)}

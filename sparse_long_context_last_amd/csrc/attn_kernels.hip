@@ -1,0 +1,430 @@
+// FlexPrefill step 3 on gfx950: causal flash attention over the key blocks a
+// plan selected for each (head, query block) -- the sparse attention the
+// pages time against FlashAttention ("Experimental setup" and "Key results"
+// of the atlas.scime.ai summary page).  The dense causal variant (every key
+// block 0..row) shares the kernel and is the speedup baseline.
+//
+// Layout of the work: one workgroup per (head, query block) row, BS / 32
+// waves, each wave owns 32 query rows.  Scores are computed transposed,
+// S^T = K Q^T, with the 32x32 MFMA: every lane then holds one query's scores
+// for half of a 32-key tile, so the row softmax needs a single cross-lane
+// exchange, and the probabilities already sit in the B-operand layout of
+// O^T = V^T P^T.  V is transposed once per call ([d][N]) so that the V^T
+// A-operand reads are contiguous in LDS.  Key tiles of 64 keys are staged
+// through double-buffered LDS; grouped-query heads map to kv head
+// h / (Hq / Hkv).
+#include "fp_common.h"
+#include "fp_launch.h"
+
+namespace fp {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kKT = 64;   // keys per LDS stage
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Row of the work list handled by workgroup `item`.
+__device__ __forceinline__ int work_row(const AttnArgs& a, int item) {
+    if (a.order) return a.order[item];
+    const int BH = a.B * a.Hq;
+    const int qb = a.nb - 1 - item / BH;      // long (late) rows first
+    return (item % BH) * a.nb + qb;
+}
+
+// ---------------------------------------------------------------------------
+// bf16 inputs, bf16 MFMA 32x32x16, fp32 accumulation and softmax
+// ---------------------------------------------------------------------------
+template <int BS>
+__global__ __launch_bounds__(2 * BS) void k_attn_bf16(AttnArgs a) {
+    constexpr int D = kHeadDim, KT = kKT, NT = 2 * BS, SPB = BS / KT;
+    constexpr int KP = D + 8;     // K tile row pitch (elements): 272 B
+    constexpr int VP = KT + 8;    // V^T tile row pitch (elements): 144 B
+    constexpr int KCH = KT * D / 8 / NT;   // 16-byte chunks per thread (K)
+    constexpr int VCH = D * KT / 8 / NT;   // 16-byte chunks per thread (V^T)
+    __shared__ __attribute__((aligned(16))) bf16_t Ks[2][KT * KP];
+    __shared__ __attribute__((aligned(16))) bf16_t Vs[2][D * VP];
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int l32 = lane & 31, hh = lane >> 5;
+    const int row = work_row(a, blockIdx.x);
+    const int bh = row / a.nb, qb = row % a.nb;
+    const int b = bh / a.Hq, h = bh % a.Hq;
+    const size_t kvbh = (size_t)b * a.Hkv + h / (a.Hq / a.Hkv);
+    const bf16_t* K = (const bf16_t*)a.k + kvbh * a.N * D;
+    const bf16_t* VT = (const bf16_t*)a.vt + kvbh * (size_t)D * a.N;
+
+    int cnt;
+    const int* lst = nullptr;
+    if (a.lists) {
+        cnt = a.counts[row];
+        lst = a.lists + (size_t)bh * a.tri + (size_t)qb * (qb + 1) / 2;
+    } else {
+        cnt = qb + 1;
+    }
+    const int nsub = cnt * SPB;
+
+    // Q fragments (B operand of S^T = K Q^T): query l32 of this wave, d = 16c + 8hh + [0, 8)
+    const int qrel = 32 * w + l32;
+    bf16x8_t qf[8];
+    {
+        const bf16_t* qp = (const bf16_t*)a.q + ((size_t)bh * a.N + (size_t)qb * BS + qrel) * D + 8 * hh;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) qf[c] = *reinterpret_cast<const bf16x8_t*>(qp + 16 * c);
+    }
+
+    f32x16_t o[4];
+#pragma unroll
+    for (int T = 0; T < 4; ++T)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[T][r] = 0.0f;
+    float m_run = -INFINITY, l_run = 0.0f;
+    const float sl = a.scale_log2;
+
+    u32x4_t kreg[KCH], vreg[VCH];
+#define FP_FETCH_BF16(s_)                                                                            \
+    {                                                                                                \
+        const int kb_ = lst ? lst[(s_) / SPB] : (s_) / SPB;                                          \
+        const int key0_ = kb_ * BS + ((s_) % SPB) * KT;                                              \
+        _Pragma("unroll") for (int r = 0; r < KCH; ++r) {                                            \
+            const int e = tid + NT * r, key = e >> 4, d8 = e & 15;                                   \
+            kreg[r] = *reinterpret_cast<const u32x4_t*>(K + (size_t)(key0_ + key) * D + 8 * d8);       \
+        }                                                                                            \
+        _Pragma("unroll") for (int r = 0; r < VCH; ++r) {                                            \
+            const int e = tid + NT * r, dv = e >> 3, k8 = e & 7;                                     \
+            vreg[r] = *reinterpret_cast<const u32x4_t*>(VT + (size_t)dv * a.N + key0_ + 8 * k8);       \
+        }                                                                                            \
+    }
+#define FP_STASH_BF16(buf_)                                                                          \
+    {                                                                                                \
+        _Pragma("unroll") for (int r = 0; r < KCH; ++r) {                                            \
+            const int e = tid + NT * r, key = e >> 4, d8 = e & 15;                                   \
+            *reinterpret_cast<u32x4_t*>(&Ks[(buf_)][key * KP + 8 * d8]) = kreg[r];                     \
+        }                                                                                            \
+        _Pragma("unroll") for (int r = 0; r < VCH; ++r) {                                            \
+            const int e = tid + NT * r, dv = e >> 3, k8 = e & 7;                                     \
+            *reinterpret_cast<u32x4_t*>(&Vs[(buf_)][dv * VP + 8 * k8]) = vreg[r];                      \
+        }                                                                                            \
+    }
+
+    FP_FETCH_BF16(0);
+    FP_STASH_BF16(0);
+    __syncthreads();
+
+    for (int s = 0; s < nsub; ++s) {
+        const int buf = s & 1;
+        const int kb = lst ? lst[s / SPB] : s / SPB;
+        const int sub = s % SPB;
+        if (s + 1 < nsub) FP_FETCH_BF16(s + 1);
+
+        // S^T tile: keys (rows) x queries (cols)
+        f32x16_t st[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) st[t][r] = 0.0f;
+            const bf16_t* kr = &Ks[buf][(32 * t + l32) * KP + 8 * hh];
+#pragma unroll
+            for (int c = 0; c < 8; ++c) {
+                const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(kr + 16 * c);
+                st[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[c], st[t], 0, 0, 0);
+            }
+        }
+        // causal mask inside the diagonal block
+        if (kb == qb) {
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int krel = sub * KT + 32 * t + 8 * (r >> 2) + 4 * hh + (r & 3);
+                    if (krel > qrel) st[t][r] = -INFINITY;
+                }
+        }
+        // online softmax (lane = one query; lane ^ 32 holds its other keys)
+        float mx = -INFINITY;
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, st[t][r]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = fast_exp2((m_run - m_new) * sl);
+        const float mb = m_new * sl;
+        float ls = 0.0f;
+        bf16x8_t pf[4];
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const float p = fast_exp2(__builtin_fmaf(st[t][r], sl, -mb));
+                ls += p;
+                pf[2 * t + (r >> 3)][r & 7] = (__bf16)p;
+            }
+        l_run = l_run * alpha + ls;
+        m_run = m_new;
+#pragma unroll
+        for (int T = 0; T < 4; ++T)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) o[T][r] *= alpha;
+
+        // O^T += V^T P^T; key order of the B operand: kc*16 + 8*(e/4) + 4*hh + e%4
+#pragma unroll
+        for (int T = 0; T < 4; ++T) {
+            const bf16_t* vr = &Vs[buf][(32 * T + l32) * VP + 4 * hh];
+#pragma unroll
+            for (int kc = 0; kc < 4; ++kc) {
+                const bf16x4_t lo = *reinterpret_cast<const bf16x4_t*>(vr + 16 * kc);
+                const bf16x4_t hi = *reinterpret_cast<const bf16x4_t*>(vr + 16 * kc + 8);
+                const bf16x8_t vf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+                o[T] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[kc], o[T], 0, 0, 0);
+            }
+        }
+        if (s + 1 < nsub) FP_STASH_BF16(buf ^ 1);
+        __syncthreads();
+    }
+#undef FP_FETCH_BF16
+#undef FP_STASH_BF16
+
+    const float l_tot = l_run + __shfl_xor(l_run, 32);
+    const float inv = 1.0f / l_tot;
+    bf16_t* op = (bf16_t*)a.o + ((size_t)bh * a.N + (size_t)qb * BS + qrel) * D;
+#pragma unroll
+    for (int T = 0; T < 4; ++T)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int dv = 32 * T + 8 * i + 4 * hh;
+            ushort4 pk;
+            pk.x = f32_to_bf16(o[T][4 * i] * inv);
+            pk.y = f32_to_bf16(o[T][4 * i + 1] * inv);
+            pk.z = f32_to_bf16(o[T][4 * i + 2] * inv);
+            pk.w = f32_to_bf16(o[T][4 * i + 3] * inv);
+            *reinterpret_cast<ushort4*>(op + dv) = pk;
+        }
+}
+
+// ---------------------------------------------------------------------------
+// fp32 inputs: fp32 MFMA 32x32x2, same structure.  Contraction index e of a
+// lane pair (hh) maps to d = c + 64 hh (scores) and to key 32t + 8i + 4hh + j
+// (values), identically for both operands.
+// ---------------------------------------------------------------------------
+template <int BS>
+__global__ __launch_bounds__(2 * BS) void k_attn_f32(AttnArgs a) {
+    constexpr int D = kHeadDim, KT = kKT, NT = 2 * BS, SPB = BS / KT;
+    constexpr int KP = D + 4;     // floats: 528 B
+    constexpr int VP = KT + 4;    // floats: 272 B
+    constexpr int KCH = KT * D / 4 / NT;
+    constexpr int VCH = D * KT / 4 / NT;
+    extern __shared__ __attribute__((aligned(16))) float smem_f32[];
+    float* Ks0 = smem_f32;
+    float* Vs0 = smem_f32 + 2 * KT * KP;
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int l32 = lane & 31, hh = lane >> 5;
+    const int row = work_row(a, blockIdx.x);
+    const int bh = row / a.nb, qb = row % a.nb;
+    const int b = bh / a.Hq, h = bh % a.Hq;
+    const size_t kvbh = (size_t)b * a.Hkv + h / (a.Hq / a.Hkv);
+    const float* K = (const float*)a.k + kvbh * a.N * D;
+    const float* VT = (const float*)a.vt + kvbh * (size_t)D * a.N;
+
+    int cnt;
+    const int* lst = nullptr;
+    if (a.lists) {
+        cnt = a.counts[row];
+        lst = a.lists + (size_t)bh * a.tri + (size_t)qb * (qb + 1) / 2;
+    } else {
+        cnt = qb + 1;
+    }
+    const int nsub = cnt * SPB;
+    const int qrel = 32 * w + l32;
+    float qf[64];
+    {
+        const float* qp = (const float*)a.q + ((size_t)bh * a.N + (size_t)qb * BS + qrel) * D + 64 * hh;
+#pragma unroll
+        for (int c = 0; c < 64; c += 4) {
+            const float4 v = *reinterpret_cast<const float4*>(qp + c);
+            qf[c] = v.x; qf[c + 1] = v.y; qf[c + 2] = v.z; qf[c + 3] = v.w;
+        }
+    }
+    f32x16_t o[4];
+#pragma unroll
+    for (int T = 0; T < 4; ++T)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[T][r] = 0.0f;
+    float m_run = -INFINITY, l_run = 0.0f;
+    const float sl = a.scale_log2;
+
+    f32x4_t kreg[KCH], vreg[VCH];
+#define FP_FETCH_F32(s_)                                                                             \
+    {                                                                                                \
+        const int kb_ = lst ? lst[(s_) / SPB] : (s_) / SPB;                                          \
+        const int key0_ = kb_ * BS + ((s_) % SPB) * KT;                                              \
+        _Pragma("unroll") for (int r = 0; r < KCH; ++r) {                                            \
+            const int e = tid + NT * r, key = e >> 5, d4 = e & 31;                                   \
+            kreg[r] = *reinterpret_cast<const f32x4_t*>(K + (size_t)(key0_ + key) * D + 4 * d4);      \
+        }                                                                                            \
+        _Pragma("unroll") for (int r = 0; r < VCH; ++r) {                                            \
+            const int e = tid + NT * r, dv = e >> 4, k4 = e & 15;                                    \
+            vreg[r] = *reinterpret_cast<const f32x4_t*>(VT + (size_t)dv * a.N + key0_ + 4 * k4);      \
+        }                                                                                            \
+    }
+#define FP_STASH_F32(buf_)                                                                           \
+    {                                                                                                \
+        float* Ks_ = Ks0 + (buf_) * KT * KP;                                                         \
+        float* Vs_ = Vs0 + (buf_) * D * VP;                                                          \
+        _Pragma("unroll") for (int r = 0; r < KCH; ++r) {                                            \
+            const int e = tid + NT * r, key = e >> 5, d4 = e & 31;                                   \
+            *reinterpret_cast<f32x4_t*>(&Ks_[key * KP + 4 * d4]) = kreg[r];                           \
+        }                                                                                            \
+        _Pragma("unroll") for (int r = 0; r < VCH; ++r) {                                            \
+            const int e = tid + NT * r, dv = e >> 4, k4 = e & 15;                                    \
+            *reinterpret_cast<f32x4_t*>(&Vs_[dv * VP + 4 * k4]) = vreg[r];                            \
+        }                                                                                            \
+    }
+
+    FP_FETCH_F32(0);
+    FP_STASH_F32(0);
+    __syncthreads();
+    for (int s = 0; s < nsub; ++s) {
+        const int buf = s & 1;
+        const float* Ks = Ks0 + buf * KT * KP;
+        const float* Vs = Vs0 + buf * D * VP;
+        const int kb = lst ? lst[s / SPB] : s / SPB;
+        const int sub = s % SPB;
+        if (s + 1 < nsub) FP_FETCH_F32(s + 1);
+        f32x16_t st[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) st[t][r] = 0.0f;
+            const float* kr = &Ks[(32 * t + l32) * KP + 64 * hh];
+#pragma unroll
+            for (int c = 0; c < 64; c += 4) {
+                const float4 kv = *reinterpret_cast<const float4*>(kr + c);
+                st[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(kv.x, qf[c], st[t], 0, 0, 0);
+                st[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(kv.y, qf[c + 1], st[t], 0, 0, 0);
+                st[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(kv.z, qf[c + 2], st[t], 0, 0, 0);
+                st[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(kv.w, qf[c + 3], st[t], 0, 0, 0);
+            }
+        }
+        if (kb == qb) {
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int krel = sub * KT + 32 * t + 8 * (r >> 2) + 4 * hh + (r & 3);
+                    if (krel > qrel) st[t][r] = -INFINITY;
+                }
+        }
+        float mx = -INFINITY;
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, st[t][r]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = fast_exp2((m_run - m_new) * sl);
+        const float mb = m_new * sl;
+        float ls = 0.0f;
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                st[t][r] = fast_exp2(__builtin_fmaf(st[t][r], sl, -mb));
+                ls += st[t][r];
+            }
+        l_run = l_run * alpha + ls;
+        m_run = m_new;
+#pragma unroll
+        for (int T = 0; T < 4; ++T)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) o[T][r] *= alpha;
+#pragma unroll
+        for (int T = 0; T < 4; ++T) {
+            const float* vr = &Vs[(32 * T + l32) * VP + 4 * hh];
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float4 vv = *reinterpret_cast<const float4*>(vr + 32 * t + 8 * i);
+                    o[T] = __builtin_amdgcn_mfma_f32_32x32x2f32(vv.x, st[t][4 * i], o[T], 0, 0, 0);
+                    o[T] = __builtin_amdgcn_mfma_f32_32x32x2f32(vv.y, st[t][4 * i + 1], o[T], 0, 0, 0);
+                    o[T] = __builtin_amdgcn_mfma_f32_32x32x2f32(vv.z, st[t][4 * i + 2], o[T], 0, 0, 0);
+                    o[T] = __builtin_amdgcn_mfma_f32_32x32x2f32(vv.w, st[t][4 * i + 3], o[T], 0, 0, 0);
+                }
+        }
+        if (s + 1 < nsub) FP_STASH_F32(buf ^ 1);
+        __syncthreads();
+    }
+#undef FP_FETCH_F32
+#undef FP_STASH_F32
+    const float l_tot = l_run + __shfl_xor(l_run, 32);
+    const float inv = 1.0f / l_tot;
+    float* op = (float*)a.o + ((size_t)bh * a.N + (size_t)qb * BS + qrel) * D;
+#pragma unroll
+    for (int T = 0; T < 4; ++T)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int dv = 32 * T + 8 * i + 4 * hh;
+            float4 v;
+            v.x = o[T][4 * i] * inv;
+            v.y = o[T][4 * i + 1] * inv;
+            v.z = o[T][4 * i + 2] * inv;
+            v.w = o[T][4 * i + 3] * inv;
+            *reinterpret_cast<float4*>(op + dv) = v;
+        }
+}
+
+// ---------------------------------------------------------------------------
+// V [heads][N][d] -> V^T [heads][d][N], 64-key tiles through LDS.
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(256) void k_transpose_v(const T* __restrict__ v, T* __restrict__ vt, int N) {
+    constexpr int D = kHeadDim, TK = 64;
+    __shared__ T tile[TK][D + 2];
+    const int head = blockIdx.y, n0 = blockIdx.x * TK, tid = threadIdx.x;
+    const T* src = v + ((size_t)head * N + n0) * D;
+    for (int e = tid; e < TK * D; e += 256) {
+        const int n = e / D, dd = e % D;
+        tile[n][dd] = src[(size_t)n * D + dd];
+    }
+    __syncthreads();
+    T* dst = vt + (size_t)head * D * N + n0;
+    for (int e = tid; e < TK * D; e += 256) {
+        const int dd = e / TK, n = e % TK;
+        dst[(size_t)dd * N + n] = tile[n][dd];
+    }
+}
+
+hipError_t launch_transpose_v(const void* v, void* vt, int dtype_bf16, int heads, int N, hipStream_t st) {
+    const dim3 g(N / 64, heads);
+    if (dtype_bf16)
+        hipLaunchKernelGGL(k_transpose_v<bf16_t>, g, dim3(256), 0, st, (const bf16_t*)v, (bf16_t*)vt, N);
+    else
+        hipLaunchKernelGGL(k_transpose_v<float>, g, dim3(256), 0, st, (const float*)v, (float*)vt, N);
+    return hipGetLastError();
+}
+
+hipError_t launch_attention(const AttnArgs& a, hipStream_t st) {
+    const unsigned items = (unsigned)(a.B * a.Hq * a.nb);
+    if (a.dtype_bf16) {
+        if (a.BS == 128) hipLaunchKernelGGL(k_attn_bf16<128>, dim3(items), dim3(256), 0, st, a);
+        else hipLaunchKernelGGL(k_attn_bf16<64>, dim3(items), dim3(128), 0, st, a);
+    } else {
+        const size_t lds = (size_t)2 * (kKT * (kHeadDim + 4) + kHeadDim * (kKT + 4)) * sizeof(float);
+        if (a.BS == 128) {
+            (void)hipFuncSetAttribute((const void*)k_attn_f32<128>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+            hipLaunchKernelGGL(k_attn_f32<128>, dim3(items), dim3(256), lds, st, a);
+        } else {
+            (void)hipFuncSetAttribute((const void*)k_attn_f32<64>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+            hipLaunchKernelGGL(k_attn_f32<64>, dim3(items), dim3(128), lds, st, a);
+        }
+    }
+    return hipGetLastError();
+}
+
+}  // namespace fp

@@ -1,0 +1,801 @@
+// FlexPrefill steps 1 and 2 on gfx950: query-aware sparse pattern
+// determination and cumulative-attention index selection (abstract items 1-2
+// on the OpenReview / codewithpapers pages; "Approach" paragraph and ablation
+// table of the atlas.scime.ai summary page).
+//
+// Every kernel here computes in the library's canonical arithmetic: each
+// float32 / float64 rounding point and every reduction order is fixed (no
+// contraction into fused multiply-adds unless a product is exact, sequential
+// sums in ascending index order, exp2 / ln from fixed series), and the gamma
+// test is done on integers.  The resulting pattern choices and block lists
+// are therefore bit-reproducible across runs and launch geometries.
+#pragma clang fp contract(off)
+
+#include "fp_common.h"
+#include "fp_launch.h"
+
+namespace fp {
+
+// ---------------------------------------------------------------------------
+// canonical elementary functions
+// ---------------------------------------------------------------------------
+
+// 2^x for x <= 0: +0 below -100; else n = rint(x), f = x - n, Horner in f of
+// the degree-7 Taylor series of 2^f (every product and sum rounded), times 2^n.
+__device__ __forceinline__ float exp2_c(float x, const Canon& K) {
+    if (!(x >= -100.0f)) return 0.0f;
+    float n = rintf(x);
+    float f = x - n;
+    float p = K.e2[7];
+#pragma unroll
+    for (int i = 6; i >= 0; --i) {
+        p = p * f;
+        p = p + K.e2[i];
+    }
+    return ldexpf(p, (int)n);
+}
+
+// ln x for x > 0 in binary64: x = m 2^e with m in [sqrt(1/2), sqrt(2)),
+// ln m = 2 artanh z, z = (m - 1)/(m + 1), series truncated after z^21.
+__device__ __forceinline__ double ln_c(double x, const Canon& K) {
+    int e;
+    double m = frexp(x, &e);
+    if (m < K.sqrt_half) {
+        m = m * 2.0;
+        e = e - 1;
+    }
+    double z = (m - 1.0) / (m + 1.0);
+    double w = z * z;
+    double s = K.lnc[10];
+#pragma unroll
+    for (int i = 9; i >= 0; --i) {
+        s = s * w;
+        s = s + K.lnc[i];
+    }
+    double a = (double)e * K.ln2;
+    double b = (2.0 * z) * s;
+    return a + b;
+}
+
+// Fixed-point mass of a value: rint(x * 2^32) (x >= 0, x <= 2^31).
+__device__ __forceinline__ unsigned long long fixed_u(float x) {
+    return (unsigned long long)rintf(x * 4294967296.0f);
+}
+
+// Ordering key: value descending, then index ascending <=> key ascending.
+__device__ __forceinline__ unsigned long long order_key(float x, long long idx, int ibits) {
+    unsigned int inv = 0x7FFFFFFFu - __float_as_uint(x);
+    return ((unsigned long long)inv << ibits) | (unsigned long long)idx;
+}
+
+// Load n consecutive elements (16-byte aligned) widened to fp32; zeros if !ok.
+template <typename T, int n> __device__ __forceinline__ void load_row_f32(const T* p, bool ok, float* out);
+template <> __device__ __forceinline__ void load_row_f32<bf16_t, kScoreDSConst>(const bf16_t* p, bool ok, float* out) {
+#pragma unroll
+    for (int v = 0; v < kScoreDSConst / 8; ++v) {
+        uint4 w = ok ? reinterpret_cast<const uint4*>(p)[v] : make_uint4(0, 0, 0, 0);
+        const unsigned int ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            out[v * 8 + 2 * e] = __uint_as_float(ws[e] << 16);
+            out[v * 8 + 2 * e + 1] = __uint_as_float(ws[e] & 0xFFFF0000u);
+        }
+    }
+}
+template <> __device__ __forceinline__ void load_row_f32<float, kScoreDSConst>(const float* p, bool ok, float* out) {
+#pragma unroll
+    for (int v = 0; v < kScoreDSConst / 4; ++v) {
+        float4 w = ok ? reinterpret_cast<const float4*>(p)[v] : make_float4(0.f, 0.f, 0.f, 0.f);
+        out[v * 4] = w.x; out[v * 4 + 1] = w.y; out[v * 4 + 2] = w.z; out[v * 4 + 3] = w.w;
+    }
+}
+
+template <typename T> struct MulAdd;
+// bf16 inputs: the product of two bf16 values is exact in fp32, so one fused
+// multiply-add rounds exactly like the product-then-sum of the definition.
+template <> struct MulAdd<bf16_t> {
+    static __device__ __forceinline__ float step(float acc, float a, float b) {
+        return __builtin_fmaf(a, b, acc);
+    }
+};
+template <> struct MulAdd<float> {
+    static __device__ __forceinline__ float step(float acc, float a, float b) {
+        float p = a * b;
+        return acc + p;
+    }
+};
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+    return v;
+}
+
+// ---------------------------------------------------------------------------
+// K1: block means ("block-pooled" queries and keys)
+// grid (nb, heads), block d threads; out[head][kb][t] = (sum_r x[kb*bs + r][t]) / bs
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(128) void k_pool(const T* __restrict__ x, float* __restrict__ out,
+                                              int N, int bs, float inv_bs) {
+    const int kb = blockIdx.x, head = blockIdx.y, t = threadIdx.x;
+    const int nb = N / bs;
+    const T* src = x + ((size_t)head * N + (size_t)kb * bs) * kHeadDim + t;
+    float acc = 0.0f;
+    for (int r = 0; r < bs; ++r) acc = acc + load_f32(src + (size_t)r * kHeadDim);
+    out[((size_t)head * nb + kb) * kHeadDim + t] = acc * inv_bs;
+}
+
+// ---------------------------------------------------------------------------
+// K2: exact scores of the last query block against every key.
+// s2[bh][i][j] = fp32(sum_t q[N-BS+i][t] * k[j][t]) * C, t ascending; plus the
+// per-(row, 256-key chunk) maxima over causal keys (j <= N-BS+i).
+// Register-blocked VALU product: 256 threads, tile BS queries x 256 keys, each
+// thread owns BS/16 queries x 16 keys; d staged through LDS in slices of 32.
+// ---------------------------------------------------------------------------
+constexpr int kScoreTK = 256;
+constexpr int kScoreDS = kScoreDSConst;
+
+template <typename T, int BS>
+__global__ __launch_bounds__(256) void k_scores(const T* __restrict__ q, const T* __restrict__ k,
+                                                float* __restrict__ s2, float* __restrict__ pmax,
+                                                int N, int Hq, int Hkv, int group, float C) {
+    constexpr int D = kHeadDim, TK = kScoreTK, DS = kScoreDS, MR = BS / 16;
+    __shared__ __attribute__((aligned(16))) float Qs[DS][BS + 4];
+    __shared__ __attribute__((aligned(16))) float Ks[DS][TK + 4];
+    const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+    const int chunk = blockIdx.x, bh = blockIdx.y;
+    const int b = bh / Hq, h = bh % Hq;
+    const size_t kvbh = (size_t)b * Hkv + h / group;
+    const T* qlast = q + ((size_t)bh * N + (N - BS)) * D;
+    const int j0 = chunk * TK;
+    const T* kbase = k + (kvbh * N + j0) * D;
+    const bool key_ok = (j0 + tid) < N;
+
+    float acc[MR][16];
+#pragma unroll
+    for (int m = 0; m < MR; ++m)
+#pragma unroll
+        for (int n = 0; n < 16; ++n) acc[m][n] = 0.0f;
+
+    for (int t0 = 0; t0 < D; t0 += DS) {
+        // Q slice, transposed: Qs[tt][i]
+        for (int e = tid; e < BS * DS; e += 256) {
+            int i = e / DS, tt = e % DS;
+            Qs[tt][i] = load_f32(qlast + (size_t)i * D + t0 + tt);
+        }
+        // K slice, transposed: thread tid owns key j0 + tid
+        {
+            float kv[DS];
+            load_row_f32<T, DS>(kbase + (size_t)tid * D + t0, key_ok, kv);
+#pragma unroll
+            for (int tt = 0; tt < DS; ++tt) Ks[tt][tid] = kv[tt];
+        }
+        __syncthreads();
+#pragma unroll 4
+        for (int tt = 0; tt < DS; ++tt) {
+            float qv[MR], kv[16];
+#pragma unroll
+            for (int m4 = 0; m4 < MR; m4 += 4) {
+                float4 v = *reinterpret_cast<const float4*>(&Qs[tt][ty * MR + m4]);
+                qv[m4] = v.x; qv[m4 + 1] = v.y; qv[m4 + 2] = v.z; qv[m4 + 3] = v.w;
+            }
+#pragma unroll
+            for (int n = 0; n < 4; ++n) {
+                float4 v = *reinterpret_cast<const float4*>(&Ks[tt][n * 64 + tx * 4]);
+                kv[n * 4] = v.x; kv[n * 4 + 1] = v.y; kv[n * 4 + 2] = v.z; kv[n * 4 + 3] = v.w;
+            }
+#pragma unroll
+            for (int m = 0; m < MR; ++m)
+#pragma unroll
+                for (int n = 0; n < 16; ++n) acc[m][n] = MulAdd<T>::step(acc[m][n], qv[m], kv[n]);
+        }
+        __syncthreads();
+    }
+
+    const int nchunks = (N + TK - 1) / TK;
+#pragma unroll
+    for (int m = 0; m < MR; ++m) {
+        const int i = ty * MR + m;
+        const int pos = N - BS + i;
+        float mx = -INFINITY;
+        float* row = s2 + ((size_t)bh * BS + i) * N;
+#pragma unroll
+        for (int n = 0; n < 4; ++n) {
+            const int j = j0 + n * 64 + tx * 4;
+            float4 v;
+            v.x = acc[m][n * 4] * C;
+            v.y = acc[m][n * 4 + 1] * C;
+            v.z = acc[m][n * 4 + 2] * C;
+            v.w = acc[m][n * 4 + 3] * C;
+            if (j < N) {
+                *reinterpret_cast<float4*>(row + j) = v;
+                if (j <= pos) mx = fmaxf(mx, v.x);
+                if (j + 1 <= pos) mx = fmaxf(mx, v.y);
+                if (j + 2 <= pos) mx = fmaxf(mx, v.z);
+                if (j + 3 <= pos) mx = fmaxf(mx, v.w);
+            }
+        }
+#pragma unroll
+        for (int o = 8; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+        if (tx == 0) pmax[((size_t)bh * nchunks + chunk) * BS + i] = mx;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// K3a: per last-block row: M = max, e = exp2_c(s - M) (0 for j > pos), written
+// over s2; zpart[kb] = sum over the block's keys ascending; Z = sum of zpart
+// over kb ascending; rz = 1 / Z.  One workgroup per (bh, row).
+// ---------------------------------------------------------------------------
+constexpr int kSeg = 2048;
+
+template <int BS>
+__global__ __launch_bounds__(256) void k_rowexp(float* __restrict__ s2, const float* __restrict__ pmax,
+                                                float* __restrict__ rowmax, float* __restrict__ rowsum,
+                                                float* __restrict__ rz, int N, Canon K) {
+    constexpr int NSB = kSeg / BS;      // key blocks per segment
+    __shared__ float es[NSB][BS + 1];
+    __shared__ float zp[kMaxBlocks];
+    __shared__ float red[256];
+    const int tid = threadIdx.x;
+    const int row = blockIdx.x, bh = blockIdx.y;
+    const int nchunks = (N + kScoreTK - 1) / kScoreTK;
+    const int pos = N - BS + row;
+    float mx = -INFINITY;
+    for (int c = tid; c < nchunks; c += 256) mx = fmaxf(mx, pmax[((size_t)bh * nchunks + c) * BS + row]);
+    red[tid] = mx;
+    __syncthreads();
+    for (int s = 128; s > 0; s >>= 1) {
+        if (tid < s) red[tid] = fmaxf(red[tid], red[tid + s]);
+        __syncthreads();
+    }
+    const float M = red[0];
+    float* srow = s2 + ((size_t)bh * BS + row) * N;
+    for (int seg0 = 0; seg0 < N; seg0 += kSeg) {
+#pragma unroll
+        for (int u = 0; u < kSeg / 256; ++u) {
+            const int jl = u * 256 + tid;      // coalesced
+            const int j = seg0 + jl;
+            if (j < N) {
+                float e = 0.0f;
+                if (j <= pos) e = exp2_c(srow[j] - M, K);
+                srow[j] = e;
+                es[jl / BS][jl % BS] = e;
+            }
+        }
+        __syncthreads();
+        if (tid < NSB && seg0 + tid * BS < N) {
+            float z = 0.0f;
+            for (int jj = 0; jj < BS; ++jj) z = z + es[tid][jj];
+            zp[seg0 / BS + tid] = z;
+        }
+        __syncthreads();
+    }
+    if (tid == 0) {
+        const int nb = N / BS;
+        float Z = 0.0f;
+        for (int kb = 0; kb < nb; ++kb) Z = Z + zp[kb];
+        rowmax[(size_t)bh * BS + row] = M;
+        rowsum[(size_t)bh * BS + row] = Z;
+        rz[(size_t)bh * BS + row] = 1.0f / Z;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// K3b: line scores of the last block's probabilities p = e * rz:
+// colsum[j] = sum_i p[i][j]; diagsum[o] = sum_{i: pos_i >= o} p[i][pos_i - o];
+// i ascending.  grid (ceil(N/256), BH).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_linesums(const float* __restrict__ e, const float* __restrict__ rz,
+                                                  float* __restrict__ colsum, float* __restrict__ diagsum,
+                                                  int N, int BS) {
+    __shared__ float srz[kMaxBlock];
+    const int tid = threadIdx.x, bh = blockIdx.y;
+    if (tid < BS) srz[tid] = rz[(size_t)bh * BS + tid];
+    __syncthreads();
+    const int j = blockIdx.x * 256 + tid;
+    if (j >= N) return;
+    const float* E = e + (size_t)bh * BS * N;
+    float c = 0.0f;
+    for (int i = 0; i < BS; ++i) {
+        float p = E[(size_t)i * N + j] * srz[i];
+        c = c + p;
+    }
+    float g = 0.0f;
+    for (int i = 0; i < BS; ++i) {
+        const int pos = N - BS + i;
+        if (pos >= j) {
+            float p = E[(size_t)i * N + (pos - j)] * srz[i];
+            g = g + p;
+        }
+    }
+    colsum[(size_t)bh * N + j] = c;
+    diagsum[(size_t)bh * N + j] = g;
+}
+
+// ---------------------------------------------------------------------------
+// K3c: block-pooled true distribution a_true[kb] = t[kb] / T, t[kb] = sum of
+// colsum over the block (ascending), T = sum of t over kb (ascending).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_atrue(const float* __restrict__ colsum, float* __restrict__ atrue,
+                                               int N, int BS) {
+    __shared__ float ts[kMaxBlocks];
+    __shared__ float Tsh;
+    const int tid = threadIdx.x, bh = blockIdx.x, nb = N / BS;
+    for (int kb = tid; kb < nb; kb += 256) {
+        const float* c = colsum + (size_t)bh * N + (size_t)kb * BS;
+        float t = 0.0f;
+        for (int jj = 0; jj < BS; ++jj) t = t + c[jj];
+        ts[kb] = t;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        float T = 0.0f;
+        for (int kb = 0; kb < nb; ++kb) T = T + ts[kb];
+        Tsh = T;
+    }
+    __syncthreads();
+    for (int kb = tid; kb < nb; kb += 256) atrue[(size_t)bh * nb + kb] = ts[kb] / Tsh;
+}
+
+// ---------------------------------------------------------------------------
+// K4: estimated block map  A[qb][kb] = softmax_{kb <= qb}(fp32(qbar_qb . kbar_kb) * C)
+// (products and sums rounded separately, t ascending; row max subtracted,
+// exp2_c, sum over kb ascending, rounded division).  Stored as the causal
+// triangle, row-major.  grid (nb, BH).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_estimate(const float* __restrict__ qbar, const float* __restrict__ kbar,
+                                                  float* __restrict__ ahat, int nb, int Hq, int Hkv,
+                                                  int group, Canon K) {
+    __shared__ float qs[kHeadDim];
+    __shared__ float sc[kMaxBlocks];
+    __shared__ float red[256];
+    __shared__ float Zsh;
+    const int tid = threadIdx.x, qb = blockIdx.x, bh = blockIdx.y;
+    const int b = bh / Hq, h = bh % Hq;
+    const size_t kvbh = (size_t)b * Hkv + h / group;
+    if (tid < kHeadDim) qs[tid] = qbar[((size_t)bh * nb + qb) * kHeadDim + tid];
+    __syncthreads();
+    float mx = -INFINITY;
+    for (int kb = tid; kb <= qb; kb += 256) {
+        const float4* kr = reinterpret_cast<const float4*>(kbar + (kvbh * nb + kb) * kHeadDim);
+        float acc = 0.0f;
+#pragma unroll 8
+        for (int c = 0; c < kHeadDim / 4; ++c) {
+            float4 v = kr[c];
+            float p;
+            p = qs[4 * c] * v.x;     acc = acc + p;
+            p = qs[4 * c + 1] * v.y; acc = acc + p;
+            p = qs[4 * c + 2] * v.z; acc = acc + p;
+            p = qs[4 * c + 3] * v.w; acc = acc + p;
+        }
+        const float s = acc * K.C;
+        sc[kb] = s;
+        mx = fmaxf(mx, s);
+    }
+    red[tid] = mx;
+    __syncthreads();
+    for (int s = 128; s > 0; s >>= 1) {
+        if (tid < s) red[tid] = fmaxf(red[tid], red[tid + s]);
+        __syncthreads();
+    }
+    const float M = red[0];
+    for (int kb = tid; kb <= qb; kb += 256) sc[kb] = exp2_c(sc[kb] - M, K);
+    __syncthreads();
+    if (tid == 0) {
+        float Z = 0.0f;
+        for (int kb = 0; kb <= qb; ++kb) Z = Z + sc[kb];
+        Zsh = Z;
+    }
+    __syncthreads();
+    const long long tri = (long long)nb * (nb + 1) / 2;
+    float* out = ahat + (size_t)bh * tri + (size_t)qb * (qb + 1) / 2;
+    for (int kb = tid; kb <= qb; kb += 256) out[kb] = sc[kb] / Zsh;
+}
+
+// ---------------------------------------------------------------------------
+// K5: pattern determination.  P = last row of the estimate, Q = a_true;
+// JSD = 0.5 * sum_kb (P ln(P/m) + Q ln(Q/m)), m = (P + Q)/2, terms with a zero
+// probability dropped, sum ascending in binary64; D = sqrt(JSD);
+// query-aware iff D < tau.  One workgroup per head.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_jsd(const float* __restrict__ ahat, const float* __restrict__ atrue,
+                                             double* __restrict__ djs, unsigned char* __restrict__ pattern,
+                                             int nb, double tau, Canon K) {
+    __shared__ double terms[kMaxBlocks];
+    const int tid = threadIdx.x, bh = blockIdx.x;
+    const long long tri = (long long)nb * (nb + 1) / 2;
+    const float* last = ahat + (size_t)bh * tri + (size_t)(nb - 1) * nb / 2;
+    for (int kb = tid; kb < nb; kb += 256) {
+        const double P = (double)last[kb];
+        const double Q = (double)atrue[(size_t)bh * nb + kb];
+        const double m = 0.5 * (P + Q);
+        double tP = 0.0, tQ = 0.0;
+        if (P > 0.0) tP = P * ln_c(P / m, K);
+        if (Q > 0.0) tQ = Q * ln_c(Q / m, K);
+        terms[kb] = tP + tQ;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        double acc = 0.0;
+        for (int kb = 0; kb < nb; ++kb) acc = acc + terms[kb];
+        const double jsd = 0.5 * acc;
+        const double D = sqrt(jsd > 0.0 ? jsd : 0.0);
+        djs[bh] = D;
+        pattern[bh] = (D < tau) ? 1 : 0;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// K6: cumulative-attention selection, exact.  For every list (per head: the
+// flattened estimate for query-aware heads; column sums and diagonal sums
+// for vertical-slash heads) find K* = the key of the last element of the
+// shortest prefix, in (value desc, index asc) order, whose fixed-point mass
+// reaches T = ceil(G U / 2^24).  Radix selection from the most significant
+// key bits, 11 bits per pass, with mass (not count) histograms.
+// ---------------------------------------------------------------------------
+struct ListRef {
+    const float* x;
+    long long len;
+};
+
+__device__ __forceinline__ ListRef list_of(const PlanDev& P, int list) {
+    const int bh = list >> 1, slot = list & 1;
+    ListRef r{nullptr, 0};
+    if (P.pattern[bh] == kPatternQueryAware) {
+        if (slot == 0) { r.x = P.ahat + (size_t)bh * P.tri; r.len = P.tri; }
+    } else {
+        r.x = (slot == 0 ? P.colsum : P.diagsum) + (size_t)bh * P.N;
+        r.len = P.N;
+    }
+    return r;
+}
+
+__global__ __launch_bounds__(256) void k_sel_reset(SelState* __restrict__ st, unsigned long long* __restrict__ hist,
+                                                   int nlists) {
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i < nlists) {
+        SelState s = {};
+        st[i] = s;
+    }
+    for (long long t = i; t < (long long)nlists * kRadixBins; t += (long long)gridDim.x * 256) hist[t] = 0ull;
+}
+
+__global__ __launch_bounds__(256) void k_sel_total(PlanDev P, SelState* __restrict__ st) {
+    __shared__ unsigned long long red[256];
+    const int list = blockIdx.y, tid = threadIdx.x;
+    const ListRef L = list_of(P, list);
+    const long long base = (long long)blockIdx.x * kSelChunk;
+    unsigned long long s = 0;
+    if (base < L.len) {
+        const long long end = min(base + (long long)kSelChunk, L.len);
+        for (long long i = base + tid; i < end; i += 256) s += fixed_u(L.x[i]);
+    }
+    red[tid] = s;
+    __syncthreads();
+    for (int o = 128; o > 0; o >>= 1) {
+        if (tid < o) red[tid] += red[tid + o];
+        __syncthreads();
+    }
+    if (tid == 0 && red[0]) atomicAdd(&st[list].U, red[0]);
+}
+
+__global__ __launch_bounds__(256) void k_sel_init(PlanDev P, SelState* __restrict__ st, int nlists,
+                                                  unsigned long long G) {
+    const int list = blockIdx.x * 256 + threadIdx.x;
+    if (list >= nlists) return;
+    const ListRef L = list_of(P, list);
+    SelState s = st[list];
+    const unsigned long long U = s.U;
+    const unsigned long long hi = U >> kGammaShift, lo = U & ((1ull << kGammaShift) - 1);
+    const unsigned long long T = G * hi + ((G * lo + ((1ull << kGammaShift) - 1)) >> kGammaShift);
+    s.T = T;
+    s.R = T;
+    s.prefix = 0;
+    s.ibits = index_bits(L.len > 0 ? L.len : 1);
+    s.pos = 31 + s.ibits;
+    s.active = (L.len > 0 && T > 0) ? 1 : 0;
+    s.has = s.active;
+    s.kstar = 0;
+    st[list] = s;
+}
+
+__global__ __launch_bounds__(256) void k_sel_hist(PlanDev P, const SelState* __restrict__ st,
+                                                  unsigned long long* __restrict__ ghist) {
+    __shared__ unsigned long long hist[kRadixBins];
+    const int list = blockIdx.y, tid = threadIdx.x;
+    const SelState s = st[list];
+    if (!s.active) return;
+    const ListRef L = list_of(P, list);
+    const long long base = (long long)blockIdx.x * kSelChunk;
+    if (base >= L.len) return;
+    for (int i = tid; i < kRadixBins; i += 256) hist[i] = 0ull;
+    __syncthreads();
+    const int w = s.pos < kRadixBits ? s.pos : kRadixBits;
+    const int shift = s.pos - w;
+    const unsigned long long dmask = (1ull << w) - 1ull;
+    const long long end = min(base + (long long)kSelChunk, L.len);
+    for (long long i = base + tid; i < end; i += 256) {
+        const float x = L.x[i];
+        const unsigned long long key = order_key(x, i, s.ibits);
+        if ((key >> s.pos) == s.prefix) {
+            const unsigned long long u = fixed_u(x);
+            if (u) atomicAdd(&hist[(key >> shift) & dmask], u);
+        }
+    }
+    __syncthreads();
+    unsigned long long* gh = ghist + (size_t)list * kRadixBins;
+    for (int i = tid; i < kRadixBins; i += 256)
+        if (hist[i]) atomicAdd(&gh[i], hist[i]);
+}
+
+__global__ __launch_bounds__(256) void k_sel_scan(SelState* __restrict__ st, unsigned long long* __restrict__ ghist) {
+    constexpr int PER = kRadixBins / 256;
+    __shared__ unsigned long long tot[256];
+    __shared__ int found;
+    const int list = blockIdx.x, tid = threadIdx.x;
+    SelState s = st[list];
+    if (!s.active) return;
+    unsigned long long* gh = ghist + (size_t)list * kRadixBins;
+    unsigned long long v[PER];
+    unsigned long long run = 0;
+#pragma unroll
+    for (int r = 0; r < PER; ++r) {
+        v[r] = gh[tid * PER + r];
+        run += v[r];
+    }
+    tot[tid] = run;
+    if (tid == 0) found = kRadixBins;
+    __syncthreads();
+    // exclusive prefix over threads (Hillis-Steele on 256 totals)
+    for (int o = 1; o < 256; o <<= 1) {
+        unsigned long long add = tid >= o ? tot[tid - o] : 0ull;
+        __syncthreads();
+        tot[tid] += add;
+        __syncthreads();
+    }
+    unsigned long long cum = tot[tid] - run;    // mass of all lower digits
+    const int w = s.pos < kRadixBits ? s.pos : kRadixBits;
+    int mine = kRadixBins;
+    unsigned long long below = 0;
+#pragma unroll
+    for (int r = 0; r < PER; ++r) {
+        const int dgt = tid * PER + r;
+        if (mine == kRadixBins && dgt < (1 << w) && cum + v[r] >= s.R) {
+            mine = dgt;
+            below = cum;
+        }
+        cum += v[r];
+    }
+    if (mine < kRadixBins) atomicMin(&found, mine);
+    __syncthreads();
+    if (mine == found && mine < kRadixBins) {
+        s.R -= below;
+        s.prefix = (s.prefix << w) | (unsigned long long)mine;
+        s.pos -= w;
+        if (s.pos == 0) {
+            s.active = 0;
+            s.kstar = s.prefix;
+        }
+        st[list] = s;
+    }
+#pragma unroll
+    for (int r = 0; r < PER; ++r) gh[tid * PER + r] = 0ull;
+}
+
+// ---------------------------------------------------------------------------
+// K7a: vertical-slash lines -> block flags (any-touch rule).
+// colblk[kb]: some selected column j in key block kb.
+// diagA[a]:   some selected offset o with o / BS == a;
+// diagB[a]:   some selected offset o with o / BS == a and o % BS > 0.
+// Block (qb, kb) is touched iff colblk[kb] or diagA[qb-kb] or diagB[qb-kb-1].
+// grid (nb, BH), BS threads.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(128) void k_vs_flags(PlanDev P, const SelState* __restrict__ st) {
+    __shared__ int f[3];
+    const int kb = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
+    if (P.mode_all || P.pattern[bh] == kPatternQueryAware) return;
+    if (tid < 3) f[tid] = 0;
+    __syncthreads();
+    const SelState sc = st[2 * bh], sg = st[2 * bh + 1];
+    const long long j = (long long)kb * P.BS + tid;
+    const float xc = P.colsum[(size_t)bh * P.N + j];
+    const float xg = P.diagsum[(size_t)bh * P.N + j];
+    const bool selc = sc.has && order_key(xc, j, sc.ibits) <= sc.kstar;
+    const bool selg = sg.has && order_key(xg, j, sg.ibits) <= sg.kstar;
+    if (selc) f[0] = 1;
+    if (selg) f[1] = 1;
+    if (selg && tid > 0) f[2] = 1;
+    __syncthreads();
+    if (tid == 0) {
+        const size_t o = (size_t)bh * P.nb + kb;
+        P.colblk[o] = (unsigned char)f[0];
+        P.diagA[o] = (unsigned char)f[1];
+        P.diagB[o] = (unsigned char)f[2];
+    }
+}
+
+// ---------------------------------------------------------------------------
+// K7b: per (head, query-block row) block list: selected blocks, topped up to
+// the minimum budget with unselected blocks nearest the diagonal first, in
+// ascending key-block order at lists[bh][row (row+1)/2 + ...].
+// One wave per row, 4 rows per workgroup.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ bool member(const PlanDev& P, const SelState& s0, int bh, int qb, int kb, bool qa,
+                                       const float* arow, long long toff) {
+    if (P.mode_all) return true;
+    if (qa) return s0.has && order_key(arow[kb], toff + kb, s0.ibits) <= s0.kstar;
+    const size_t base = (size_t)bh * P.nb;
+    const int a = qb - kb;
+    return P.colblk[base + kb] || P.diagA[base + a] || (a >= 1 && P.diagB[base + a - 1]);
+}
+
+__global__ __launch_bounds__(256) void k_lists(PlanDev P, const SelState* __restrict__ st) {
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int bh = blockIdx.y, qb = blockIdx.x * 4 + wv;
+    if (qb >= P.nb) return;
+    const bool qa = P.pattern[bh] == kPatternQueryAware;
+    const SelState s0 = st[2 * bh];
+    const long long toff = (long long)qb * (qb + 1) / 2;
+    const float* arow = P.ahat + (size_t)bh * P.tri + toff;
+    int cnt = 0;
+    for (int base = 0; base <= qb; base += 64) {
+        const int kb = base + lane;
+        const bool m = kb <= qb && member(P, s0, bh, qb, kb, qa, arow, toff);
+        cnt += __popcll(__ballot(m));
+    }
+    const int want = min(qb + 1, P.floor_blocks);
+    int need = want - cnt;
+    int cut = qb + 1;
+    if (need > 0) {
+        for (int top = qb; top >= 0; top -= 64) {
+            const int kb = top - lane;
+            const bool un = kb >= 0 && !member(P, s0, bh, qb, kb, qa, arow, toff);
+            unsigned long long bal = __ballot(un);
+            const int c = __popcll(bal);
+            if (need <= c) {
+                for (int t = 1; t < need; ++t) bal &= bal - 1ull;
+                cut = top - (__ffsll((long long)bal) - 1);
+                break;
+            }
+            need -= c;
+        }
+    }
+    int* out = P.lists + (size_t)bh * P.tri + toff;
+    int total = 0;
+    for (int base = 0; base <= qb; base += 64) {
+        const int kb = base + lane;
+        const bool f = kb <= qb && (kb >= cut || member(P, s0, bh, qb, kb, qa, arow, toff));
+        const unsigned long long bal = __ballot(f);
+        if (f) out[total + __popcll(bal & ((1ull << lane) - 1ull))] = kb;
+        total += __popcll(bal);
+    }
+    if (lane == 0) {
+        P.counts[(size_t)bh * P.nb + qb] = total;
+        atomicAdd(P.total_blocks, (unsigned long long)total);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Attention work order: rows sorted by selected-block count, longest first
+// (counting sort; order among equal counts is arbitrary).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_order_hist(PlanDev P, int* __restrict__ hist, int rows) {
+    const int r = blockIdx.x * 256 + threadIdx.x;
+    if (r < rows) atomicAdd(&hist[P.counts[r]], 1);
+}
+
+__global__ __launch_bounds__(256) void k_order_scan(int* __restrict__ hist, int* __restrict__ start, int nb) {
+    if (threadIdx.x == 0 && blockIdx.x == 0) {
+        int acc = 0;
+        for (int c = nb; c >= 0; --c) {
+            start[c] = acc;
+            acc += hist[c];
+        }
+    }
+}
+
+__global__ __launch_bounds__(256) void k_order_scatter(PlanDev P, int* __restrict__ start, int rows) {
+    const int r = blockIdx.x * 256 + threadIdx.x;
+    if (r < rows) P.order[atomicAdd(&start[P.counts[r]], 1)] = r;
+}
+
+__global__ __launch_bounds__(256) void k_fill_u32(unsigned int* __restrict__ p, unsigned int v, long long n) {
+    for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < n; i += (long long)gridDim.x * 256) p[i] = v;
+}
+
+// probes of the canonical functions
+__global__ __launch_bounds__(256) void k_probe_exp2(const float* x, float* y, long long n, Canon K) {
+    const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (i < n) y[i] = exp2_c(x[i], K);
+}
+__global__ __launch_bounds__(256) void k_probe_ln(const double* x, double* y, long long n, Canon K) {
+    const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (i < n) y[i] = ln_c(x[i], K);
+}
+__global__ __launch_bounds__(256) void k_probe_sqrt(const double* x, double* y, long long n) {
+    const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (i < n) y[i] = sqrt(x[i]);
+}
+
+// ---------------------------------------------------------------------------
+// host launchers
+// ---------------------------------------------------------------------------
+static inline unsigned grid1(long long n, int per = 256) { return (unsigned)((n + per - 1) / per); }
+
+hipError_t launch_plan(const PlanArgs& a, PlanDev& P, hipStream_t st) {
+    const int BS = P.BS, nb = P.nb, N = P.N, BH = P.BH;
+    const int bkv = a.B * a.Hkv;
+    const float inv_bs = 1.0f / (float)BS;
+    // K1
+    if (a.dtype_bf16) {
+        hipLaunchKernelGGL(k_pool<bf16_t>, dim3(nb, BH), dim3(kHeadDim), 0, st, (const bf16_t*)a.q, P.qbar, N, BS, inv_bs);
+        hipLaunchKernelGGL(k_pool<bf16_t>, dim3(nb, bkv), dim3(kHeadDim), 0, st, (const bf16_t*)a.k, P.kbar, N, BS, inv_bs);
+    } else {
+        hipLaunchKernelGGL(k_pool<float>, dim3(nb, BH), dim3(kHeadDim), 0, st, (const float*)a.q, P.qbar, N, BS, inv_bs);
+        hipLaunchKernelGGL(k_pool<float>, dim3(nb, bkv), dim3(kHeadDim), 0, st, (const float*)a.k, P.kbar, N, BS, inv_bs);
+    }
+    // K2
+    const dim3 gs((N + kScoreTK - 1) / kScoreTK, BH);
+    const int group = a.Hq / a.Hkv;
+#define FP_SCORES(T, B_)                                                                                   \
+    hipLaunchKernelGGL((k_scores<T, B_>), gs, dim3(256), 0, st, (const T*)a.q, (const T*)a.k, a.s2, a.pmax, \
+                       N, a.Hq, a.Hkv, group, a.canon.C)
+    if (a.dtype_bf16) {
+        if (BS == 128) FP_SCORES(bf16_t, 128); else FP_SCORES(bf16_t, 64);
+    } else {
+        if (BS == 128) FP_SCORES(float, 128); else FP_SCORES(float, 64);
+    }
+#undef FP_SCORES
+    // K3
+    if (BS == 128)
+        hipLaunchKernelGGL(k_rowexp<128>, dim3(BS, BH), dim3(256), 0, st, a.s2, a.pmax, P.rowmax, P.rowsum, a.rz, N, a.canon);
+    else
+        hipLaunchKernelGGL(k_rowexp<64>, dim3(BS, BH), dim3(256), 0, st, a.s2, a.pmax, P.rowmax, P.rowsum, a.rz, N, a.canon);
+    hipLaunchKernelGGL(k_linesums, dim3(grid1(N), BH), dim3(256), 0, st, a.s2, a.rz, P.colsum, P.diagsum, N, BS);
+    hipLaunchKernelGGL(k_atrue, dim3(BH), dim3(256), 0, st, P.colsum, P.atrue, N, BS);
+    // K4, K5
+    hipLaunchKernelGGL(k_estimate, dim3(nb, BH), dim3(256), 0, st, P.qbar, P.kbar, P.ahat, nb, a.Hq, a.Hkv, group, a.canon);
+    hipLaunchKernelGGL(k_jsd, dim3(BH), dim3(256), 0, st, P.ahat, P.atrue, P.djs, P.pattern, nb, a.tau, a.canon);
+    // K6
+    const int nlists = 2 * BH;
+    if (!P.mode_all) {
+        hipLaunchKernelGGL(k_sel_reset, dim3(grid1((long long)nlists * kRadixBins)), dim3(256), 0, st, P.sel, P.hist, nlists);
+        const long long maxlen = P.tri > N ? P.tri : N;
+        const dim3 gc((unsigned)((maxlen + kSelChunk - 1) / kSelChunk), nlists);
+        hipLaunchKernelGGL(k_sel_total, gc, dim3(256), 0, st, P, P.sel);
+        hipLaunchKernelGGL(k_sel_init, dim3(grid1(nlists)), dim3(256), 0, st, P, P.sel, nlists, a.G);
+        const int kbits = 31 + index_bits(maxlen);
+        const int passes = (kbits + kRadixBits - 1) / kRadixBits;
+        for (int p = 0; p < passes; ++p) {
+            hipLaunchKernelGGL(k_sel_hist, gc, dim3(256), 0, st, P, P.sel, P.hist);
+            hipLaunchKernelGGL(k_sel_scan, dim3(nlists), dim3(256), 0, st, P.sel, P.hist);
+        }
+        hipLaunchKernelGGL(k_vs_flags, dim3(nb, BH), dim3(BS), 0, st, P, P.sel);
+    }
+    // K7
+    hipLaunchKernelGGL(k_fill_u32, dim3(1), dim3(256), 0, st, (unsigned int*)P.total_blocks, 0u, 2LL);
+    hipLaunchKernelGGL(k_lists, dim3((nb + 3) / 4, BH), dim3(256), 0, st, P, P.sel);
+    const int rows = BH * nb;
+    hipLaunchKernelGGL(k_fill_u32, dim3(grid1(2 * (nb + 1))), dim3(256), 0, st, (unsigned int*)a.ord_tmp, 0u,
+                       (long long)2 * (nb + 1));
+    hipLaunchKernelGGL(k_order_hist, dim3(grid1(rows)), dim3(256), 0, st, P, a.ord_tmp, rows);
+    hipLaunchKernelGGL(k_order_scan, dim3(1), dim3(64), 0, st, a.ord_tmp, a.ord_tmp + (nb + 1), nb);
+    hipLaunchKernelGGL(k_order_scatter, dim3(grid1(rows)), dim3(256), 0, st, P, a.ord_tmp + (nb + 1), rows);
+    return hipGetLastError();
+}
+
+hipError_t launch_probe_exp2(const float* x, float* y, long long n, const Canon& K, hipStream_t st) {
+    if (n > 0) hipLaunchKernelGGL(k_probe_exp2, dim3(grid1(n)), dim3(256), 0, st, x, y, n, K);
+    return hipGetLastError();
+}
+hipError_t launch_probe_ln(const double* x, double* y, long long n, const Canon& K, hipStream_t st) {
+    if (n > 0) hipLaunchKernelGGL(k_probe_ln, dim3(grid1(n)), dim3(256), 0, st, x, y, n, K);
+    return hipGetLastError();
+}
+hipError_t launch_probe_sqrt(const double* x, double* y, long long n, hipStream_t st) {
+    if (n > 0) hipLaunchKernelGGL(k_probe_sqrt, dim3(grid1(n)), dim3(256), 0, st, x, y, n);
+    return hipGetLastError();
+}
+
+}  // namespace fp

@@ -1,0 +1,119 @@
+"""The C-ABI library loads, exports every symbol include/fp_prefill.h
+declares, and validates arguments on the host (no GPU needed: every call here
+fails validation or is an empty problem before any HIP call)."""
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp_prefill.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from sparse_long_context_last_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        from sparse_long_context_last_amd import build
+        build.build()
+    return _lib.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fp_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ("fp_prefill_plan", "fp_prefill_attend", "fp_dense_attend", "fp_plan_info_get",
+              "fp_plan_copy_out", "fp_plan_destroy", "fp_status_str", "fp_last_error"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    from sparse_long_context_last_amd import _lib
+    names = declared_functions()
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(_lib.SIGNATURES), "binding and header disagree"
+
+
+def test_status_strings(lib):
+    for code, name in [(0, "FP_OK"), (-1, "FP_ERR_INVALID_ARG"), (-2, "FP_ERR_UNSUPPORTED"),
+                       (-3, "FP_ERR_SHAPE"), (-4, "FP_ERR_OOM"), (-5, "FP_ERR_HIP")]:
+        assert lib.fp_status_str(code).decode() == name
+
+
+def _plan(lib, dtype=0, B=1, Hq=4, Hkv=4, N=1024, d=128, block=128, gamma=0.95, tau=0.1,
+          min_budget=1024, q=1, k=1, out=True):
+    h = C.c_void_p()
+    st = lib.fp_prefill_plan(q, k, dtype, B, Hq, Hkv, N, d, block, gamma, tau, min_budget, None,
+                             C.byref(h) if out else None)
+    return st, h
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(d=64), -2), (dict(d=256), -2), (dict(block=32), -2), (dict(dtype=7), -2),
+    (dict(N=1000), -3), (dict(Hq=6, Hkv=4), -3), (dict(N=128 * 4097), -3), (dict(Hkv=0), -3),
+    (dict(gamma=0.0), -1), (dict(gamma=1.5), -1), (dict(gamma=float("nan")), -1),
+    (dict(tau=-0.1), -1), (dict(tau=float("inf")), -1), (dict(min_budget=-1), -1),
+    (dict(q=None), -1), (dict(k=None), -1), (dict(B=-1), -1), (dict(out=False), -1),
+])
+def test_plan_validation(lib, kw, code):
+    st, h = _plan(lib, **kw)
+    assert st == code, lib.fp_last_error()
+    assert lib.fp_last_error().decode()
+    if kw.get("out", True):
+        assert h.value is None
+
+
+def test_empty_problems_need_no_device(lib):
+    from sparse_long_context_last_amd._lib import PlanInfo
+    for kw in (dict(B=0), dict(Hq=0), dict(N=0)):
+        st, h = _plan(lib, q=None, k=None, **kw)
+        assert st == 0, lib.fp_last_error()
+        info = PlanInfo()
+        assert lib.fp_plan_info_get(h, C.byref(info)) == 0
+        assert info.total_blocks == 0 and info.dense_blocks == 0
+        rp = np.ones(1, np.int32)
+        assert lib.fp_plan_copy_out(h, None, None, rp.ctypes.data, rp.ctypes.data, None) == 0
+        assert rp[0] == 0
+        assert lib.fp_prefill_attend(h, None, None, None, None, None) == 0
+        lib.fp_plan_destroy(h)
+    assert lib.fp_dense_attend(None, None, None, None, 0, 0, 4, 4, 1024, 128, 128, None) == 0
+    lib.fp_plan_destroy(None)
+
+
+def test_attend_validation(lib):
+    assert lib.fp_prefill_attend(None, 1, 1, 1, 1, None) == -1
+    assert lib.fp_dense_attend(1, 1, 1, 1, 0, 1, 4, 4, 1024, 64, 128, None) == -2
+    assert lib.fp_dense_attend(1, 1, 1, 1, 0, 1, 4, 3, 1024, 128, 128, None) == -3
+    assert lib.fp_dense_attend(None, 1, 1, 1, 0, 1, 4, 4, 1024, 128, 128, None) == -1
+    assert lib.fp_plan_copy_debug(None, 0, None, 0) == -1
+    assert lib.fp_plan_copy_out(None, None, None, None, None, None) == -1
+
+
+def test_canonical_constants_match_the_oracle(lib):
+    """The library derives its constants on its own (long double on the
+    host); they must equal the oracle's (exact rationals) bit for bit."""
+    import sparse_long_context_last_amd as F
+    for d in (64, 128):
+        c = F.canonical_constants(d)
+        assert np.array_equal(c["e2"], np.array(O.EXP2_COEF, np.float32))
+        assert np.array_equal(c["lnc"], np.array(O.LN_COEF, np.float64))
+        assert c["ln2"] == O.LN2_F64 and c["sqrt_half"] == O.SQRT_HALF_F64
+        assert c["C"] == O.score_scale(d)
+
+
+def test_product_path_has_no_fallback():
+    """The binding refuses to run without the compiled library."""
+    src = open(os.path.join(ROOT, "sparse_long_context_last_amd", "__init__.py")).read()
+    src += open(os.path.join(ROOT, "sparse_long_context_last_amd", "_lib.py")).read()
+    assert "oracle" not in src and "synth" not in src
+    assert "there is no fallback" in src

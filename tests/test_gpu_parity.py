@@ -1,0 +1,171 @@
+"""GPU parity of the HIP path (through the C ABI) with the CPU oracle on
+seeded inputs small enough for the oracle to run on every head and row:
+pattern choices, divergences, block lists and every selection intermediate
+bit-exact; attention outputs within max-abs 2e-2 / mean-abs 2e-3 (bf16) or
+1e-4 (fp32) of the float64 oracle."""
+import numpy as np
+import pytest
+
+import oracle as O
+from synth import BY_NAME, LayerGen
+from tests._parity import check_attention, compare_head, list_properties
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def F():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import sparse_long_context_last_amd as F
+    from sparse_long_context_last_amd import _lib
+    _lib.load()
+    return F
+
+
+def to_dev(x, dtype):
+    t = torch.from_numpy(np.ascontiguousarray(x))
+    return t.to(device="cuda", dtype=torch.bfloat16 if dtype == "bf16" else torch.float32).contiguous()
+
+
+def run_and_compare(F, cfg, q, k, v, attention=True, dense=True):
+    dt = cfg.dtype
+    qd, kd, vd = to_dev(q, dt), to_dev(k, dt), to_dev(v, dt)
+    P = F.plan(qd, kd, block=cfg.block, gamma=cfg.gamma, tau=cfg.tau, min_budget=cfg.min_budget)
+    dbg = {it: P.debug(it) for it in ("qbar", "kbar", "rowmax", "rowsum", "colsum", "diagsum",
+                                      "atrue", "ahat")}
+    pattern, djs, _, _ = P.copy_out()
+    lists = P.lists()
+    out = F.attend(P, qd, kd, vd) if attention else None
+    outd = F.dense_attend(qd, kd, vd, block=cfg.block) if dense else None
+    torch.cuda.synchronize()
+    B, Hq = q.shape[0], q.shape[1]
+    group = Hq // k.shape[1]
+    plans = {}
+    for b in range(B):
+        for kv in range(k.shape[1]):
+            np.testing.assert_array_equal(dbg["kbar"][b * k.shape[1] + kv], O.pool_mean(k[b, kv], cfg.block))
+        for h in range(Hq):
+            bh = b * Hq + h
+            hp = O.plan_head(q[b, h], k[b, h // group], cfg.block, cfg.gamma, cfg.tau, cfg.min_budget)
+            compare_head(P, dbg, pattern, djs, lists, bh, hp)
+            list_properties(lists[bh], cfg.nb, O.floor_blocks(cfg.min_budget, cfg.block))
+            plans[bh] = hp
+            if attention:
+                ref = O.attend_head(q[b, h], k[b, h // group], v[b, h // group], hp.mask, cfg.block)
+                check_attention(out[b, h].float().cpu().numpy(), ref, dt, f"sparse b{b} h{h}")
+            if dense:
+                refd = O.attend_head(q[b, h], k[b, h // group], v[b, h // group], O.dense_mask(cfg.nb), cfg.block)
+                check_attention(outd[b, h].float().cpu().numpy(), refd, dt, f"dense b{b} h{h}")
+    info = P.info()
+    assert info.total_blocks == sum(sum(len(x) for x in hp.lists) for hp in plans.values())
+    assert info.query_aware_heads == sum(hp.pattern for hp in plans.values())
+    return P, plans, out, outd
+
+
+SMALL = {
+    # the tiny fp32 layer in full (one head of each planted type)
+    "tiny_fp32_4k": BY_NAME["tiny_fp32_4k"],
+    # Llama-shaped GQA 4:1, bf16, 16 blocks
+    "gqa_bf16_2k": BY_NAME["llama8b_32k"].with_(Hq=8, Hkv=2, N=2048, mix=(0.25, 0.25, 0.25, 0.25)),
+    # 9 blocks: the score kernel's last 256-key chunk is half full
+    "ragged_bf16_1152": BY_NAME["llama8b_32k"].with_(Hq=4, Hkv=1, N=1152, min_budget=256,
+                                                      explicit_types=("V", "S", "QA", "N")),
+    # block 64, 17 blocks, two batches
+    "bs64_bf16_1088_b2": BY_NAME["glm9b_64k_bs64"].with_(B=2, Hq=4, Hkv=2, N=1088, min_budget=256,
+                                                          explicit_types=("QA", "V", "S", "N")),
+    # fp32 at block 64
+    "bs64_fp32_1024": BY_NAME["tiny_fp32_4k"].with_(N=1024, block=64, min_budget=128),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_small_layer_parity(F, name):
+    cfg = SMALL[name]
+    q, k, v = LayerGen(cfg).numpy_layer()
+    run_and_compare(F, cfg, q, k, v)
+
+
+def test_probes_match_oracle(F):
+    rng = np.random.default_rng(0)
+    x = np.concatenate([np.linspace(-100, 0, 200_001, dtype=np.float32),
+                        -np.abs(rng.standard_normal(50_000).astype(np.float32)) * 60,
+                        np.array([-100.5, -np.inf, 0.0, -0.0], np.float32)])
+    xd = torch.from_numpy(x).cuda()
+    yd = torch.empty_like(xd)
+    from sparse_long_context_last_amd import _lib
+    lib = _lib.load()
+    s = torch.cuda.current_stream().cuda_stream
+    _lib.check(lib.fp_probe_exp2(xd.data_ptr(), yd.data_ptr(), x.size, s), "probe")
+    np.testing.assert_array_equal(yd.cpu().numpy(), O.exp2_c(x))
+    z = np.concatenate([np.exp(rng.uniform(-700, 700, 100_000)), rng.uniform(0, 2, 100_000),
+                        [0.5, 1.0, 2.0, 1e-300]])
+    zd = torch.from_numpy(z).cuda()
+    wd = torch.empty_like(zd)
+    _lib.check(lib.fp_probe_ln(zd.data_ptr(), wd.data_ptr(), z.size, s), "probe")
+    np.testing.assert_array_equal(wd.cpu().numpy(), O.ln_c(z))
+    sq = np.concatenate([rng.uniform(0, np.log(2), 200_000), rng.uniform(0, 1e-6, 50_000),
+                         np.exp(rng.uniform(-700, 700, 50_000)), [0.0, 1.0, 2.0]])
+    sd = torch.from_numpy(sq).cuda()
+    rd = torch.empty_like(sd)
+    _lib.check(lib.fp_probe_sqrt(sd.data_ptr(), rd.data_ptr(), sq.size, s), "probe")
+    np.testing.assert_array_equal(rd.cpu().numpy(), np.sqrt(sq))
+
+
+def test_gamma_one_equals_dense(F):
+    cfg = SMALL["gqa_bf16_2k"].with_(gamma=1.0)
+    q, k, v = LayerGen(cfg).numpy_layer()
+    P, plans, out, outd = run_and_compare(F, cfg, q, k, v)
+    assert P.info().total_blocks == P.info().dense_blocks
+    # identical block visits in identical order: the outputs agree bit for bit
+    assert torch.equal(out, outd)
+
+
+def test_tau_extremes_and_budget(F):
+    base = SMALL["gqa_bf16_2k"]
+    q, k, v = LayerGen(base).numpy_layer()
+    _, plans, _, _ = run_and_compare(F, base.with_(tau=0.0), q, k, v, dense=False)
+    assert all(hp.pattern == O.VERTICAL_SLASH for hp in plans.values())
+    _, plans, _, _ = run_and_compare(F, base.with_(tau=0.84), q, k, v, dense=False)
+    assert all(hp.pattern == O.QUERY_AWARE for hp in plans.values())
+    P, _, _, _ = run_and_compare(F, base.with_(min_budget=base.N), q, k, v, dense=False)
+    assert P.info().total_blocks == P.info().dense_blocks
+    run_and_compare(F, base.with_(gamma=0.5, min_budget=0), q, k, v, dense=False)
+
+
+def test_single_block_and_zero_inputs(F):
+    cfg = SMALL["ragged_bf16_1152"].with_(N=128)
+    q, k, v = LayerGen(cfg).numpy_layer()
+    P, plans, _, _ = run_and_compare(F, cfg, q, k, v)
+    assert all(hp.D == 0.0 for hp in plans.values())
+    # all-zero queries and keys: uniform attention, every selection decided by
+    # the index tie-break
+    cfg = SMALL["ragged_bf16_1152"].with_(gamma=0.6, min_budget=0)
+    z = np.zeros((1, cfg.Hq, cfg.N, cfg.d), np.float32)
+    zk = np.zeros((1, cfg.Hkv, cfg.N, cfg.d), np.float32)
+    v = LayerGen(cfg).numpy_layer()[2]
+    run_and_compare(F, cfg, z, zk, v)
+
+
+def test_plans_are_deterministic(F):
+    cfg = SMALL["gqa_bf16_2k"]
+    q, k, v = LayerGen(cfg).numpy_layer()
+    qd, kd = to_dev(q, "bf16"), to_dev(k, "bf16")
+    a = F.plan(qd, kd, block=cfg.block, gamma=cfg.gamma, tau=cfg.tau, min_budget=cfg.min_budget)
+    b = F.plan(qd, kd, block=cfg.block, gamma=cfg.gamma, tau=cfg.tau, min_budget=cfg.min_budget)
+    for x, y in zip(a.copy_out(), b.copy_out()):
+        np.testing.assert_array_equal(x, y)
+    for it in ("colsum", "diagsum", "ahat"):
+        np.testing.assert_array_equal(a.debug(it), b.debug(it))
+
+
+def test_empty_problem_on_device(F):
+    cfg = SMALL["gqa_bf16_2k"]
+    q = torch.zeros((0, cfg.Hq, cfg.N, cfg.d), device="cuda", dtype=torch.bfloat16)
+    k = torch.zeros((0, cfg.Hkv, cfg.N, cfg.d), device="cuda", dtype=torch.bfloat16)
+    P = F.plan(q, k, block=128)
+    assert P.info().total_blocks == 0
+    out = F.attend(P, q, k, k)
+    assert out.shape == q.shape
