@@ -1,0 +1,263 @@
+"""Benchmark of one layer's FlexPrefill causal prefill on one MI355X.
+
+A step is one pass of the whole hot path over one batch of synthetic input:
+fp_prefill_plan (pattern determination + cumulative-attention selection)
+followed by fp_prefill_attend (block-sparse attention).  Inputs are resident
+in HBM before the timed region.  Default workload: the Llama-3.1-8B-shaped
+layer (32 query / 8 key-value heads, head dim 128, bf16) at N = 131072,
+block 128, gamma 0.95, tau 0.1, minimum budget 1024 tokens.
+
+Prints ONE JSON line: sparse ms per layer (the metric), its parts, the dense
+causal baseline with the same tile kernel, effective TFLOP/s over computed
+blocks, the attention kernel's roofline (time from HIP events recorded by
+the library around that kernel), and the CPU oracle timed on a bounded
+sample (cpu_baseline).
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "sparse prefill ms/layer + effective TFLOP/s & speedup vs dense @128k, 1 GPU"
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_FP32_TFLOPS = 157.3      # MI355X fp32 matrix
+PEAK_HBM_GBS = 8000.0
+ATTN_SOURCES = ("attn_kernels.hip",)
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "attention_counters_llama8b_128k.md")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for s in ATTN_SOURCES:
+        with open(os.path.join(ROOT, "sparse_long_context_last_amd", "csrc", s), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(workload: str):
+    """HBM bytes per attention launch from the committed counter summary, if
+    it was taken on the current attention kernel source and this workload."""
+    if not os.path.exists(COUNTERS_FILE):
+        return None
+    m = re.search(r"```json\n(.*?)\n```", open(COUNTERS_FILE).read(), re.S)
+    if not m:
+        return None
+    rec = json.loads(m.group(1))
+    if rec.get("kernel_source_sha256_16") != kernel_source_hash() or rec.get("workload") != workload:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(cfg, total_blocks_by_head, sample_rows: int, budget_s: float):
+    """The oracle as it stands on the host cores: one query head planned in
+    full, float64 attention on a sample of that head's query blocks,
+    extrapolated to the whole layer by head count and selected-block count."""
+    import numpy as np
+    import oracle as O
+    from synth import LayerGen
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:
+        threads = 1
+    gen = LayerGen(cfg)
+    h = 0
+    q = gen.q_head(0, h)
+    k = gen.k_head(0, h // cfg.group)
+    v = gen.v_head(0, h // cfg.group)
+    t0 = time.perf_counter()
+    hp = O.plan_head(q, k, cfg.block, cfg.gamma, cfg.tau, cfg.min_budget)
+    t_plan = time.perf_counter() - t0
+    rng = np.random.default_rng(7)
+    rows = sorted(set([0, cfg.nb - 1] + rng.choice(cfg.nb, size=min(cfg.nb, sample_rows), replace=False).tolist()))
+    t0 = time.perf_counter()
+    done_blocks = 0
+    for r in rows:
+        O.attend_rows(q, k, v, hp.mask, cfg.block, [r])
+        done_blocks += len(hp.lists[r])
+        if time.perf_counter() - t0 > budget_s:
+            break
+    t_attn = time.perf_counter() - t0
+    per_block = t_attn / max(done_blocks, 1)
+    total_blocks = sum(total_blocks_by_head)
+    est_s = t_plan * cfg.B * cfg.Hq + per_block * total_blocks
+    return {"value": round(est_s * 1e3, 1), "unit": "ms/layer", "cores": threads, "kind": "oracle",
+            "sample": (f"query head {h} planned in full (N={cfg.N}, {t_plan:.1f} s) and float64 "
+                       f"attention on {done_blocks} selected blocks of that head ({t_attn:.1f} s); "
+                       f"extrapolated to {cfg.B * cfg.Hq} heads and {total_blocks} selected blocks")}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--config", default="llama8b_128k")
+    ap.add_argument("--dense-reps", type=int, default=3)
+    ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=24)
+    ap.add_argument("--cpu-budget-s", type=float, default=15.0)
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="also run a plain device copy of this many MiB (counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        return 2
+
+    import numpy as np
+    import torch
+
+    import sparse_long_context_last_amd as F
+    from synth import BY_NAME, LayerGen
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU"}))
+        return 1
+    cfg = BY_NAME[args.config]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    t0 = time.perf_counter()
+    q, k, v = LayerGen(cfg).torch_layer(dev)
+    torch.cuda.synchronize()
+    gen_s = time.perf_counter() - t0
+    print(f"[bench] inputs {cfg.name} generated in {gen_s:.1f}s", file=sys.stderr, flush=True)
+    out = torch.empty_like(q)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        P = F.plan(q, k, block=cfg.block, gamma=cfg.gamma, tau=cfg.tau, min_budget=cfg.min_budget)
+        F.attend(P, q, k, v, out=out)
+        return P
+
+    for _ in range(args.warmup):
+        P = step()
+    torch.cuda.synchronize()
+    # timed steps: whole hot path; the library's events time the attention kernel
+    F.profile_enable(True)
+    F.profile_read(reset=True)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    plans = []
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        P = F.plan(q, k, block=cfg.block, gamma=cfg.gamma, tau=cfg.tau, min_budget=cfg.min_budget)
+        ev[i][1].record(stream)
+        F.attend(P, q, k, v, out=out)
+        ev[i][2].record(stream)
+        plans.append(P)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t_wall) * 1e3 / args.steps
+    plan_ms = float(np.median([a.elapsed_time(b) for a, b, _ in ev]))
+    attend_ms = float(np.median([b.elapsed_time(c) for _, b, c in ev]))
+    step_ms = float(np.mean([a.elapsed_time(c) for a, _, c in ev]))
+    kern_ms, kern_n, _, _ = F.profile_read(reset=True)
+    F.profile_enable(False)
+    info = plans[-1].info()
+    counts = plans[-1].debug("counts")
+    pattern, djs, _, _ = plans[-1].copy_out()
+    del plans
+    blocks_by_head = counts.sum(axis=1).tolist()
+
+    flop_per_block = 4.0 * cfg.block * cfg.block * cfg.d
+    sparse_flop = info.total_blocks * flop_per_block
+    dense_flop = info.dense_blocks * flop_per_block
+    kern_avg_ms = kern_ms / max(kern_n, 1)
+    peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_FP32_TFLOPS
+    achieved = sparse_flop / (kern_avg_ms * 1e-3) / 1e12
+
+    dense_ms = None
+    if not args.no_dense:
+        F.profile_enable(True)
+        F.profile_read(reset=True)
+        outd = torch.empty_like(q)
+        F.dense_attend(q, k, v, block=cfg.block, out=outd)      # warm-up
+        torch.cuda.synchronize()
+        F.profile_read(reset=True)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.dense_reps):
+            F.dense_attend(q, k, v, block=cfg.block, out=outd)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        dense_ms = e0.elapsed_time(e1) / args.dense_reps
+        _, _, dk_ms, dk_n = F.profile_read(reset=True)
+        F.profile_enable(False)
+        dense_kernel_ms = dk_ms / max(dk_n, 1)
+        del outd
+
+    if args.calib_copy_mib:
+        n = args.calib_copy_mib * (1 << 20) // 4
+        a = torch.ones(n, device=dev, dtype=torch.float32)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    traffic = read_traffic(cfg.name)
+    roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
+            "frac": round(achieved / peak, 4), "traffic": traffic,
+            "kernel": "k_attn_bf16<128>" if cfg.dtype == "bf16" and cfg.block == 128 else
+                      f"k_attn_{cfg.dtype}<{cfg.block}>",
+            "algorithmic_flop_per_launch": sparse_flop, "avg_kernel_ms": round(kern_avg_ms, 4),
+            "launches": kern_n}
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(cfg, blocks_by_head, args.cpu_rows, args.cpu_budget_s)
+
+    rec = {
+        "metric": METRIC,
+        "value": round(step_ms, 3),
+        "unit": "ms/layer",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 3),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic (seeded planted head types; no datasets or weights)",
+        "config": {"workload": cfg.name, "B": cfg.B, "Hq": cfg.Hq, "Hkv": cfg.Hkv, "N": cfg.N,
+                   "d": cfg.d, "block": cfg.block, "gamma": cfg.gamma, "tau": cfg.tau,
+                   "min_budget": cfg.min_budget, "parallelism": "single GPU"},
+        "plan_ms": round(plan_ms, 3),
+        "attend_ms": round(attend_ms, 3),
+        "attention_kernel_ms": round(kern_avg_ms, 3),
+        "wall_ms_per_step": round(wall_ms, 3),
+        "dense_ms": round(dense_ms, 3) if dense_ms is not None else None,
+        "dense_kernel_ms": round(dense_kernel_ms, 3) if dense_ms is not None else None,
+        "speedup_vs_dense": round(dense_ms / step_ms, 3) if dense_ms is not None else None,
+        "computed_blocks": info.total_blocks,
+        "dense_blocks": info.dense_blocks,
+        "density": round(info.total_blocks / max(info.dense_blocks, 1), 5),
+        "query_aware_heads": info.query_aware_heads,
+        "eff_tflops_attention_kernel": round(achieved, 1),
+        "eff_tflops_layer": round(sparse_flop / (step_ms * 1e-3) / 1e12, 1),
+        "mfma_frac_attention_kernel": round(achieved / peak, 4),
+        "dense_eff_tflops": round(dense_flop / (dense_kernel_ms * 1e-3) / 1e12, 1) if dense_ms else None,
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "input_generation_s": round(gen_s, 1),
+    }
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
