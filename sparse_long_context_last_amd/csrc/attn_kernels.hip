@@ -25,6 +25,7 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kKT = 64;   // keys per LDS stage
+constexpr float kLazy = 8.0f;   // log2 growth of a row maximum that forces a rescale
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -40,7 +41,7 @@ __device__ __forceinline__ int work_row(const AttnArgs& a, int item) {
 // bf16 inputs, bf16 MFMA 32x32x16, fp32 accumulation and softmax
 // ---------------------------------------------------------------------------
 template <int BS>
-__global__ __launch_bounds__(2 * BS) void k_attn_bf16(AttnArgs a) {
+__global__ __launch_bounds__(2 * BS, BS == 128 ? 2 : 1) void k_attn_bf16(AttnArgs a) {
     constexpr int D = kHeadDim, KT = kKT, NT = 2 * BS, SPB = BS / KT;
     constexpr int KP = D + 8;     // K tile row pitch (elements): 272 B
     constexpr int VP = KT + 8;    // V^T tile row pitch (elements): 144 B
@@ -144,16 +145,30 @@ __global__ __launch_bounds__(2 * BS) void k_attn_bf16(AttnArgs a) {
                     if (krel > qrel) st[t][r] = -INFINITY;
                 }
         }
-        // online softmax (lane = one query; lane ^ 32 holds its other keys)
+        // online softmax (lane = one query; lane ^ 32 holds its other keys).
+        // The reference maximum only moves when the row maximum grows by more
+        // than 2^kLazy in the exp2 domain, so exp2 values stay <= 2^kLazy and
+        // the accumulators are rescaled only on those (rare) stages; the
+        // final division by the row sum makes the result independent of the
+        // reference chosen.
         float mx = -INFINITY;
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll
             for (int r = 0; r < 16; ++r) mx = fmaxf(mx, st[t][r]);
         mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float m_new = fmaxf(m_run, mx);
-        const float alpha = fast_exp2((m_run - m_new) * sl);
-        const float mb = m_new * sl;
+        const bool grow = !(m_run * sl + kLazy >= mx * sl);   // also true while m_run = -inf
+        if (__ballot(grow)) {
+            const float m_new = grow ? fmaxf(m_run, mx) : m_run;
+            const float alpha = fast_exp2((m_run - m_new) * sl);
+            l_run *= alpha;
+#pragma unroll
+            for (int T = 0; T < 4; ++T)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) o[T][r] *= alpha;
+            m_run = m_new;
+        }
+        const float mb = m_run == -INFINITY ? 0.0f : m_run * sl;
         float ls = 0.0f;
         bf16x8_t pf[4];
 #pragma unroll
@@ -164,12 +179,7 @@ __global__ __launch_bounds__(2 * BS) void k_attn_bf16(AttnArgs a) {
                 ls += p;
                 pf[2 * t + (r >> 3)][r & 7] = (__bf16)p;
             }
-        l_run = l_run * alpha + ls;
-        m_run = m_new;
-#pragma unroll
-        for (int T = 0; T < 4; ++T)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) o[T][r] *= alpha;
+        l_run += ls;
 
         // O^T += V^T P^T; key order of the B operand: kc*16 + 8*(e/4) + 4*hh + e%4
 #pragma unroll
@@ -326,9 +336,18 @@ __global__ __launch_bounds__(2 * BS) void k_attn_f32(AttnArgs a) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) mx = fmaxf(mx, st[t][r]);
         mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float m_new = fmaxf(m_run, mx);
-        const float alpha = fast_exp2((m_run - m_new) * sl);
-        const float mb = m_new * sl;
+        const bool grow = !(m_run * sl + kLazy >= mx * sl);
+        if (__ballot(grow)) {
+            const float m_new = grow ? fmaxf(m_run, mx) : m_run;
+            const float alpha = fast_exp2((m_run - m_new) * sl);
+            l_run *= alpha;
+#pragma unroll
+            for (int T = 0; T < 4; ++T)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) o[T][r] *= alpha;
+            m_run = m_new;
+        }
+        const float mb = m_run == -INFINITY ? 0.0f : m_run * sl;
         float ls = 0.0f;
 #pragma unroll
         for (int t = 0; t < 2; ++t)
@@ -337,12 +356,7 @@ __global__ __launch_bounds__(2 * BS) void k_attn_f32(AttnArgs a) {
                 st[t][r] = fast_exp2(__builtin_fmaf(st[t][r], sl, -mb));
                 ls += st[t][r];
             }
-        l_run = l_run * alpha + ls;
-        m_run = m_new;
-#pragma unroll
-        for (int T = 0; T < 4; ++T)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) o[T][r] *= alpha;
+        l_run += ls;
 #pragma unroll
         for (int T = 0; T < 4; ++T) {
             const float* vr = &Vs[(32 * T + l32) * VP + 4 * hh];
