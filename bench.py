@@ -211,8 +211,7 @@ def main() -> int:
     traffic = read_traffic(cfg.name)
     roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
             "frac": round(achieved / peak, 4), "traffic": traffic,
-            "kernel": "k_attn_bf16<128>" if cfg.dtype == "bf16" and cfg.block == 128 else
-                      f"k_attn_{cfg.dtype}<{cfg.block}>",
+            "kernel": f"fp::k_attn_{'bf16' if cfg.dtype == 'bf16' else 'f32'}<{cfg.block}, true>",
             "algorithmic_flop_per_launch": sparse_flop, "avg_kernel_ms": round(kern_avg_ms, 4),
             "launches": kern_n}
     cpu = None

@@ -173,7 +173,6 @@ fp_status attend_common(const void* q, const void* k, const void* v, void* o, fp
     if (plan) {
         a.lists = plan->dev.lists;
         a.counts = plan->dev.counts;
-        a.order = plan->dev.order;
     }
     EvPair ev{};
     bool prof;
@@ -293,7 +292,6 @@ fp_status fp_prefill_plan(const void* q, const void* k, fp_dtype dtype, int B, i
     PALLOC(P.diagB, (size_t)BH * nb);
     PALLOC(P.lists, (size_t)BH * P.tri);
     PALLOC(P.counts, (size_t)BH * nb);
-    PALLOC(P.order, (size_t)BH * nb);
     PALLOC(P.total_blocks, (size_t)1);
 #undef PALLOC
 
@@ -304,20 +302,18 @@ fp_status fp_prefill_plan(const void* q, const void* k, fp_dtype dtype, int B, i
     a.G = G;
     a.canon = make_canon(d);
     const int nchunks = (N + 255) / 256;
-    void *s2 = nullptr, *pmax = nullptr, *rz = nullptr, *ord = nullptr;
+    void *s2 = nullptr, *pmax = nullptr, *rz = nullptr;
     hipStream_t st = p->stream;
     he = hipMallocAsync(&s2, (size_t)BH * block * N * sizeof(float), st);
     if (he == hipSuccess) he = hipMallocAsync(&pmax, (size_t)BH * nchunks * block * sizeof(float), st);
     if (he == hipSuccess) he = hipMallocAsync(&rz, (size_t)BH * block * sizeof(float), st);
-    if (he == hipSuccess) he = hipMallocAsync(&ord, (size_t)2 * (nb + 1) * sizeof(int), st);
     if (he == hipSuccess) {
-        a.s2 = (float*)s2; a.pmax = (float*)pmax; a.rz = (float*)rz; a.ord_tmp = (int*)ord;
+        a.s2 = (float*)s2; a.pmax = (float*)pmax; a.rz = (float*)rz;
         he = launch_plan(a, P, st);
     }
     if (s2) (void)hipFreeAsync(s2, st);
     if (pmax) (void)hipFreeAsync(pmax, st);
     if (rz) (void)hipFreeAsync(rz, st);
-    if (ord) (void)hipFreeAsync(ord, st);
     if (he != hipSuccess) {
         free_plan(p);
         return hip_fail(he, "planning");

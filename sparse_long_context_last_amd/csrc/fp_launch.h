@@ -51,7 +51,6 @@ struct PlanDev {
     unsigned char* diagB;        // [BH][nb]
     int* lists;                  // [BH][tri]  row r's list at offset r (r + 1) / 2
     int* counts;                 // [BH][nb]
-    int* order;                  // [BH nb] rows, longest list first
     unsigned long long* total_blocks;  // [1]
 };
 
@@ -67,7 +66,6 @@ struct PlanArgs {
     float* s2;        // [BH][BS][N] transient
     float* pmax;      // [BH][ceil(N/256)][BS] transient
     float* rz;        // [BH][BS] transient
-    int* ord_tmp;     // [2 (nb + 1)] transient
 };
 
 struct AttnArgs {
@@ -79,7 +77,6 @@ struct AttnArgs {
     int B, Hq, Hkv, N, BS, nb;
     const int* lists;    // nullptr: dense causal
     const int* counts;
-    const int* order;    // nullptr: natural order
     long long tri;
     float scale_log2;    // log2(e) / sqrt(d)
 };

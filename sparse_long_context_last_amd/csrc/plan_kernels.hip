@@ -676,30 +676,6 @@ __global__ __launch_bounds__(256) void k_lists(PlanDev P, const SelState* __rest
     }
 }
 
-// ---------------------------------------------------------------------------
-// Attention work order: rows sorted by selected-block count, longest first
-// (counting sort; order among equal counts is arbitrary).
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_order_hist(PlanDev P, int* __restrict__ hist, int rows) {
-    const int r = blockIdx.x * 256 + threadIdx.x;
-    if (r < rows) atomicAdd(&hist[P.counts[r]], 1);
-}
-
-__global__ __launch_bounds__(256) void k_order_scan(int* __restrict__ hist, int* __restrict__ start, int nb) {
-    if (threadIdx.x == 0 && blockIdx.x == 0) {
-        int acc = 0;
-        for (int c = nb; c >= 0; --c) {
-            start[c] = acc;
-            acc += hist[c];
-        }
-    }
-}
-
-__global__ __launch_bounds__(256) void k_order_scatter(PlanDev P, int* __restrict__ start, int rows) {
-    const int r = blockIdx.x * 256 + threadIdx.x;
-    if (r < rows) P.order[atomicAdd(&start[P.counts[r]], 1)] = r;
-}
-
 __global__ __launch_bounds__(256) void k_fill_u32(unsigned int* __restrict__ p, unsigned int v, long long n) {
     for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < n; i += (long long)gridDim.x * 256) p[i] = v;
 }
@@ -776,12 +752,6 @@ hipError_t launch_plan(const PlanArgs& a, PlanDev& P, hipStream_t st) {
     // K7
     hipLaunchKernelGGL(k_fill_u32, dim3(1), dim3(256), 0, st, (unsigned int*)P.total_blocks, 0u, 2LL);
     hipLaunchKernelGGL(k_lists, dim3((nb + 3) / 4, BH), dim3(256), 0, st, P, P.sel);
-    const int rows = BH * nb;
-    hipLaunchKernelGGL(k_fill_u32, dim3(grid1(2 * (nb + 1))), dim3(256), 0, st, (unsigned int*)a.ord_tmp, 0u,
-                       (long long)2 * (nb + 1));
-    hipLaunchKernelGGL(k_order_hist, dim3(grid1(rows)), dim3(256), 0, st, P, a.ord_tmp, rows);
-    hipLaunchKernelGGL(k_order_scan, dim3(1), dim3(64), 0, st, a.ord_tmp, a.ord_tmp + (nb + 1), nb);
-    hipLaunchKernelGGL(k_order_scatter, dim3(grid1(rows)), dim3(256), 0, st, P, a.ord_tmp + (nb + 1), rows);
     return hipGetLastError();
 }
 
