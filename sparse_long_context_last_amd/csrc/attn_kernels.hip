@@ -56,21 +56,25 @@ __device__ __forceinline__ RowId work_row(const AttnArgs& a, int item) {
 // ---------------------------------------------------------------------------
 template <int BS, bool SPARSE>
 __global__ __launch_bounds__(2 * BS, BS == 128 ? 2 : 1) void k_attn_bf16(AttnArgs a) {
-    constexpr int D = kHeadDim, KT = kKT, NT = 2 * BS, SPB = BS / KT;
-    constexpr int KP = D + 8;     // K tile row pitch (elements): 272 B
-    constexpr int VP = KT + 8;    // V^T tile row pitch (elements): 144 B
-    constexpr int KCH = KT * D / 8 / NT;   // 16-byte chunks per thread (K)
-    constexpr int VCH = D * KT / 8 / NT;   // 16-byte chunks per thread (V^T)
-    __shared__ __attribute__((aligned(16))) bf16_t Ks[2][KT * KP];
-    __shared__ __attribute__((aligned(16))) bf16_t Vs[2][D * VP];
+    constexpr int D = kHeadDim, KT = kKT, NW = BS / 32, SPB = BS / KT;
+    constexpr int TILE = KT * D * 2;            // bytes of one K (or V^T) tile
+    constexpr int LOADS = TILE / 1024 / NW;     // 1 KB direct loads per wave per tile
+    // Tiles are unpadded and XOR-swizzled at 16-byte granularity:
+    //   K   [64 keys][256 B]: chunk c of row r at chunk c ^ (r & 15)
+    //   V^T [128 dv][128 B]:  chunk c of row r at chunk c ^ gray(r) & 7
+    // so that the MFMA fragment reads below hit distinct banks.
+    __shared__ __attribute__((aligned(1024))) unsigned char Ks[2][TILE];
+    __shared__ __attribute__((aligned(1024))) unsigned char Vs[2][TILE];
 
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index (uniform)
     const int l32 = lane & 31, hh = lane >> 5;
     const RowId rid = work_row(a, blockIdx.x);
     const int bh = rid.bh, qb = rid.qb;
     const size_t kvbh = rid.kvbh;
-    const bf16_t* K = (const bf16_t*)a.k + kvbh * a.N * D;
-    const bf16_t* VT = (const bf16_t*)a.vt + kvbh * (size_t)D * a.N;
+    const unsigned char* K = (const unsigned char*)a.k + kvbh * a.N * D * 2;
+    const unsigned char* VT = (const unsigned char*)a.vt + kvbh * (size_t)D * a.N * 2;
+    const size_t vrow = (size_t)a.N * 2;        // bytes per V^T row
 
     int cnt;
     const int* lst = nullptr;
@@ -99,41 +103,44 @@ __global__ __launch_bounds__(2 * BS, BS == 128 ? 2 : 1) void k_attn_bf16(AttnArg
     float m_run = -INFINITY, l_run = 0.0f;
     const float sl = a.scale_log2;
 
-    u32x4_t kreg[KCH], vreg[VCH];
-#define FP_FETCH_BF16(s_)                                                                            \
-    {                                                                                                \
-        const int kb_ = SPARSE ? lst[(s_) / SPB] : (s_) / SPB;                                          \
-        const int key0_ = kb_ * BS + ((s_) % SPB) * KT;                                              \
-        _Pragma("unroll") for (int r = 0; r < KCH; ++r) {                                            \
-            const int e = tid + NT * r, key = e >> 4, d8 = e & 15;                                   \
-            kreg[r] = *reinterpret_cast<const u32x4_t*>(K + (size_t)(key0_ + key) * D + 8 * d8);       \
-        }                                                                                            \
-        _Pragma("unroll") for (int r = 0; r < VCH; ++r) {                                            \
-            const int e = tid + NT * r, dv = e >> 3, k8 = e & 7;                                     \
-            vreg[r] = *reinterpret_cast<const u32x4_t*>(VT + (size_t)dv * a.N + key0_ + 8 * k8);       \
-        }                                                                                            \
+    // Per-lane source offsets of the direct loads (independent of the stage).
+    // K load j of wave w covers rows 4J..4J+3 (J = w + NW j); lane -> row 4J + lane/16,
+    // stored chunk lane%16 holds logical chunk (lane%16) ^ (row & 15).
+    // V^T load j covers rows 8J..8J+7; lane -> row 8J + lane/8, stored chunk lane%8
+    // holds logical chunk (lane%8) ^ gray(row) & 7.
+    unsigned koff[LOADS], voff[LOADS];
+#pragma unroll
+    for (int j = 0; j < LOADS; ++j) {
+        const int J = w + NW * j;
+        const int kr = 4 * J + (lane >> 4);
+        koff[j] = (unsigned)(kr * D * 2 + 16 * ((lane & 15) ^ (kr & 15)));
+        const int vr = 8 * J + (lane >> 3);
+        voff[j] = (unsigned)((size_t)vr * vrow + 16 * ((lane & 7) ^ ((vr ^ (vr >> 1)) & 7)));
     }
-#define FP_STASH_BF16(buf_)                                                                          \
-    {                                                                                                \
-        _Pragma("unroll") for (int r = 0; r < KCH; ++r) {                                            \
-            const int e = tid + NT * r, key = e >> 4, d8 = e & 15;                                   \
-            *reinterpret_cast<u32x4_t*>(&Ks[(buf_)][key * KP + 8 * d8]) = kreg[r];                     \
-        }                                                                                            \
-        _Pragma("unroll") for (int r = 0; r < VCH; ++r) {                                            \
-            const int e = tid + NT * r, dv = e >> 3, k8 = e & 7;                                     \
-            *reinterpret_cast<u32x4_t*>(&Vs[(buf_)][dv * VP + 8 * k8]) = vreg[r];                      \
-        }                                                                                            \
+#define FP_FETCH_BF16(s_, buf_)                                                                          \
+    {                                                                                                    \
+        const int kb_ = SPARSE ? lst[(s_) / SPB] : (s_) / SPB;                                          \
+        const int key0_ = kb_ * BS + ((s_) % SPB) * KT;                                                 \
+        const unsigned char* kg_ = K + (size_t)key0_ * D * 2;                                           \
+        const unsigned char* vg_ = VT + (size_t)key0_ * 2;                                              \
+        _Pragma("unroll") for (int j = 0; j < LOADS; ++j) {                                             \
+            const int J = w + NW * j;                                                                   \
+            __builtin_amdgcn_global_load_lds((const void*)(kg_ + koff[j]),                              \
+                (__attribute__((address_space(3))) void*)(&Ks[(buf_)][J * 1024]), 16, 0, 0);           \
+            __builtin_amdgcn_global_load_lds((const void*)(vg_ + voff[j]),                              \
+                (__attribute__((address_space(3))) void*)(&Vs[(buf_)][J * 1024]), 16, 0, 0);           \
+        }                                                                                                \
     }
 
-    FP_FETCH_BF16(0);
-    FP_STASH_BF16(0);
+    FP_FETCH_BF16(0, 0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
 
     for (int s = 0; s < nsub; ++s) {
         const int buf = s & 1;
         const int kb = SPARSE ? lst[s / SPB] : s / SPB;
         const int sub = s % SPB;
-        if (s + 1 < nsub) FP_FETCH_BF16(s + 1);
+        if (s + 1 < nsub) FP_FETCH_BF16(s + 1, buf ^ 1);
 
         // S^T tile: keys (rows) x queries (cols)
         f32x16_t st[2];
@@ -141,10 +148,11 @@ __global__ __launch_bounds__(2 * BS, BS == 128 ? 2 : 1) void k_attn_bf16(AttnArg
         for (int t = 0; t < 2; ++t) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) st[t][r] = 0.0f;
-            const bf16_t* kr = &Ks[buf][(32 * t + l32) * KP + 8 * hh];
+            const int row = 32 * t + l32;
+            const unsigned char* kr = &Ks[buf][row * D * 2];
 #pragma unroll
             for (int c = 0; c < 8; ++c) {
-                const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(kr + 16 * c);
+                const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(kr + 16 * ((2 * c + hh) ^ (row & 15)));
                 st[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[c], st[t], 0, 0, 0);
             }
         }
@@ -194,23 +202,24 @@ __global__ __launch_bounds__(2 * BS, BS == 128 ? 2 : 1) void k_attn_bf16(AttnArg
             }
         l_run += ls;
 
-        // O^T += V^T P^T; key order of the B operand: kc*16 + 8*(e/4) + 4*hh + e%4
+        // O^T += V^T P^T; key order of the B operand: kc*16 + 8*(e/4) + 4*hh + e%4.
+        // V^T rows store each 16-key chunk as key groups [0-3, 8-11, 4-7, 12-15],
+        // so those 8 keys are one contiguous 16-byte chunk (logical chunk 2kc + hh).
 #pragma unroll
         for (int T = 0; T < 4; ++T) {
-            const bf16_t* vr = &Vs[buf][(32 * T + l32) * VP + 4 * hh];
+            const int row = 32 * T + l32;
+            const int g = (row ^ (row >> 1)) & 7;
+            const unsigned char* vr = &Vs[buf][row * KT * 2];
 #pragma unroll
             for (int kc = 0; kc < 4; ++kc) {
-                const bf16x4_t lo = *reinterpret_cast<const bf16x4_t*>(vr + 16 * kc);
-                const bf16x4_t hi = *reinterpret_cast<const bf16x4_t*>(vr + 16 * kc + 8);
-                const bf16x8_t vf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+                const bf16x8_t vf = *reinterpret_cast<const bf16x8_t*>(vr + 16 * ((2 * kc + hh) ^ g));
                 o[T] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[kc], o[T], 0, 0, 0);
             }
         }
-        if (s + 1 < nsub) FP_STASH_BF16(buf ^ 1);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
     }
 #undef FP_FETCH_BF16
-#undef FP_STASH_BF16
 
     const float l_tot = l_run + __shfl_xor(l_run, 32);
     const float inv = 1.0f / l_tot;
@@ -406,9 +415,11 @@ __global__ __launch_bounds__(2 * BS) void k_attn_f32(AttnArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// V [heads][N][d] -> V^T [heads][d][N], 64-key tiles through LDS.
+// V [heads][N][d] -> V^T [heads][d][N], 64-key tiles through LDS.  With
+// PERMUTE, key n of every 16-key chunk is stored at position
+// (n & ~12) | ((n & 4) << 1) | ((n & 8) >> 1): key groups [0-3, 8-11, 4-7, 12-15].
 // ---------------------------------------------------------------------------
-template <typename T>
+template <typename T, bool PERMUTE>
 __global__ __launch_bounds__(256) void k_transpose_v(const T* __restrict__ v, T* __restrict__ vt, int N) {
     constexpr int D = kHeadDim, TK = 64;
     __shared__ T tile[TK][D + 2];
@@ -421,17 +432,18 @@ __global__ __launch_bounds__(256) void k_transpose_v(const T* __restrict__ v, T*
     __syncthreads();
     T* dst = vt + (size_t)head * D * N + n0;
     for (int e = tid; e < TK * D; e += 256) {
-        const int dd = e / TK, n = e % TK;
-        dst[(size_t)dd * N + n] = tile[n][dd];
+        const int dd = e / TK, p = e % TK;
+        const int n = PERMUTE ? ((p & ~12) | ((p & 4) << 1) | ((p & 8) >> 1)) : p;
+        dst[(size_t)dd * N + p] = tile[n][dd];
     }
 }
 
 hipError_t launch_transpose_v(const void* v, void* vt, int dtype_bf16, int heads, int N, hipStream_t st) {
     const dim3 g(N / 64, heads);
     if (dtype_bf16)
-        hipLaunchKernelGGL(k_transpose_v<bf16_t>, g, dim3(256), 0, st, (const bf16_t*)v, (bf16_t*)vt, N);
+        hipLaunchKernelGGL((k_transpose_v<bf16_t, true>), g, dim3(256), 0, st, (const bf16_t*)v, (bf16_t*)vt, N);
     else
-        hipLaunchKernelGGL(k_transpose_v<float>, g, dim3(256), 0, st, (const float*)v, (float*)vt, N);
+        hipLaunchKernelGGL((k_transpose_v<float, false>), g, dim3(256), 0, st, (const float*)v, (float*)vt, N);
     return hipGetLastError();
 }
 
