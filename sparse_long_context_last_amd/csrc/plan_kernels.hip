@@ -113,17 +113,53 @@ __device__ __forceinline__ float wave_max(float v) {
 
 // ---------------------------------------------------------------------------
 // K1: block means ("block-pooled" queries and keys)
-// grid (nb, heads), block d threads; out[head][kb][t] = (sum_r x[kb*bs + r][t]) / bs
+// out[head][kb][t] = (sum_r x[kb*bs + r][t], r ascending) * (1/bs).
+// 256 threads = 16 key blocks x 16 column groups of 8; each thread keeps 8
+// sequential sums and reads 16-byte (bf16) / 32-byte (fp32) row pieces.
+// grid (ceil(nb / 16), heads).
 // ---------------------------------------------------------------------------
 template <typename T>
-__global__ __launch_bounds__(128) void k_pool(const T* __restrict__ x, float* __restrict__ out,
+__device__ __forceinline__ void load8_f32(const T* p, float* v);
+template <> __device__ __forceinline__ void load8_f32<bf16_t>(const bf16_t* p, float* v) {
+    const uint4 w = *reinterpret_cast<const uint4*>(p);
+    const unsigned int ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        v[2 * e] = __uint_as_float(ws[e] << 16);
+        v[2 * e + 1] = __uint_as_float(ws[e] & 0xFFFF0000u);
+    }
+}
+template <> __device__ __forceinline__ void load8_f32<float>(const float* p, float* v) {
+    const float4 a = reinterpret_cast<const float4*>(p)[0];
+    const float4 b = reinterpret_cast<const float4*>(p)[1];
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void k_pool(const T* __restrict__ x, float* __restrict__ out,
                                               int N, int bs, float inv_bs) {
-    const int kb = blockIdx.x, head = blockIdx.y, t = threadIdx.x;
+    const int tid = threadIdx.x, cg = tid & 15;
+    const int kb = blockIdx.x * 16 + (tid >> 4), head = blockIdx.y;
     const int nb = N / bs;
-    const T* src = x + ((size_t)head * N + (size_t)kb * bs) * kHeadDim + t;
-    float acc = 0.0f;
-    for (int r = 0; r < bs; ++r) acc = acc + load_f32(src + (size_t)r * kHeadDim);
-    out[((size_t)head * nb + kb) * kHeadDim + t] = acc * inv_bs;
+    if (kb >= nb) return;
+    const T* src = x + ((size_t)head * N + (size_t)kb * bs) * kHeadDim + 8 * cg;
+    float acc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
+#pragma unroll 8
+    for (int r = 0; r < bs; ++r) {
+        float v[8];
+        load8_f32<T>(src + (size_t)r * kHeadDim, v);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] = acc[e] + v[e];
+    }
+    float* dst = out + ((size_t)head * nb + kb) * kHeadDim + 8 * cg;
+    float4 lo, hi;
+    lo.x = acc[0] * inv_bs; lo.y = acc[1] * inv_bs; lo.z = acc[2] * inv_bs; lo.w = acc[3] * inv_bs;
+    hi.x = acc[4] * inv_bs; hi.y = acc[5] * inv_bs; hi.z = acc[6] * inv_bs; hi.w = acc[7] * inv_bs;
+    reinterpret_cast<float4*>(dst)[0] = lo;
+    reinterpret_cast<float4*>(dst)[1] = hi;
 }
 
 // ---------------------------------------------------------------------------
@@ -225,16 +261,18 @@ __global__ __launch_bounds__(256) void k_scores(const T* __restrict__ q, const T
 // ---------------------------------------------------------------------------
 // K3a: per last-block row: M = max, e = exp2_c(s - M) (0 for j > pos), written
 // over s2; zpart[kb] = sum over the block's keys ascending; Z = sum of zpart
-// over kb ascending; rz = 1 / Z.  One workgroup per (bh, row).
+// over kb ascending; rz = 1 / Z.  One workgroup per (bh, row); the row is
+// walked in segments of 64 key blocks staged through LDS, where one thread
+// per key block forms its sequential sum.
 // ---------------------------------------------------------------------------
-constexpr int kSeg = 2048;
+constexpr int kSegBlocks = 64;
 
 template <int BS>
 __global__ __launch_bounds__(256) void k_rowexp(float* __restrict__ s2, const float* __restrict__ pmax,
                                                 float* __restrict__ rowmax, float* __restrict__ rowsum,
                                                 float* __restrict__ rz, int N, Canon K) {
-    constexpr int NSB = kSeg / BS;      // key blocks per segment
-    __shared__ float es[NSB][BS + 1];
+    constexpr int SEG = kSegBlocks * BS;
+    __shared__ float es[kSegBlocks][BS + 1];
     __shared__ float zp[kMaxBlocks];
     __shared__ float red[256];
     const int tid = threadIdx.x;
@@ -251,20 +289,24 @@ __global__ __launch_bounds__(256) void k_rowexp(float* __restrict__ s2, const fl
     }
     const float M = red[0];
     float* srow = s2 + ((size_t)bh * BS + row) * N;
-    for (int seg0 = 0; seg0 < N; seg0 += kSeg) {
-#pragma unroll
-        for (int u = 0; u < kSeg / 256; ++u) {
-            const int jl = u * 256 + tid;      // coalesced
+    for (int seg0 = 0; seg0 < N; seg0 += SEG) {
+#pragma unroll 4
+        for (int u = 0; u < SEG / 1024; ++u) {
+            const int jl = u * 1024 + 4 * tid;      // 4 consecutive keys, coalesced
             const int j = seg0 + jl;
             if (j < N) {
-                float e = 0.0f;
-                if (j <= pos) e = exp2_c(srow[j] - M, K);
-                srow[j] = e;
-                es[jl / BS][jl % BS] = e;
+                float4 v = *reinterpret_cast<const float4*>(srow + j);
+                v.x = j <= pos ? exp2_c(v.x - M, K) : 0.0f;
+                v.y = j + 1 <= pos ? exp2_c(v.y - M, K) : 0.0f;
+                v.z = j + 2 <= pos ? exp2_c(v.z - M, K) : 0.0f;
+                v.w = j + 3 <= pos ? exp2_c(v.w - M, K) : 0.0f;
+                *reinterpret_cast<float4*>(srow + j) = v;
+                float* e = &es[jl / BS][jl % BS];
+                e[0] = v.x; e[1] = v.y; e[2] = v.z; e[3] = v.w;
             }
         }
         __syncthreads();
-        if (tid < NSB && seg0 + tid * BS < N) {
+        if (tid < kSegBlocks && seg0 + tid * BS < N) {
             float z = 0.0f;
             for (int jj = 0; jj < BS; ++jj) z = z + es[tid][jj];
             zp[seg0 / BS + tid] = z;
@@ -342,55 +384,88 @@ __global__ __launch_bounds__(256) void k_atrue(const float* __restrict__ colsum,
 // K4: estimated block map  A[qb][kb] = softmax_{kb <= qb}(fp32(qbar_qb . kbar_kb) * C)
 // (products and sums rounded separately, t ascending; row max subtracted,
 // exp2_c, sum over kb ascending, rounded division).  Stored as the causal
-// triangle, row-major.  grid (nb, BH).
+// triangle, row-major.  A workgroup handles R consecutive query-block rows,
+// so every pooled key row it reads serves R dot products.
+// grid (ceil(nb / R), BH), dynamic LDS R * nb floats.
 // ---------------------------------------------------------------------------
+template <int R>
 __global__ __launch_bounds__(256) void k_estimate(const float* __restrict__ qbar, const float* __restrict__ kbar,
                                                   float* __restrict__ ahat, int nb, int Hq, int Hkv,
                                                   int group, Canon K) {
-    __shared__ float qs[kHeadDim];
-    __shared__ float sc[kMaxBlocks];
-    __shared__ float red[256];
-    __shared__ float Zsh;
-    const int tid = threadIdx.x, qb = blockIdx.x, bh = blockIdx.y;
+    extern __shared__ float sc[];              // [R][nb]
+    __shared__ __attribute__((aligned(16))) float qs[R][kHeadDim];
+    __shared__ float red[R][256];
+    __shared__ float Mr[R], Zr[R];
+    const int tid = threadIdx.x, bh = blockIdx.y;
+    const int q0 = blockIdx.x * R;
     const int b = bh / Hq, h = bh % Hq;
     const size_t kvbh = (size_t)b * Hkv + h / group;
-    if (tid < kHeadDim) qs[tid] = qbar[((size_t)bh * nb + qb) * kHeadDim + tid];
-    __syncthreads();
-    float mx = -INFINITY;
-    for (int kb = tid; kb <= qb; kb += 256) {
-        const float4* kr = reinterpret_cast<const float4*>(kbar + (kvbh * nb + kb) * kHeadDim);
-        float acc = 0.0f;
-#pragma unroll 8
-        for (int c = 0; c < kHeadDim / 4; ++c) {
-            float4 v = kr[c];
-            float p;
-            p = qs[4 * c] * v.x;     acc = acc + p;
-            p = qs[4 * c + 1] * v.y; acc = acc + p;
-            p = qs[4 * c + 2] * v.z; acc = acc + p;
-            p = qs[4 * c + 3] * v.w; acc = acc + p;
-        }
-        const float s = acc * K.C;
-        sc[kb] = s;
-        mx = fmaxf(mx, s);
+    for (int e = tid; e < R * kHeadDim; e += 256) {
+        const int r = e / kHeadDim, t = e % kHeadDim;
+        qs[r][t] = (q0 + r < nb) ? qbar[((size_t)bh * nb + q0 + r) * kHeadDim + t] : 0.0f;
     }
-    red[tid] = mx;
+    __syncthreads();
+    const int qlast = min(q0 + R - 1, nb - 1);
+    float mx[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) mx[r] = -INFINITY;
+    for (int kb = tid; kb <= qlast; kb += 256) {
+        const float4* kr = reinterpret_cast<const float4*>(kbar + (kvbh * nb + kb) * kHeadDim);
+        float acc[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) acc[r] = 0.0f;
+#pragma unroll 4
+        for (int c = 0; c < kHeadDim / 4; ++c) {
+            const float4 v = kr[c];
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const float4 qv = *reinterpret_cast<const float4*>(&qs[r][4 * c]);
+                float p;
+                p = qv.x * v.x; acc[r] = acc[r] + p;
+                p = qv.y * v.y; acc[r] = acc[r] + p;
+                p = qv.z * v.z; acc[r] = acc[r] + p;
+                p = qv.w * v.w; acc[r] = acc[r] + p;
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            if (kb <= q0 + r) {
+                const float s = acc[r] * K.C;
+                sc[r * nb + kb] = s;
+                mx[r] = fmaxf(mx[r], s);
+            }
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) red[r][tid] = mx[r];
     __syncthreads();
     for (int s = 128; s > 0; s >>= 1) {
-        if (tid < s) red[tid] = fmaxf(red[tid], red[tid + s]);
+        if (tid < s)
+#pragma unroll
+            for (int r = 0; r < R; ++r) red[r][tid] = fmaxf(red[r][tid], red[r][tid + s]);
         __syncthreads();
     }
-    const float M = red[0];
-    for (int kb = tid; kb <= qb; kb += 256) sc[kb] = exp2_c(sc[kb] - M, K);
+    if (tid < R) Mr[tid] = red[tid][0];
     __syncthreads();
-    if (tid == 0) {
+    for (int kb = tid; kb <= qlast; kb += 256)
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+            if (kb <= q0 + r) sc[r * nb + kb] = exp2_c(sc[r * nb + kb] - Mr[r], K);
+    __syncthreads();
+    if (tid < R && q0 + tid < nb) {
         float Z = 0.0f;
-        for (int kb = 0; kb <= qb; ++kb) Z = Z + sc[kb];
-        Zsh = Z;
+        for (int kb = 0; kb <= q0 + tid; ++kb) Z = Z + sc[tid * nb + kb];
+        Zr[tid] = Z;
     }
     __syncthreads();
     const long long tri = (long long)nb * (nb + 1) / 2;
-    float* out = ahat + (size_t)bh * tri + (size_t)qb * (qb + 1) / 2;
-    for (int kb = tid; kb <= qb; kb += 256) out[kb] = sc[kb] / Zsh;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int qb = q0 + r;
+        if (qb >= nb) break;
+        float* out = ahat + (size_t)bh * tri + (size_t)qb * (qb + 1) / 2;
+        for (int kb = tid; kb <= qb; kb += 256) out[kb] = sc[r * nb + kb] / Zr[r];
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -631,6 +706,8 @@ __device__ __forceinline__ bool member(const PlanDev& P, const SelState& s0, int
 }
 
 __global__ __launch_bounds__(256) void k_lists(PlanDev P, const SelState* __restrict__ st) {
+    // membership of each 64-block chunk of the row, one ballot per chunk
+    __shared__ unsigned long long masks[4][kMaxBlocks / 64];
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int bh = blockIdx.y, qb = blockIdx.x * 4 + wv;
     if (qb >= P.nb) return;
@@ -638,34 +715,39 @@ __global__ __launch_bounds__(256) void k_lists(PlanDev P, const SelState* __rest
     const SelState s0 = st[2 * bh];
     const long long toff = (long long)qb * (qb + 1) / 2;
     const float* arow = P.ahat + (size_t)bh * P.tri + toff;
+    const int nch = qb / 64 + 1;
+    unsigned long long* mk = masks[wv];
     int cnt = 0;
-    for (int base = 0; base <= qb; base += 64) {
-        const int kb = base + lane;
-        const bool m = kb <= qb && member(P, s0, bh, qb, kb, qa, arow, toff);
-        cnt += __popcll(__ballot(m));
+    for (int ch = 0; ch < nch; ++ch) {
+        const int kb = 64 * ch + lane;
+        const unsigned long long bal = __ballot(kb <= qb && member(P, s0, bh, qb, kb, qa, arow, toff));
+        if (lane == 0) mk[ch] = bal;
+        cnt += __popcll(bal);
     }
+    __builtin_amdgcn_wave_barrier();
+    // minimum budget: the `need` unselected blocks nearest the diagonal, i.e.
+    // every unselected kb >= cut
     const int want = min(qb + 1, P.floor_blocks);
     int need = want - cnt;
     int cut = qb + 1;
-    if (need > 0) {
-        for (int top = qb; top >= 0; top -= 64) {
-            const int kb = top - lane;
-            const bool un = kb >= 0 && !member(P, s0, bh, qb, kb, qa, arow, toff);
-            unsigned long long bal = __ballot(un);
-            const int c = __popcll(bal);
-            if (need <= c) {
-                for (int t = 1; t < need; ++t) bal &= bal - 1ull;
-                cut = top - (__ffsll((long long)bal) - 1);
-                break;
-            }
+    for (int ch = nch - 1; need > 0 && ch >= 0; --ch) {
+        const int valid = min(64, qb + 1 - 64 * ch);
+        const unsigned long long vmask = valid == 64 ? ~0ull : ((1ull << valid) - 1ull);
+        unsigned long long un = ~mk[ch] & vmask;
+        const int c = __popcll(un);
+        if (need <= c) {
+            for (int t = 1; t < need; ++t) un &= ~(1ull << (63 - __clzll((long long)un)));
+            cut = 64 * ch + (63 - __clzll((long long)un));
+            need = 0;
+        } else {
             need -= c;
         }
     }
     int* out = P.lists + (size_t)bh * P.tri + toff;
     int total = 0;
-    for (int base = 0; base <= qb; base += 64) {
-        const int kb = base + lane;
-        const bool f = kb <= qb && (kb >= cut || member(P, s0, bh, qb, kb, qa, arow, toff));
+    for (int ch = 0; ch < nch; ++ch) {
+        const int kb = 64 * ch + lane;
+        const bool f = kb <= qb && (kb >= cut || ((mk[ch] >> lane) & 1ull));
         const unsigned long long bal = __ballot(f);
         if (f) out[total + __popcll(bal & ((1ull << lane) - 1ull))] = kb;
         total += __popcll(bal);
@@ -704,12 +786,13 @@ hipError_t launch_plan(const PlanArgs& a, PlanDev& P, hipStream_t st) {
     const int bkv = a.B * a.Hkv;
     const float inv_bs = 1.0f / (float)BS;
     // K1
+    const unsigned pg = (unsigned)((nb + 15) / 16);
     if (a.dtype_bf16) {
-        hipLaunchKernelGGL(k_pool<bf16_t>, dim3(nb, BH), dim3(kHeadDim), 0, st, (const bf16_t*)a.q, P.qbar, N, BS, inv_bs);
-        hipLaunchKernelGGL(k_pool<bf16_t>, dim3(nb, bkv), dim3(kHeadDim), 0, st, (const bf16_t*)a.k, P.kbar, N, BS, inv_bs);
+        hipLaunchKernelGGL(k_pool<bf16_t>, dim3(pg, BH), dim3(256), 0, st, (const bf16_t*)a.q, P.qbar, N, BS, inv_bs);
+        hipLaunchKernelGGL(k_pool<bf16_t>, dim3(pg, bkv), dim3(256), 0, st, (const bf16_t*)a.k, P.kbar, N, BS, inv_bs);
     } else {
-        hipLaunchKernelGGL(k_pool<float>, dim3(nb, BH), dim3(kHeadDim), 0, st, (const float*)a.q, P.qbar, N, BS, inv_bs);
-        hipLaunchKernelGGL(k_pool<float>, dim3(nb, bkv), dim3(kHeadDim), 0, st, (const float*)a.k, P.kbar, N, BS, inv_bs);
+        hipLaunchKernelGGL(k_pool<float>, dim3(pg, BH), dim3(256), 0, st, (const float*)a.q, P.qbar, N, BS, inv_bs);
+        hipLaunchKernelGGL(k_pool<float>, dim3(pg, bkv), dim3(256), 0, st, (const float*)a.k, P.kbar, N, BS, inv_bs);
     }
     // K2
     const dim3 gs((N + kScoreTK - 1) / kScoreTK, BH);
@@ -731,7 +814,15 @@ hipError_t launch_plan(const PlanArgs& a, PlanDev& P, hipStream_t st) {
     hipLaunchKernelGGL(k_linesums, dim3(grid1(N), BH), dim3(256), 0, st, a.s2, a.rz, P.colsum, P.diagsum, N, BS);
     hipLaunchKernelGGL(k_atrue, dim3(BH), dim3(256), 0, st, P.colsum, P.atrue, N, BS);
     // K4, K5
-    hipLaunchKernelGGL(k_estimate, dim3(nb, BH), dim3(256), 0, st, P.qbar, P.kbar, P.ahat, nb, a.Hq, a.Hkv, group, a.canon);
+    if (nb <= 1024) {
+        const size_t lds = (size_t)8 * nb * sizeof(float);
+        hipLaunchKernelGGL(k_estimate<8>, dim3((nb + 7) / 8, BH), dim3(256), lds, st, P.qbar, P.kbar, P.ahat, nb,
+                           a.Hq, a.Hkv, group, a.canon);
+    } else {
+        const size_t lds = (size_t)2 * nb * sizeof(float);
+        hipLaunchKernelGGL(k_estimate<2>, dim3((nb + 1) / 2, BH), dim3(256), lds, st, P.qbar, P.kbar, P.ahat, nb,
+                           a.Hq, a.Hkv, group, a.canon);
+    }
     hipLaunchKernelGGL(k_jsd, dim3(BH), dim3(256), 0, st, P.ahat, P.atrue, P.djs, P.pattern, nb, a.tau, a.canon);
     // K6
     const int nlists = 2 * BH;
