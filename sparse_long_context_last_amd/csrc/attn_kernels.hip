@@ -142,6 +142,10 @@ __global__ __launch_bounds__(2 * BS, BS == 128 ? 2 : 1) void k_attn_bf16(AttnArg
         const int sub = s % SPB;
         if (s + 1 < nsub) FP_FETCH_BF16(s + 1, buf ^ 1);
 
+        // Wave priority is raised while this wave issues MFMAs, so the other
+        // resident wave on the SIMD fills the matrix unit's busy time with its
+        // softmax VALU work instead of competing for issue slots.
+        __builtin_amdgcn_s_setprio(1);
         // S^T tile: keys (rows) x queries (cols)
         f32x16_t st[2];
 #pragma unroll
@@ -156,6 +160,7 @@ __global__ __launch_bounds__(2 * BS, BS == 128 ? 2 : 1) void k_attn_bf16(AttnArg
                 st[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[c], st[t], 0, 0, 0);
             }
         }
+        __builtin_amdgcn_s_setprio(0);
         // causal mask inside the diagonal block
         if (kb == qb) {
 #pragma unroll
@@ -202,6 +207,7 @@ __global__ __launch_bounds__(2 * BS, BS == 128 ? 2 : 1) void k_attn_bf16(AttnArg
             }
         l_run += ls;
 
+        __builtin_amdgcn_s_setprio(1);
         // O^T += V^T P^T; key order of the B operand: kc*16 + 8*(e/4) + 4*hh + e%4.
         // V^T rows store each 16-key chunk as key groups [0-3, 8-11, 4-7, 12-15],
         // so those 8 keys are one contiguous 16-byte chunk (logical chunk 2kc + hh).
@@ -216,6 +222,7 @@ __global__ __launch_bounds__(2 * BS, BS == 128 ? 2 : 1) void k_attn_bf16(AttnArg
                 o[T] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[kc], o[T], 0, 0, 0);
             }
         }
+        __builtin_amdgcn_s_setprio(0);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
     }

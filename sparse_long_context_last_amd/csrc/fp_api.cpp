@@ -292,7 +292,7 @@ fp_status fp_prefill_plan(const void* q, const void* k, fp_dtype dtype, int B, i
     PALLOC(P.diagB, (size_t)BH * nb);
     PALLOC(P.lists, (size_t)BH * P.tri);
     PALLOC(P.counts, (size_t)BH * nb);
-    PALLOC(P.total_blocks, (size_t)1);
+    PALLOC(P.total_blocks, (size_t)BH);
 #undef PALLOC
 
     PlanArgs a{};
@@ -349,9 +349,12 @@ fp_status fp_plan_info_get(const fp_plan* plan, fp_plan_info* out) {
     I.dense_blocks = BH * plan->nb * (long long)(plan->nb + 1) / 2;
     if (BH > 0 && plan->N > 0) {
         FP_HIP(hipStreamSynchronize(plan->stream), "hipStreamSynchronize");
-        unsigned long long tot = 0;
-        FP_HIP(hipMemcpy(&tot, plan->dev.total_blocks, sizeof tot, hipMemcpyDeviceToHost), "hipMemcpy");
-        I.total_blocks = (long long)tot;
+        std::vector<unsigned long long> per_head((size_t)BH);
+        FP_HIP(hipMemcpy(per_head.data(), plan->dev.total_blocks, per_head.size() * sizeof(unsigned long long),
+                         hipMemcpyDeviceToHost), "hipMemcpy");
+        long long tot = 0;
+        for (unsigned long long x : per_head) tot += (long long)x;
+        I.total_blocks = tot;
         std::vector<unsigned char> pat((size_t)BH);
         FP_HIP(hipMemcpy(pat.data(), plan->dev.pattern, pat.size(), hipMemcpyDeviceToHost), "hipMemcpy");
         for (unsigned char c : pat) I.query_aware_heads += c == kPatternQueryAware;

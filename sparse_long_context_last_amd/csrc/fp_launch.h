@@ -51,7 +51,7 @@ struct PlanDev {
     unsigned char* diagB;        // [BH][nb]
     int* lists;                  // [BH][tri]  row r's list at offset r (r + 1) / 2
     int* counts;                 // [BH][nb]
-    unsigned long long* total_blocks;  // [1]
+    unsigned long long* total_blocks;  // [BH] selected blocks per head
 };
 
 // Inputs and transient workspace of one planning call.

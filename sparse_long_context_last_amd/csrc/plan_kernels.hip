@@ -754,7 +754,7 @@ __global__ __launch_bounds__(256) void k_lists(PlanDev P, const SelState* __rest
     }
     if (lane == 0) {
         P.counts[(size_t)bh * P.nb + qb] = total;
-        atomicAdd(P.total_blocks, (unsigned long long)total);
+        atomicAdd(&P.total_blocks[bh], (unsigned long long)total);
     }
 }
 
@@ -841,7 +841,8 @@ hipError_t launch_plan(const PlanArgs& a, PlanDev& P, hipStream_t st) {
         hipLaunchKernelGGL(k_vs_flags, dim3(nb, BH), dim3(BS), 0, st, P, P.sel);
     }
     // K7
-    hipLaunchKernelGGL(k_fill_u32, dim3(1), dim3(256), 0, st, (unsigned int*)P.total_blocks, 0u, 2LL);
+    hipLaunchKernelGGL(k_fill_u32, dim3(grid1(2LL * BH)), dim3(256), 0, st, (unsigned int*)P.total_blocks, 0u,
+                       2LL * BH);
     hipLaunchKernelGGL(k_lists, dim3((nb + 3) / 4, BH), dim3(256), 0, st, P, P.sel);
     return hipGetLastError();
 }
