@@ -259,8 +259,8 @@ __global__ __launch_bounds__(256) void k_scores(const T* __restrict__ q, const T
 }
 
 // ---------------------------------------------------------------------------
-// K3a: per last-block row: M = max, e = exp2_c(s - M) (0 for j > pos), written
-// over s2; zpart[kb] = sum over the block's keys ascending; Z = sum of zpart
+// K3a: per last-block row: M = max, e = exp2_c(s - M) (0 for j > pos);
+// zpart[kb] = sum over the block's keys ascending; Z = sum of zpart
 // over kb ascending; rz = 1 / Z.  One workgroup per (bh, row); the row is
 // walked in segments of 64 key blocks staged through LDS, where one thread
 // per key block forms its sequential sum.
@@ -268,7 +268,7 @@ __global__ __launch_bounds__(256) void k_scores(const T* __restrict__ q, const T
 constexpr int kSegBlocks = 64;
 
 template <int BS>
-__global__ __launch_bounds__(256) void k_rowexp(float* __restrict__ s2, const float* __restrict__ pmax,
+__global__ __launch_bounds__(256) void k_rowexp(const float* __restrict__ s2, const float* __restrict__ pmax,
                                                 float* __restrict__ rowmax, float* __restrict__ rowsum,
                                                 float* __restrict__ rz, int N, Canon K) {
     constexpr int SEG = kSegBlocks * BS;
@@ -288,7 +288,7 @@ __global__ __launch_bounds__(256) void k_rowexp(float* __restrict__ s2, const fl
         __syncthreads();
     }
     const float M = red[0];
-    float* srow = s2 + ((size_t)bh * BS + row) * N;
+    const float* srow = s2 + ((size_t)bh * BS + row) * N;
     for (int seg0 = 0; seg0 < N; seg0 += SEG) {
 #pragma unroll 4
         for (int u = 0; u < SEG / 1024; ++u) {
@@ -300,7 +300,6 @@ __global__ __launch_bounds__(256) void k_rowexp(float* __restrict__ s2, const fl
                 v.y = j + 1 <= pos ? exp2_c(v.y - M, K) : 0.0f;
                 v.z = j + 2 <= pos ? exp2_c(v.z - M, K) : 0.0f;
                 v.w = j + 3 <= pos ? exp2_c(v.w - M, K) : 0.0f;
-                *reinterpret_cast<float4*>(srow + j) = v;
                 float* e = &es[jl / BS][jl % BS];
                 e[0] = v.x; e[1] = v.y; e[2] = v.z; e[3] = v.w;
             }
@@ -324,35 +323,93 @@ __global__ __launch_bounds__(256) void k_rowexp(float* __restrict__ s2, const fl
 }
 
 // ---------------------------------------------------------------------------
-// K3b: line scores of the last block's probabilities p = e * rz:
-// colsum[j] = sum_i p[i][j]; diagsum[o] = sum_{i: pos_i >= o} p[i][pos_i - o];
-// i ascending.  grid (ceil(N/256), BH).
+// K3b: line scores of the last block's probabilities p = exp2_c(s - M) * rz
+// (0 for j > pos):
+//   colsum[j]  = sum_i p[i][j],                        i ascending;
+//   diagsum[o] = sum_{i: pos_i >= o} p[i][pos_i - o],  i ascending.
+// Workgroup x owns columns j0 .. j0+W-1 and the offsets o = N - BS - j0 - t,
+// t in [0, W): row i of such an offset reads column j0 + t + i, so one LDS
+// tile of W + BS columns per row serves both sums.  Rows are staged 16 at a
+// time; every thread keeps its sums in registers across the chunks.
+// Offsets above N - BS are done by k_diagtail.  grid (ceil(N / W), BH).
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_linesums(const float* __restrict__ e, const float* __restrict__ rz,
-                                                  float* __restrict__ colsum, float* __restrict__ diagsum,
-                                                  int N, int BS) {
-    __shared__ float srz[kMaxBlock];
+constexpr int kLineW = 512;
+constexpr int kLineRC = 16;
+
+template <int BS>
+__global__ __launch_bounds__(256) void k_linesums(const float* __restrict__ s2, const float* __restrict__ rowmax,
+                                                  const float* __restrict__ rz, float* __restrict__ colsum,
+                                                  float* __restrict__ diagsum, int N, Canon K) {
+    constexpr int W = kLineW, RC = kLineRC, TW = W + BS;
+    __shared__ __attribute__((aligned(16))) float es[RC][TW];
+    __shared__ float sM[BS], sR[BS];
     const int tid = threadIdx.x, bh = blockIdx.y;
-    if (tid < BS) srz[tid] = rz[(size_t)bh * BS + tid];
+    const int j0 = blockIdx.x * W;
+    if (tid < BS) {
+        sM[tid] = rowmax[(size_t)bh * BS + tid];
+        sR[tid] = rz[(size_t)bh * BS + tid];
+    }
+    float cacc[W / 256], gacc[W / 256];
+#pragma unroll
+    for (int q = 0; q < W / 256; ++q) cacc[q] = gacc[q] = 0.0f;
+    const float* S = s2 + (size_t)bh * BS * N;
     __syncthreads();
-    const int j = blockIdx.x * 256 + tid;
-    if (j >= N) return;
-    const float* E = e + (size_t)bh * BS * N;
-    float c = 0.0f;
-    for (int i = 0; i < BS; ++i) {
-        float p = E[(size_t)i * N + j] * srz[i];
-        c = c + p;
-    }
-    float g = 0.0f;
-    for (int i = 0; i < BS; ++i) {
-        const int pos = N - BS + i;
-        if (pos >= j) {
-            float p = E[(size_t)i * N + (pos - j)] * srz[i];
-            g = g + p;
+    for (int i0 = 0; i0 < BS; i0 += RC) {
+        for (int e4 = tid; e4 < RC * TW / 4; e4 += 256) {
+            const int ii = e4 / (TW / 4), cc = 4 * (e4 % (TW / 4));
+            const int i = i0 + ii, j = j0 + cc, pos = N - BS + i;
+            float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (j < N) v = *reinterpret_cast<const float4*>(S + (size_t)i * N + j);
+            const float M = sM[i];
+            float4 x;
+            x.x = j <= pos ? exp2_c(v.x - M, K) : 0.0f;
+            x.y = j + 1 <= pos ? exp2_c(v.y - M, K) : 0.0f;
+            x.z = j + 2 <= pos ? exp2_c(v.z - M, K) : 0.0f;
+            x.w = j + 3 <= pos ? exp2_c(v.w - M, K) : 0.0f;
+            *reinterpret_cast<float4*>(&es[ii][cc]) = x;
         }
+        __syncthreads();
+#pragma unroll 4
+        for (int ii = 0; ii < RC; ++ii) {
+            const int i = i0 + ii;
+            const float r = sR[i];
+#pragma unroll
+            for (int q = 0; q < W / 256; ++q) {
+                const int t = tid + 256 * q;
+                float p = es[ii][t] * r;
+                cacc[q] = cacc[q] + p;
+                p = es[ii][t + i] * r;
+                gacc[q] = gacc[q] + p;
+            }
+        }
+        __syncthreads();
     }
-    colsum[(size_t)bh * N + j] = c;
-    diagsum[(size_t)bh * N + j] = g;
+#pragma unroll
+    for (int q = 0; q < W / 256; ++q) {
+        const int t = tid + 256 * q;
+        const int j = j0 + t;
+        if (j < N) colsum[(size_t)bh * N + j] = cacc[q];
+        const int o = N - BS - j0 - t;
+        if (o >= 0) diagsum[(size_t)bh * N + o] = gacc[q];
+    }
+}
+
+// Offsets o = N - BS + 1 + t (t < BS - 1): only rows i > t reach them,
+// at column i - t - 1.  grid (BH), BS threads.
+template <int BS>
+__global__ __launch_bounds__(BS) void k_diagtail(const float* __restrict__ s2, const float* __restrict__ rowmax,
+                                                 const float* __restrict__ rz, float* __restrict__ diagsum,
+                                                 int N, Canon K) {
+    const int t = threadIdx.x, bh = blockIdx.x;
+    if (t >= BS - 1) return;
+    const float* S = s2 + (size_t)bh * BS * N;
+    float g = 0.0f;
+    for (int i = t + 1; i < BS; ++i) {
+        const float e = exp2_c(S[(size_t)i * N + (i - t - 1)] - rowmax[(size_t)bh * BS + i], K);
+        const float p = e * rz[(size_t)bh * BS + i];
+        g = g + p;
+    }
+    diagsum[(size_t)bh * N + (N - BS + 1 + t)] = g;
 }
 
 // ---------------------------------------------------------------------------
@@ -811,7 +868,14 @@ hipError_t launch_plan(const PlanArgs& a, PlanDev& P, hipStream_t st) {
         hipLaunchKernelGGL(k_rowexp<128>, dim3(BS, BH), dim3(256), 0, st, a.s2, a.pmax, P.rowmax, P.rowsum, a.rz, N, a.canon);
     else
         hipLaunchKernelGGL(k_rowexp<64>, dim3(BS, BH), dim3(256), 0, st, a.s2, a.pmax, P.rowmax, P.rowsum, a.rz, N, a.canon);
-    hipLaunchKernelGGL(k_linesums, dim3(grid1(N), BH), dim3(256), 0, st, a.s2, a.rz, P.colsum, P.diagsum, N, BS);
+    const dim3 gl((N + kLineW - 1) / kLineW, BH);
+    if (BS == 128) {
+        hipLaunchKernelGGL(k_linesums<128>, gl, dim3(256), 0, st, a.s2, P.rowmax, a.rz, P.colsum, P.diagsum, N, a.canon);
+        hipLaunchKernelGGL(k_diagtail<128>, dim3(BH), dim3(128), 0, st, a.s2, P.rowmax, a.rz, P.diagsum, N, a.canon);
+    } else {
+        hipLaunchKernelGGL(k_linesums<64>, gl, dim3(256), 0, st, a.s2, P.rowmax, a.rz, P.colsum, P.diagsum, N, a.canon);
+        hipLaunchKernelGGL(k_diagtail<64>, dim3(BH), dim3(64), 0, st, a.s2, P.rowmax, a.rz, P.diagsum, N, a.canon);
+    }
     hipLaunchKernelGGL(k_atrue, dim3(BH), dim3(256), 0, st, P.colsum, P.atrue, N, BS);
     // K4, K5
     if (nb <= 1024) {
