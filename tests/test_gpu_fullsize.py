@@ -77,3 +77,39 @@ def test_full_size_layer(F, name):
                 check_attention(outd[0, h, sl].float().cpu().numpy(), refd[r], cfg.dtype, f"dense h{h} row {r}")
     del q, k, v, out, outd, P
     torch.cuda.empty_cache()
+
+
+EDGE = {
+    # the largest supported row count, N / block = 4096 (block 64, N = 262144)
+    "max_blocks_262k_bs64": BY_NAME["glm9b_64k_bs64"].with_(Hq=2, Hkv=1, N=262144, explicit_types=("V", "QA")),
+    # just past the estimate kernel's 1024-block path (1025 blocks)
+    "blocks_1025_bs64": BY_NAME["glm9b_64k_bs64"].with_(Hq=2, Hkv=1, N=1025 * 64, explicit_types=("QA", "N")),
+}
+
+
+@pytest.mark.parametrize("name", list(EDGE))
+def test_size_limits(F, name):
+    cfg = EDGE[name]
+    gen = LayerGen(cfg)
+    q, k, v = gen.torch_layer("cuda")
+    P = F.plan(q, k, block=cfg.block, gamma=cfg.gamma, tau=cfg.tau, min_budget=cfg.min_budget)
+    out = F.attend(P, q, k, v)
+    torch.cuda.synchronize()
+    pattern, djs, _, _ = P.copy_out()
+    colsum, diagsum, ahat, atrue = (P.debug(x) for x in ("colsum", "diagsum", "ahat", "atrue"))
+    lists = P.lists()
+    rng = np.random.default_rng(5)
+    for h in range(cfg.Hq):
+        hp = O.plan_head(gen.q_head(0, h), gen.k_head(0, 0), cfg.block, cfg.gamma, cfg.tau, cfg.min_budget)
+        np.testing.assert_array_equal(colsum[h], hp.stats.c)
+        np.testing.assert_array_equal(diagsum[h], hp.stats.g)
+        np.testing.assert_array_equal(atrue[h], hp.stats.a_true)
+        np.testing.assert_array_equal(ahat[h], O.tri_values(hp.A))
+        assert djs[h] == hp.D and int(pattern[h]) == hp.pattern
+        for r in range(cfg.nb):
+            assert np.array_equal(lists[h][r], hp.lists[r]), (h, r)
+        rows = sorted(set([0, cfg.nb - 1] + rng.choice(cfg.nb, 2, replace=False).tolist()))
+        ref = O.attend_rows(gen.q_head(0, h), gen.k_head(0, 0), gen.v_head(0, 0), hp.mask, cfg.block, rows)
+        for r in rows:
+            sl = slice(r * cfg.block, (r + 1) * cfg.block)
+            check_attention(out[0, h, sl].float().cpu().numpy(), ref[r], cfg.dtype, f"{name} h{h} row {r}")
