@@ -26,6 +26,30 @@ typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kKT = 64;   // keys per LDS stage
 constexpr float kLazy = 8.0f;   // log2 growth of a row maximum that forces a rescale
+constexpr float kSumLimit = 65536.0f;   // per-lane probability sum that forces a new reference
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// p = exp2(s * sl - mb) for the 32 scores a lane holds, packed as bf16 in
+// the B-operand order of O^T += V^T P^T; returns the lane's sum of the
+// bf16-rounded values (the same values the numerator uses).
+__device__ __forceinline__ float exp_pack(const f32x16_t (&st)[2], float sl, float mb, bf16x8_t (&pf)[4]) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            pf[2 * t + (r >> 3)][r & 7] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(st[t][r], sl, -mb));
+    const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
+    float ls = 0.0f;
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) {
+        ls = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf[kc], pf[kc], 0, 1), ones, ls, false);
+        ls = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf[kc], pf[kc], 2, 3), ones, ls, false);
+        ls = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf[kc], pf[kc], 4, 5), ones, ls, false);
+        ls = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf[kc], pf[kc], 6, 7), ones, ls, false);
+    }
+    return ls;
+}
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -172,39 +196,38 @@ __global__ __launch_bounds__(2 * BS, BS == 128 ? 2 : 1) void k_attn_bf16(AttnArg
                 }
         }
         // online softmax (lane = one query; lane ^ 32 holds its other keys).
-        // The reference maximum only moves when the row maximum grows by more
-        // than 2^kLazy in the exp2 domain, so exp2 values stay <= 2^kLazy and
-        // the accumulators are rescaled only on those (rare) stages; the
+        // After a row's first stage the exp2 arguments use the reference
+        // maximum of earlier stages; as long as every lane's sum of the new
+        // probabilities stays <= kSumLimit (so each is <= kSumLimit) that
+        // reference is kept and no maximum is formed at all.  Otherwise (and
+        // on the first stage) the exact maximum becomes the reference, the
+        // accumulators are rescaled and the probabilities recomputed.  The
         // final division by the row sum makes the result independent of the
         // reference chosen.
-        float mx = -INFINITY;
+        bf16x8_t pf[4];
+        float ls = 0.0f;
+        bool exact = s == 0;
+        if (!exact) {
+            ls = exp_pack(st, sl, m_run * sl, pf);
+            exact = __ballot(!(ls <= kSumLimit)) != 0;
+        }
+        if (exact) {
+            float mx = -INFINITY;
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
+            for (int t = 0; t < 2; ++t)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, st[t][r]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const bool grow = !(m_run * sl + kLazy >= mx * sl);   // also true while m_run = -inf
-        if (__ballot(grow)) {
-            const float m_new = grow ? fmaxf(m_run, mx) : m_run;
-            const float alpha = fast_exp2((m_run - m_new) * sl);
+                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, st[t][r]);
+            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            const float m_new = fmaxf(m_run, mx);
+            const float alpha = fast_exp2((m_run - m_new) * sl);   // 0 while m_run = -inf
             l_run *= alpha;
 #pragma unroll
             for (int T = 0; T < 4; ++T)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) o[T][r] *= alpha;
             m_run = m_new;
+            ls = exp_pack(st, sl, m_run * sl, pf);
         }
-        const float mb = m_run == -INFINITY ? 0.0f : m_run * sl;
-        float ls = 0.0f;
-        bf16x8_t pf[4];
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const float p = fast_exp2(__builtin_fmaf(st[t][r], sl, -mb));
-                ls += p;
-                pf[2 * t + (r >> 3)][r & 7] = (__bf16)p;
-            }
         l_run += ls;
 
         __builtin_amdgcn_s_setprio(1);
