@@ -59,7 +59,7 @@ def read_traffic(workload: str):
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(cfg, total_blocks_by_head, sample_rows: int, budget_s: float):
+def cpu_baseline(cfg, total_blocks_by_head, sample_rows: int, budget_s: float, max_budget: int = 0):
     """The oracle as it stands on the host cores: one query head planned in
     full, float64 attention on a sample of that head's query blocks,
     extrapolated to the whole layer by head count and selected-block count."""
@@ -77,7 +77,7 @@ def cpu_baseline(cfg, total_blocks_by_head, sample_rows: int, budget_s: float):
     k = gen.k_head(0, h // cfg.group)
     v = gen.v_head(0, h // cfg.group)
     t0 = time.perf_counter()
-    hp = O.plan_head(q, k, cfg.block, cfg.gamma, cfg.tau, cfg.min_budget)
+    hp = O.plan_head(q, k, cfg.block, cfg.gamma, cfg.tau, cfg.min_budget, max_budget)
     t_plan = time.perf_counter() - t0
     rng = np.random.default_rng(7)
     rows = sorted(set([0, cfg.nb - 1] + rng.choice(cfg.nb, size=min(cfg.nb, sample_rows), replace=False).tolist()))
@@ -109,6 +109,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=24)
     ap.add_argument("--cpu-budget-s", type=float, default=15.0)
+    ap.add_argument("--max-budget", type=int, default=0,
+                    help="cap every query-block row at this many keys (0: uncapped)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -137,7 +139,8 @@ def main() -> int:
     stream = torch.cuda.current_stream()
 
     def step():
-        P = F.plan(q, k, block=cfg.block, gamma=cfg.gamma, tau=cfg.tau, min_budget=cfg.min_budget)
+        P = F.plan(q, k, block=cfg.block, gamma=cfg.gamma, tau=cfg.tau, min_budget=cfg.min_budget,
+                   max_budget=args.max_budget)
         F.attend(P, q, k, v, out=out)
         return P
 
@@ -154,7 +157,8 @@ def main() -> int:
     t_wall = time.perf_counter()
     for i in range(args.steps):
         ev[i][0].record(stream)
-        P = F.plan(q, k, block=cfg.block, gamma=cfg.gamma, tau=cfg.tau, min_budget=cfg.min_budget)
+        P = F.plan(q, k, block=cfg.block, gamma=cfg.gamma, tau=cfg.tau, min_budget=cfg.min_budget,
+                   max_budget=args.max_budget)
         ev[i][1].record(stream)
         F.attend(P, q, k, v, out=out)
         ev[i][2].record(stream)
@@ -217,7 +221,7 @@ def main() -> int:
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(cfg, blocks_by_head, args.cpu_rows, args.cpu_budget_s)
+        cpu = cpu_baseline(cfg, blocks_by_head, args.cpu_rows, args.cpu_budget_s, args.max_budget)
 
     rec = {
         "metric": METRIC,
@@ -234,7 +238,8 @@ def main() -> int:
         "data": "synthetic (seeded planted head types; no datasets or weights)",
         "config": {"workload": cfg.name, "B": cfg.B, "Hq": cfg.Hq, "Hkv": cfg.Hkv, "N": cfg.N,
                    "d": cfg.d, "block": cfg.block, "gamma": cfg.gamma, "tau": cfg.tau,
-                   "min_budget": cfg.min_budget, "parallelism": "single GPU"},
+                   "min_budget": cfg.min_budget, "max_budget": args.max_budget,
+                   "parallelism": "single GPU"},
         "plan_ms": round(plan_ms, 3),
         "attend_ms": round(attend_ms, 3),
         "attention_kernel_ms": round(kern_avg_ms, 3),

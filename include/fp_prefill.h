@@ -69,6 +69,7 @@ typedef struct fp_plan_info {
     long long total_blocks;            /* selected (query-block, key-block) pairs, all heads */
     long long dense_blocks;            /* B * Hq * nb (nb + 1) / 2 */
     int query_aware_heads;             /* heads whose pattern is query-aware */
+    int max_budget;                    /* tokens, 0 = uncapped */
 } fp_plan_info;
 
 /*
@@ -89,6 +90,24 @@ fp_status fp_prefill_plan(const void* q, const void* k, fp_dtype dtype,
                           int B, int Hq, int Hkv, int N, int d, int block,
                           float gamma, float tau, int min_budget,
                           void* stream, fp_plan** out);
+
+/*
+ * fp_prefill_plan_ex -- fp_prefill_plan with a maximum budget (ablation
+ *   table of the atlas.scime.ai summary page: the computational budget capped
+ *   at 8k or 32k tokens per row; uncapped is the method's default).  max_budget = 0: identical to fp_prefill_plan.
+ *   max_budget > 0: every query-block row keeps at most
+ *   ceil(max_budget / block) blocks -- after the minimum-budget fill, the
+ *   row's blocks with the largest score stay, where the score is the
+ *   estimated block attention for query-aware heads (and for gamma = 1) and
+ *   the selected column plus diagonal line mass through the block for
+ *   vertical-slash heads; ties keep the block nearer the diagonal.
+ *   FP_ERR_INVALID_ARG if max_budget < 0 or if it allows fewer blocks per
+ *   row than min_budget asks for.
+ */
+fp_status fp_prefill_plan_ex(const void* q, const void* k, fp_dtype dtype,
+                             int B, int Hq, int Hkv, int N, int d, int block,
+                             float gamma, float tau, int min_budget, int max_budget,
+                             void* stream, fp_plan** out);
 
 /*
  * fp_prefill_attend -- step 3: O = causal softmax(Q K^T / sqrt(d)) V with

@@ -43,7 +43,11 @@ the design notes of the repository):
     own total, and turned into blocks by the any-touch rule;
   * minimum budget = ceil(min_budget / block) blocks per query-block row
     (at least 1), filled nearest-first from the diagonal;
-  * gamma = 1 selects the whole causal triangle.
+  * gamma = 1 selects the whole causal triangle;
+  * an optional maximum budget caps every query-block row at
+    ceil(max_budget / block) blocks, keeping the blocks with the largest
+    estimate (query-aware) or selected line mass (vertical-slash), ties
+    to the block nearest the diagonal.
 
 Pins (tests in ``tests/test_oracle_*.py``): exp2_c / ln_c against libm
 within a few ulp; JSD against scipy and closed forms; canonical softmax
@@ -390,6 +394,55 @@ def apply_floor(mask: np.ndarray, min_budget: int, bs: int) -> np.ndarray:
     return mask
 
 
+def cap_blocks(max_budget: int, bs: int) -> int:
+    """Blocks per query-block row the maximum budget (tokens) allows; 0 means
+    uncapped (the pages' default, ablation table)."""
+    return 0 if max_budget <= 0 else -(-int(max_budget) // bs)
+
+
+def vs_block_scores(c: np.ndarray, g: np.ndarray, sel_cols: np.ndarray, sel_diags: np.ndarray,
+                    bs: int) -> np.ndarray:
+    """Line mass a vertical-slash selection carries through each block:
+    score(qb, kb) = colmass[kb] + diagmass[qb - kb], where colmass[kb] is the
+    sum of the selected column scores c[j] in key block kb and diagmass[a] the
+    sum of the selected diagonal scores g[o] whose offset touches block
+    diagonal a (o // bs == a, or o // bs == a - 1 with o % bs > 0).  Sums in
+    float32, ascending index."""
+    N = c.shape[0]
+    nb = N // bs
+    colmass = np.zeros(nb, dtype=F32)
+    diagmass = np.zeros(nb + 1, dtype=F32)
+    for j in np.nonzero(sel_cols)[0]:
+        colmass[j // bs] = colmass[j // bs] + c[j]
+    for o in np.nonzero(sel_diags)[0]:
+        a = o // bs
+        diagmass[a] = diagmass[a] + g[o]
+    for o in np.nonzero(sel_diags)[0]:
+        if o % bs > 0:
+            diagmass[o // bs + 1] = diagmass[o // bs + 1] + g[o]
+    qb = np.arange(nb)[:, None]
+    kb = np.arange(nb)[None, :]
+    return (colmass[kb] + diagmass[np.clip(qb - kb, 0, nb)]).astype(F32)
+
+
+def apply_cap(mask: np.ndarray, scores: np.ndarray, max_budget: int, bs: int) -> np.ndarray:
+    """Keep at most cap_blocks(max_budget) blocks per query-block row: the
+    row's blocks ordered by score descending, then key block descending
+    (nearest the diagonal first); the first `cap` of them stay."""
+    cap = cap_blocks(max_budget, bs)
+    if cap == 0:
+        return mask
+    mask = mask.copy()
+    for qb in range(mask.shape[0]):
+        kbs = np.nonzero(mask[qb, : qb + 1])[0]
+        if len(kbs) <= cap:
+            continue
+        order = sorted(kbs.tolist(), key=lambda kb: (-float(scores[qb, kb]), -kb))
+        mask[qb, :] = False
+        mask[qb, order[:cap]] = True
+    return mask
+
+
 # --------------------------------------------------------------------------
 # A whole head's plan.
 # --------------------------------------------------------------------------
@@ -419,9 +472,10 @@ class HeadPlan:
 
 
 def plan_head(q: np.ndarray, k: np.ndarray, bs: int, gamma: float, tau: float,
-              min_budget: int) -> HeadPlan:
+              min_budget: int, max_budget: int = 0) -> HeadPlan:
     """Pattern determination and index selection for one query head q [N, d]
-    against its key/value head's keys k [N, d]."""
+    against its key/value head's keys k [N, d]; max_budget > 0 caps every
+    query-block row (applied after the minimum-budget fill)."""
     q = np.asarray(q, dtype=F32)
     k = np.asarray(k, dtype=F32)
     N, d = q.shape
@@ -445,6 +499,12 @@ def plan_head(q: np.ndarray, k: np.ndarray, bs: int, gamma: float, tau: float,
         sel_s = select_cumulative(st.g, gamma)
         mask = vs_block_mask(sel_v, sel_s, bs)
     mask = apply_floor(mask, min_budget, bs)
+    if cap_blocks(max_budget, bs):
+        if pattern == QUERY_AWARE or sel_v is None:
+            scores = A
+        else:
+            scores = vs_block_scores(st.c, st.g, sel_v, sel_s, bs)
+        mask = apply_cap(mask, scores, max_budget, bs)
     lists = [np.nonzero(mask[qb, : qb + 1])[0].astype(np.int32) for qb in range(nb)]
     return HeadPlan(qbar, kbar, st, A, jsd, D, pattern, sel_qa, sel_v, sel_s, mask, lists)
 

@@ -125,8 +125,9 @@ class Plan:
 
 
 def plan(q, k, block: int = 128, gamma: float = 0.95, tau: float = 0.1,
-         min_budget: int = 1024, stream=None) -> Plan:
-    """Pattern determination and index selection (fp_prefill_plan)."""
+         min_budget: int = 1024, max_budget: int = 0, stream=None) -> Plan:
+    """Pattern determination and index selection (fp_prefill_plan_ex;
+    max_budget = 0 leaves rows uncapped)."""
     _check_tensor(q, "q")
     _check_tensor(k, "k")
     if q.dtype != k.dtype:
@@ -137,9 +138,9 @@ def plan(q, k, block: int = 128, gamma: float = 0.95, tau: float = 0.1,
         raise ValueError("k must be [B, Hkv, N, d] with q's B, N and d")
     dt = _dtype_code(q)
     h = C.c_void_p()
-    _lib.check(_lib.load().fp_prefill_plan(q.data_ptr(), k.data_ptr(), dt, B, Hq, Hkv, N, d, block,
-                                           float(gamma), float(tau), int(min_budget),
-                                           _stream_ptr(stream), C.byref(h)), "fp_prefill_plan")
+    _lib.check(_lib.load().fp_prefill_plan_ex(q.data_ptr(), k.data_ptr(), dt, B, Hq, Hkv, N, d, block,
+                                              float(gamma), float(tau), int(min_budget), int(max_budget),
+                                              _stream_ptr(stream), C.byref(h)), "fp_prefill_plan_ex")
     return Plan(h, (B, Hq, Hkv, N, d, block), dt, stream)
 
 

@@ -7,6 +7,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <algorithm>
 #include <mutex>
 #include <new>
 #include <vector>
@@ -20,7 +21,7 @@ struct fp_plan {
     int B, Hq, Hkv, N, d, bs, nb;
     fp_dtype dtype;
     float gamma, tau;
-    int min_budget;
+    int min_budget, max_budget;
     int device;
     hipStream_t stream;
     PlanDev dev;
@@ -228,6 +229,12 @@ fp_status fp_canonical_constants(int d, float* e2, double* lnc, double* ln2, dou
 
 fp_status fp_prefill_plan(const void* q, const void* k, fp_dtype dtype, int B, int Hq, int Hkv, int N, int d,
                           int block, float gamma, float tau, int min_budget, void* stream, fp_plan** out) {
+    return fp_prefill_plan_ex(q, k, dtype, B, Hq, Hkv, N, d, block, gamma, tau, min_budget, 0, stream, out);
+}
+
+fp_status fp_prefill_plan_ex(const void* q, const void* k, fp_dtype dtype, int B, int Hq, int Hkv, int N, int d,
+                             int block, float gamma, float tau, int min_budget, int max_budget, void* stream,
+                             fp_plan** out) {
     if (!out) return fail(FP_ERR_INVALID_ARG, "out is NULL");
     *out = nullptr;
     fp_status s = check_shape(dtype, B, Hq, Hkv, N, d, block);
@@ -235,6 +242,14 @@ fp_status fp_prefill_plan(const void* q, const void* k, fp_dtype dtype, int B, i
     if (!(gamma > 0.0f && gamma <= 1.0f)) return fail(FP_ERR_INVALID_ARG, "gamma %g outside (0, 1]", (double)gamma);
     if (!(tau >= 0.0f) || std::isinf(tau)) return fail(FP_ERR_INVALID_ARG, "tau %g must be finite and >= 0", (double)tau);
     if (min_budget < 0) return fail(FP_ERR_INVALID_ARG, "min_budget %d < 0", min_budget);
+    if (max_budget < 0) return fail(FP_ERR_INVALID_ARG, "max_budget %d < 0", max_budget);
+    {
+        const long long floor_b = std::max(1LL, ((long long)min_budget + block - 1) / block);
+        const long long cap_b = ((long long)max_budget + block - 1) / block;
+        if (max_budget > 0 && cap_b < floor_b)
+            return fail(FP_ERR_INVALID_ARG, "max_budget %d allows %lld blocks per row, min_budget needs %lld",
+                        max_budget, cap_b, floor_b);
+    }
     const bool empty = empty_problem(B, Hq, N);
     if (!empty && (!q || !k)) return fail(FP_ERR_INVALID_ARG, "q or k is NULL");
 
@@ -242,6 +257,7 @@ fp_status fp_prefill_plan(const void* q, const void* k, fp_dtype dtype, int B, i
     if (!p) return fail(FP_ERR_OOM, "host allocation failed");
     p->B = B; p->Hq = Hq; p->Hkv = Hkv; p->N = N; p->d = d; p->bs = block;
     p->nb = N / block; p->dtype = dtype; p->gamma = gamma; p->tau = tau; p->min_budget = min_budget;
+    p->max_budget = max_budget;
     p->stream = (hipStream_t)stream;
     if (empty) {
         p->device = -1;
@@ -266,6 +282,7 @@ fp_status fp_prefill_plan(const void* q, const void* k, fp_dtype dtype, int B, i
     P.mode_all = G >= (1ull << kGammaShift);
     P.floor_blocks = (min_budget + block - 1) / block;
     if (P.floor_blocks < 1) P.floor_blocks = 1;
+    P.cap_blocks = (int)(((long long)max_budget + block - 1) / block);
 
 #define PALLOC(ptr, n)                          \
     do {                                        \
@@ -290,6 +307,8 @@ fp_status fp_prefill_plan(const void* q, const void* k, fp_dtype dtype, int B, i
     PALLOC(P.colblk, (size_t)BH * nb);
     PALLOC(P.diagA, (size_t)BH * nb);
     PALLOC(P.diagB, (size_t)BH * nb);
+    PALLOC(P.colmass, P.cap_blocks > 0 ? (size_t)BH * nb : 0);
+    PALLOC(P.diagmass, P.cap_blocks > 0 ? (size_t)BH * nb : 0);
     PALLOC(P.lists, (size_t)BH * P.tri);
     PALLOC(P.counts, (size_t)BH * nb);
     PALLOC(P.total_blocks, (size_t)BH);
@@ -345,6 +364,7 @@ fp_status fp_plan_info_get(const fp_plan* plan, fp_plan_info* out) {
     I.B = plan->B; I.Hq = plan->Hq; I.Hkv = plan->Hkv; I.N = plan->N; I.d = plan->d;
     I.block = plan->bs; I.nb = plan->nb; I.dtype = plan->dtype; I.gamma = plan->gamma; I.tau = plan->tau;
     I.min_budget = plan->min_budget;
+    I.max_budget = plan->max_budget;
     const long long BH = (long long)plan->B * plan->Hq;
     I.dense_blocks = BH * plan->nb * (long long)(plan->nb + 1) / 2;
     if (BH > 0 && plan->N > 0) {

@@ -34,6 +34,7 @@ struct PlanDev {
     long long tri;               // nb (nb + 1) / 2
     int mode_all;                // gamma == 1: every causal block
     int floor_blocks;            // max(1, ceil(min_budget / BS))
+    int cap_blocks;              // ceil(max_budget / BS), 0 = uncapped
     unsigned char* pattern;      // [BH]
     double* djs;                 // [BH]
     float* qbar;                 // [BH][nb][d]
@@ -49,6 +50,8 @@ struct PlanDev {
     unsigned char* colblk;       // [BH][nb]
     unsigned char* diagA;        // [BH][nb]
     unsigned char* diagB;        // [BH][nb]
+    float* colmass;              // [BH][nb]  selected column mass per key block (cap only)
+    float* diagmass;             // [BH][nb]  selected diagonal mass per block diagonal (cap only)
     int* lists;                  // [BH][tri]  row r's list at offset r (r + 1) / 2
     int* counts;                 // [BH][nb]
     unsigned long long* total_blocks;  // [BH] selected blocks per head

@@ -725,6 +725,7 @@ __global__ __launch_bounds__(256) void k_sel_scan(SelState* __restrict__ st, uns
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(128) void k_vs_flags(PlanDev P, const SelState* __restrict__ st) {
     __shared__ int f[3];
+    __shared__ unsigned char selc_s[kMaxBlock], selg_s[kMaxBlock];
     const int kb = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
     if (P.mode_all || P.pattern[bh] == kPatternQueryAware) return;
     if (tid < 3) f[tid] = 0;
@@ -738,6 +739,8 @@ __global__ __launch_bounds__(128) void k_vs_flags(PlanDev P, const SelState* __r
     if (selc) f[0] = 1;
     if (selg) f[1] = 1;
     if (selg && tid > 0) f[2] = 1;
+    selc_s[tid] = selc;
+    selg_s[tid] = selg;
     __syncthreads();
     if (tid == 0) {
         const size_t o = (size_t)bh * P.nb + kb;
@@ -745,6 +748,37 @@ __global__ __launch_bounds__(128) void k_vs_flags(PlanDev P, const SelState* __r
         P.diagA[o] = (unsigned char)f[1];
         P.diagB[o] = (unsigned char)f[2];
     }
+    if (P.cap_blocks > 0 && tid == 0) {
+        // line mass for the per-row cap, float32 sums in ascending index:
+        // colmass[kb] = selected c[j] of this key block; diagmass[kb] starts
+        // with the selected g[o] of offsets in block kb (the terms with
+        // o % BS > 0 of block kb - 1 are added by k_diag_mass afterwards)
+        const float* cs = P.colsum + (size_t)bh * P.N + (size_t)kb * P.BS;
+        const float* gs = P.diagsum + (size_t)bh * P.N + (size_t)kb * P.BS;
+        float cm = 0.0f, dm = 0.0f;
+        for (int r = 0; r < P.BS; ++r) {
+            if (selc_s[r]) cm = cm + cs[r];
+            if (selg_s[r]) dm = dm + gs[r];
+        }
+        P.colmass[(size_t)bh * P.nb + kb] = cm;
+        P.diagmass[(size_t)bh * P.nb + kb] = dm;
+    }
+}
+
+// Second half of diagmass[a]: the selected offsets o of block a - 1 with
+// o % BS > 0, ascending, added after the first half.  grid (nb, BH).
+__global__ __launch_bounds__(64) void k_diag_mass(PlanDev P, const SelState* __restrict__ st) {
+    const int a = blockIdx.x, bh = blockIdx.y;
+    if (threadIdx.x != 0 || a == 0 || P.mode_all || P.pattern[bh] == kPatternQueryAware) return;
+    const SelState sg = st[2 * bh + 1];
+    const long long base = (long long)(a - 1) * P.BS;
+    const float* gs = P.diagsum + (size_t)bh * P.N;
+    float dm = P.diagmass[(size_t)bh * P.nb + a];
+    for (int r = 1; r < P.BS; ++r) {
+        const float x = gs[base + r];
+        if (sg.has && order_key(x, base + r, sg.ibits) <= sg.kstar) dm = dm + x;
+    }
+    P.diagmass[(size_t)bh * P.nb + a] = dm;
 }
 
 // ---------------------------------------------------------------------------
@@ -760,6 +794,18 @@ __device__ __forceinline__ bool member(const PlanDev& P, const SelState& s0, int
     const size_t base = (size_t)bh * P.nb;
     const int a = qb - kb;
     return P.colblk[base + kb] || P.diagA[base + a] || (a >= 1 && P.diagB[base + a - 1]);
+}
+
+// Score of block kb in row qb for the maximum-budget cap (>= 0).
+__device__ __forceinline__ float cap_score(const PlanDev& P, int bh, int qb, int kb, bool qa, const float* arow) {
+    if (qa || P.mode_all) return arow[kb];
+    const size_t base = (size_t)bh * P.nb;
+    return P.colmass[base + kb] + P.diagmass[base + (qb - kb)];
+}
+
+// Cap order: score descending, then key block descending (nearest the diagonal).
+__device__ __forceinline__ unsigned long long cap_key(float score, int kb) {
+    return ((unsigned long long)(0x7FFFFFFFu - __float_as_uint(score)) << 12) | (unsigned long long)(4095 - kb);
 }
 
 __global__ __launch_bounds__(256) void k_lists(PlanDev P, const SelState* __restrict__ st) {
@@ -800,18 +846,62 @@ __global__ __launch_bounds__(256) void k_lists(PlanDev P, const SelState* __rest
             need -= c;
         }
     }
-    int* out = P.lists + (size_t)bh * P.tri + toff;
+    // final membership: selected, or filled for the minimum budget
     int total = 0;
     for (int ch = 0; ch < nch; ++ch) {
+        const int valid = min(64, qb + 1 - 64 * ch);
+        const unsigned long long vmask = valid == 64 ? ~0ull : ((1ull << valid) - 1ull);
+        unsigned long long fill = 0ull;
+        if (cut <= 64 * ch + 63) fill = cut <= 64 * ch ? ~0ull : ~((1ull << (cut - 64 * ch)) - 1ull);
+        const unsigned long long m = (mk[ch] | fill) & vmask;
+        if (lane == 0) mk[ch] = m;
+        total += __popcll(m);
+    }
+    __builtin_amdgcn_wave_barrier();
+    // maximum budget: keep the cap_blocks members with the smallest cap keys
+    if (P.cap_blocks > 0 && total > P.cap_blocks) {
+        unsigned long long prefix = 0ull;
+        int rem = P.cap_blocks;
+        for (int b = 42; b >= 0; --b) {
+            int c0 = 0;
+            for (int ch = 0; ch < nch; ++ch) {
+                const int kb = 64 * ch + lane;
+                bool in = false;
+                if ((mk[ch] >> lane) & 1ull) {
+                    const unsigned long long key = cap_key(cap_score(P, bh, qb, kb, qa, arow), kb);
+                    in = (key >> (b + 1)) == (prefix >> (b + 1)) && !((key >> b) & 1ull);
+                }
+                c0 += __popcll(__ballot(in));
+            }
+            if (rem > c0) {
+                rem -= c0;
+                prefix |= 1ull << b;
+            }
+        }
+        // prefix is now the key of the cap_blocks-th kept block
+        total = 0;
+        for (int ch = 0; ch < nch; ++ch) {
+            const int kb = 64 * ch + lane;
+            bool keep = false;
+            if ((mk[ch] >> lane) & 1ull) keep = cap_key(cap_score(P, bh, qb, kb, qa, arow), kb) <= prefix;
+            const unsigned long long m = __ballot(keep);
+            if (lane == 0) mk[ch] = m;
+            total += __popcll(m);
+        }
+        __builtin_amdgcn_wave_barrier();
+    }
+    int* out = P.lists + (size_t)bh * P.tri + toff;
+    int written = 0;
+    for (int ch = 0; ch < nch; ++ch) {
         const int kb = 64 * ch + lane;
-        const bool f = kb <= qb && (kb >= cut || ((mk[ch] >> lane) & 1ull));
-        const unsigned long long bal = __ballot(f);
-        if (f) out[total + __popcll(bal & ((1ull << lane) - 1ull))] = kb;
-        total += __popcll(bal);
+        const unsigned long long m = mk[ch];
+        const bool f = (m >> lane) & 1ull;
+        if (f) out[written + __popcll(m & ((1ull << lane) - 1ull))] = kb;
+        written += __popcll(m);
     }
     if (lane == 0) {
-        P.counts[(size_t)bh * P.nb + qb] = total;
-        atomicAdd(&P.total_blocks[bh], (unsigned long long)total);
+        P.counts[(size_t)bh * P.nb + qb] = written;
+        atomicAdd(&P.total_blocks[bh], (unsigned long long)written);
     }
 }
 
@@ -903,6 +993,7 @@ hipError_t launch_plan(const PlanArgs& a, PlanDev& P, hipStream_t st) {
             hipLaunchKernelGGL(k_sel_scan, dim3(nlists), dim3(256), 0, st, P.sel, P.hist);
         }
         hipLaunchKernelGGL(k_vs_flags, dim3(nb, BH), dim3(BS), 0, st, P, P.sel);
+        if (P.cap_blocks > 0) hipLaunchKernelGGL(k_diag_mass, dim3(nb, BH), dim3(64), 0, st, P, P.sel);
     }
     // K7
     hipLaunchKernelGGL(k_fill_u32, dim3(grid1(2LL * BH)), dim3(256), 0, st, (unsigned int*)P.total_blocks, 0u,

@@ -117,3 +117,18 @@ def test_product_path_has_no_fallback():
     src += open(os.path.join(ROOT, "sparse_long_context_last_amd", "_lib.py")).read()
     assert "oracle" not in src and "synth" not in src
     assert "there is no fallback" in src
+
+
+def test_max_budget_validation(lib):
+    def plan_ex(max_budget, min_budget=1024, block=128):
+        h = C.c_void_p()
+        return lib.fp_prefill_plan_ex(1, 1, 0, 1, 4, 4, 1024, 128, block, 0.95, 0.1, min_budget, max_budget,
+                                      None, C.byref(h))
+    assert plan_ex(-1) == -1
+    assert plan_ex(896) == -1          # 7 blocks < the 8 the minimum budget needs
+    assert "max_budget" in lib.fp_last_error().decode()
+    h = C.c_void_p()
+    # a valid cap on an empty problem needs no device
+    assert lib.fp_prefill_plan_ex(None, None, 0, 0, 4, 4, 1024, 128, 128, 0.95, 0.1, 1024, 8192, None,
+                                  C.byref(h)) == 0
+    lib.fp_plan_destroy(h)

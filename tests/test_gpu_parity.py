@@ -169,3 +169,46 @@ def test_empty_problem_on_device(F):
     assert P.info().total_blocks == 0
     out = F.attend(P, q, k, k)
     assert out.shape == q.shape
+
+
+def run_capped(F, cfg, q, k, v, max_budget):
+    dt = cfg.dtype
+    qd, kd, vd = to_dev(q, dt), to_dev(k, dt), to_dev(v, dt)
+    P = F.plan(qd, kd, block=cfg.block, gamma=cfg.gamma, tau=cfg.tau, min_budget=cfg.min_budget,
+               max_budget=max_budget)
+    out = F.attend(P, qd, kd, vd)
+    torch.cuda.synchronize()
+    assert P.info().max_budget == max_budget
+    lists = P.lists()
+    group = cfg.Hq // cfg.Hkv
+    cap = O.cap_blocks(max_budget, cfg.block)
+    capped_rows = 0
+    for b in range(cfg.B):
+        for h in range(cfg.Hq):
+            bh = b * cfg.Hq + h
+            hp = O.plan_head(q[b, h], k[b, h // group], cfg.block, cfg.gamma, cfg.tau, cfg.min_budget, max_budget)
+            for r in range(cfg.nb):
+                assert np.array_equal(lists[bh][r], hp.lists[r]), (bh, r, lists[bh][r][:12], hp.lists[r][:12])
+                assert len(hp.lists[r]) <= cap
+            capped_rows += sum(1 for x in O.plan_head(q[b, h], k[b, h // group], cfg.block, cfg.gamma, cfg.tau,
+                                                      cfg.min_budget).lists if len(x) > cap)
+            ref = O.attend_head(q[b, h], k[b, h // group], v[b, h // group], hp.mask, cfg.block)
+            check_attention(out[b, h].float().cpu().numpy(), ref, dt, f"capped b{b} h{h}")
+    return capped_rows
+
+
+@pytest.mark.parametrize("name,max_budget", [("gqa_bf16_2k", 1024), ("gqa_bf16_2k", 1536),
+                                             ("bs64_bf16_1088_b2", 512), ("tiny_fp32_4k", 2048)])
+def test_max_budget_parity(F, name, max_budget):
+    cfg = SMALL[name]
+    q, k, v = LayerGen(cfg).numpy_layer()
+    assert run_capped(F, cfg, q, k, v, max_budget) > 0     # the cap was exercised
+
+
+def test_max_budget_with_gamma_one_and_ties(F):
+    cfg = SMALL["ragged_bf16_1152"].with_(gamma=1.0)
+    q, k, v = LayerGen(cfg).numpy_layer()
+    assert run_capped(F, cfg, q, k, v, 512) > 0
+    z = np.zeros((1, cfg.Hq, cfg.N, cfg.d), np.float32)            # every score ties
+    zk = np.zeros((1, cfg.Hkv, cfg.N, cfg.d), np.float32)
+    run_capped(F, cfg.with_(gamma=0.7), z, zk, v, 384)

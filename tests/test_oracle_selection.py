@@ -143,3 +143,53 @@ def test_qa_mask_maps_flattened_triangle():
     assert sorted(zip(*np.nonzero(m))) == [(0, 0), (2, 1), (5, 5)]
     A = np.arange(nb * nb, dtype=F32).reshape(nb, nb)
     assert O.tri_values(A)[4] == A[2, 1]
+
+
+@pytest.mark.parametrize("seed", range(20))
+def test_cap_keeps_highest_scoring_blocks(seed):
+    rng = np.random.default_rng(300 + seed)
+    nb, bs = int(rng.integers(1, 14)), 16
+    mask = np.tril(rng.random((nb, nb)) < rng.uniform(0.2, 1.0))
+    mask = O.apply_floor(mask, bs, bs)
+    scores = rng.choice(np.array([0.0, 0.25, 0.5, 1.0], np.float32), size=(nb, nb)) if seed % 2 \
+        else rng.random((nb, nb)).astype(np.float32)
+    cap = int(rng.integers(1, 6))
+    out = O.apply_cap(mask, scores, cap * bs, bs)
+    assert np.array_equal(O.apply_cap(mask, scores, 0, bs), mask)
+    for qb in range(nb):
+        kept = set(np.nonzero(out[qb])[0].tolist())
+        had = np.nonzero(mask[qb])[0].tolist()
+        assert kept <= set(had)
+        if len(had) <= cap:
+            assert kept == set(had)
+            continue
+        assert len(kept) == cap
+        # brute force: the cap-subset that is first in (score desc, kb desc) order
+        ranked = sorted(had, key=lambda kb: (-float(scores[qb, kb]), -kb))
+        assert kept == set(ranked[:cap])
+    assert O.cap_blocks(8192, 128) == 64 and O.cap_blocks(1, 64) == 1 and O.cap_blocks(0, 64) == 0
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_vs_block_scores_equal_touching_line_mass(seed):
+    """score(qb, kb) = mass of the selected lines that touch block (qb, kb),
+    enumerated at token level (a column j or an offset o touches the block iff
+    some causal (i, j) in it has that column or that offset)."""
+    rng = np.random.default_rng(400 + seed)
+    bs, nb = 8, int(rng.integers(1, 7))
+    N = bs * nb
+    c = rng.random(N).astype(np.float32)
+    g = rng.random(N).astype(np.float32)
+    sel_c = rng.random(N) < 0.3
+    sel_g = rng.random(N) < 0.3
+    got = O.vs_block_scores(c, g, sel_c, sel_g, bs)
+    for qb in range(nb):
+        for kb in range(qb + 1):
+            i = qb * bs + np.arange(bs)[:, None]
+            j = kb * bs + np.arange(bs)[None, :]
+            i, j = np.broadcast_arrays(i, j)
+            causal = j <= i
+            cols = {int(x) for x in j[causal].ravel()}
+            offs = {int(x) for x in (i - j)[causal].ravel()}
+            ref = sum(float(c[x]) for x in cols if sel_c[x]) + sum(float(g[x]) for x in offs if sel_g[x])
+            assert abs(float(got[qb, kb]) - ref) <= 1e-5 * max(1.0, ref)
