@@ -47,7 +47,9 @@ the design notes of the repository):
   * an optional maximum budget caps every query-block row at
     ceil(max_budget / block) blocks, keeping the blocks with the largest
     estimate (query-aware) or selected line mass (vertical-slash), ties
-    to the block nearest the diagonal.
+    to the block nearest the diagonal;
+  * the optional query-wise selection applies the same cumulative rule to
+    each estimated row on its own instead of to the flattened map.
 
 Pins (tests in ``tests/test_oracle_*.py``): exp2_c / ln_c against libm
 within a few ulp; JSD against scipy and closed forms; canonical softmax
@@ -370,6 +372,20 @@ def qa_block_mask(sel_tri: np.ndarray, nb: int) -> np.ndarray:
     return mask
 
 
+def qa_querywise_mask(A: np.ndarray, gamma: float) -> np.ndarray:
+    """Query-wise variant of the query-aware selection (ablation table:
+    "query-wise index selection instead of flattening the estimated attention
+    map"): every query-block row qb selects on its own, from its estimated
+    row A[qb, 0..qb], the minimal set of key blocks whose mass reaches gamma
+    of that row's total, with the same fixed-point test and tie order (value
+    descending, key block ascending)."""
+    nb = A.shape[0]
+    mask = np.zeros((nb, nb), dtype=bool)
+    for qb in range(nb):
+        mask[qb, : qb + 1] = select_cumulative(A[qb, : qb + 1], gamma)
+    return mask
+
+
 def floor_blocks(min_budget: int, bs: int) -> int:
     """Blocks per query-block row that the minimum budget (in tokens, ablation
     table) asks for; every row keeps at least its diagonal block."""
@@ -471,11 +487,19 @@ class HeadPlan:
         return np.array([len(x) for x in self.lists], dtype=np.int64)
 
 
+QA_FLATTENED = "flattened"
+QA_QUERYWISE = "querywise"
+
+
 def plan_head(q: np.ndarray, k: np.ndarray, bs: int, gamma: float, tau: float,
-              min_budget: int, max_budget: int = 0) -> HeadPlan:
+              min_budget: int, max_budget: int = 0, qa_selection: str = QA_FLATTENED) -> HeadPlan:
     """Pattern determination and index selection for one query head q [N, d]
     against its key/value head's keys k [N, d]; max_budget > 0 caps every
-    query-block row (applied after the minimum-budget fill)."""
+    query-block row (applied after the minimum-budget fill); qa_selection
+    picks the flattened (default) or the query-wise selection for a
+    query-aware head."""
+    if qa_selection not in (QA_FLATTENED, QA_QUERYWISE):
+        raise ValueError(f"unknown qa_selection {qa_selection!r}")
     q = np.asarray(q, dtype=F32)
     k = np.asarray(k, dtype=F32)
     N, d = q.shape
@@ -491,6 +515,9 @@ def plan_head(q: np.ndarray, k: np.ndarray, bs: int, gamma: float, tau: float,
     sel_qa = sel_v = sel_s = None
     if gamma_fixed(gamma) >= (1 << GAMMA_SHIFT):
         mask = np.tril(np.ones((nb, nb), dtype=bool))
+    elif pattern == QUERY_AWARE and qa_selection == QA_QUERYWISE:
+        mask = qa_querywise_mask(A, gamma)
+        sel_qa = tri_values(mask)
     elif pattern == QUERY_AWARE:
         sel_qa = select_cumulative(tri_values(A), gamma)
         mask = qa_block_mask(sel_qa, nb)

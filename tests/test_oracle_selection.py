@@ -193,3 +193,47 @@ def test_vs_block_scores_equal_touching_line_mass(seed):
             offs = {int(x) for x in (i - j)[causal].ravel()}
             ref = sum(float(c[x]) for x in cols if sel_c[x]) + sum(float(g[x]) for x in offs if sel_g[x])
             assert abs(float(got[qb, kb]) - ref) <= 1e-5 * max(1.0, ref)
+
+
+def test_querywise_selection_rows():
+    """Each row of the query-wise mask is the brute-force minimal set of its
+    own estimated row; gamma = 1 keeps every nonzero entry."""
+    rng = np.random.default_rng(77)
+    nb = 7
+    A = np.zeros((nb, nb), F32)
+    for qb in range(nb):
+        row = rng.dirichlet(np.ones(qb + 1) * 0.5).astype(F32)
+        if qb == 3:
+            row[:] = F32(0.25)             # exact ties: lower key blocks first
+        A[qb, : qb + 1] = row
+    for gamma in (0.3, 0.7, 0.95):
+        m = O.qa_querywise_mask(A, gamma)
+        assert not np.triu(m, 1).any()
+        for qb in range(nb):
+            assert set(np.nonzero(m[qb])[0].tolist()) == brute_force_select(A[qb, : qb + 1], gamma)
+    assert np.nonzero(O.qa_querywise_mask(A, 0.5)[3])[0].tolist() == [0, 1]
+
+
+def test_querywise_plan_differs_only_for_query_aware_heads():
+    from synth import BY_NAME, LayerGen
+    cfg = BY_NAME["tiny_fp32_4k"].with_(N=2048)
+    q, k, _ = LayerGen(cfg).numpy_layer()
+    seen = set()
+    for h in range(cfg.Hq):
+        a = O.plan_head(q[0, h], k[0, h], cfg.block, cfg.gamma, cfg.tau, cfg.min_budget)
+        b = O.plan_head(q[0, h], k[0, h], cfg.block, cfg.gamma, cfg.tau, cfg.min_budget,
+                        qa_selection=O.QA_QUERYWISE)
+        assert a.pattern == b.pattern and a.D == b.D
+        seen.add(a.pattern)
+        if a.pattern == O.VERTICAL_SLASH:
+            assert np.array_equal(a.mask, b.mask)
+        else:
+            # every row reaches gamma of its own estimated mass (before the floor)
+            sel = O.qa_querywise_mask(a.A, cfg.gamma)
+            for qb in range(cfg.nb):
+                row = a.A[qb, : qb + 1].astype(np.float64)
+                assert row[sel[qb, : qb + 1]].sum() >= cfg.gamma * row.sum() - 1e-6
+            assert np.array_equal(b.mask, O.apply_floor(sel, cfg.min_budget, cfg.block))
+    assert seen == {O.QUERY_AWARE, O.VERTICAL_SLASH}
+    with pytest.raises(ValueError):
+        O.plan_head(q[0, 0], k[0, 0], cfg.block, cfg.gamma, cfg.tau, cfg.min_budget, qa_selection="rows")
