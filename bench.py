@@ -45,10 +45,11 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def read_traffic(workload: str):
+def read_traffic(workload: str, default_settings: bool):
     """HBM bytes per attention launch from the committed counter summary, if
-    it was taken on the current attention kernel source and this workload."""
-    if not os.path.exists(COUNTERS_FILE):
+    it was taken on the current attention kernel source and this workload
+    (planned with the default settings)."""
+    if not default_settings or not os.path.exists(COUNTERS_FILE):
         return None
     m = re.search(r"```json\n(.*?)\n```", open(COUNTERS_FILE).read(), re.S)
     if not m:
@@ -59,7 +60,8 @@ def read_traffic(workload: str):
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(cfg, total_blocks_by_head, sample_rows: int, budget_s: float, max_budget: int = 0):
+def cpu_baseline(cfg, total_blocks_by_head, sample_rows: int, budget_s: float, max_budget: int = 0,
+                 qa_selection: str = "flattened"):
     """The oracle as it stands on the host cores: one query head planned in
     full, float64 attention on a sample of that head's query blocks,
     extrapolated to the whole layer by head count and selected-block count."""
@@ -77,7 +79,7 @@ def cpu_baseline(cfg, total_blocks_by_head, sample_rows: int, budget_s: float, m
     k = gen.k_head(0, h // cfg.group)
     v = gen.v_head(0, h // cfg.group)
     t0 = time.perf_counter()
-    hp = O.plan_head(q, k, cfg.block, cfg.gamma, cfg.tau, cfg.min_budget, max_budget)
+    hp = O.plan_head(q, k, cfg.block, cfg.gamma, cfg.tau, cfg.min_budget, max_budget, qa_selection)
     t_plan = time.perf_counter() - t0
     rng = np.random.default_rng(7)
     rows = sorted(set([0, cfg.nb - 1] + rng.choice(cfg.nb, size=min(cfg.nb, sample_rows), replace=False).tolist()))
@@ -111,6 +113,8 @@ def main() -> int:
     ap.add_argument("--cpu-budget-s", type=float, default=15.0)
     ap.add_argument("--max-budget", type=int, default=0,
                     help="cap every query-block row at this many keys (0: uncapped)")
+    ap.add_argument("--qa-selection", default="flattened", choices=["flattened", "querywise"],
+                    help="how query-aware heads select blocks from the estimated map")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -140,7 +144,7 @@ def main() -> int:
 
     def step():
         P = F.plan(q, k, block=cfg.block, gamma=cfg.gamma, tau=cfg.tau, min_budget=cfg.min_budget,
-                   max_budget=args.max_budget)
+                   max_budget=args.max_budget, qa_selection=args.qa_selection)
         F.attend(P, q, k, v, out=out)
         return P
 
@@ -158,7 +162,7 @@ def main() -> int:
     for i in range(args.steps):
         ev[i][0].record(stream)
         P = F.plan(q, k, block=cfg.block, gamma=cfg.gamma, tau=cfg.tau, min_budget=cfg.min_budget,
-                   max_budget=args.max_budget)
+                   max_budget=args.max_budget, qa_selection=args.qa_selection)
         ev[i][1].record(stream)
         F.attend(P, q, k, v, out=out)
         ev[i][2].record(stream)
@@ -212,7 +216,7 @@ def main() -> int:
         torch.cuda.synchronize()
         del a, b
 
-    traffic = read_traffic(cfg.name)
+    traffic = read_traffic(cfg.name, args.max_budget == 0 and args.qa_selection == "flattened")
     roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
             "frac": round(achieved / peak, 4), "traffic": traffic,
             "kernel": f"fp::k_attn_{'bf16' if cfg.dtype == 'bf16' else 'f32'}<{cfg.block}, true>",
@@ -221,7 +225,8 @@ def main() -> int:
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(cfg, blocks_by_head, args.cpu_rows, args.cpu_budget_s, args.max_budget)
+        cpu = cpu_baseline(cfg, blocks_by_head, args.cpu_rows, args.cpu_budget_s, args.max_budget,
+                           args.qa_selection)
 
     rec = {
         "metric": METRIC,
@@ -239,6 +244,7 @@ def main() -> int:
         "config": {"workload": cfg.name, "B": cfg.B, "Hq": cfg.Hq, "Hkv": cfg.Hkv, "N": cfg.N,
                    "d": cfg.d, "block": cfg.block, "gamma": cfg.gamma, "tau": cfg.tau,
                    "min_budget": cfg.min_budget, "max_budget": args.max_budget,
+                   "qa_selection": args.qa_selection,
                    "parallelism": "single GPU"},
         "plan_ms": round(plan_ms, 3),
         "attend_ms": round(attend_ms, 3),

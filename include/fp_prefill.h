@@ -70,7 +70,20 @@ typedef struct fp_plan_info {
     long long dense_blocks;            /* B * Hq * nb (nb + 1) / 2 */
     int query_aware_heads;             /* heads whose pattern is query-aware */
     int max_budget;                    /* tokens, 0 = uncapped */
+    int qa_selection;                  /* fp_qa_selection */
 } fp_plan_info;
+
+/* How a query-aware head selects its blocks from the estimated block map. */
+typedef enum fp_qa_selection {
+    FP_QA_FLATTENED = 0,   /* one list over the whole causal triangle (the method's default) */
+    FP_QA_QUERYWISE = 1    /* every query-block row selects from its own row */
+} fp_qa_selection;
+
+/* Optional planning settings; a NULL pointer means all defaults (zeros). */
+typedef struct fp_plan_options {
+    int max_budget;        /* tokens per query-block row, 0 = uncapped */
+    int qa_selection;      /* fp_qa_selection */
+} fp_plan_options;
 
 /*
  * fp_prefill_plan -- steps 1 and 2 for every (batch, query head).
@@ -92,21 +105,29 @@ fp_status fp_prefill_plan(const void* q, const void* k, fp_dtype dtype,
                           void* stream, fp_plan** out);
 
 /*
- * fp_prefill_plan_ex -- fp_prefill_plan with a maximum budget (ablation
- *   table of the atlas.scime.ai summary page: the computational budget capped
- *   at 8k or 32k tokens per row; uncapped is the method's default).  max_budget = 0: identical to fp_prefill_plan.
- *   max_budget > 0: every query-block row keeps at most
- *   ceil(max_budget / block) blocks -- after the minimum-budget fill, the
- *   row's blocks with the largest score stay, where the score is the
- *   estimated block attention for query-aware heads (and for gamma = 1) and
- *   the selected column plus diagonal line mass through the block for
- *   vertical-slash heads; ties keep the block nearer the diagonal.
- *   FP_ERR_INVALID_ARG if max_budget < 0 or if it allows fewer blocks per
- *   row than min_budget asks for.
+ * fp_prefill_plan_ex -- fp_prefill_plan with optional settings (`options`
+ *   may be NULL: identical to fp_prefill_plan).  Both variants come from the
+ *   ablation table of the atlas.scime.ai summary page.
+ *   options->max_budget > 0 (the table caps the computational budget at 8k
+ *   or 32k tokens; uncapped is the method's default): every query-block row
+ *   keeps at most ceil(max_budget / block) blocks -- after the
+ *   minimum-budget fill, the row's blocks with the largest score stay, where
+ *   the score is the estimated block attention for query-aware heads (and
+ *   for gamma = 1) and the selected column plus diagonal line mass through
+ *   the block for vertical-slash heads; ties keep the block nearer the
+ *   diagonal.
+ *   options->qa_selection = FP_QA_QUERYWISE (the table's alternative to
+ *   selecting over the flattened estimated map): a query-aware head applies the cumulative rule to each estimated row on
+ *   its own -- the minimal set of the row's key blocks, value descending
+ *   then key block ascending, whose fixed-point mass reaches gamma of the
+ *   row's total.  Vertical-slash heads are unaffected.
+ *   FP_ERR_INVALID_ARG if max_budget < 0, if it allows fewer blocks per row
+ *   than min_budget asks for, or if qa_selection is not a listed value.
  */
 fp_status fp_prefill_plan_ex(const void* q, const void* k, fp_dtype dtype,
                              int B, int Hq, int Hkv, int N, int d, int block,
-                             float gamma, float tau, int min_budget, int max_budget,
+                             float gamma, float tau, int min_budget,
+                             const fp_plan_options* options,
                              void* stream, fp_plan** out);
 
 /*

@@ -359,8 +359,8 @@ def vs_block_mask(sel_cols: np.ndarray, sel_diags: np.ndarray, bs: int) -> np.nd
 
 def tri_values(A: np.ndarray) -> np.ndarray:
     """The causal entries of a block map flattened row-major: index
-    qb (qb + 1) / 2 + kb for kb <= qb ("flattening the estimated attention
-    map", ablation table)."""
+    qb (qb + 1) / 2 + kb for kb <= qb (the ablation table's default: the
+    estimated map is flattened into one list)."""
     r, c = np.tril_indices(A.shape[0])
     return A[r, c]
 
@@ -373,12 +373,12 @@ def qa_block_mask(sel_tri: np.ndarray, nb: int) -> np.ndarray:
 
 
 def qa_querywise_mask(A: np.ndarray, gamma: float) -> np.ndarray:
-    """Query-wise variant of the query-aware selection (ablation table:
-    "query-wise index selection instead of flattening the estimated attention
-    map"): every query-block row qb selects on its own, from its estimated
-    row A[qb, 0..qb], the minimal set of key blocks whose mass reaches gamma
-    of that row's total, with the same fixed-point test and tie order (value
-    descending, key block ascending)."""
+    """Query-wise variant of the query-aware selection (an ablation-table
+    alternative to selecting over the flattened map): every query-block row
+    qb selects on its own, from its estimated row A[qb, 0..qb], the minimal
+    set of key blocks whose mass reaches gamma of that row's total, with the
+    same fixed-point test and tie order (value descending, key block
+    ascending)."""
     nb = A.shape[0]
     mask = np.zeros((nb, nb), dtype=bool)
     for qb in range(nb):

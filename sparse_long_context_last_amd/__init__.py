@@ -125,9 +125,11 @@ class Plan:
 
 
 def plan(q, k, block: int = 128, gamma: float = 0.95, tau: float = 0.1,
-         min_budget: int = 1024, max_budget: int = 0, stream=None) -> Plan:
+         min_budget: int = 1024, max_budget: int = 0, qa_selection: str = "flattened",
+         stream=None) -> Plan:
     """Pattern determination and index selection (fp_prefill_plan_ex;
-    max_budget = 0 leaves rows uncapped)."""
+    max_budget = 0 leaves rows uncapped; qa_selection "flattened" or
+    "querywise")."""
     _check_tensor(q, "q")
     _check_tensor(k, "k")
     if q.dtype != k.dtype:
@@ -137,9 +139,12 @@ def plan(q, k, block: int = 128, gamma: float = 0.95, tau: float = 0.1,
     if tuple(k.shape) != (B, Hkv, N, d):
         raise ValueError("k must be [B, Hkv, N, d] with q's B, N and d")
     dt = _dtype_code(q)
+    if qa_selection not in _lib.QA_SELECTION:
+        raise ValueError(f"qa_selection must be one of {sorted(_lib.QA_SELECTION)}")
+    opts = _lib.PlanOptions(int(max_budget), _lib.QA_SELECTION[qa_selection])
     h = C.c_void_p()
     _lib.check(_lib.load().fp_prefill_plan_ex(q.data_ptr(), k.data_ptr(), dt, B, Hq, Hkv, N, d, block,
-                                              float(gamma), float(tau), int(min_budget), int(max_budget),
+                                              float(gamma), float(tau), int(min_budget), C.byref(opts),
                                               _stream_ptr(stream), C.byref(h)), "fp_prefill_plan_ex")
     return Plan(h, (B, Hq, Hkv, N, d, block), dt, stream)
 

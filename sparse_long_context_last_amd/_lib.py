@@ -26,7 +26,15 @@ class PlanInfo(C.Structure):
                 ("d", C.c_int), ("block", C.c_int), ("nb", C.c_int), ("dtype", C.c_int),
                 ("gamma", C.c_float), ("tau", C.c_float), ("min_budget", C.c_int),
                 ("total_blocks", C.c_longlong), ("dense_blocks", C.c_longlong),
-                ("query_aware_heads", C.c_int), ("max_budget", C.c_int)]
+                ("query_aware_heads", C.c_int), ("max_budget", C.c_int),
+                ("qa_selection", C.c_int)]
+
+
+class PlanOptions(C.Structure):
+    _fields_ = [("max_budget", C.c_int), ("qa_selection", C.c_int)]
+
+
+QA_SELECTION = {"flattened": 0, "querywise": 1}
 
 
 # name -> (restype, argtypes)
@@ -36,7 +44,7 @@ SIGNATURES = {
                                   C.c_void_p, C.POINTER(C.c_void_p)]),
     "fp_prefill_plan_ex": (C.c_int, [C.c_void_p, C.c_void_p, C.c_int, C.c_int, C.c_int, C.c_int,
                                      C.c_int, C.c_int, C.c_int, C.c_float, C.c_float, C.c_int,
-                                     C.c_int, C.c_void_p, C.POINTER(C.c_void_p)]),
+                                     C.POINTER(PlanOptions), C.c_void_p, C.POINTER(C.c_void_p)]),
     "fp_prefill_attend": (C.c_int, [C.c_void_p] * 6),
     "fp_dense_attend": (C.c_int, [C.c_void_p] * 4 + [C.c_int] * 7 + [C.c_void_p]),
     "fp_plan_info_get": (C.c_int, [C.c_void_p, C.POINTER(PlanInfo)]),

@@ -21,7 +21,7 @@ struct fp_plan {
     int B, Hq, Hkv, N, d, bs, nb;
     fp_dtype dtype;
     float gamma, tau;
-    int min_budget, max_budget;
+    int min_budget, max_budget, qa_selection;
     int device;
     hipStream_t stream;
     PlanDev dev;
@@ -229,13 +229,15 @@ fp_status fp_canonical_constants(int d, float* e2, double* lnc, double* ln2, dou
 
 fp_status fp_prefill_plan(const void* q, const void* k, fp_dtype dtype, int B, int Hq, int Hkv, int N, int d,
                           int block, float gamma, float tau, int min_budget, void* stream, fp_plan** out) {
-    return fp_prefill_plan_ex(q, k, dtype, B, Hq, Hkv, N, d, block, gamma, tau, min_budget, 0, stream, out);
+    return fp_prefill_plan_ex(q, k, dtype, B, Hq, Hkv, N, d, block, gamma, tau, min_budget, nullptr, stream, out);
 }
 
 fp_status fp_prefill_plan_ex(const void* q, const void* k, fp_dtype dtype, int B, int Hq, int Hkv, int N, int d,
-                             int block, float gamma, float tau, int min_budget, int max_budget, void* stream,
-                             fp_plan** out) {
+                             int block, float gamma, float tau, int min_budget, const fp_plan_options* options,
+                             void* stream, fp_plan** out) {
     if (!out) return fail(FP_ERR_INVALID_ARG, "out is NULL");
+    const int max_budget = options ? options->max_budget : 0;
+    const int qa_selection = options ? options->qa_selection : FP_QA_FLATTENED;
     *out = nullptr;
     fp_status s = check_shape(dtype, B, Hq, Hkv, N, d, block);
     if (s != FP_OK) return s;
@@ -243,6 +245,8 @@ fp_status fp_prefill_plan_ex(const void* q, const void* k, fp_dtype dtype, int B
     if (!(tau >= 0.0f) || std::isinf(tau)) return fail(FP_ERR_INVALID_ARG, "tau %g must be finite and >= 0", (double)tau);
     if (min_budget < 0) return fail(FP_ERR_INVALID_ARG, "min_budget %d < 0", min_budget);
     if (max_budget < 0) return fail(FP_ERR_INVALID_ARG, "max_budget %d < 0", max_budget);
+    if (qa_selection != FP_QA_FLATTENED && qa_selection != FP_QA_QUERYWISE)
+        return fail(FP_ERR_INVALID_ARG, "qa_selection %d is not FP_QA_FLATTENED or FP_QA_QUERYWISE", qa_selection);
     {
         const long long floor_b = std::max(1LL, ((long long)min_budget + block - 1) / block);
         const long long cap_b = ((long long)max_budget + block - 1) / block;
@@ -258,6 +262,7 @@ fp_status fp_prefill_plan_ex(const void* q, const void* k, fp_dtype dtype, int B
     p->B = B; p->Hq = Hq; p->Hkv = Hkv; p->N = N; p->d = d; p->bs = block;
     p->nb = N / block; p->dtype = dtype; p->gamma = gamma; p->tau = tau; p->min_budget = min_budget;
     p->max_budget = max_budget;
+    p->qa_selection = qa_selection;
     p->stream = (hipStream_t)stream;
     if (empty) {
         p->device = -1;
@@ -283,6 +288,8 @@ fp_status fp_prefill_plan_ex(const void* q, const void* k, fp_dtype dtype, int B
     P.floor_blocks = (min_budget + block - 1) / block;
     if (P.floor_blocks < 1) P.floor_blocks = 1;
     P.cap_blocks = (int)(((long long)max_budget + block - 1) / block);
+    P.qa_querywise = qa_selection == FP_QA_QUERYWISE;
+    P.G = G;
 
 #define PALLOC(ptr, n)                          \
     do {                                        \
@@ -365,6 +372,7 @@ fp_status fp_plan_info_get(const fp_plan* plan, fp_plan_info* out) {
     I.block = plan->bs; I.nb = plan->nb; I.dtype = plan->dtype; I.gamma = plan->gamma; I.tau = plan->tau;
     I.min_budget = plan->min_budget;
     I.max_budget = plan->max_budget;
+    I.qa_selection = plan->qa_selection;
     const long long BH = (long long)plan->B * plan->Hq;
     I.dense_blocks = BH * plan->nb * (long long)(plan->nb + 1) / 2;
     if (BH > 0 && plan->N > 0) {

@@ -35,6 +35,8 @@ struct PlanDev {
     int mode_all;                // gamma == 1: every causal block
     int floor_blocks;            // max(1, ceil(min_budget / BS))
     int cap_blocks;              // ceil(max_budget / BS), 0 = uncapped
+    int qa_querywise;            // query-aware heads select row by row
+    unsigned long long G;        // rint(gamma 2^24)
     unsigned char* pattern;      // [BH]
     double* djs;                 // [BH]
     float* qbar;                 // [BH][nb][d]

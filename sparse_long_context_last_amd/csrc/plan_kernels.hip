@@ -575,7 +575,8 @@ __device__ __forceinline__ ListRef list_of(const PlanDev& P, int list) {
     const int bh = list >> 1, slot = list & 1;
     ListRef r{nullptr, 0};
     if (P.pattern[bh] == kPatternQueryAware) {
-        if (slot == 0) { r.x = P.ahat + (size_t)bh * P.tri; r.len = P.tri; }
+        // the query-wise variant selects row by row in k_lists instead
+        if (slot == 0 && !P.qa_querywise) { r.x = P.ahat + (size_t)bh * P.tri; r.len = P.tri; }
     } else {
         r.x = (slot == 0 ? P.colsum : P.diagsum) + (size_t)bh * P.N;
         r.len = P.N;
@@ -787,13 +788,75 @@ __global__ __launch_bounds__(64) void k_diag_mass(PlanDev P, const SelState* __r
 // ascending key-block order at lists[bh][row (row+1)/2 + ...].
 // One wave per row, 4 rows per workgroup.
 // ---------------------------------------------------------------------------
+// Row-selection keys: value descending, then key block ascending.
+constexpr int kRowIdxBits = 12;
+
 __device__ __forceinline__ bool member(const PlanDev& P, const SelState& s0, int bh, int qb, int kb, bool qa,
-                                       const float* arow, long long toff) {
+                                       const float* arow, long long toff, bool rhas, unsigned long long rkey) {
     if (P.mode_all) return true;
+    if (qa && P.qa_querywise) return rhas && order_key(arow[kb], kb, kRowIdxBits) <= rkey;
     if (qa) return s0.has && order_key(arow[kb], toff + kb, s0.ibits) <= s0.kstar;
     const size_t base = (size_t)bh * P.nb;
     const int a = qb - kb;
     return P.colblk[base + kb] || P.diagA[base + a] || (a >= 1 && P.diagB[base + a - 1]);
+}
+
+__device__ __forceinline__ unsigned long long wave_sum_u64(unsigned long long v) {
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+    return v;
+}
+__device__ __forceinline__ unsigned long long wave_min_u64(unsigned long long v) {
+    for (int o = 32; o >= 1; o >>= 1) { const unsigned long long w = __shfl_xor(v, o); v = w < v ? w : v; }
+    return v;
+}
+__device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v) {
+    for (int o = 32; o >= 1; o >>= 1) { const unsigned long long w = __shfl_xor(v, o); v = w > v ? w : v; }
+    return v;
+}
+
+// Query-wise selection of one estimated row a[0..len) by one wave: the
+// smallest key K with mass(keys <= K) >= T, T = ceil(G U / 2^24) of the
+// row's own fixed-point total U, found bit by bit from the highest bit in
+// which the row's keys differ.  Returns false when T = 0 (nothing selected).
+__device__ bool row_select(const float* a, int len, unsigned long long G, unsigned long long* kout) {
+    const int lane = threadIdx.x & 63;
+    unsigned long long U = 0ull, kmin = ~0ull, kmax = 0ull;
+    for (int kb = lane; kb < len; kb += 64) {
+        const float x = a[kb];
+        U += fixed_u(x);
+        const unsigned long long key = order_key(x, kb, kRowIdxBits);
+        kmin = key < kmin ? key : kmin;
+        kmax = key > kmax ? key : kmax;
+    }
+    U = wave_sum_u64(U);
+    kmin = wave_min_u64(kmin);
+    kmax = wave_max_u64(kmax);
+    const unsigned long long hi = U >> kGammaShift, lo = U & ((1ull << kGammaShift) - 1);
+    const unsigned long long T = G * hi + ((G * lo + ((1ull << kGammaShift) - 1)) >> kGammaShift);
+    if (T == 0ull) return false;
+    const unsigned long long diff = kmin ^ kmax;
+    if (diff == 0ull) {
+        *kout = kmin;
+        return true;
+    }
+    const int top = 63 - __clzll((long long)diff);
+    unsigned long long prefix = kmin & ~((2ull << top) - 1ull);
+    unsigned long long below = 0ull;    // mass of the keys below the current range
+    for (int b = top; b >= 0; --b) {
+        unsigned long long m0 = 0ull;
+        for (int kb = lane; kb < len; kb += 64) {
+            const float x = a[kb];
+            const unsigned long long key = order_key(x, kb, kRowIdxBits);
+            if ((key >> (b + 1)) == (prefix >> (b + 1)) && !((key >> b) & 1ull)) m0 += fixed_u(x);
+        }
+        m0 = wave_sum_u64(m0);
+        if (below + m0 < T) {
+            below += m0;
+            prefix |= 1ull << b;
+        }
+    }
+    *kout = prefix;
+    return true;
 }
 
 // Score of block kb in row qb for the maximum-budget cap (>= 0).
@@ -820,10 +883,13 @@ __global__ __launch_bounds__(256) void k_lists(PlanDev P, const SelState* __rest
     const float* arow = P.ahat + (size_t)bh * P.tri + toff;
     const int nch = qb / 64 + 1;
     unsigned long long* mk = masks[wv];
+    unsigned long long rkey = 0ull;
+    const bool rhas = qa && P.qa_querywise && !P.mode_all && row_select(arow, qb + 1, P.G, &rkey);
     int cnt = 0;
     for (int ch = 0; ch < nch; ++ch) {
         const int kb = 64 * ch + lane;
-        const unsigned long long bal = __ballot(kb <= qb && member(P, s0, bh, qb, kb, qa, arow, toff));
+        const unsigned long long bal =
+            __ballot(kb <= qb && member(P, s0, bh, qb, kb, qa, arow, toff, rhas, rkey));
         if (lane == 0) mk[ch] = bal;
         cnt += __popcll(bal);
     }

@@ -119,16 +119,27 @@ def test_product_path_has_no_fallback():
     assert "there is no fallback" in src
 
 
-def test_max_budget_validation(lib):
-    def plan_ex(max_budget, min_budget=1024, block=128):
+def test_plan_options_validation(lib):
+    from sparse_long_context_last_amd._lib import PlanOptions
+
+    def plan_ex(max_budget=0, qa_selection=0, min_budget=1024, block=128):
         h = C.c_void_p()
-        return lib.fp_prefill_plan_ex(1, 1, 0, 1, 4, 4, 1024, 128, block, 0.95, 0.1, min_budget, max_budget,
+        opt = PlanOptions(max_budget, qa_selection)
+        return lib.fp_prefill_plan_ex(1, 1, 0, 1, 4, 4, 1024, 128, block, 0.95, 0.1, min_budget, C.byref(opt),
                                       None, C.byref(h))
-    assert plan_ex(-1) == -1
-    assert plan_ex(896) == -1          # 7 blocks < the 8 the minimum budget needs
+    assert plan_ex(max_budget=-1) == -1
+    assert plan_ex(max_budget=896) == -1          # 7 blocks < the 8 the minimum budget needs
     assert "max_budget" in lib.fp_last_error().decode()
-    h = C.c_void_p()
-    # a valid cap on an empty problem needs no device
-    assert lib.fp_prefill_plan_ex(None, None, 0, 0, 4, 4, 1024, 128, 128, 0.95, 0.1, 1024, 8192, None,
-                                  C.byref(h)) == 0
-    lib.fp_plan_destroy(h)
+    assert plan_ex(qa_selection=2) == -1
+    assert "qa_selection" in lib.fp_last_error().decode()
+    assert plan_ex(qa_selection=-1) == -1
+    from sparse_long_context_last_amd._lib import PlanInfo
+    for opt in (None, PlanOptions(8192, 1)):
+        # valid settings on an empty problem need no device
+        h = C.c_void_p()
+        assert lib.fp_prefill_plan_ex(None, None, 0, 0, 4, 4, 1024, 128, 128, 0.95, 0.1, 1024,
+                                      C.byref(opt) if opt is not None else None, None, C.byref(h)) == 0
+        info = PlanInfo()
+        assert lib.fp_plan_info_get(h, C.byref(info)) == 0
+        assert (info.max_budget, info.qa_selection) == ((8192, 1) if opt is not None else (0, 0))
+        lib.fp_plan_destroy(h)

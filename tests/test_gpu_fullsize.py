@@ -115,18 +115,22 @@ def test_size_limits(F, name):
             check_attention(out[0, h, sl].float().cpu().numpy(), ref[r], cfg.dtype, f"{name} h{h} row {r}")
 
 
-@pytest.mark.parametrize("name,max_budget", [("llama8b_32k", 4096), ("glm9b_64k_bs64", 8192)])
-def test_full_size_max_budget(F, name, max_budget):
-    """The capped plan at full size: every row within the cap, sampled heads'
-    lists bit-exact with the oracle's capped plan, sampled rows of attention."""
+@pytest.mark.parametrize("name,max_budget,qa_selection", [("llama8b_32k", 4096, "flattened"),
+                                                          ("glm9b_64k_bs64", 8192, "flattened"),
+                                                          ("llama8b_128k", 0, "querywise"),
+                                                          ("glm9b_64k_bs64", 0, "querywise")])
+def test_full_size_plan_options(F, name, max_budget, qa_selection):
+    """The optional settings at full size: every row within the cap, sampled
+    heads' lists bit-exact with the oracle's plan under the same settings,
+    sampled rows of attention."""
     cfg = BY_NAME[name]
     gen = LayerGen(cfg)
     q, k, v = gen.torch_layer("cuda")
     P = F.plan(q, k, block=cfg.block, gamma=cfg.gamma, tau=cfg.tau, min_budget=cfg.min_budget,
-               max_budget=max_budget)
+               max_budget=max_budget, qa_selection=qa_selection)
     out = F.attend(P, q, k, v)
     torch.cuda.synchronize()
-    cap = O.cap_blocks(max_budget, cfg.block)
+    cap = O.cap_blocks(max_budget, cfg.block) or cfg.nb
     lists = P.lists()
     floor = O.floor_blocks(cfg.min_budget, cfg.block)
     for bh in range(cfg.B * cfg.Hq):
@@ -136,8 +140,8 @@ def test_full_size_max_budget(F, name, max_budget):
     for h in sampled_heads(gen, ("V", "S", "QA")):
         kv = h // cfg.group
         qh, kh, vh = gen.q_head(0, h), gen.k_head(0, kv), gen.v_head(0, kv)
-        hp = O.plan_head(qh, kh, cfg.block, cfg.gamma, cfg.tau, cfg.min_budget, max_budget)
-        print(f"[{name} cap {max_budget}] head {h} ({gen.types[h]}): "
+        hp = O.plan_head(qh, kh, cfg.block, cfg.gamma, cfg.tau, cfg.min_budget, max_budget, qa_selection)
+        print(f"[{name} cap {max_budget} {qa_selection}] head {h} ({gen.types[h]}): "
               f"{sum(len(x) for x in hp.lists)} blocks", flush=True)
         for r in range(cfg.nb):
             assert np.array_equal(lists[h][r], hp.lists[r]), (h, r)

@@ -171,27 +171,33 @@ def test_empty_problem_on_device(F):
     assert out.shape == q.shape
 
 
-def run_capped(F, cfg, q, k, v, max_budget):
+def run_capped(F, cfg, q, k, v, max_budget, qa_selection="flattened"):
+    """Plan with the optional settings; lists bit-exact with the oracle's,
+    attention within tolerance; returns how many rows the cap shortened."""
     dt = cfg.dtype
     qd, kd, vd = to_dev(q, dt), to_dev(k, dt), to_dev(v, dt)
     P = F.plan(qd, kd, block=cfg.block, gamma=cfg.gamma, tau=cfg.tau, min_budget=cfg.min_budget,
-               max_budget=max_budget)
+               max_budget=max_budget, qa_selection=qa_selection)
     out = F.attend(P, qd, kd, vd)
     torch.cuda.synchronize()
     assert P.info().max_budget == max_budget
+    assert P.info().qa_selection == (1 if qa_selection == "querywise" else 0)
+    pattern, djs, _, _ = P.copy_out()
     lists = P.lists()
     group = cfg.Hq // cfg.Hkv
-    cap = O.cap_blocks(max_budget, cfg.block)
+    cap = O.cap_blocks(max_budget, cfg.block) or cfg.nb
     capped_rows = 0
     for b in range(cfg.B):
         for h in range(cfg.Hq):
             bh = b * cfg.Hq + h
-            hp = O.plan_head(q[b, h], k[b, h // group], cfg.block, cfg.gamma, cfg.tau, cfg.min_budget, max_budget)
+            hp = O.plan_head(q[b, h], k[b, h // group], cfg.block, cfg.gamma, cfg.tau, cfg.min_budget, max_budget,
+                             qa_selection)
+            assert int(pattern[bh]) == hp.pattern and djs[bh] == hp.D
             for r in range(cfg.nb):
                 assert np.array_equal(lists[bh][r], hp.lists[r]), (bh, r, lists[bh][r][:12], hp.lists[r][:12])
                 assert len(hp.lists[r]) <= cap
             capped_rows += sum(1 for x in O.plan_head(q[b, h], k[b, h // group], cfg.block, cfg.gamma, cfg.tau,
-                                                      cfg.min_budget).lists if len(x) > cap)
+                                                      cfg.min_budget, 0, qa_selection).lists if len(x) > cap)
             ref = O.attend_head(q[b, h], k[b, h // group], v[b, h // group], hp.mask, cfg.block)
             check_attention(out[b, h].float().cpu().numpy(), ref, dt, f"capped b{b} h{h}")
     return capped_rows
@@ -212,3 +218,21 @@ def test_max_budget_with_gamma_one_and_ties(F):
     z = np.zeros((1, cfg.Hq, cfg.N, cfg.d), np.float32)            # every score ties
     zk = np.zeros((1, cfg.Hkv, cfg.N, cfg.d), np.float32)
     run_capped(F, cfg.with_(gamma=0.7), z, zk, v, 384)
+
+
+@pytest.mark.parametrize("name,max_budget", [("gqa_bf16_2k", 0), ("tiny_fp32_4k", 0), ("bs64_bf16_1088_b2", 0),
+                                             ("ragged_bf16_1152", 0), ("gqa_bf16_2k", 1024)])
+def test_querywise_selection_parity(F, name, max_budget):
+    cfg = SMALL[name]
+    q, k, v = LayerGen(cfg).numpy_layer()
+    run_capped(F, cfg, q, k, v, max_budget, qa_selection="querywise")
+
+
+def test_querywise_all_query_aware_and_ties(F):
+    base = SMALL["gqa_bf16_2k"]
+    q, k, v = LayerGen(base).numpy_layer()
+    run_capped(F, base.with_(tau=0.84, gamma=0.8, min_budget=0), q, k, v, 0, qa_selection="querywise")
+    cfg = SMALL["ragged_bf16_1152"].with_(gamma=0.6, min_budget=0, tau=0.84)
+    z = np.zeros((1, cfg.Hq, cfg.N, cfg.d), np.float32)            # uniform rows: pure tie-break
+    zk = np.zeros((1, cfg.Hkv, cfg.N, cfg.d), np.float32)
+    run_capped(F, cfg, z, zk, LayerGen(cfg).numpy_layer()[2], 0, qa_selection="querywise")
