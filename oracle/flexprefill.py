@@ -187,15 +187,21 @@ def dot_seq(a: np.ndarray, b: np.ndarray, chunk: int = 4096) -> np.ndarray:
 
 def pool_mean(x: np.ndarray, bs: int) -> np.ndarray:
     """Block average ("block-pooled", Approach paragraph): for each block of
-    ``bs`` rows the rows are summed in ascending order in float32 and the sum
-    is multiplied by 1/bs (a power of two for the supported block sizes)."""
+    ``bs`` rows (the last block holds the remaining N - (nb-1) bs rows when
+    N is not a multiple of bs) the rows are summed in ascending order in
+    float32 and the sum is divided by the block's row count (one rounded
+    division; for a full block it equals the exact scaling by 1/bs)."""
     x = np.asarray(x, dtype=F32)
     n, d = x.shape
-    xb = x.reshape(n // bs, bs, d)
-    acc = np.zeros((n // bs, d), dtype=F32)
-    for r in range(bs):
-        acc = acc + xb[:, r, :]
-    return acc * F32(1.0 / bs)
+    nb = -(-n // bs)
+    out = np.zeros((nb, d), dtype=F32)
+    for kb in range(nb):
+        rows = x[kb * bs: min(n, kb * bs + bs)]
+        acc = np.zeros(d, dtype=F32)
+        for r in range(rows.shape[0]):
+            acc = acc + rows[r]
+        out[kb] = acc / F32(rows.shape[0])
+    return out
 
 
 def seq_sum_rows(x: np.ndarray) -> np.ndarray:
@@ -222,41 +228,52 @@ class LastBlockStats:
     a_true: np.ndarray   # [nb] block-pooled true distribution
 
 
+def _pad_blocks(x: np.ndarray, nb: int, bs: int) -> np.ndarray:
+    """x [..., N] zero-padded to [..., nb, bs] (padding adds +0 to sums)."""
+    pad = nb * bs - x.shape[-1]
+    if pad:
+        x = np.concatenate([x, np.zeros(x.shape[:-1] + (pad,), dtype=x.dtype)], axis=-1)
+    return x.reshape(x.shape[:-1] + (nb, bs))
+
+
 def last_block_stats(q: np.ndarray, k: np.ndarray, bs: int) -> LastBlockStats:
     """Exact causal softmax attention of the last ``bs`` queries over all keys
     (the "true distribution" of the Approach paragraph), summarised three ways:
     per key column, per diagonal offset and per key block.
 
-    Query row i sits at position pos_i = N - bs + i and sees keys j <= pos_i.
+    The representative rows are the last R = min(bs, N) queries; row i sits
+    at position pos_i = N - R + i and sees keys j <= pos_i.
     s[i, j] = fp32(dot_seq(q_i, k_j)) * C; M_i = max_j s[i, j];
     e = exp2_c(s - M_i) (0 for j > pos_i); zpart[i, kb] = sequential sum over
     the keys of block kb; Z_i = sequential sum of zpart over kb;
     p = e * fp32(1 / Z_i).  c[j] = sum over i ascending of p[i, j];
     g[o] = sum over i ascending with pos_i >= o of p[i, pos_i - o];
     a_true[kb] = t[kb] / T with t[kb] the sequential sum of c over block kb
-    and T the sequential sum of t."""
+    and T the sequential sum of t.  A partial last key block simply holds
+    fewer keys."""
     q = np.asarray(q, dtype=F32)
     k = np.asarray(k, dtype=F32)
     N, d = q.shape
-    nb = N // bs
+    nb = -(-N // bs)
+    R = min(bs, N)
     C = score_scale(d)
-    pos = N - bs + np.arange(bs)
-    s = dot_seq(q[N - bs:], k) * C
+    pos = N - R + np.arange(R)
+    s = dot_seq(q[N - R:], k) * C
     valid = np.arange(N)[None, :] <= pos[:, None]
     M = np.where(valid, s, F32(-np.inf)).max(axis=1).astype(F32)
     x = np.where(valid, s - M[:, None], F32(-np.inf)).astype(F32)
     e = exp2_c(x)
-    zpart = seq_sum_rows(e.reshape(bs, nb, bs))
+    zpart = seq_sum_rows(_pad_blocks(e, nb, bs))
     Z = seq_sum_rows(zpart)
     rZ = F32(1.0) / Z
     p = e * rZ[:, None]
     c = np.zeros(N, dtype=F32)
     g = np.zeros(N, dtype=F32)
-    for i in range(bs):
+    for i in range(R):
         c = c + p[i]
         pi = pos[i]
         g[: pi + 1] = g[: pi + 1] + p[i, pi::-1]
-    t = seq_sum_rows(c.reshape(nb, bs))
+    t = seq_sum_rows(_pad_blocks(c, nb, bs))
     T = seq_sum_rows(t[None, :])[0]
     a_true = t / T
     return LastBlockStats(M=M, zpart=zpart, Z=Z, c=c, g=g, a_true=a_true.astype(F32))
@@ -337,24 +354,32 @@ def select_cumulative(values: np.ndarray, gamma: float) -> np.ndarray:
 
 
 def vs_block_mask(sel_cols: np.ndarray, sel_diags: np.ndarray, bs: int) -> np.ndarray:
-    """Blocks touched by the selected vertical lines (key columns j) and slash
-    lines (offsets o = i - j), causally: block (qb, kb) with kb <= qb is
-    computed iff it contains at least one query/key pair (i, j), j <= i, with
-    j selected or i - j selected.  Closed form: column j touches kb = j // bs
-    in every row qb >= kb; offset o = a*bs + r touches the block diagonals
-    qb - kb = a and, when r > 0, qb - kb = a + 1."""
+    """Selected vertical columns and slash offsets -> causal block mask.
+
+    Any-touch rule (the block kernel computes whole blocks): block (qb, kb) is
+    computed iff it contains at least one query/key pair (i, j), j <= i < N,
+    with j selected or i - j selected.  Closed form: column j touches
+    kb = j // bs in every row qb >= kb; offset o = a*bs + r touches the block
+    diagonals qb - kb = a + 1 when r > 0 and qb - kb = a when r < tail(qb),
+    where tail(qb) is the number of query rows of block row qb (bs except
+    for a partial last block, N - (nb-1) bs)."""
     N = sel_cols.shape[0]
-    nb = N // bs
+    nb = -(-N // bs)
+    tail = N - (nb - 1) * bs
     col = np.zeros(nb, dtype=bool)
     col[np.nonzero(sel_cols)[0] // bs] = True
-    dg = np.zeros(nb + 1, dtype=bool)
     o = np.nonzero(sel_diags)[0]
-    dg[o // bs] = True
-    dg[(o[o % bs > 0] // bs) + 1] = True
+    dA = np.zeros(nb + 1, dtype=bool)          # some offset in diagonal a (any r)
+    dA[o // bs] = True
+    dT = np.zeros(nb + 1, dtype=bool)          # some offset in diagonal a with r < tail
+    dT[o[o % bs < tail] // bs] = True
+    dB = np.zeros(nb + 1, dtype=bool)          # some offset in diagonal a - 1 with r > 0
+    dB[(o[o % bs > 0] // bs) + 1] = True
     qb = np.arange(nb)[:, None]
     kb = np.arange(nb)[None, :]
     dist = np.clip(qb - kb, 0, nb)
-    return (kb <= qb) & (col[kb] | dg[dist])
+    own = np.where(qb == nb - 1, dT[dist], dA[dist])
+    return (kb <= qb) & (col[kb] | own | dB[dist])
 
 
 def tri_values(A: np.ndarray) -> np.ndarray:
@@ -423,9 +448,10 @@ def vs_block_scores(c: np.ndarray, g: np.ndarray, sel_cols: np.ndarray, sel_diag
     sum of the selected column scores c[j] in key block kb and diagmass[a] the
     sum of the selected diagonal scores g[o] whose offset touches block
     diagonal a (o // bs == a, or o // bs == a - 1 with o % bs > 0).  Sums in
-    float32, ascending index."""
+    float32, ascending index.  The partial last row of a ragged sequence uses
+    the same per-diagonal masses (a score, not an exact touch count)."""
     N = c.shape[0]
-    nb = N // bs
+    nb = -(-N // bs)
     colmass = np.zeros(nb, dtype=F32)
     diagmass = np.zeros(nb + 1, dtype=F32)
     for j in np.nonzero(sel_cols)[0]:
@@ -503,9 +529,9 @@ def plan_head(q: np.ndarray, k: np.ndarray, bs: int, gamma: float, tau: float,
     q = np.asarray(q, dtype=F32)
     k = np.asarray(k, dtype=F32)
     N, d = q.shape
-    if N % bs:
-        raise ValueError("N must be a multiple of the block size")
-    nb = N // bs
+    if N < 1:
+        raise ValueError("a head needs at least one token")
+    nb = -(-N // bs)
     qbar = pool_mean(q, bs)
     kbar = pool_mean(k, bs)
     st = last_block_stats(q, k, bs)
@@ -545,15 +571,16 @@ def attend_rows(q: np.ndarray, k: np.ndarray, v: np.ndarray, mask: np.ndarray,
                 bs: int, qbs: Iterable[int]) -> Dict[int, np.ndarray]:
     """float64 attention outputs of the query blocks ``qbs``: for query i the
     keys j <= i whose block (i // bs, j // bs) is in ``mask``; scores
-    q_i . k_j / sqrt(d); softmax; weighted sum of v_j."""
+    q_i . k_j / sqrt(d); softmax; weighted sum of v_j.  A partial last block
+    (N not a multiple of bs) has N - qb bs rows."""
     q = np.asarray(q, dtype=F64)
     k = np.asarray(k, dtype=F64)
     v = np.asarray(v, dtype=F64)
-    d = q.shape[1]
+    N, d = q.shape
     out = {}
     for qb in qbs:
-        i = qb * bs + np.arange(bs)
-        end = (qb + 1) * bs
+        end = min(N, (qb + 1) * bs)
+        i = np.arange(qb * bs, end)
         s = (q[i] @ k[:end].T) / math.sqrt(d)
         j = np.arange(end)
         keep = (j[None, :] <= i[:, None]) & mask[qb, j // bs][None, :]
@@ -566,7 +593,7 @@ def attend_rows(q: np.ndarray, k: np.ndarray, v: np.ndarray, mask: np.ndarray,
 
 
 def attend_head(q, k, v, mask, bs) -> np.ndarray:
-    nb = q.shape[0] // bs
+    nb = -(-q.shape[0] // bs)
     rows = attend_rows(q, k, v, mask, bs, range(nb))
     return np.concatenate([rows[qb] for qb in range(nb)], axis=0)
 

@@ -60,6 +60,36 @@ def brute_force_attention(q, k, v, mask, bs):
     return out
 
 
+@pytest.mark.parametrize("N,bs", [(1000, 128), (200, 64), (70, 128)])
+def test_ragged_gamma_one_is_full_causal_attention(N, bs):
+    cfg = BY_NAME["tiny_fp32_4k"].with_(N=1024)
+    q, k, v = (x[0, 0, :N] for x in LayerGen(cfg).numpy_layer())
+    P = O.plan_head(q, k, bs, 1.0, 0.1, 0)
+    nb = -(-N // bs)
+    assert np.array_equal(P.mask, O.dense_mask(nb)) and len(P.lists) == nb
+    out = O.attend_head(q, k, v, P.mask, bs)
+    assert out.shape == (N, 128)
+    np.testing.assert_allclose(out, sdpa_causal(q, k, v), rtol=0, atol=1e-12)
+
+
+def test_ragged_plan_lists_and_masked_attention():
+    """A ragged sequence's plan keeps the floor and causality, and its
+    attention equals the per-token brute force under the plan's mask."""
+    rng = np.random.default_rng(23)
+    bs, N, d = 8, 45, 16
+    q = rng.standard_normal((N, d)).astype(F32)
+    k = rng.standard_normal((N, d)).astype(F32)
+    v = rng.standard_normal((N, d)).astype(F32)
+    for tau in (0.0, 0.84):
+        P = O.plan_head(q, k, bs, 0.6, tau, 2 * bs)
+        nb = -(-N // bs)
+        assert len(P.lists) == nb
+        for qb, lst in enumerate(P.lists):
+            assert len(lst) >= min(qb + 1, 2) and lst.max() <= qb
+        np.testing.assert_allclose(O.attend_head(q, k, v, P.mask, bs),
+                                   brute_force_attention(q, k, v, P.mask, bs), rtol=0, atol=1e-12)
+
+
 def test_masked_attention_equals_per_token_brute_force():
     rng = np.random.default_rng(21)
     bs, nb, d = 8, 5, 16

@@ -97,21 +97,43 @@ def test_pool_mean_matches_avg_pool():
         np.testing.assert_allclose(p, ref, rtol=0, atol=1e-6)
 
 
+def test_pool_mean_ragged_tail_is_the_mean_of_the_rows_present():
+    rng = np.random.default_rng(41)
+    for n, bs in ((1000, 128), (64 * 3 + 1, 64), (37, 64)):
+        x = rng.standard_normal((n, 128)).astype(F32)
+        p = O.pool_mean(x, bs)
+        nb = -(-n // bs)
+        assert p.shape == (nb, 128)
+        for kb in range(nb):
+            ref = x[kb * bs: (kb + 1) * bs].astype(F64).mean(axis=0)
+            np.testing.assert_allclose(p[kb], ref, rtol=0, atol=2e-6)
+        # full blocks: identical to the exact 1/bs scaling
+        full = n // bs
+        if full:
+            acc = np.zeros((full, 128), F32)
+            for r in range(bs):
+                acc = acc + x[: full * bs].reshape(full, bs, 128)[:, r]
+            assert np.array_equal(p[:full], acc * F32(1.0 / bs))
+
+
 def _ideal_last_block(q, k, bs):
-    """float64 causal softmax of the last block, via torch library calls."""
+    """float64 causal softmax of the last min(bs, N) queries, via torch
+    library calls."""
     N, d = q.shape
-    qt = torch.from_numpy(q).double()[N - bs:]
+    R = min(bs, N)
+    qt = torch.from_numpy(q).double()[N - R:]
     kt = torch.from_numpy(k).double()
     s = qt @ kt.T / math.sqrt(d)
-    pos = torch.arange(N - bs, N)[:, None]
+    pos = torch.arange(N - R, N)[:, None]
     s = s.masked_fill(torch.arange(N)[None, :] > pos, float("-inf"))
     p = torch.softmax(s, dim=1)
     c = p.sum(0)
     # diagonal sums: g[o] = sum_i p[i, pos_i - o] -> put p in an N x N causal frame
     full = torch.zeros(N, N, dtype=torch.float64)
-    full[N - bs:] = p
+    full[N - R:] = p
     g = torch.stack([torch.diagonal(full, offset=-o).sum() for o in range(N)])
-    a = c.reshape(N // bs, bs).sum(1)
+    nb = -(-N // bs)
+    a = torch.nn.functional.pad(c, (0, nb * bs - N)).reshape(nb, bs).sum(1)
     return p.numpy(), c.numpy(), g.numpy(), (a / a.sum()).numpy()
 
 
@@ -132,6 +154,23 @@ def test_last_block_stats_match_float64_softmax(bs):
     assert abs(float(st.g.astype(F64).sum()) - bs) < 1e-3
     # causality: the last query row sees the whole sequence, the first only N-bs+1 keys
     assert st.g[N - bs + 1:].max() <= c.max()
+
+
+@pytest.mark.parametrize("N,bs", [(1000, 128), (8 * 64 + 5, 64), (100, 128), (1, 64)])
+def test_last_block_stats_ragged(N, bs):
+    """N not a multiple of the block (and N below one block): the last
+    min(bs, N) queries, a partial last key block."""
+    rng = np.random.default_rng(N)
+    q = rng.standard_normal((N, 128)).astype(F32)
+    k = rng.standard_normal((N, 128)).astype(F32)
+    st = O.last_block_stats(q, k, bs)
+    p, c, g, a = _ideal_last_block(q, k, bs)
+    R = min(bs, N)
+    assert st.M.shape == (R,) and st.a_true.shape == (-(-N // bs),)
+    np.testing.assert_allclose(st.c, c, rtol=2e-5, atol=1e-8)
+    np.testing.assert_allclose(st.g, g, rtol=2e-5, atol=1e-8)
+    np.testing.assert_allclose(st.a_true, a, rtol=2e-5, atol=1e-9)
+    assert abs(float(st.c.astype(F64).sum()) - R) < 1e-3
 
 
 def test_estimate_map_matches_float64_softmax():

@@ -94,7 +94,8 @@ def token_level_vs_blocks(sel_cols, sel_diags, bs):
     i = np.arange(N)[:, None]
     j = np.arange(N)[None, :]
     tok = (j <= i) & (sel_cols[j] | sel_diags[np.clip(i - j, 0, N - 1)])
-    nb = N // bs
+    nb = -(-N // bs)
+    tok = np.pad(tok, ((0, nb * bs - N), (0, nb * bs - N)))
     return tok.reshape(nb, bs, nb, bs).any(axis=(1, 3))
 
 
@@ -111,6 +112,19 @@ def test_vs_block_mask_equals_token_level_any(seed):
         sel_diags[bs] = True           # r = 0: exactly one block diagonal
     got = O.vs_block_mask(sel_cols, sel_diags, bs)
     assert np.array_equal(got, token_level_vs_blocks(sel_cols, sel_diags, bs))
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_vs_block_mask_ragged_equals_token_level_any(seed):
+    """A partial last query block: an offset reaches its own block diagonal
+    there only if its remainder is below the block's row count."""
+    rng = np.random.default_rng(500 + seed)
+    bs = int(rng.choice([4, 8, 16]))
+    N = int(rng.integers(1, 10 * bs))
+    sel_cols = rng.random(N) < rng.uniform(0, 0.15)
+    sel_diags = rng.random(N) < rng.uniform(0, 0.3)
+    got = O.vs_block_mask(sel_cols, sel_diags, bs)
+    assert np.array_equal(got, token_level_vs_blocks(sel_cols, sel_diags, bs)), (N, bs)
 
 
 def test_floor_tops_up_nearest_first():
