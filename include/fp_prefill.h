@@ -19,12 +19,23 @@
  * in one fixed ("canonical") arithmetic, so plans are bit-reproducible.
  *
  * Conventions shared by every entry point
- *   Layout: Q [B, Hq, N, d], K and V [B, Hkv, N, d], O [B, Hq, N, d]; dense,
- *     row-major, device pointers.  Query head h reads key/value head
- *     h / (Hq / Hkv) (grouped-query attention).  Q, K, V and O share one dtype.
- *   Supported shapes: d = 128; block in {64, 128}; N a multiple of block,
- *     1 <= N / block <= 4096; Hq a multiple of Hkv.  B, Hq or N equal to 0
- *     is an empty problem: FP_OK, nothing is launched.
+ *   Layouts (dense, row-major, device pointers; Q, K, V and O share one dtype):
+ *     FP_LAYOUT_BHND  Q [B, Hq, N, d], K and V [B, Hkv, N, d], O like Q --
+ *                     B sequences of N tokens (fp_prefill_plan[_ex],
+ *                     fp_dense_attend);
+ *     FP_LAYOUT_THD   packed sequences of different lengths, Q [T, Hq, d],
+ *                     K and V [T, Hkv, d], O like Q; sequence b holds tokens
+ *                     cu_seqlens[b] .. cu_seqlens[b+1]-1 (the *_varlen calls).
+ *     Query head h reads key/value head h / (Hq / Hkv) (grouped-query
+ *     attention).  Sequences are independent.
+ *   Sequence lengths: any L >= 0.  A sequence has nb = ceil(L / block) query
+ *     and key blocks; when L is not a multiple of the block, the last block
+ *     holds the remaining L - (nb - 1) block tokens (its block mean averages
+ *     those rows; the representative queries of step 1 are the last
+ *     min(block, L) tokens).
+ *   Supported shapes: d = 128; block in {64, 128}; nb <= 4096 per sequence;
+ *     Hq a multiple of Hkv.  A problem without tokens or heads is empty:
+ *     FP_OK, nothing is launched.
  *   Streams: `stream` is a hipStream_t (NULL = the legacy default stream).
  *     All device work is enqueued on it asynchronously; no call below blocks
  *     the host unless its comment says "synchronizes".
@@ -49,7 +60,7 @@ typedef enum fp_status {
     FP_OK = 0,
     FP_ERR_INVALID_ARG = -1,   /* null pointer, gamma outside (0,1], tau < 0, ... */
     FP_ERR_UNSUPPORTED = -2,   /* d != 128, block not 64/128, unknown dtype */
-    FP_ERR_SHAPE = -3,         /* N % block != 0, Hq % Hkv != 0, sizes too large */
+    FP_ERR_SHAPE = -3,         /* Hq % Hkv != 0, more than 4096 blocks, sizes too large */
     FP_ERR_OOM = -4,           /* device allocation failed */
     FP_ERR_HIP = -5            /* a HIP runtime call failed */
 } fp_status;
@@ -59,18 +70,23 @@ typedef enum fp_dtype { FP_BF16 = 0, FP_FP32 = 1 } fp_dtype;
 /* Head pattern codes (fp_plan_copy_out `pattern`). */
 enum { FP_PATTERN_VERTICAL_SLASH = 0, FP_PATTERN_QUERY_AWARE = 1 };
 
+typedef enum fp_layout { FP_LAYOUT_BHND = 0, FP_LAYOUT_THD = 1 } fp_layout;
+
 typedef struct fp_plan fp_plan;   /* opaque; device-resident block lists */
 
 typedef struct fp_plan_info {
-    int B, Hq, Hkv, N, d, block, nb;   /* nb = N / block */
+    int B, Hq, Hkv, N, d, block, nb;   /* B sequences; N = longest, nb = ceil(N / block) */
     fp_dtype dtype;
     float gamma, tau;
     int min_budget;
     long long total_blocks;            /* selected (query-block, key-block) pairs, all heads */
-    long long dense_blocks;            /* B * Hq * nb (nb + 1) / 2 */
+    long long dense_blocks;            /* causal blocks: sum over sequences of Hq * nb (nb + 1) / 2 */
     int query_aware_heads;             /* heads whose pattern is query-aware */
     int max_budget;                    /* tokens, 0 = uncapped */
     int qa_selection;                  /* fp_qa_selection */
+    int layout;                        /* fp_layout */
+    long long tokens;                  /* B * N (BHND) or T (THD) */
+    long long rows;                    /* query-block rows of all heads: sum over sequences of Hq * nb */
 } fp_plan_info;
 
 /* How a query-aware head selects its blocks from the estimated block map. */
@@ -97,7 +113,8 @@ typedef struct fp_plan_options {
  *     filled nearest-first from the diagonal (pages: 1024 default, 2048).
  *   On FP_OK *out receives a new plan (released with fp_plan_destroy).  The
  *   plan's buffers are allocated stream-ordered on `stream`; a transient
- *   workspace of B*Hq*block*N*4 bytes is used and released within the call.
+ *   workspace of B*Hq*block*ceil(N/256)*256*4 bytes is used and released
+ *   within the call.
  */
 fp_status fp_prefill_plan(const void* q, const void* k, fp_dtype dtype,
                           int B, int Hq, int Hkv, int N, int d, int block,
@@ -134,11 +151,32 @@ fp_status fp_prefill_plan_ex(const void* q, const void* k, fp_dtype dtype,
  * fp_prefill_attend -- step 3: O = causal softmax(Q K^T / sqrt(d)) V with
  *   each query block attending only to the key blocks its plan selected.
  *   q must be the tensor the plan was built from (the plan stores lists,
- *   not values); k and v of the plan's shape.  o is written in full.
- *   Uses a stream-ordered workspace of B*Hkv*N*d elements (V transposed).
+ *   not values); k and v of the plan's shape and layout.  Every token row
+ *   of o is written.  Uses a stream-ordered workspace of V transposed, per
+ *   sequence Hkv*d*nb*block elements.
  */
 fp_status fp_prefill_attend(const fp_plan* plan, const void* q, const void* k,
                             const void* v, void* o, void* stream);
+
+/*
+ * fp_prefill_plan_varlen -- fp_prefill_plan_ex for packed sequences of
+ *   different lengths (FP_LAYOUT_THD): q [T, Hq, d], k [T, Hkv, d] with
+ *   T = cu_seqlens[nseq].  cu_seqlens is a HOST array of nseq + 1 ints,
+ *   cu_seqlens[0] = 0, non-decreasing (a zero-length sequence has no rows;
+ *   its heads report pattern 0 and divergence 0).  Every sequence is planned
+ *   exactly as fp_prefill_plan_ex would plan it alone; the call reuses one
+ *   transient workspace of Hq*block*ceil(L/256)*256*4 bytes for the longest
+ *   sequence L.  The plan records the layout: fp_prefill_attend then takes
+ *   packed q, k, v and o.
+ *   FP_ERR_INVALID_ARG for a NULL or malformed cu_seqlens; FP_ERR_SHAPE for a
+ *   sequence of more than 4096 blocks.
+ */
+fp_status fp_prefill_plan_varlen(const void* q, const void* k, fp_dtype dtype,
+                                 int nseq, const int* cu_seqlens,
+                                 int Hq, int Hkv, int d, int block,
+                                 float gamma, float tau, int min_budget,
+                                 const fp_plan_options* options,
+                                 void* stream, fp_plan** out);
 
 /*
  * fp_dense_attend -- full causal attention with the same tile kernel (every
@@ -150,6 +188,11 @@ fp_status fp_dense_attend(const void* q, const void* k, const void* v, void* o,
                           fp_dtype dtype, int B, int Hq, int Hkv, int N, int d,
                           int block, void* stream);
 
+/* fp_dense_attend for packed sequences (FP_LAYOUT_THD, host cu_seqlens). */
+fp_status fp_dense_attend_varlen(const void* q, const void* k, const void* v, void* o,
+                                 fp_dtype dtype, int nseq, const int* cu_seqlens,
+                                 int Hq, int Hkv, int d, int block, void* stream);
+
 /* Plan summary.  Synchronizes the plan's stream. */
 fp_status fp_plan_info_get(const fp_plan* plan, fp_plan_info* out);
 
@@ -157,7 +200,8 @@ fp_status fp_plan_info_get(const fp_plan* plan, fp_plan_info* out);
  * fp_plan_copy_out -- host copies of the plan (synchronizes `stream`).
  *   pattern [B*Hq]          FP_PATTERN_* per head        (may be NULL)
  *   djs     [B*Hq]          sqrt(JSD) per head            (may be NULL)
- *   row_ptr [B*Hq*nb + 1]   CSR row offsets, rows ordered (b, h, row)
+ *   row_ptr [rows + 1]      CSR row offsets, rows ordered (b, h, row); a
+ *                           sequence contributes Hq * its nb rows
  *   col_idx [total_blocks]  key-block indices, ascending within a row
  *   row_ptr and col_idx may both be NULL; if one is given both must be.
  */
@@ -166,11 +210,15 @@ fp_status fp_plan_copy_out(const fp_plan* plan, unsigned char* pattern, double* 
 
 /*
  * fp_plan_copy_debug -- host copy of an intermediate of steps 1-2
- *   (synchronizes the plan's stream).  `bytes` must equal the item's size:
+ *   (synchronizes the plan's stream).  `bytes` must equal the item's size.
+ *   Shapes for B sequences of N tokens; with packed sequences the arrays of
+ *   the non-empty sequences follow one another, each with its own N and nb:
  *   FP_DBG_QBAR   float [B*Hq][nb][d]      block means of Q
  *   FP_DBG_KBAR   float [B*Hkv][nb][d]     block means of K
- *   FP_DBG_ROWMAX float [B*Hq][block]      last-block row maxima (scaled scores)
- *   FP_DBG_ROWSUM float [B*Hq][block]      last-block row sums of exp2
+ *   FP_DBG_ROWMAX float [B*Hq][block]      last-block row maxima (scaled scores);
+ *                                          rows i < block - min(block, N) do not
+ *                                          exist and read 0
+ *   FP_DBG_ROWSUM float [B*Hq][block]      last-block row sums of exp2 (same rows)
  *   FP_DBG_COLSUM float [B*Hq][N]          vertical line scores
  *   FP_DBG_DIAGSUM float [B*Hq][N]         slash line scores (offset i - j)
  *   FP_DBG_ATRUE  float [B*Hq][nb]         block-pooled true distribution

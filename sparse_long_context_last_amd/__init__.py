@@ -7,6 +7,9 @@ step of the method runs in the library's HIP kernels.
     plan = plan(q, k, block=128, gamma=0.95, tau=0.1, min_budget=1024)
     o = attend(plan, q, k, v)          # block-sparse causal attention
     o_dense = dense_attend(q, k, v, block=128)
+    # packed sequences of different lengths: q [T, Hq, d], k, v [T, Hkv, d]
+    p = plan_varlen(q, k, cu_seqlens, block=128)
+    o = attend(p, q, k, v)
 """
 from __future__ import annotations
 
@@ -18,8 +21,8 @@ import numpy as np
 from . import _lib
 from ._lib import FpError, PlanInfo  # noqa: F401
 
-__all__ = ["Plan", "plan", "attend", "dense_attend", "profile_enable", "profile_read",
-           "canonical_constants", "FpError"]
+__all__ = ["Plan", "plan", "plan_varlen", "attend", "dense_attend", "dense_attend_varlen",
+           "profile_enable", "profile_read", "canonical_constants", "FpError"]
 
 
 def _torch():
@@ -36,13 +39,13 @@ def _dtype_code(t) -> int:
     raise TypeError(f"unsupported dtype {t.dtype} (bfloat16 or float32)")
 
 
-def _check_tensor(t, name: str) -> None:
+def _check_tensor(t, name: str, ndim: int = 4) -> None:
     if not t.is_cuda:
         raise ValueError(f"{name} must be a device tensor")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
-    if t.dim() != 4:
-        raise ValueError(f"{name} must be [B, H, N, d]")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must be " + ("[B, H, N, d]" if ndim == 4 else "[T, H, d]"))
 
 
 def _stream_ptr(stream=None) -> int:
@@ -51,13 +54,31 @@ def _stream_ptr(stream=None) -> int:
     return s.cuda_stream
 
 
+def _cu_array(cu_seqlens) -> np.ndarray:
+    """Host int32 copy of cu_seqlens (list, numpy array or CPU tensor)."""
+    if hasattr(cu_seqlens, "detach"):
+        cu_seqlens = cu_seqlens.detach().cpu().numpy()
+    cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int64))
+    if cu.ndim != 1 or cu.size < 1:
+        raise ValueError("cu_seqlens must be a 1-d array of nseq + 1 offsets")
+    if cu.max(initial=0) > np.iinfo(np.int32).max:
+        raise ValueError("cu_seqlens exceeds int32")
+    return cu.astype(np.int32)
+
+
 class Plan:
     """Device-resident FlexPrefill plan (pattern per head, block lists)."""
 
-    def __init__(self, handle: C.c_void_p, shape, dtype_code: int, stream):
+    def __init__(self, handle: C.c_void_p, Hq, Hkv, d, block, seqlens, layout: int, dtype_code: int, stream,
+                 N: Optional[int] = None):
         self._h = handle
-        self.B, self.Hq, self.Hkv, self.N, self.d, self.block = shape
-        self.nb = self.N // self.block if self.block else 0
+        self.Hq, self.Hkv, self.d, self.block = Hq, Hkv, d, block
+        self.seqlens = [int(x) for x in seqlens]
+        self.layout = layout
+        self.B = len(self.seqlens)
+        self.N = max(self.seqlens, default=0) if N is None else int(N)
+        self.nb = -(-self.N // block) if block else 0
+        self.nbs = [-(-L // block) for L in self.seqlens]
         self.dtype_code = dtype_code
         self._stream = stream
 
@@ -78,7 +99,7 @@ class Plan:
         BH = self.B * self.Hq
         pattern = np.zeros(BH, np.uint8)
         djs = np.zeros(BH, np.float64)
-        row_ptr = np.zeros(BH * self.nb + 1, np.int32)
+        row_ptr = np.zeros(inf.rows + 1, np.int32)
         col_idx = np.zeros(max(inf.total_blocks, 1), np.int32)
         _lib.check(_lib.load().fp_plan_copy_out(
             self.handle, pattern.ctypes.data, djs.ctypes.data, row_ptr.ctypes.data,
@@ -86,31 +107,59 @@ class Plan:
         return pattern, djs, row_ptr, col_idx[: inf.total_blocks]
 
     def lists(self):
-        """Per (b*Hq + h) a list of per-row int32 arrays of key-block indices."""
+        """Per (b*Hq + h) a list of per-row int32 arrays of key-block indices
+        (sequence b has ceil(L_b / block) rows)."""
         pattern, djs, row_ptr, col_idx = self.copy_out()
         out = []
-        for bh in range(self.B * self.Hq):
-            rows = []
-            for r in range(self.nb):
-                i = bh * self.nb + r
-                rows.append(col_idx[row_ptr[i]: row_ptr[i + 1]].copy())
-            out.append(rows)
+        i = 0
+        for b in range(self.B):
+            for h in range(self.Hq):
+                rows = []
+                for r in range(self.nbs[b]):
+                    rows.append(col_idx[row_ptr[i]: row_ptr[i + 1]].copy())
+                    i += 1
+                out.append(rows)
+        return out
+
+    def _item_shape(self, item: str, L: int, nb: int):
+        d, bs = self.d, self.block
+        return {"qbar": ((self.Hq, nb, d), np.float32), "kbar": ((self.Hkv, nb, d), np.float32),
+                "rowmax": ((self.Hq, bs), np.float32), "rowsum": ((self.Hq, bs), np.float32),
+                "colsum": ((self.Hq, L), np.float32), "diagsum": ((self.Hq, L), np.float32),
+                "atrue": ((self.Hq, nb), np.float32), "ahat": ((self.Hq, nb * (nb + 1) // 2), np.float32),
+                "counts": ((self.Hq, nb), np.int32)}[item]
+
+    def debug_seqs(self, item: str):
+        """An intermediate of steps 1-2 per sequence: a list over sequences of
+        arrays [Hq, ...] ([Hkv, ...] for kbar), None for an empty sequence."""
+        parts, total, dt = [], 0, np.float32
+        for L, nb in zip(self.seqlens, self.nbs):
+            shape, dt = self._item_shape(item, L, nb)
+            parts.append(shape if L > 0 else None)
+            total += int(np.prod(shape)) if L > 0 else 0
+        flat = np.zeros(total, dt)
+        _lib.check(_lib.load().fp_plan_copy_debug(self.handle, _lib.DEBUG_ITEMS[item],
+                                                  flat.ctypes.data, flat.nbytes), "fp_plan_copy_debug")
+        out, o = [], 0
+        for shape in parts:
+            if shape is None:
+                out.append(None)
+                continue
+            n = int(np.prod(shape))
+            out.append(flat[o: o + n].reshape(shape))
+            o += n
         return out
 
     def debug(self, item: str) -> np.ndarray:
-        BH, nb, bs, N = self.B * self.Hq, self.nb, self.block, self.N
-        shapes = {"qbar": ((BH, nb, self.d), np.float32),
-                  "kbar": ((self.B * self.Hkv, nb, self.d), np.float32),
-                  "rowmax": ((BH, bs), np.float32), "rowsum": ((BH, bs), np.float32),
-                  "colsum": ((BH, N), np.float32), "diagsum": ((BH, N), np.float32),
-                  "atrue": ((BH, nb), np.float32),
-                  "ahat": ((BH, nb * (nb + 1) // 2), np.float32),
-                  "counts": ((BH, nb), np.int32)}
-        shape, dt = shapes[item]
-        arr = np.zeros(shape, dt)
-        _lib.check(_lib.load().fp_plan_copy_debug(self.handle, _lib.DEBUG_ITEMS[item],
-                                                  arr.ctypes.data, arr.nbytes), "fp_plan_copy_debug")
-        return arr
+        """An intermediate for sequences of one length, stacked over
+        (b, head): [B*Hq, ...] ([B*Hkv, ...] for kbar)."""
+        if len(set(self.seqlens)) > 1:
+            raise ValueError("sequences differ in length: use debug_seqs")
+        parts = [x for x in self.debug_seqs(item) if x is not None]
+        if not parts:
+            shape, dt = self._item_shape(item, self.N, self.nb)
+            return np.zeros((0,) + shape[1:], dt)
+        return np.concatenate(parts, axis=0)
 
     def destroy(self) -> None:
         if self._h is not None:
@@ -124,12 +173,18 @@ class Plan:
             pass
 
 
+def _options(max_budget: int, qa_selection: str):
+    if qa_selection not in _lib.QA_SELECTION:
+        raise ValueError(f"qa_selection must be one of {sorted(_lib.QA_SELECTION)}")
+    return _lib.PlanOptions(int(max_budget), _lib.QA_SELECTION[qa_selection])
+
+
 def plan(q, k, block: int = 128, gamma: float = 0.95, tau: float = 0.1,
          min_budget: int = 1024, max_budget: int = 0, qa_selection: str = "flattened",
          stream=None) -> Plan:
-    """Pattern determination and index selection (fp_prefill_plan_ex;
-    max_budget = 0 leaves rows uncapped; qa_selection "flattened" or
-    "querywise")."""
+    """Pattern determination and index selection for q [B, Hq, N, d],
+    k [B, Hkv, N, d] (fp_prefill_plan_ex; max_budget = 0 leaves rows
+    uncapped; qa_selection "flattened" or "querywise")."""
     _check_tensor(q, "q")
     _check_tensor(k, "k")
     if q.dtype != k.dtype:
@@ -139,30 +194,57 @@ def plan(q, k, block: int = 128, gamma: float = 0.95, tau: float = 0.1,
     if tuple(k.shape) != (B, Hkv, N, d):
         raise ValueError("k must be [B, Hkv, N, d] with q's B, N and d")
     dt = _dtype_code(q)
-    if qa_selection not in _lib.QA_SELECTION:
-        raise ValueError(f"qa_selection must be one of {sorted(_lib.QA_SELECTION)}")
-    opts = _lib.PlanOptions(int(max_budget), _lib.QA_SELECTION[qa_selection])
+    opts = _options(max_budget, qa_selection)
     h = C.c_void_p()
     _lib.check(_lib.load().fp_prefill_plan_ex(q.data_ptr(), k.data_ptr(), dt, B, Hq, Hkv, N, d, block,
                                               float(gamma), float(tau), int(min_budget), C.byref(opts),
                                               _stream_ptr(stream), C.byref(h)), "fp_prefill_plan_ex")
-    return Plan(h, (B, Hq, Hkv, N, d, block), dt, stream)
+    return Plan(h, Hq, Hkv, d, block, [N] * B, _lib.FP_LAYOUT_BHND, dt, stream, N=N)
+
+
+def plan_varlen(q, k, cu_seqlens, block: int = 128, gamma: float = 0.95, tau: float = 0.1,
+                min_budget: int = 1024, max_budget: int = 0, qa_selection: str = "flattened",
+                stream=None) -> Plan:
+    """The same for packed sequences: q [T, Hq, d], k [T, Hkv, d], sequence b
+    at tokens cu_seqlens[b] .. cu_seqlens[b+1]-1 (fp_prefill_plan_varlen)."""
+    _check_tensor(q, "q", 3)
+    _check_tensor(k, "k", 3)
+    if q.dtype != k.dtype:
+        raise TypeError("q and k must share a dtype")
+    T, Hq, d = q.shape
+    Hkv = k.shape[1]
+    cu = _cu_array(cu_seqlens)
+    if tuple(k.shape) != (T, Hkv, d) or int(cu[-1]) != T:
+        raise ValueError("k must be [T, Hkv, d] and cu_seqlens[-1] must equal T")
+    dt = _dtype_code(q)
+    opts = _options(max_budget, qa_selection)
+    h = C.c_void_p()
+    _lib.check(_lib.load().fp_prefill_plan_varlen(q.data_ptr(), k.data_ptr(), dt, cu.size - 1, cu.ctypes.data,
+                                                  Hq, Hkv, d, block, float(gamma), float(tau), int(min_budget),
+                                                  C.byref(opts), _stream_ptr(stream), C.byref(h)),
+               "fp_prefill_plan_varlen")
+    return Plan(h, Hq, Hkv, d, block, np.diff(cu).tolist(), _lib.FP_LAYOUT_THD, dt, stream)
 
 
 def attend(p: Plan, q, k, v, out=None, stream=None):
     """Block-sparse causal attention over the plan's selection (fp_prefill_attend)."""
     torch = _torch()
+    ndim = 4 if p.layout == _lib.FP_LAYOUT_BHND else 3
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
-        _check_tensor(t, n)
-    if tuple(q.shape) != (p.B, p.Hq, p.N, p.d) or tuple(k.shape) != (p.B, p.Hkv, p.N, p.d) \
-            or k.shape != v.shape:
+        _check_tensor(t, n, ndim)
+    if ndim == 4:
+        ok = tuple(q.shape) == (p.B, p.Hq, p.N, p.d) and tuple(k.shape) == (p.B, p.Hkv, p.N, p.d)
+    else:
+        T = sum(p.seqlens)
+        ok = tuple(q.shape) == (T, p.Hq, p.d) and tuple(k.shape) == (T, p.Hkv, p.d)
+    if not ok or k.shape != v.shape:
         raise ValueError("q / k / v shapes do not match the plan")
     if _dtype_code(q) != p.dtype_code or k.dtype != q.dtype or v.dtype != q.dtype:
         raise TypeError("q, k, v must have the plan's dtype")
     if out is None:
         out = torch.empty_like(q)
     else:
-        _check_tensor(out, "out")
+        _check_tensor(out, "out", ndim)
         if out.shape != q.shape or out.dtype != q.dtype:
             raise ValueError("out must match q")
     _lib.check(_lib.load().fp_prefill_attend(p.handle, q.data_ptr(), k.data_ptr(), v.data_ptr(),
@@ -185,6 +267,25 @@ def dense_attend(q, k, v, block: int = 128, out=None, stream=None):
     _lib.check(_lib.load().fp_dense_attend(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                                            dt, B, Hq, Hkv, N, d, block, _stream_ptr(stream)),
                "fp_dense_attend")
+    return out
+
+
+def dense_attend_varlen(q, k, v, cu_seqlens, block: int = 128, out=None, stream=None):
+    """Full causal attention of packed sequences (fp_dense_attend_varlen)."""
+    torch = _torch()
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _check_tensor(t, n, 3)
+    T, Hq, d = q.shape
+    Hkv = k.shape[1]
+    cu = _cu_array(cu_seqlens)
+    if tuple(k.shape) != (T, Hkv, d) or k.shape != v.shape or int(cu[-1]) != T:
+        raise ValueError("k and v must be [T, Hkv, d] and cu_seqlens[-1] must equal T")
+    dt = _dtype_code(q)
+    if out is None:
+        out = torch.empty_like(q)
+    _lib.check(_lib.load().fp_dense_attend_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                                  dt, cu.size - 1, cu.ctypes.data, Hq, Hkv, d, block,
+                                                  _stream_ptr(stream)), "fp_dense_attend_varlen")
     return out
 
 

@@ -17,6 +17,8 @@ FP_BF16 = 0
 FP_FP32 = 1
 FP_PATTERN_VERTICAL_SLASH = 0
 FP_PATTERN_QUERY_AWARE = 1
+FP_LAYOUT_BHND = 0
+FP_LAYOUT_THD = 1
 DEBUG_ITEMS = {"qbar": 0, "kbar": 1, "rowmax": 2, "rowsum": 3, "colsum": 4,
                "diagsum": 5, "atrue": 6, "ahat": 7, "counts": 8}
 
@@ -27,7 +29,8 @@ class PlanInfo(C.Structure):
                 ("gamma", C.c_float), ("tau", C.c_float), ("min_budget", C.c_int),
                 ("total_blocks", C.c_longlong), ("dense_blocks", C.c_longlong),
                 ("query_aware_heads", C.c_int), ("max_budget", C.c_int),
-                ("qa_selection", C.c_int)]
+                ("qa_selection", C.c_int), ("layout", C.c_int), ("tokens", C.c_longlong),
+                ("rows", C.c_longlong)]
 
 
 class PlanOptions(C.Structure):
@@ -45,8 +48,13 @@ SIGNATURES = {
     "fp_prefill_plan_ex": (C.c_int, [C.c_void_p, C.c_void_p, C.c_int, C.c_int, C.c_int, C.c_int,
                                      C.c_int, C.c_int, C.c_int, C.c_float, C.c_float, C.c_int,
                                      C.POINTER(PlanOptions), C.c_void_p, C.POINTER(C.c_void_p)]),
+    "fp_prefill_plan_varlen": (C.c_int, [C.c_void_p, C.c_void_p, C.c_int, C.c_int, C.c_void_p, C.c_int,
+                                         C.c_int, C.c_int, C.c_int, C.c_float, C.c_float, C.c_int,
+                                         C.POINTER(PlanOptions), C.c_void_p, C.POINTER(C.c_void_p)]),
     "fp_prefill_attend": (C.c_int, [C.c_void_p] * 6),
     "fp_dense_attend": (C.c_int, [C.c_void_p] * 4 + [C.c_int] * 7 + [C.c_void_p]),
+    "fp_dense_attend_varlen": (C.c_int, [C.c_void_p] * 4 + [C.c_int, C.c_int, C.c_void_p] + [C.c_int] * 4
+                               + [C.c_void_p]),
     "fp_plan_info_get": (C.c_int, [C.c_void_p, C.POINTER(PlanInfo)]),
     "fp_plan_copy_out": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
                                    C.c_void_p]),

@@ -61,17 +61,42 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // (Grouping the query heads of one key/value head per XCD, or interleaving
 // all heads per query block, measured 1.6x-4.6x slower on the sparse 128k
 // layer: head-to-head density differences then unbalance the XCDs.)
+// With several segments (sequences of different lengths) the items of each
+// segment follow one another; a workgroup finds its segment by binary
+// search in the segment table.
 struct RowId {
-    int bh, qb;
-    size_t kvbh;
+    int qb, L, cnt;
+    size_t q0, k0, vt0;     // element offsets: token 0 of the query head, of its kv head; its V^T rows
+    int NT;                 // V^T row length
+    const int* lst;
 };
 
-__device__ __forceinline__ RowId work_row(const AttnArgs& a, int item) {
-    const int group = a.Hq / a.Hkv;
+__device__ __forceinline__ RowId work_row(const AttnArgs& a, long long item, bool sparse) {
+    int lo = 0, hi = a.nseg - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (a.segs[mid].item0 <= item) lo = mid;
+        else hi = mid - 1;
+    }
+    const AttnSeg sg = a.segs[lo];
+    const long long local = item - sg.item0;
+    const int bh = (int)(local / sg.nb);
     RowId r;
-    r.bh = item / a.nb;
-    r.qb = a.nb - 1 - item % a.nb;
-    r.kvbh = (size_t)(r.bh / a.Hq) * a.Hkv + (r.bh % a.Hq) / group;
+    r.qb = sg.nb - 1 - (int)(local % sg.nb);
+    r.L = sg.L;
+    r.NT = sg.NT;
+    const int bl = bh / a.Hq, h = bh % a.Hq, kvh = h / (a.Hq / a.Hkv);
+    r.q0 = (size_t)sg.qoff + (size_t)bl * a.qs.bst + (size_t)h * a.qs.hs;
+    r.k0 = (size_t)sg.koff + (size_t)bl * a.ks.bst + (size_t)kvh * a.ks.hs;
+    r.vt0 = (size_t)sg.vtoff + (size_t)(bl * a.Hkv + kvh) * kHeadDim * sg.NT;
+    if (sparse) {
+        const long long tri = (long long)sg.nb * (sg.nb + 1) / 2;
+        r.cnt = a.counts[sg.coff + (long long)bh * sg.nb + r.qb];
+        r.lst = a.lists + sg.loff + (long long)bh * tri + (long long)r.qb * (r.qb + 1) / 2;
+    } else {
+        r.cnt = r.qb + 1;
+        r.lst = nullptr;
+    }
     return r;
 }
 
@@ -93,28 +118,24 @@ __global__ __launch_bounds__(2 * BS, BS == 128 ? 2 : 1) void k_attn_bf16(AttnArg
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index (uniform)
     const int l32 = lane & 31, hh = lane >> 5;
-    const RowId rid = work_row(a, blockIdx.x);
-    const int bh = rid.bh, qb = rid.qb;
-    const size_t kvbh = rid.kvbh;
-    const unsigned char* K = (const unsigned char*)a.k + kvbh * a.N * D * 2;
-    const unsigned char* VT = (const unsigned char*)a.vt + kvbh * (size_t)D * a.N * 2;
-    const size_t vrow = (size_t)a.N * 2;        // bytes per V^T row
+    const RowId rid = work_row(a, blockIdx.x, SPARSE);
+    const int qb = rid.qb, L = rid.L;
+    const unsigned char* K = (const unsigned char*)a.k + rid.k0 * 2;
+    const unsigned char* VT = (const unsigned char*)a.vt + rid.vt0 * 2;
+    const size_t vrow = (size_t)rid.NT * 2;      // bytes per V^T row
+    const size_t krs = (size_t)a.ks.rs * 2;      // bytes per key row
 
-    int cnt;
-    const int* lst = nullptr;
-    if (SPARSE) {
-        cnt = a.counts[(size_t)bh * a.nb + qb];
-        lst = a.lists + (size_t)bh * a.tri + (size_t)qb * (qb + 1) / 2;
-    } else {
-        cnt = qb + 1;
-    }
+    const int cnt = rid.cnt;
+    const int* lst = rid.lst;
     const int nsub = cnt * SPB;
 
-    // Q fragments (B operand of S^T = K Q^T): query l32 of this wave, d = 16c + 8hh + [0, 8)
+    // Q fragments (B operand of S^T = K Q^T): query l32 of this wave, d = 16c + 8hh + [0, 8).
+    // Rows past the sequence end (a partial last block) read its last row and are not stored.
     const int qrel = 32 * w + l32;
+    const int qrow = qb * BS + qrel;
     bf16x8_t qf[8];
     {
-        const bf16_t* qp = (const bf16_t*)a.q + ((size_t)bh * a.N + (size_t)qb * BS + qrel) * D + 8 * hh;
+        const bf16_t* qp = (const bf16_t*)a.q + rid.q0 + (size_t)min(qrow, L - 1) * a.qs.rs + 8 * hh;
 #pragma unroll
         for (int c = 0; c < 8; ++c) qf[c] = *reinterpret_cast<const bf16x8_t*>(qp + 16 * c);
     }
@@ -137,19 +158,28 @@ __global__ __launch_bounds__(2 * BS, BS == 128 ? 2 : 1) void k_attn_bf16(AttnArg
     for (int j = 0; j < LOADS; ++j) {
         const int J = w + NW * j;
         const int kr = 4 * J + (lane >> 4);
-        koff[j] = (unsigned)(kr * D * 2 + 16 * ((lane & 15) ^ (kr & 15)));
+        koff[j] = (unsigned)(kr * krs + 16 * ((lane & 15) ^ (kr & 15)));
         const int vr = 8 * J + (lane >> 3);
         voff[j] = (unsigned)((size_t)vr * vrow + 16 * ((lane & 7) ^ ((vr ^ (vr >> 1)) & 7)));
     }
+    // A tile reaching past the sequence end (only in the last key block) reads
+    // the last key for the missing rows: finite values that the causal mask
+    // removes; V^T is zero there.
 #define FP_FETCH_BF16(s_, buf_)                                                                          \
     {                                                                                                    \
         const int kb_ = SPARSE ? lst[(s_) / SPB] : (s_) / SPB;                                          \
         const int key0_ = kb_ * BS + ((s_) % SPB) * KT;                                                 \
-        const unsigned char* kg_ = K + (size_t)key0_ * D * 2;                                           \
+        const unsigned char* kg_ = K + (size_t)key0_ * krs;                                             \
         const unsigned char* vg_ = VT + (size_t)key0_ * 2;                                              \
+        const bool full_ = key0_ + KT <= L;                                                             \
         _Pragma("unroll") for (int j = 0; j < LOADS; ++j) {                                             \
             const int J = w + NW * j;                                                                   \
-            __builtin_amdgcn_global_load_lds((const void*)(kg_ + koff[j]),                              \
+            const unsigned char* ka_ = kg_ + koff[j];                                                   \
+            if (!full_) {                                                                               \
+                const int kr_ = 4 * J + (lane >> 4);                                                    \
+                ka_ = K + (size_t)min(key0_ + kr_, L - 1) * krs + 16 * ((lane & 15) ^ (kr_ & 15));      \
+            }                                                                                           \
+            __builtin_amdgcn_global_load_lds((const void*)ka_,                                          \
                 (__attribute__((address_space(3))) void*)(&Ks[(buf_)][J * 1024]), 16, 0, 0);           \
             __builtin_amdgcn_global_load_lds((const void*)(vg_ + voff[j]),                              \
                 (__attribute__((address_space(3))) void*)(&Vs[(buf_)][J * 1024]), 16, 0, 0);           \
@@ -253,7 +283,8 @@ __global__ __launch_bounds__(2 * BS, BS == 128 ? 2 : 1) void k_attn_bf16(AttnArg
 
     const float l_tot = l_run + __shfl_xor(l_run, 32);
     const float inv = 1.0f / l_tot;
-    bf16_t* op = (bf16_t*)a.o + ((size_t)bh * a.N + (size_t)qb * BS + qrel) * D;
+    if (qrow >= L) return;
+    bf16_t* op = (bf16_t*)a.o + rid.q0 + (size_t)qrow * a.qs.rs;
 #pragma unroll
     for (int T = 0; T < 4; ++T)
 #pragma unroll
@@ -286,25 +317,21 @@ __global__ __launch_bounds__(2 * BS) void k_attn_f32(AttnArgs a) {
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int l32 = lane & 31, hh = lane >> 5;
-    const RowId rid = work_row(a, blockIdx.x);
-    const int bh = rid.bh, qb = rid.qb;
-    const size_t kvbh = rid.kvbh;
-    const float* K = (const float*)a.k + kvbh * a.N * D;
-    const float* VT = (const float*)a.vt + kvbh * (size_t)D * a.N;
+    const RowId rid = work_row(a, blockIdx.x, SPARSE);
+    const int qb = rid.qb, L = rid.L;
+    const float* K = (const float*)a.k + rid.k0;
+    const float* VT = (const float*)a.vt + rid.vt0;
+    const size_t krs = (size_t)a.ks.rs;
+    const size_t NTv = (size_t)rid.NT;
 
-    int cnt;
-    const int* lst = nullptr;
-    if (SPARSE) {
-        cnt = a.counts[(size_t)bh * a.nb + qb];
-        lst = a.lists + (size_t)bh * a.tri + (size_t)qb * (qb + 1) / 2;
-    } else {
-        cnt = qb + 1;
-    }
+    const int cnt = rid.cnt;
+    const int* lst = rid.lst;
     const int nsub = cnt * SPB;
     const int qrel = 32 * w + l32;
+    const int qrow = qb * BS + qrel;
     float qf[64];
     {
-        const float* qp = (const float*)a.q + ((size_t)bh * a.N + (size_t)qb * BS + qrel) * D + 64 * hh;
+        const float* qp = (const float*)a.q + rid.q0 + (size_t)min(qrow, L - 1) * a.qs.rs + 64 * hh;
 #pragma unroll
         for (int c = 0; c < 64; c += 4) {
             const float4 v = *reinterpret_cast<const float4*>(qp + c);
@@ -326,11 +353,11 @@ __global__ __launch_bounds__(2 * BS) void k_attn_f32(AttnArgs a) {
         const int key0_ = kb_ * BS + ((s_) % SPB) * KT;                                              \
         _Pragma("unroll") for (int r = 0; r < KCH; ++r) {                                            \
             const int e = tid + NT * r, key = e >> 5, d4 = e & 31;                                   \
-            kreg[r] = *reinterpret_cast<const f32x4_t*>(K + (size_t)(key0_ + key) * D + 4 * d4);      \
+            kreg[r] = *reinterpret_cast<const f32x4_t*>(K + (size_t)min(key0_ + key, L - 1) * krs + 4 * d4); \
         }                                                                                            \
         _Pragma("unroll") for (int r = 0; r < VCH; ++r) {                                            \
             const int e = tid + NT * r, dv = e >> 4, k4 = e & 15;                                    \
-            vreg[r] = *reinterpret_cast<const f32x4_t*>(VT + (size_t)dv * a.N + key0_ + 4 * k4);      \
+            vreg[r] = *reinterpret_cast<const f32x4_t*>(VT + (size_t)dv * NTv + key0_ + 4 * k4);      \
         }                                                                                            \
     }
 #define FP_STASH_F32(buf_)                                                                           \
@@ -429,7 +456,8 @@ __global__ __launch_bounds__(2 * BS) void k_attn_f32(AttnArgs a) {
 #undef FP_STASH_F32
     const float l_tot = l_run + __shfl_xor(l_run, 32);
     const float inv = 1.0f / l_tot;
-    float* op = (float*)a.o + ((size_t)bh * a.N + (size_t)qb * BS + qrel) * D;
+    if (qrow >= L) return;
+    float* op = (float*)a.o + rid.q0 + (size_t)qrow * a.qs.rs;
 #pragma unroll
     for (int T = 0; T < 4; ++T)
 #pragma unroll
@@ -445,41 +473,46 @@ __global__ __launch_bounds__(2 * BS) void k_attn_f32(AttnArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// V [heads][N][d] -> V^T [heads][d][N], 64-key tiles through LDS.  With
-// PERMUTE, key n of every 16-key chunk is stored at position
+// V -> V^T [heads][d][NT] for one segment (head = b * Hkv + h), 64-key tiles
+// through LDS; columns from L to NT (the rest of the last block) are zero.
+// With PERMUTE, key n of every 16-key chunk is stored at position
 // (n & ~12) | ((n & 4) << 1) | ((n & 8) >> 1): key groups [0-3, 8-11, 4-7, 12-15].
 // ---------------------------------------------------------------------------
 template <typename T, bool PERMUTE>
-__global__ __launch_bounds__(256) void k_transpose_v(const T* __restrict__ v, T* __restrict__ vt, int N) {
+__global__ __launch_bounds__(256) void k_transpose_v(const T* __restrict__ v, TokStride vs, int Hkv,
+                                                     T* __restrict__ vt, int L, int NT) {
     constexpr int D = kHeadDim, TK = 64;
     __shared__ T tile[TK][D + 2];
     const int head = blockIdx.y, n0 = blockIdx.x * TK, tid = threadIdx.x;
-    const T* src = v + ((size_t)head * N + n0) * D;
+    const T* src = v + (size_t)(head / Hkv) * vs.bst + (size_t)(head % Hkv) * vs.hs;
     for (int e = tid; e < TK * D; e += 256) {
         const int n = e / D, dd = e % D;
-        tile[n][dd] = src[(size_t)n * D + dd];
+        tile[n][dd] = n0 + n < L ? src[(size_t)(n0 + n) * vs.rs + dd] : (T)0;
     }
     __syncthreads();
-    T* dst = vt + (size_t)head * D * N + n0;
+    T* dst = vt + (size_t)head * D * NT + n0;
     for (int e = tid; e < TK * D; e += 256) {
         const int dd = e / TK, p = e % TK;
         const int n = PERMUTE ? ((p & ~12) | ((p & 4) << 1) | ((p & 8) >> 1)) : p;
-        dst[(size_t)dd * N + p] = tile[n][dd];
+        dst[(size_t)dd * NT + p] = tile[n][dd];
     }
 }
 
-hipError_t launch_transpose_v(const void* v, void* vt, int dtype_bf16, int heads, int N, hipStream_t st) {
-    const dim3 g(N / 64, heads);
+hipError_t launch_transpose_v(const void* v, const TokStride& vs, void* vt, int dtype_bf16, int nseq, int Hkv,
+                              int L, int NT, hipStream_t st) {
+    const dim3 g(NT / 64, nseq * Hkv);
     if (dtype_bf16)
-        hipLaunchKernelGGL((k_transpose_v<bf16_t, true>), g, dim3(256), 0, st, (const bf16_t*)v, (bf16_t*)vt, N);
+        hipLaunchKernelGGL((k_transpose_v<bf16_t, true>), g, dim3(256), 0, st, (const bf16_t*)v, vs, Hkv,
+                           (bf16_t*)vt, L, NT);
     else
-        hipLaunchKernelGGL((k_transpose_v<float, false>), g, dim3(256), 0, st, (const float*)v, (float*)vt, N);
+        hipLaunchKernelGGL((k_transpose_v<float, false>), g, dim3(256), 0, st, (const float*)v, vs, Hkv,
+                           (float*)vt, L, NT);
     return hipGetLastError();
 }
 
 template <bool SPARSE>
 static void launch_attention_t(const AttnArgs& a, hipStream_t st) {
-    const unsigned items = (unsigned)(a.B * a.Hq * a.nb);
+    const unsigned items = (unsigned)a.items;
     if (a.dtype_bf16) {
         if (a.BS == 128) hipLaunchKernelGGL((k_attn_bf16<128, SPARSE>), dim3(items), dim3(256), 0, st, a);
         else hipLaunchKernelGGL((k_attn_bf16<64, SPARSE>), dim3(items), dim3(128), 0, st, a);

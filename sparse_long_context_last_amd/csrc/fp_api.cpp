@@ -17,14 +17,39 @@
 
 using namespace fp;
 
+// One segment of a problem: heads that share one sequence length.  The
+// [B, H, N, d] layout is one segment of B sequences; the packed [T, H, d]
+// layout has one segment per non-empty sequence.
+struct SegHost {
+    int b0, nseq;            // first sequence, sequences in the segment
+    int L, nb;               // tokens, blocks
+    long long tri;           // nb (nb + 1) / 2
+    long long qoff, koff;    // element offsets of the segment base in Q/O and K/V
+};
+
 struct fp_plan {
-    int B, Hq, Hkv, N, d, bs, nb;
+    int B, Hq, Hkv, N, d, bs, nb;     // N, nb: longest sequence
     fp_dtype dtype;
     float gamma, tau;
     int min_budget, max_budget, qa_selection;
+    int layout;
+    long long tokens, rows, dense_blocks;
+    std::vector<int> seqlens;
+    TokStride qs, ks;
+    std::vector<SegHost> segs;
+    std::vector<PlanDev> dev;        // per segment (views into the buffers below)
+    std::vector<AttnSeg> aseg_host;  // the attention segment table (host copy)
+    AttnSeg* aseg;                   // ... on the device
+    // whole-plan buffers; each segment owns a contiguous slice
+    unsigned char* pattern;
+    double* djs;
+    unsigned long long* total_blocks;
+    int* lists;
+    int* counts;
+    float *qbar, *kbar, *rowmax, *rowsum, *colsum, *diagsum, *atrue, *ahat;
+    size_t n_qbar, n_kbar, n_rowmax, n_colsum, n_atrue, n_ahat, n_counts, n_lists;
     int device;
     hipStream_t stream;
-    PlanDev dev;
     std::vector<void*> allocs;
 };
 
@@ -51,18 +76,76 @@ fp_status hip_fail(hipError_t e, const char* what) {
     } while (0)
 
 // ---------------------------------------------------------------- validation
-fp_status check_shape(fp_dtype dtype, int B, int Hq, int Hkv, int N, int d, int block) {
+fp_status check_common(fp_dtype dtype, int Hq, int Hkv, int d, int block) {
     if (dtype != FP_BF16 && dtype != FP_FP32) return fail(FP_ERR_UNSUPPORTED, "unknown dtype %d", (int)dtype);
-    if (B < 0 || Hq < 0 || Hkv < 0 || N < 0) return fail(FP_ERR_INVALID_ARG, "negative size");
+    if (Hq < 0 || Hkv < 0) return fail(FP_ERR_INVALID_ARG, "negative size");
     if (d != kHeadDim) return fail(FP_ERR_UNSUPPORTED, "head dim %d (supported: %d)", d, kHeadDim);
     if (block != 64 && block != 128) return fail(FP_ERR_UNSUPPORTED, "block %d (supported: 64, 128)", block);
     if (Hkv == 0 && Hq != 0) return fail(FP_ERR_SHAPE, "Hkv = 0 with Hq = %d", Hq);
     if (Hkv > 0 && Hq % Hkv != 0) return fail(FP_ERR_SHAPE, "Hq %d not a multiple of Hkv %d", Hq, Hkv);
-    if (N % block != 0) return fail(FP_ERR_SHAPE, "N %d not a multiple of block %d", N, block);
-    if (N / block > kMaxBlocks) return fail(FP_ERR_SHAPE, "N / block = %d exceeds %d", N / block, kMaxBlocks);
-    const long long rows = (long long)B * Hq * (N / block);
+    return FP_OK;
+}
+
+fp_status check_length(int L, int block) {
+    const long long nb = ((long long)L + block - 1) / block;
+    if (nb > kMaxBlocks) return fail(FP_ERR_SHAPE, "sequence of %d tokens: %lld blocks exceed %d", L, nb, kMaxBlocks);
+    return FP_OK;
+}
+
+fp_status check_shape(fp_dtype dtype, int B, int Hq, int Hkv, int N, int d, int block) {
+    fp_status s = check_common(dtype, Hq, Hkv, d, block);
+    if (s != FP_OK) return s;
+    if (B < 0 || N < 0) return fail(FP_ERR_INVALID_ARG, "negative size");
+    s = check_length(N, block);
+    if (s != FP_OK) return s;
+    const long long rows = (long long)B * Hq * ((N + block - 1) / block);
     if (rows > 0x7FFFFFFFLL) return fail(FP_ERR_SHAPE, "too many query-block rows");
     return FP_OK;
+}
+
+fp_status check_varlen(fp_dtype dtype, int nseq, const int* cu, int Hq, int Hkv, int d, int block) {
+    fp_status s = check_common(dtype, Hq, Hkv, d, block);
+    if (s != FP_OK) return s;
+    if (nseq < 0) return fail(FP_ERR_INVALID_ARG, "nseq %d < 0", nseq);
+    if (nseq == 0) return FP_OK;
+    if (!cu) return fail(FP_ERR_INVALID_ARG, "cu_seqlens is NULL");
+    if (cu[0] != 0) return fail(FP_ERR_INVALID_ARG, "cu_seqlens[0] = %d, must be 0", cu[0]);
+    long long rows = 0;
+    for (int b = 0; b < nseq; ++b) {
+        if (cu[b + 1] < cu[b]) return fail(FP_ERR_INVALID_ARG, "cu_seqlens decreases at %d", b + 1);
+        s = check_length(cu[b + 1] - cu[b], block);
+        if (s != FP_OK) return s;
+        rows += (long long)Hq * ((cu[b + 1] - cu[b] + block - 1) / block);
+    }
+    if (rows > 0x7FFFFFFFLL) return fail(FP_ERR_SHAPE, "too many query-block rows");
+    return FP_OK;
+}
+
+// Segments of a [B, H, N, d] problem (one) or of a packed problem (one per
+// non-empty sequence), with the token strides of Q/O and K/V.
+void build_segments(int layout, int B, int N, const int* cu, int Hq, int Hkv, int bs, std::vector<SegHost>& segs,
+                    TokStride& qs, TokStride& ks) {
+    segs.clear();
+    const long long D = kHeadDim;
+    if (layout == FP_LAYOUT_BHND) {
+        qs = TokStride{D, (long long)N * D, (long long)Hq * N * D};
+        ks = TokStride{D, (long long)N * D, (long long)Hkv * N * D};
+        if (B > 0 && Hq > 0 && N > 0) {
+            const int nb = (N + bs - 1) / bs;
+            segs.push_back(SegHost{0, B, N, nb, (long long)nb * (nb + 1) / 2, 0, 0});
+        }
+        return;
+    }
+    qs = TokStride{(long long)Hq * D, D, 0};
+    ks = TokStride{(long long)Hkv * D, D, 0};
+    if (Hq == 0) return;
+    for (int b = 0; b < B; ++b) {
+        const int L = cu[b + 1] - cu[b];
+        if (L == 0) continue;
+        const int nb = (L + bs - 1) / bs;
+        segs.push_back(SegHost{b, 1, L, nb, (long long)nb * (nb + 1) / 2, (long long)cu[b] * Hq * D,
+                               (long long)cu[b] * Hkv * D});
+    }
 }
 
 bool empty_problem(int B, int Hq, int N) { return B == 0 || Hq == 0 || N == 0; }
@@ -143,37 +226,77 @@ void free_plan(fp_plan* p) {
     delete p;
 }
 
-fp_status attend_common(const void* q, const void* k, const void* v, void* o, fp_dtype dtype, int B, int Hq,
-                        int Hkv, int N, int block, const fp_plan* plan, hipStream_t st) {
-    const int nb = N / block;
+// The attention segment table of a problem and the V^T workspace size.
+void attention_table(const std::vector<SegHost>& segs, int Hq, int Hkv, int bs, std::vector<AttnSeg>& t,
+                     long long& items, size_t& vt_elems) {
+    t.clear();
+    items = 0;
+    long long vt = 0, loff = 0, coff = 0;
+    for (const SegHost& g : segs) {
+        AttnSeg a{};
+        a.item0 = items;
+        a.qoff = g.qoff;
+        a.koff = g.koff;
+        a.vtoff = vt;
+        a.loff = loff;
+        a.coff = coff;
+        a.nseq = g.nseq;
+        a.L = g.L;
+        a.nb = g.nb;
+        a.NT = g.nb * bs;
+        t.push_back(a);
+        const long long nbh = (long long)g.nseq * Hq;
+        items += nbh * g.nb;
+        vt += (long long)g.nseq * Hkv * kHeadDim * a.NT;
+        loff += nbh * g.tri;
+        coff += nbh * g.nb;
+    }
+    vt_elems = (size_t)vt;
+}
+
+fp_status attend_common(const void* q, const void* k, const void* v, void* o, fp_dtype dtype, int Hq, int Hkv,
+                        int block, const std::vector<SegHost>& segs, const TokStride& qs, const TokStride& ks,
+                        const fp_plan* plan, hipStream_t st) {
     const size_t esz = dtype == FP_BF16 ? 2 : 4;
     int dev = 0;
     FP_HIP(hipGetDevice(&dev), "hipGetDevice");
     set_pool_threshold(dev);
+    std::vector<AttnSeg> table;
+    long long items = 0;
+    size_t vt_elems = 0;
+    attention_table(segs, Hq, Hkv, block, table, items, vt_elems);
+    if (items == 0) return FP_OK;
     void* vt = nullptr;
-    FP_HIP(hipMallocAsync(&vt, (size_t)B * Hkv * N * kHeadDim * esz, st), "hipMallocAsync (V^T)");
-    hipError_t e = launch_transpose_v(v, vt, dtype == FP_BF16, B * Hkv, N, st);
-    if (e != hipSuccess) {
-        (void)hipFreeAsync(vt, st);
-        return hip_fail(e, "transpose V");
+    AttnSeg* dtab = plan ? plan->aseg : nullptr;
+    FP_HIP(hipMallocAsync(&vt, vt_elems * esz, st), "hipMallocAsync (V^T)");
+    hipError_t e = hipSuccess;
+    if (!dtab) {
+        e = hipMallocAsync((void**)&dtab, table.size() * sizeof(AttnSeg), st);
+        if (e == hipSuccess)
+            e = hipMemcpyAsync(dtab, table.data(), table.size() * sizeof(AttnSeg), hipMemcpyHostToDevice, st);
     }
+    for (size_t i = 0; i < segs.size() && e == hipSuccess; ++i)
+        e = launch_transpose_v((const unsigned char*)v + (size_t)segs[i].koff * esz, ks,
+                               (unsigned char*)vt + (size_t)table[i].vtoff * esz, dtype == FP_BF16, segs[i].nseq,
+                               Hkv, segs[i].L, table[i].NT, st);
     AttnArgs a{};
     a.q = q;
     a.k = k;
     a.vt = vt;
     a.o = o;
     a.dtype_bf16 = dtype == FP_BF16;
-    a.B = B;
     a.Hq = Hq;
     a.Hkv = Hkv;
-    a.N = N;
     a.BS = block;
-    a.nb = nb;
-    a.tri = (long long)nb * (nb + 1) / 2;
+    a.qs = qs;
+    a.ks = ks;
+    a.segs = dtab;
+    a.nseg = (int)table.size();
+    a.items = items;
     a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)kHeadDim));
     if (plan) {
-        a.lists = plan->dev.lists;
-        a.counts = plan->dev.counts;
+        a.lists = plan->lists;
+        a.counts = plan->counts;
     }
     EvPair ev{};
     bool prof;
@@ -181,20 +304,237 @@ fp_status attend_common(const void* q, const void* k, const void* v, void* o, fp
         std::lock_guard<std::mutex> g(g_prof_mu);
         prof = g_prof_on;
     }
-    if (prof) {
+    if (e == hipSuccess && prof) {
         FP_HIP(hipEventCreate(&ev.a), "hipEventCreate");
         FP_HIP(hipEventCreate(&ev.b), "hipEventCreate");
         ev.dense = plan == nullptr;
         FP_HIP(hipEventRecord(ev.a, st), "hipEventRecord");
     }
-    e = launch_attention(a, st);
-    if (prof) {
+    if (e == hipSuccess) e = launch_attention(a, st);
+    if (e == hipSuccess && prof) {
         FP_HIP(hipEventRecord(ev.b, st), "hipEventRecord");
         std::lock_guard<std::mutex> g(g_prof_mu);
         g_prof_events.push_back(ev);
     }
     (void)hipFreeAsync(vt, st);
-    if (e != hipSuccess) return hip_fail(e, "attention launch");
+    if (!plan && dtab) (void)hipFreeAsync(dtab, st);
+    if (e != hipSuccess) return hip_fail(e, "attention");
+    return FP_OK;
+}
+
+// Plan for every segment of a validated problem.
+fp_status make_plan(const void* q, const void* k, fp_dtype dtype, int layout, int B, int N, const int* cu, int Hq,
+                    int Hkv, int d, int block, float gamma, float tau, int min_budget,
+                    const fp_plan_options* options, void* stream, fp_plan** out) {
+    const int max_budget = options ? options->max_budget : 0;
+    const int qa_selection = options ? options->qa_selection : FP_QA_FLATTENED;
+    if (!(gamma > 0.0f && gamma <= 1.0f)) return fail(FP_ERR_INVALID_ARG, "gamma %g outside (0, 1]", (double)gamma);
+    if (!(tau >= 0.0f) || std::isinf(tau)) return fail(FP_ERR_INVALID_ARG, "tau %g must be finite and >= 0", (double)tau);
+    if (min_budget < 0) return fail(FP_ERR_INVALID_ARG, "min_budget %d < 0", min_budget);
+    if (max_budget < 0) return fail(FP_ERR_INVALID_ARG, "max_budget %d < 0", max_budget);
+    if (qa_selection != FP_QA_FLATTENED && qa_selection != FP_QA_QUERYWISE)
+        return fail(FP_ERR_INVALID_ARG, "qa_selection %d is not FP_QA_FLATTENED or FP_QA_QUERYWISE", qa_selection);
+    {
+        const long long floor_b = std::max(1LL, ((long long)min_budget + block - 1) / block);
+        const long long cap_b = ((long long)max_budget + block - 1) / block;
+        if (max_budget > 0 && cap_b < floor_b)
+            return fail(FP_ERR_INVALID_ARG, "max_budget %d allows %lld blocks per row, min_budget needs %lld",
+                        max_budget, cap_b, floor_b);
+    }
+    std::vector<SegHost> segs;
+    TokStride qs, ks;
+    build_segments(layout, B, N, cu, Hq, Hkv, block, segs, qs, ks);
+    if (!segs.empty() && (!q || !k)) return fail(FP_ERR_INVALID_ARG, "q or k is NULL");
+
+    fp_plan* p = new (std::nothrow) fp_plan();
+    if (!p) return fail(FP_ERR_OOM, "host allocation failed");
+    p->B = B; p->Hq = Hq; p->Hkv = Hkv; p->d = d; p->bs = block;
+    p->dtype = dtype; p->gamma = gamma; p->tau = tau; p->min_budget = min_budget;
+    p->max_budget = max_budget;
+    p->qa_selection = qa_selection;
+    p->layout = layout;
+    p->stream = (hipStream_t)stream;
+    p->qs = qs;
+    p->ks = ks;
+    p->segs = segs;
+    p->seqlens.resize((size_t)B);
+    for (int b = 0; b < B; ++b) p->seqlens[(size_t)b] = layout == FP_LAYOUT_BHND ? N : cu[b + 1] - cu[b];
+    p->N = 0;
+    for (int L : p->seqlens) p->N = std::max(p->N, L);
+    if (B == 0) p->N = layout == FP_LAYOUT_BHND ? N : 0;
+    p->nb = (p->N + block - 1) / block;
+    p->tokens = layout == FP_LAYOUT_BHND ? (long long)B * N : (B > 0 ? (long long)cu[B] : 0);
+    p->rows = 0;
+    p->dense_blocks = 0;
+    long long lists_n = 0;
+    size_t n_qbar = 0, n_kbar = 0, n_rowmax = 0, n_colsum = 0, n_atrue = 0, n_ahat = 0;
+    int max_bh = 0;
+    size_t s2_max = 0, pmax_max = 0, rz_max = 0;
+    for (const SegHost& g : segs) {
+        const long long nbh = (long long)g.nseq * Hq;
+        const int NS = (g.L + 255) / 256 * 256;
+        p->rows += nbh * g.nb;
+        p->dense_blocks += nbh * g.tri;
+        lists_n += nbh * g.tri;
+        n_qbar += (size_t)nbh * g.nb * kHeadDim;
+        n_kbar += (size_t)g.nseq * Hkv * g.nb * kHeadDim;
+        n_rowmax += (size_t)nbh * block;
+        n_colsum += (size_t)nbh * g.L;
+        n_atrue += (size_t)nbh * g.nb;
+        n_ahat += (size_t)nbh * g.tri;
+        max_bh = std::max(max_bh, (int)nbh);
+        s2_max = std::max(s2_max, (size_t)nbh * block * NS);
+        pmax_max = std::max(pmax_max, (size_t)nbh * (NS / 256) * block);
+        rz_max = std::max(rz_max, (size_t)nbh * block);
+    }
+    p->n_qbar = n_qbar; p->n_kbar = n_kbar; p->n_rowmax = n_rowmax; p->n_colsum = n_colsum;
+    p->n_atrue = n_atrue; p->n_ahat = n_ahat; p->n_counts = (size_t)p->rows; p->n_lists = (size_t)lists_n;
+    if (segs.empty()) {
+        p->device = -1;
+        *out = p;
+        return FP_OK;
+    }
+    hipError_t he = hipGetDevice(&p->device);
+    if (he != hipSuccess) {
+        delete p;
+        return hip_fail(he, "hipGetDevice");
+    }
+    set_pool_threshold(p->device);
+    const double Gd = std::nearbyint((double)gamma * (double)(1 << kGammaShift));
+    const unsigned long long G = (unsigned long long)Gd;
+    const size_t BHall = (size_t)B * Hq;
+    const bool cap = max_budget > 0;
+
+#define PALLOC(ptr, n)                          \
+    do {                                        \
+        fp_status s_ = palloc(p, &(ptr), (n));  \
+        if (s_ != FP_OK) {                      \
+            free_plan(p);                       \
+            return s_;                          \
+        }                                       \
+    } while (0)
+    unsigned char *colblk, *diagA, *diagB, *diagT;
+    float *colmass = nullptr, *diagmass = nullptr;
+    SelState* sel;
+    unsigned long long* hist;
+    AttnSeg* aseg;
+    PALLOC(p->pattern, (BHall + 3) / 4 * 4);
+    PALLOC(p->djs, BHall);
+    PALLOC(p->total_blocks, BHall);
+    PALLOC(p->qbar, n_qbar);
+    PALLOC(p->kbar, n_kbar);
+    PALLOC(p->rowmax, n_rowmax);
+    PALLOC(p->rowsum, n_rowmax);
+    PALLOC(p->colsum, n_colsum);
+    PALLOC(p->diagsum, n_colsum);
+    PALLOC(p->atrue, n_atrue);
+    PALLOC(p->ahat, n_ahat);
+    PALLOC(p->lists, (size_t)lists_n);
+    PALLOC(p->counts, (size_t)p->rows);
+    PALLOC(colblk, (size_t)p->rows);
+    PALLOC(diagA, (size_t)p->rows);
+    PALLOC(diagB, (size_t)p->rows);
+    PALLOC(diagT, (size_t)p->rows);
+    if (cap) {
+        PALLOC(colmass, (size_t)p->rows);
+        PALLOC(diagmass, (size_t)p->rows);
+    }
+    PALLOC(sel, (size_t)2 * max_bh);
+    PALLOC(hist, (size_t)2 * max_bh * kRadixBins);
+    PALLOC(aseg, segs.size());
+#undef PALLOC
+    p->aseg = aseg;
+    long long items = 0;
+    size_t vt_elems = 0;
+    attention_table(segs, Hq, Hkv, block, p->aseg_host, items, vt_elems);
+    hipStream_t st = p->stream;
+    he = hipMemcpyAsync(aseg, p->aseg_host.data(), segs.size() * sizeof(AttnSeg), hipMemcpyHostToDevice, st);
+    // heads of empty sequences keep pattern 0, divergence 0 and no blocks
+    if (he == hipSuccess) he = launch_fill_u32((unsigned int*)p->pattern, 0u, (long long)(BHall + 3) / 4, st);
+    if (he == hipSuccess) he = launch_fill_u32((unsigned int*)p->djs, 0u, 2LL * (long long)BHall, st);
+    if (he == hipSuccess) he = launch_fill_u32((unsigned int*)p->total_blocks, 0u, 2LL * (long long)BHall, st);
+
+    // per-segment views
+    size_t o_qbar = 0, o_kbar = 0, o_rowmax = 0, o_colsum = 0, o_atrue = 0, o_ahat = 0, o_rows = 0;
+    p->dev.resize(segs.size());
+    for (size_t i = 0; i < segs.size(); ++i) {
+        const SegHost& g = segs[i];
+        const int nbh = g.nseq * Hq;
+        PlanDev& P = p->dev[i];
+        memset(&P, 0, sizeof P);
+        P.BH = nbh; P.BS = block; P.L = g.L; P.NS = (g.L + 255) / 256 * 256; P.nb = g.nb;
+        P.tail = g.L - (g.nb - 1) * block;
+        P.tri = g.tri;
+        P.mode_all = G >= (1ull << kGammaShift);
+        P.floor_blocks = std::max(1, (min_budget + block - 1) / block);
+        P.cap_blocks = (int)(((long long)max_budget + block - 1) / block);
+        P.qa_querywise = qa_selection == FP_QA_QUERYWISE;
+        P.G = G;
+        P.pattern = p->pattern + (size_t)g.b0 * Hq;
+        P.djs = p->djs + (size_t)g.b0 * Hq;
+        P.total_blocks = p->total_blocks + (size_t)g.b0 * Hq;
+        P.qbar = p->qbar + o_qbar;
+        P.kbar = p->kbar + o_kbar;
+        P.rowmax = p->rowmax + o_rowmax;
+        P.rowsum = p->rowsum + o_rowmax;
+        P.colsum = p->colsum + o_colsum;
+        P.diagsum = p->diagsum + o_colsum;
+        P.atrue = p->atrue + o_atrue;
+        P.ahat = p->ahat + o_ahat;
+        P.lists = p->lists + o_ahat;
+        P.counts = p->counts + o_rows;
+        P.colblk = colblk + o_rows;
+        P.diagA = diagA + o_rows;
+        P.diagB = diagB + o_rows;
+        P.diagT = diagT + o_rows;
+        if (cap) {
+            P.colmass = colmass + o_rows;
+            P.diagmass = diagmass + o_rows;
+        }
+        P.sel = sel;
+        P.hist = hist;
+        o_qbar += (size_t)nbh * g.nb * kHeadDim;
+        o_kbar += (size_t)g.nseq * Hkv * g.nb * kHeadDim;
+        o_rowmax += (size_t)nbh * block;
+        o_colsum += (size_t)nbh * g.L;
+        o_atrue += (size_t)nbh * g.nb;
+        o_ahat += (size_t)nbh * g.tri;
+        o_rows += (size_t)nbh * g.nb;
+    }
+
+    // one transient score workspace, reused segment after segment (stream order)
+    void *s2 = nullptr, *pmax = nullptr, *rz = nullptr;
+    if (he == hipSuccess) he = hipMallocAsync(&s2, s2_max * sizeof(float), st);
+    if (he == hipSuccess) he = hipMallocAsync(&pmax, pmax_max * sizeof(float), st);
+    if (he == hipSuccess) he = hipMallocAsync(&rz, rz_max * sizeof(float), st);
+    const size_t esz = dtype == FP_BF16 ? 2 : 4;
+    const Canon canon = make_canon(d);
+    for (size_t i = 0; i < segs.size() && he == hipSuccess; ++i) {
+        PlanArgs a{};
+        a.q = (const unsigned char*)q + (size_t)segs[i].qoff * esz;
+        a.k = (const unsigned char*)k + (size_t)segs[i].koff * esz;
+        a.qs = qs;
+        a.ks = ks;
+        a.dtype_bf16 = dtype == FP_BF16;
+        a.nseq = segs[i].nseq;
+        a.Hq = Hq;
+        a.Hkv = Hkv;
+        a.tau = (double)tau;
+        a.G = G;
+        a.canon = canon;
+        a.s2 = (float*)s2;
+        a.pmax = (float*)pmax;
+        a.rz = (float*)rz;
+        he = launch_plan(a, p->dev[i], st);
+    }
+    if (s2) (void)hipFreeAsync(s2, st);
+    if (pmax) (void)hipFreeAsync(pmax, st);
+    if (rz) (void)hipFreeAsync(rz, st);
+    if (he != hipSuccess) {
+        free_plan(p);
+        return hip_fail(he, "planning");
+    }
+    *out = p;
     return FP_OK;
 }
 
@@ -236,124 +576,30 @@ fp_status fp_prefill_plan_ex(const void* q, const void* k, fp_dtype dtype, int B
                              int block, float gamma, float tau, int min_budget, const fp_plan_options* options,
                              void* stream, fp_plan** out) {
     if (!out) return fail(FP_ERR_INVALID_ARG, "out is NULL");
-    const int max_budget = options ? options->max_budget : 0;
-    const int qa_selection = options ? options->qa_selection : FP_QA_FLATTENED;
     *out = nullptr;
     fp_status s = check_shape(dtype, B, Hq, Hkv, N, d, block);
     if (s != FP_OK) return s;
-    if (!(gamma > 0.0f && gamma <= 1.0f)) return fail(FP_ERR_INVALID_ARG, "gamma %g outside (0, 1]", (double)gamma);
-    if (!(tau >= 0.0f) || std::isinf(tau)) return fail(FP_ERR_INVALID_ARG, "tau %g must be finite and >= 0", (double)tau);
-    if (min_budget < 0) return fail(FP_ERR_INVALID_ARG, "min_budget %d < 0", min_budget);
-    if (max_budget < 0) return fail(FP_ERR_INVALID_ARG, "max_budget %d < 0", max_budget);
-    if (qa_selection != FP_QA_FLATTENED && qa_selection != FP_QA_QUERYWISE)
-        return fail(FP_ERR_INVALID_ARG, "qa_selection %d is not FP_QA_FLATTENED or FP_QA_QUERYWISE", qa_selection);
-    {
-        const long long floor_b = std::max(1LL, ((long long)min_budget + block - 1) / block);
-        const long long cap_b = ((long long)max_budget + block - 1) / block;
-        if (max_budget > 0 && cap_b < floor_b)
-            return fail(FP_ERR_INVALID_ARG, "max_budget %d allows %lld blocks per row, min_budget needs %lld",
-                        max_budget, cap_b, floor_b);
-    }
-    const bool empty = empty_problem(B, Hq, N);
-    if (!empty && (!q || !k)) return fail(FP_ERR_INVALID_ARG, "q or k is NULL");
+    return make_plan(q, k, dtype, FP_LAYOUT_BHND, B, N, nullptr, Hq, Hkv, d, block, gamma, tau, min_budget, options,
+                     stream, out);
+}
 
-    fp_plan* p = new (std::nothrow) fp_plan();
-    if (!p) return fail(FP_ERR_OOM, "host allocation failed");
-    p->B = B; p->Hq = Hq; p->Hkv = Hkv; p->N = N; p->d = d; p->bs = block;
-    p->nb = N / block; p->dtype = dtype; p->gamma = gamma; p->tau = tau; p->min_budget = min_budget;
-    p->max_budget = max_budget;
-    p->qa_selection = qa_selection;
-    p->stream = (hipStream_t)stream;
-    if (empty) {
-        p->device = -1;
-        memset(&p->dev, 0, sizeof p->dev);
-        *out = p;
-        return FP_OK;
-    }
-    hipError_t he = hipGetDevice(&p->device);
-    if (he != hipSuccess) {
-        delete p;
-        return hip_fail(he, "hipGetDevice");
-    }
-    set_pool_threshold(p->device);
-
-    PlanDev& P = p->dev;
-    memset(&P, 0, sizeof P);
-    const int BH = B * Hq, nb = p->nb;
-    P.BH = BH; P.BS = block; P.N = N; P.nb = nb;
-    P.tri = (long long)nb * (nb + 1) / 2;
-    const double Gd = std::nearbyint((double)gamma * (double)(1 << kGammaShift));
-    const unsigned long long G = (unsigned long long)Gd;
-    P.mode_all = G >= (1ull << kGammaShift);
-    P.floor_blocks = (min_budget + block - 1) / block;
-    if (P.floor_blocks < 1) P.floor_blocks = 1;
-    P.cap_blocks = (int)(((long long)max_budget + block - 1) / block);
-    P.qa_querywise = qa_selection == FP_QA_QUERYWISE;
-    P.G = G;
-
-#define PALLOC(ptr, n)                          \
-    do {                                        \
-        fp_status s_ = palloc(p, &(ptr), (n));  \
-        if (s_ != FP_OK) {                      \
-            free_plan(p);                       \
-            return s_;                          \
-        }                                       \
-    } while (0)
-    PALLOC(P.pattern, (size_t)BH);
-    PALLOC(P.djs, (size_t)BH);
-    PALLOC(P.qbar, (size_t)BH * nb * kHeadDim);
-    PALLOC(P.kbar, (size_t)B * Hkv * nb * kHeadDim);
-    PALLOC(P.rowmax, (size_t)BH * block);
-    PALLOC(P.rowsum, (size_t)BH * block);
-    PALLOC(P.colsum, (size_t)BH * N);
-    PALLOC(P.diagsum, (size_t)BH * N);
-    PALLOC(P.atrue, (size_t)BH * nb);
-    PALLOC(P.ahat, (size_t)BH * P.tri);
-    PALLOC(P.sel, (size_t)2 * BH);
-    PALLOC(P.hist, (size_t)2 * BH * kRadixBins);
-    PALLOC(P.colblk, (size_t)BH * nb);
-    PALLOC(P.diagA, (size_t)BH * nb);
-    PALLOC(P.diagB, (size_t)BH * nb);
-    PALLOC(P.colmass, P.cap_blocks > 0 ? (size_t)BH * nb : 0);
-    PALLOC(P.diagmass, P.cap_blocks > 0 ? (size_t)BH * nb : 0);
-    PALLOC(P.lists, (size_t)BH * P.tri);
-    PALLOC(P.counts, (size_t)BH * nb);
-    PALLOC(P.total_blocks, (size_t)BH);
-#undef PALLOC
-
-    PlanArgs a{};
-    a.q = q; a.k = k; a.dtype_bf16 = dtype == FP_BF16;
-    a.B = B; a.Hq = Hq; a.Hkv = Hkv;
-    a.tau = (double)tau;
-    a.G = G;
-    a.canon = make_canon(d);
-    const int nchunks = (N + 255) / 256;
-    void *s2 = nullptr, *pmax = nullptr, *rz = nullptr;
-    hipStream_t st = p->stream;
-    he = hipMallocAsync(&s2, (size_t)BH * block * N * sizeof(float), st);
-    if (he == hipSuccess) he = hipMallocAsync(&pmax, (size_t)BH * nchunks * block * sizeof(float), st);
-    if (he == hipSuccess) he = hipMallocAsync(&rz, (size_t)BH * block * sizeof(float), st);
-    if (he == hipSuccess) {
-        a.s2 = (float*)s2; a.pmax = (float*)pmax; a.rz = (float*)rz;
-        he = launch_plan(a, P, st);
-    }
-    if (s2) (void)hipFreeAsync(s2, st);
-    if (pmax) (void)hipFreeAsync(pmax, st);
-    if (rz) (void)hipFreeAsync(rz, st);
-    if (he != hipSuccess) {
-        free_plan(p);
-        return hip_fail(he, "planning");
-    }
-    *out = p;
-    return FP_OK;
+fp_status fp_prefill_plan_varlen(const void* q, const void* k, fp_dtype dtype, int nseq, const int* cu_seqlens,
+                                 int Hq, int Hkv, int d, int block, float gamma, float tau, int min_budget,
+                                 const fp_plan_options* options, void* stream, fp_plan** out) {
+    if (!out) return fail(FP_ERR_INVALID_ARG, "out is NULL");
+    *out = nullptr;
+    fp_status s = check_varlen(dtype, nseq, cu_seqlens, Hq, Hkv, d, block);
+    if (s != FP_OK) return s;
+    return make_plan(q, k, dtype, FP_LAYOUT_THD, nseq, 0, cu_seqlens, Hq, Hkv, d, block, gamma, tau, min_budget,
+                     options, stream, out);
 }
 
 fp_status fp_prefill_attend(const fp_plan* plan, const void* q, const void* k, const void* v, void* o, void* stream) {
     if (!plan) return fail(FP_ERR_INVALID_ARG, "plan is NULL");
-    if (empty_problem(plan->B, plan->Hq, plan->N)) return FP_OK;
+    if (plan->segs.empty()) return FP_OK;
     if (!q || !k || !v || !o) return fail(FP_ERR_INVALID_ARG, "q, k, v or o is NULL");
-    return attend_common(q, k, v, o, plan->dtype, plan->B, plan->Hq, plan->Hkv, plan->N, plan->bs, plan,
-                         (hipStream_t)stream);
+    return attend_common(q, k, v, o, plan->dtype, plan->Hq, plan->Hkv, plan->bs, plan->segs, plan->qs, plan->ks,
+                         plan, (hipStream_t)stream);
 }
 
 fp_status fp_dense_attend(const void* q, const void* k, const void* v, void* o, fp_dtype dtype, int B, int Hq,
@@ -362,7 +608,22 @@ fp_status fp_dense_attend(const void* q, const void* k, const void* v, void* o, 
     if (s != FP_OK) return s;
     if (empty_problem(B, Hq, N)) return FP_OK;
     if (!q || !k || !v || !o) return fail(FP_ERR_INVALID_ARG, "q, k, v or o is NULL");
-    return attend_common(q, k, v, o, dtype, B, Hq, Hkv, N, block, nullptr, (hipStream_t)stream);
+    std::vector<SegHost> segs;
+    TokStride qs, ks;
+    build_segments(FP_LAYOUT_BHND, B, N, nullptr, Hq, Hkv, block, segs, qs, ks);
+    return attend_common(q, k, v, o, dtype, Hq, Hkv, block, segs, qs, ks, nullptr, (hipStream_t)stream);
+}
+
+fp_status fp_dense_attend_varlen(const void* q, const void* k, const void* v, void* o, fp_dtype dtype, int nseq,
+                                 const int* cu_seqlens, int Hq, int Hkv, int d, int block, void* stream) {
+    fp_status s = check_varlen(dtype, nseq, cu_seqlens, Hq, Hkv, d, block);
+    if (s != FP_OK) return s;
+    std::vector<SegHost> segs;
+    TokStride qs, ks;
+    build_segments(FP_LAYOUT_THD, nseq, 0, cu_seqlens, Hq, Hkv, block, segs, qs, ks);
+    if (segs.empty()) return FP_OK;
+    if (!q || !k || !v || !o) return fail(FP_ERR_INVALID_ARG, "q, k, v or o is NULL");
+    return attend_common(q, k, v, o, dtype, Hq, Hkv, block, segs, qs, ks, nullptr, (hipStream_t)stream);
 }
 
 fp_status fp_plan_info_get(const fp_plan* plan, fp_plan_info* out) {
@@ -373,18 +634,21 @@ fp_status fp_plan_info_get(const fp_plan* plan, fp_plan_info* out) {
     I.min_budget = plan->min_budget;
     I.max_budget = plan->max_budget;
     I.qa_selection = plan->qa_selection;
+    I.layout = plan->layout;
+    I.tokens = plan->tokens;
+    I.rows = plan->rows;
+    I.dense_blocks = plan->dense_blocks;
     const long long BH = (long long)plan->B * plan->Hq;
-    I.dense_blocks = BH * plan->nb * (long long)(plan->nb + 1) / 2;
-    if (BH > 0 && plan->N > 0) {
+    if (!plan->segs.empty()) {
         FP_HIP(hipStreamSynchronize(plan->stream), "hipStreamSynchronize");
         std::vector<unsigned long long> per_head((size_t)BH);
-        FP_HIP(hipMemcpy(per_head.data(), plan->dev.total_blocks, per_head.size() * sizeof(unsigned long long),
+        FP_HIP(hipMemcpy(per_head.data(), plan->total_blocks, per_head.size() * sizeof(unsigned long long),
                          hipMemcpyDeviceToHost), "hipMemcpy");
         long long tot = 0;
         for (unsigned long long x : per_head) tot += (long long)x;
         I.total_blocks = tot;
         std::vector<unsigned char> pat((size_t)BH);
-        FP_HIP(hipMemcpy(pat.data(), plan->dev.pattern, pat.size(), hipMemcpyDeviceToHost), "hipMemcpy");
+        FP_HIP(hipMemcpy(pat.data(), plan->pattern, pat.size(), hipMemcpyDeviceToHost), "hipMemcpy");
         for (unsigned char c : pat) I.query_aware_heads += c == kPatternQueryAware;
     }
     *out = I;
@@ -396,34 +660,38 @@ fp_status fp_plan_copy_out(const fp_plan* plan, unsigned char* pattern, double* 
     if (!plan) return fail(FP_ERR_INVALID_ARG, "plan is NULL");
     if ((row_ptr == nullptr) != (col_idx == nullptr)) return fail(FP_ERR_INVALID_ARG, "give both row_ptr and col_idx");
     const long long BH = (long long)plan->B * plan->Hq;
-    const int nb = plan->nb;
-    if (BH == 0 || plan->N == 0) {
+    if (plan->segs.empty()) {
         if (row_ptr) row_ptr[0] = 0;
+        if (pattern) memset(pattern, 0, (size_t)BH);
+        if (djs) memset(djs, 0, (size_t)BH * sizeof(double));
         return FP_OK;
     }
     hipStream_t st = (hipStream_t)stream;
     FP_HIP(hipStreamSynchronize(plan->stream), "hipStreamSynchronize");
-    if (pattern) FP_HIP(hipMemcpyAsync(pattern, plan->dev.pattern, (size_t)BH, hipMemcpyDeviceToHost, st), "copy pattern");
-    if (djs) FP_HIP(hipMemcpyAsync(djs, plan->dev.djs, (size_t)BH * sizeof(double), hipMemcpyDeviceToHost, st), "copy djs");
+    if (pattern) FP_HIP(hipMemcpyAsync(pattern, plan->pattern, (size_t)BH, hipMemcpyDeviceToHost, st), "copy pattern");
+    if (djs) FP_HIP(hipMemcpyAsync(djs, plan->djs, (size_t)BH * sizeof(double), hipMemcpyDeviceToHost, st), "copy djs");
     if (row_ptr) {
-        std::vector<int> counts((size_t)BH * nb);
-        const long long tri = plan->dev.tri;
-        std::vector<int> lists((size_t)(BH * tri));
-        FP_HIP(hipMemcpyAsync(counts.data(), plan->dev.counts, counts.size() * sizeof(int), hipMemcpyDeviceToHost, st),
+        std::vector<int> counts(plan->n_counts);
+        std::vector<int> lists(plan->n_lists);
+        FP_HIP(hipMemcpyAsync(counts.data(), plan->counts, counts.size() * sizeof(int), hipMemcpyDeviceToHost, st),
                "copy counts");
-        FP_HIP(hipMemcpyAsync(lists.data(), plan->dev.lists, lists.size() * sizeof(int), hipMemcpyDeviceToHost, st),
+        FP_HIP(hipMemcpyAsync(lists.data(), plan->lists, lists.size() * sizeof(int), hipMemcpyDeviceToHost, st),
                "copy lists");
         FP_HIP(hipStreamSynchronize(st), "hipStreamSynchronize");
-        long long acc = 0;
-        for (long long bh = 0; bh < BH; ++bh)
-            for (int r = 0; r < nb; ++r) {
-                const long long i = bh * nb + r;
-                row_ptr[i] = (int)acc;
-                const int c = counts[(size_t)i];
-                memcpy(col_idx + acc, lists.data() + bh * tri + (long long)r * (r + 1) / 2, (size_t)c * sizeof(int));
-                acc += c;
-            }
-        row_ptr[BH * nb] = (int)acc;
+        long long acc = 0, row = 0, loff = 0;
+        for (const SegHost& g : plan->segs) {
+            const long long nbh = (long long)g.nseq * plan->Hq;
+            for (long long bh = 0; bh < nbh; ++bh)
+                for (int r = 0; r < g.nb; ++r, ++row) {
+                    row_ptr[row] = (int)acc;
+                    const int c = counts[(size_t)row];
+                    memcpy(col_idx + acc, lists.data() + loff + bh * g.tri + (long long)r * (r + 1) / 2,
+                           (size_t)c * sizeof(int));
+                    acc += c;
+                }
+            loff += nbh * g.tri;
+        }
+        row_ptr[row] = (int)acc;
     }
     FP_HIP(hipStreamSynchronize(st), "hipStreamSynchronize");
     return FP_OK;
@@ -431,20 +699,18 @@ fp_status fp_plan_copy_out(const fp_plan* plan, unsigned char* pattern, double* 
 
 fp_status fp_plan_copy_debug(const fp_plan* plan, int which, void* host_dst, size_t bytes) {
     if (!plan || !host_dst) return fail(FP_ERR_INVALID_ARG, "plan or destination is NULL");
-    const PlanDev& P = plan->dev;
-    const size_t BH = (size_t)plan->B * plan->Hq, nb = (size_t)plan->nb;
     const void* src = nullptr;
     size_t need = 0;
     switch (which) {
-        case FP_DBG_QBAR: src = P.qbar; need = BH * nb * kHeadDim * 4; break;
-        case FP_DBG_KBAR: src = P.kbar; need = (size_t)plan->B * plan->Hkv * nb * kHeadDim * 4; break;
-        case FP_DBG_ROWMAX: src = P.rowmax; need = BH * plan->bs * 4; break;
-        case FP_DBG_ROWSUM: src = P.rowsum; need = BH * plan->bs * 4; break;
-        case FP_DBG_COLSUM: src = P.colsum; need = BH * plan->N * 4; break;
-        case FP_DBG_DIAGSUM: src = P.diagsum; need = BH * plan->N * 4; break;
-        case FP_DBG_ATRUE: src = P.atrue; need = BH * nb * 4; break;
-        case FP_DBG_AHAT: src = P.ahat; need = BH * (size_t)P.tri * 4; break;
-        case FP_DBG_COUNTS: src = P.counts; need = BH * nb * 4; break;
+        case FP_DBG_QBAR: src = plan->qbar; need = plan->n_qbar * 4; break;
+        case FP_DBG_KBAR: src = plan->kbar; need = plan->n_kbar * 4; break;
+        case FP_DBG_ROWMAX: src = plan->rowmax; need = plan->n_rowmax * 4; break;
+        case FP_DBG_ROWSUM: src = plan->rowsum; need = plan->n_rowmax * 4; break;
+        case FP_DBG_COLSUM: src = plan->colsum; need = plan->n_colsum * 4; break;
+        case FP_DBG_DIAGSUM: src = plan->diagsum; need = plan->n_colsum * 4; break;
+        case FP_DBG_ATRUE: src = plan->atrue; need = plan->n_atrue * 4; break;
+        case FP_DBG_AHAT: src = plan->ahat; need = plan->n_ahat * 4; break;
+        case FP_DBG_COUNTS: src = plan->counts; need = plan->n_counts * 4; break;
         default: return fail(FP_ERR_INVALID_ARG, "unknown debug item %d", which);
     }
     if (bytes != need) return fail(FP_ERR_INVALID_ARG, "item %d has %zu bytes, %zu given", which, need, bytes);

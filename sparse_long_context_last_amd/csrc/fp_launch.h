@@ -28,9 +28,25 @@ struct SelState {
     int has;                    // list selects at least one element
 };
 
-// Device buffers of a plan (passed by value to kernels).
+// Token addressing of a Q/O or K/V tensor inside one segment: element c of
+// token t of head h of the segment's sequence b sits at
+//   base + b * bst + h * hs + t * rs + c
+// (base: the segment's first token, applied on the host).  [B, H, N, d]
+// tensors have rs = d, hs = N d, bst = H N d; packed [T, H, d] tensors have
+// rs = H d, hs = d and one sequence per segment.
+struct TokStride {
+    long long rs, hs, bst;
+};
+
+// Device buffers of one plan segment: heads that share one sequence length L
+// (passed by value to kernels).  Every length L >= 1 is allowed; the last
+// block of a sequence holds L - (nb - 1) BS tokens.
 struct PlanDev {
-    int BH, BS, N, nb;
+    int BH, BS;
+    int L;                       // tokens of every head of the segment
+    int NS;                      // row stride of the last-block score workspace (multiple of 256, >= L)
+    int nb;                      // ceil(L / BS)
+    int tail;                    // query rows of the last block row, L - (nb - 1) BS
     long long tri;               // nb (nb + 1) / 2
     int mode_all;                // gamma == 1: every causal block
     int floor_blocks;            // max(1, ceil(min_budget / BS))
@@ -40,11 +56,11 @@ struct PlanDev {
     unsigned char* pattern;      // [BH]
     double* djs;                 // [BH]
     float* qbar;                 // [BH][nb][d]
-    float* kbar;                 // [B*Hkv][nb][d]
+    float* kbar;                 // [sequences * Hkv][nb][d]
     float* rowmax;               // [BH][BS]
     float* rowsum;               // [BH][BS]
-    float* colsum;               // [BH][N]
-    float* diagsum;              // [BH][N]
+    float* colsum;               // [BH][L]
+    float* diagsum;              // [BH][L]
     float* atrue;                // [BH][nb]
     float* ahat;                 // [BH][tri]
     SelState* sel;               // [2 BH]
@@ -52,6 +68,7 @@ struct PlanDev {
     unsigned char* colblk;       // [BH][nb]
     unsigned char* diagA;        // [BH][nb]
     unsigned char* diagB;        // [BH][nb]
+    unsigned char* diagT;        // [BH][nb]
     float* colmass;              // [BH][nb]  selected column mass per key block (cap only)
     float* diagmass;             // [BH][nb]  selected diagonal mass per block diagonal (cap only)
     int* lists;                  // [BH][tri]  row r's list at offset r (r + 1) / 2
@@ -59,38 +76,54 @@ struct PlanDev {
     unsigned long long* total_blocks;  // [BH] selected blocks per head
 };
 
-// Inputs and transient workspace of one planning call.
+// Inputs and transient workspace of one segment's planning call.
 struct PlanArgs {
-    const void* q;
+    const void* q;    // the segment's first token of head 0 of its first sequence
     const void* k;
+    TokStride qs, ks;
     int dtype_bf16;
-    int B, Hq, Hkv;
+    int nseq, Hq, Hkv;  // sequences in the segment (BH = nseq Hq)
     double tau;
     unsigned long long G;
     Canon canon;
-    float* s2;        // [BH][BS][N] transient
-    float* pmax;      // [BH][ceil(N/256)][BS] transient
+    float* s2;        // [BH][BS][NS] transient
+    float* pmax;      // [BH][NS/256][BS] transient
     float* rz;        // [BH][BS] transient
+};
+
+// One segment of the attention work (device table, one entry per segment).
+struct AttnSeg {
+    long long item0;      // first work item (one per head and query block)
+    long long qoff, koff; // element offsets of the segment base in Q/O and in K/V
+    long long vtoff;      // element offset of the segment in the V^T workspace
+    long long loff, coff; // offsets of the segment in the plan's lists and counts
+    int nseq;             // sequences (query heads = nseq Hq)
+    int L, nb, NT;        // tokens, blocks, V^T row length nb BS
 };
 
 struct AttnArgs {
     const void* q;
     const void* k;
-    const void* vt;      // V transposed: [B*Hkv][d][N]
+    const void* vt;      // V transposed, per segment [nseq Hkv][d][NT], zero past L
     void* o;
     int dtype_bf16;
-    int B, Hq, Hkv, N, BS, nb;
+    int Hq, Hkv, BS;
+    TokStride qs, ks;
+    const AttnSeg* segs; // device
+    int nseg;
+    long long items;
     const int* lists;    // nullptr: dense causal
     const int* counts;
-    long long tri;
     float scale_log2;    // log2(e) / sqrt(d)
 };
 
 hipError_t launch_plan(const PlanArgs& a, PlanDev& P, hipStream_t st);
+hipError_t launch_fill_u32(unsigned int* p, unsigned int v, long long n, hipStream_t st);
 hipError_t launch_probe_exp2(const float* x, float* y, long long n, const Canon& K, hipStream_t st);
 hipError_t launch_probe_ln(const double* x, double* y, long long n, const Canon& K, hipStream_t st);
 hipError_t launch_probe_sqrt(const double* x, double* y, long long n, hipStream_t st);
-hipError_t launch_transpose_v(const void* v, void* vt, int dtype_bf16, int heads, int N, hipStream_t st);
+hipError_t launch_transpose_v(const void* v, const TokStride& vs, void* vt, int dtype_bf16, int nseq, int Hkv,
+                              int L, int NT, hipStream_t st);
 hipError_t launch_attention(const AttnArgs& a, hipStream_t st);
 
 }  // namespace fp

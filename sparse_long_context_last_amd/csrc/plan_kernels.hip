@@ -113,10 +113,12 @@ __device__ __forceinline__ float wave_max(float v) {
 
 // ---------------------------------------------------------------------------
 // K1: block means ("block-pooled" queries and keys)
-// out[head][kb][t] = (sum_r x[kb*bs + r][t], r ascending) * (1/bs).
+// out[head][kb][t] = (sum_r x[kb*bs + r][t], r ascending) / rows(kb), where
+// rows(kb) = bs except for a partial last block (for a full block the
+// division is the exact scaling by 1/bs).
 // 256 threads = 16 key blocks x 16 column groups of 8; each thread keeps 8
 // sequential sums and reads 16-byte (bf16) / 32-byte (fp32) row pieces.
-// grid (ceil(nb / 16), heads).
+// grid (ceil(nb / 16), heads), head = b * H + h.
 // ---------------------------------------------------------------------------
 template <typename T>
 __device__ __forceinline__ void load8_f32(const T* p, float* v);
@@ -137,35 +139,39 @@ template <> __device__ __forceinline__ void load8_f32<float>(const float* p, flo
 }
 
 template <typename T>
-__global__ __launch_bounds__(256) void k_pool(const T* __restrict__ x, float* __restrict__ out,
-                                              int N, int bs, float inv_bs) {
+__global__ __launch_bounds__(256) void k_pool(const T* __restrict__ x, TokStride xs, int H,
+                                              float* __restrict__ out, int L, int bs) {
     const int tid = threadIdx.x, cg = tid & 15;
     const int kb = blockIdx.x * 16 + (tid >> 4), head = blockIdx.y;
-    const int nb = N / bs;
+    const int nb = (L + bs - 1) / bs;
     if (kb >= nb) return;
-    const T* src = x + ((size_t)head * N + (size_t)kb * bs) * kHeadDim + 8 * cg;
+    const int rows = min(bs, L - kb * bs);
+    const T* src = x + (size_t)(head / H) * xs.bst + (size_t)(head % H) * xs.hs + (size_t)kb * bs * xs.rs + 8 * cg;
     float acc[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
 #pragma unroll 8
-    for (int r = 0; r < bs; ++r) {
+    for (int r = 0; r < rows; ++r) {
         float v[8];
-        load8_f32<T>(src + (size_t)r * kHeadDim, v);
+        load8_f32<T>(src + (size_t)r * xs.rs, v);
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[e] = acc[e] + v[e];
     }
     float* dst = out + ((size_t)head * nb + kb) * kHeadDim + 8 * cg;
+    const float fr = (float)rows;
     float4 lo, hi;
-    lo.x = acc[0] * inv_bs; lo.y = acc[1] * inv_bs; lo.z = acc[2] * inv_bs; lo.w = acc[3] * inv_bs;
-    hi.x = acc[4] * inv_bs; hi.y = acc[5] * inv_bs; hi.z = acc[6] * inv_bs; hi.w = acc[7] * inv_bs;
+    lo.x = acc[0] / fr; lo.y = acc[1] / fr; lo.z = acc[2] / fr; lo.w = acc[3] / fr;
+    hi.x = acc[4] / fr; hi.y = acc[5] / fr; hi.z = acc[6] / fr; hi.w = acc[7] / fr;
     reinterpret_cast<float4*>(dst)[0] = lo;
     reinterpret_cast<float4*>(dst)[1] = hi;
 }
 
 // ---------------------------------------------------------------------------
 // K2: exact scores of the last query block against every key.
-// s2[bh][i][j] = fp32(sum_t q[N-BS+i][t] * k[j][t]) * C, t ascending; plus the
-// per-(row, 256-key chunk) maxima over causal keys (j <= N-BS+i).
+// s2[bh][i][j] = fp32(sum_t q[L-BS+i][t] * k[j][t]) * C, t ascending; plus the
+// per-(row, 256-key chunk) maxima over causal keys (j <= L-BS+i).  Rows with
+// L-BS+i < 0 (a sequence shorter than one block) do not exist: their maxima
+// stay -inf and later kernels skip them.
 // Register-blocked VALU product: 256 threads, tile BS queries x 256 keys, each
 // thread owns BS/16 queries x 16 keys; d staged through LDS in slices of 32.
 // ---------------------------------------------------------------------------
@@ -174,19 +180,19 @@ constexpr int kScoreDS = kScoreDSConst;
 
 template <typename T, int BS>
 __global__ __launch_bounds__(256) void k_scores(const T* __restrict__ q, const T* __restrict__ k,
-                                                float* __restrict__ s2, float* __restrict__ pmax,
-                                                int N, int Hq, int Hkv, int group, float C) {
+                                                TokStride qs, TokStride ks, float* __restrict__ s2,
+                                                float* __restrict__ pmax, int L, int NS, int Hq, int group,
+                                                float C) {
     constexpr int D = kHeadDim, TK = kScoreTK, DS = kScoreDS, MR = BS / 16;
     __shared__ __attribute__((aligned(16))) float Qs[DS][BS + 4];
     __shared__ __attribute__((aligned(16))) float Ks[DS][TK + 4];
     const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
     const int chunk = blockIdx.x, bh = blockIdx.y;
     const int b = bh / Hq, h = bh % Hq;
-    const size_t kvbh = (size_t)b * Hkv + h / group;
-    const T* qlast = q + ((size_t)bh * N + (N - BS)) * D;
+    const T* qhead = q + (size_t)b * qs.bst + (size_t)h * qs.hs;
     const int j0 = chunk * TK;
-    const T* kbase = k + (kvbh * N + j0) * D;
-    const bool key_ok = (j0 + tid) < N;
+    const T* kbase = k + (size_t)b * ks.bst + (size_t)(h / group) * ks.hs;
+    const bool key_ok = (j0 + tid) < L;
 
     float acc[MR][16];
 #pragma unroll
@@ -198,12 +204,13 @@ __global__ __launch_bounds__(256) void k_scores(const T* __restrict__ q, const T
         // Q slice, transposed: Qs[tt][i]
         for (int e = tid; e < BS * DS; e += 256) {
             int i = e / DS, tt = e % DS;
-            Qs[tt][i] = load_f32(qlast + (size_t)i * D + t0 + tt);
+            const int pos = L - BS + i;
+            Qs[tt][i] = pos >= 0 ? load_f32(qhead + (size_t)pos * qs.rs + t0 + tt) : 0.0f;
         }
         // K slice, transposed: thread tid owns key j0 + tid
         {
             float kv[DS];
-            load_row_f32<T, DS>(kbase + (size_t)tid * D + t0, key_ok, kv);
+            load_row_f32<T, DS>(kbase + (size_t)(key_ok ? j0 + tid : 0) * ks.rs + t0, key_ok, kv);
 #pragma unroll
             for (int tt = 0; tt < DS; ++tt) Ks[tt][tid] = kv[tt];
         }
@@ -229,13 +236,13 @@ __global__ __launch_bounds__(256) void k_scores(const T* __restrict__ q, const T
         __syncthreads();
     }
 
-    const int nchunks = (N + TK - 1) / TK;
+    const int nchunks = NS / TK;
 #pragma unroll
     for (int m = 0; m < MR; ++m) {
         const int i = ty * MR + m;
-        const int pos = N - BS + i;
+        const int pos = L - BS + i;
         float mx = -INFINITY;
-        float* row = s2 + ((size_t)bh * BS + i) * N;
+        float* row = s2 + ((size_t)bh * BS + i) * NS;
 #pragma unroll
         for (int n = 0; n < 4; ++n) {
             const int j = j0 + n * 64 + tx * 4;
@@ -244,7 +251,7 @@ __global__ __launch_bounds__(256) void k_scores(const T* __restrict__ q, const T
             v.y = acc[m][n * 4 + 1] * C;
             v.z = acc[m][n * 4 + 2] * C;
             v.w = acc[m][n * 4 + 3] * C;
-            if (j < N) {
+            {
                 *reinterpret_cast<float4*>(row + j) = v;
                 if (j <= pos) mx = fmaxf(mx, v.x);
                 if (j + 1 <= pos) mx = fmaxf(mx, v.y);
@@ -263,22 +270,31 @@ __global__ __launch_bounds__(256) void k_scores(const T* __restrict__ q, const T
 // zpart[kb] = sum over the block's keys ascending; Z = sum of zpart
 // over kb ascending; rz = 1 / Z.  One workgroup per (bh, row); the row is
 // walked in segments of 64 key blocks staged through LDS, where one thread
-// per key block forms its sequential sum.
+// per key block forms its sequential sum.  A row that does not exist
+// (pos < 0) gets M = Z = rz = 0, so it adds exact zeros downstream.
 // ---------------------------------------------------------------------------
 constexpr int kSegBlocks = 64;
 
 template <int BS>
 __global__ __launch_bounds__(256) void k_rowexp(const float* __restrict__ s2, const float* __restrict__ pmax,
                                                 float* __restrict__ rowmax, float* __restrict__ rowsum,
-                                                float* __restrict__ rz, int N, Canon K) {
+                                                float* __restrict__ rz, int L, int NS, Canon K) {
     constexpr int SEG = kSegBlocks * BS;
     __shared__ float es[kSegBlocks][BS + 1];
     __shared__ float zp[kMaxBlocks];
     __shared__ float red[256];
     const int tid = threadIdx.x;
     const int row = blockIdx.x, bh = blockIdx.y;
-    const int nchunks = (N + kScoreTK - 1) / kScoreTK;
-    const int pos = N - BS + row;
+    const int nchunks = NS / kScoreTK;
+    const int pos = L - BS + row;
+    if (pos < 0) {
+        if (tid == 0) {
+            rowmax[(size_t)bh * BS + row] = 0.0f;
+            rowsum[(size_t)bh * BS + row] = 0.0f;
+            rz[(size_t)bh * BS + row] = 0.0f;
+        }
+        return;
+    }
     float mx = -INFINITY;
     for (int c = tid; c < nchunks; c += 256) mx = fmaxf(mx, pmax[((size_t)bh * nchunks + c) * BS + row]);
     red[tid] = mx;
@@ -288,14 +304,14 @@ __global__ __launch_bounds__(256) void k_rowexp(const float* __restrict__ s2, co
         __syncthreads();
     }
     const float M = red[0];
-    const float* srow = s2 + ((size_t)bh * BS + row) * N;
-    for (int seg0 = 0; seg0 < N; seg0 += SEG) {
+    const float* srow = s2 + ((size_t)bh * BS + row) * NS;
+    for (int seg0 = 0; seg0 < L; seg0 += SEG) {
 #pragma unroll 4
         for (int u = 0; u < SEG / 1024; ++u) {
             const int jl = u * 1024 + 4 * tid;      // 4 consecutive keys, coalesced
             const int j = seg0 + jl;
-            if (j < N) {
-                float4 v = *reinterpret_cast<const float4*>(srow + j);
+            {
+                float4 v = j < L ? *reinterpret_cast<const float4*>(srow + j) : make_float4(0.f, 0.f, 0.f, 0.f);
                 v.x = j <= pos ? exp2_c(v.x - M, K) : 0.0f;
                 v.y = j + 1 <= pos ? exp2_c(v.y - M, K) : 0.0f;
                 v.z = j + 2 <= pos ? exp2_c(v.z - M, K) : 0.0f;
@@ -305,7 +321,7 @@ __global__ __launch_bounds__(256) void k_rowexp(const float* __restrict__ s2, co
             }
         }
         __syncthreads();
-        if (tid < kSegBlocks && seg0 + tid * BS < N) {
+        if (tid < kSegBlocks && seg0 + tid * BS < L) {
             float z = 0.0f;
             for (int jj = 0; jj < BS; ++jj) z = z + es[tid][jj];
             zp[seg0 / BS + tid] = z;
@@ -313,7 +329,7 @@ __global__ __launch_bounds__(256) void k_rowexp(const float* __restrict__ s2, co
         __syncthreads();
     }
     if (tid == 0) {
-        const int nb = N / BS;
+        const int nb = (L + BS - 1) / BS;
         float Z = 0.0f;
         for (int kb = 0; kb < nb; ++kb) Z = Z + zp[kb];
         rowmax[(size_t)bh * BS + row] = M;
@@ -327,11 +343,12 @@ __global__ __launch_bounds__(256) void k_rowexp(const float* __restrict__ s2, co
 // (0 for j > pos):
 //   colsum[j]  = sum_i p[i][j],                        i ascending;
 //   diagsum[o] = sum_{i: pos_i >= o} p[i][pos_i - o],  i ascending.
-// Workgroup x owns columns j0 .. j0+W-1 and the offsets o = N - BS - j0 - t,
+// Workgroup x owns columns j0 .. j0+W-1 and the offsets o = L - BS - j0 - t,
 // t in [0, W): row i of such an offset reads column j0 + t + i, so one LDS
 // tile of W + BS columns per row serves both sums.  Rows are staged 16 at a
 // time; every thread keeps its sums in registers across the chunks.
-// Offsets above N - BS are done by k_diagtail.  grid (ceil(N / W), BH).
+// Offsets above L - BS are done by k_diagtail.  grid (ceil(L / W), BH).
+// Rows that do not exist (L < BS) have M = rz = 0 and contribute zeros.
 // ---------------------------------------------------------------------------
 constexpr int kLineW = 512;
 constexpr int kLineRC = 16;
@@ -339,7 +356,7 @@ constexpr int kLineRC = 16;
 template <int BS>
 __global__ __launch_bounds__(256) void k_linesums(const float* __restrict__ s2, const float* __restrict__ rowmax,
                                                   const float* __restrict__ rz, float* __restrict__ colsum,
-                                                  float* __restrict__ diagsum, int N, Canon K) {
+                                                  float* __restrict__ diagsum, int L, int NS, Canon K) {
     constexpr int W = kLineW, RC = kLineRC, TW = W + BS;
     __shared__ __attribute__((aligned(16))) float es[RC][TW];
     __shared__ float sM[BS], sR[BS];
@@ -352,14 +369,14 @@ __global__ __launch_bounds__(256) void k_linesums(const float* __restrict__ s2, 
     float cacc[W / 256], gacc[W / 256];
 #pragma unroll
     for (int q = 0; q < W / 256; ++q) cacc[q] = gacc[q] = 0.0f;
-    const float* S = s2 + (size_t)bh * BS * N;
+    const float* S = s2 + (size_t)bh * BS * NS;
     __syncthreads();
     for (int i0 = 0; i0 < BS; i0 += RC) {
         for (int e4 = tid; e4 < RC * TW / 4; e4 += 256) {
             const int ii = e4 / (TW / 4), cc = 4 * (e4 % (TW / 4));
-            const int i = i0 + ii, j = j0 + cc, pos = N - BS + i;
+            const int i = i0 + ii, j = j0 + cc, pos = L - BS + i;
             float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (j < N) v = *reinterpret_cast<const float4*>(S + (size_t)i * N + j);
+            if (j < L) v = *reinterpret_cast<const float4*>(S + (size_t)i * NS + j);
             const float M = sM[i];
             float4 x;
             x.x = j <= pos ? exp2_c(v.x - M, K) : 0.0f;
@@ -388,28 +405,29 @@ __global__ __launch_bounds__(256) void k_linesums(const float* __restrict__ s2, 
     for (int q = 0; q < W / 256; ++q) {
         const int t = tid + 256 * q;
         const int j = j0 + t;
-        if (j < N) colsum[(size_t)bh * N + j] = cacc[q];
-        const int o = N - BS - j0 - t;
-        if (o >= 0) diagsum[(size_t)bh * N + o] = gacc[q];
+        if (j < L) colsum[(size_t)bh * L + j] = cacc[q];
+        const int o = L - BS - j0 - t;
+        if (o >= 0) diagsum[(size_t)bh * L + o] = gacc[q];
     }
 }
 
-// Offsets o = N - BS + 1 + t (t < BS - 1): only rows i > t reach them,
-// at column i - t - 1.  grid (BH), BS threads.
+// Offsets o = L - BS + 1 + t (t < BS - 1, o >= 0): only rows i > t reach
+// them, at column i - t - 1.  grid (BH), BS threads.
 template <int BS>
 __global__ __launch_bounds__(BS) void k_diagtail(const float* __restrict__ s2, const float* __restrict__ rowmax,
                                                  const float* __restrict__ rz, float* __restrict__ diagsum,
-                                                 int N, Canon K) {
+                                                 int L, int NS, Canon K) {
     const int t = threadIdx.x, bh = blockIdx.x;
-    if (t >= BS - 1) return;
-    const float* S = s2 + (size_t)bh * BS * N;
+    const int o = L - BS + 1 + t;
+    if (t >= BS - 1 || o < 0) return;
+    const float* S = s2 + (size_t)bh * BS * NS;
     float g = 0.0f;
     for (int i = t + 1; i < BS; ++i) {
-        const float e = exp2_c(S[(size_t)i * N + (i - t - 1)] - rowmax[(size_t)bh * BS + i], K);
+        const float e = exp2_c(S[(size_t)i * NS + (i - t - 1)] - rowmax[(size_t)bh * BS + i], K);
         const float p = e * rz[(size_t)bh * BS + i];
         g = g + p;
     }
-    diagsum[(size_t)bh * N + (N - BS + 1 + t)] = g;
+    diagsum[(size_t)bh * L + o] = g;
 }
 
 // ---------------------------------------------------------------------------
@@ -417,14 +435,15 @@ __global__ __launch_bounds__(BS) void k_diagtail(const float* __restrict__ s2, c
 // colsum over the block (ascending), T = sum of t over kb (ascending).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_atrue(const float* __restrict__ colsum, float* __restrict__ atrue,
-                                               int N, int BS) {
+                                               int L, int BS) {
     __shared__ float ts[kMaxBlocks];
     __shared__ float Tsh;
-    const int tid = threadIdx.x, bh = blockIdx.x, nb = N / BS;
+    const int tid = threadIdx.x, bh = blockIdx.x, nb = (L + BS - 1) / BS;
     for (int kb = tid; kb < nb; kb += 256) {
-        const float* c = colsum + (size_t)bh * N + (size_t)kb * BS;
+        const float* c = colsum + (size_t)bh * L + (size_t)kb * BS;
+        const int n = min(BS, L - kb * BS);
         float t = 0.0f;
-        for (int jj = 0; jj < BS; ++jj) t = t + c[jj];
+        for (int jj = 0; jj < n; ++jj) t = t + c[jj];
         ts[kb] = t;
     }
     __syncthreads();
@@ -578,8 +597,8 @@ __device__ __forceinline__ ListRef list_of(const PlanDev& P, int list) {
         // the query-wise variant selects row by row in k_lists instead
         if (slot == 0 && !P.qa_querywise) { r.x = P.ahat + (size_t)bh * P.tri; r.len = P.tri; }
     } else {
-        r.x = (slot == 0 ? P.colsum : P.diagsum) + (size_t)bh * P.N;
-        r.len = P.N;
+        r.x = (slot == 0 ? P.colsum : P.diagsum) + (size_t)bh * P.L;
+        r.len = P.L;
     }
     return r;
 }
@@ -721,25 +740,29 @@ __global__ __launch_bounds__(256) void k_sel_scan(SelState* __restrict__ st, uns
 // colblk[kb]: some selected column j in key block kb.
 // diagA[a]:   some selected offset o with o / BS == a;
 // diagB[a]:   some selected offset o with o / BS == a and o % BS > 0.
-// Block (qb, kb) is touched iff colblk[kb] or diagA[qb-kb] or diagB[qb-kb-1].
-// grid (nb, BH), BS threads.
+// diagT[a]:   some selected offset o with o / BS == a and o % BS < tail
+//             (tail = query rows of the last, possibly partial, block row).
+// Block (qb, kb) is touched iff colblk[kb] or diagA[qb-kb] (diagT[qb-kb] in
+// the last block row) or diagB[qb-kb-1].  grid (nb, BH), BS threads.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(128) void k_vs_flags(PlanDev P, const SelState* __restrict__ st) {
-    __shared__ int f[3];
+    __shared__ int f[4];
     __shared__ unsigned char selc_s[kMaxBlock], selg_s[kMaxBlock];
     const int kb = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
     if (P.mode_all || P.pattern[bh] == kPatternQueryAware) return;
-    if (tid < 3) f[tid] = 0;
+    if (tid < 4) f[tid] = 0;
     __syncthreads();
     const SelState sc = st[2 * bh], sg = st[2 * bh + 1];
     const long long j = (long long)kb * P.BS + tid;
-    const float xc = P.colsum[(size_t)bh * P.N + j];
-    const float xg = P.diagsum[(size_t)bh * P.N + j];
-    const bool selc = sc.has && order_key(xc, j, sc.ibits) <= sc.kstar;
-    const bool selg = sg.has && order_key(xg, j, sg.ibits) <= sg.kstar;
+    const bool in = j < P.L;
+    const float xc = in ? P.colsum[(size_t)bh * P.L + j] : 0.0f;
+    const float xg = in ? P.diagsum[(size_t)bh * P.L + j] : 0.0f;
+    const bool selc = in && sc.has && order_key(xc, j, sc.ibits) <= sc.kstar;
+    const bool selg = in && sg.has && order_key(xg, j, sg.ibits) <= sg.kstar;
     if (selc) f[0] = 1;
     if (selg) f[1] = 1;
     if (selg && tid > 0) f[2] = 1;
+    if (selg && tid < P.tail) f[3] = 1;
     selc_s[tid] = selc;
     selg_s[tid] = selg;
     __syncthreads();
@@ -748,14 +771,15 @@ __global__ __launch_bounds__(128) void k_vs_flags(PlanDev P, const SelState* __r
         P.colblk[o] = (unsigned char)f[0];
         P.diagA[o] = (unsigned char)f[1];
         P.diagB[o] = (unsigned char)f[2];
+        P.diagT[o] = (unsigned char)f[3];
     }
     if (P.cap_blocks > 0 && tid == 0) {
         // line mass for the per-row cap, float32 sums in ascending index:
         // colmass[kb] = selected c[j] of this key block; diagmass[kb] starts
         // with the selected g[o] of offsets in block kb (the terms with
         // o % BS > 0 of block kb - 1 are added by k_diag_mass afterwards)
-        const float* cs = P.colsum + (size_t)bh * P.N + (size_t)kb * P.BS;
-        const float* gs = P.diagsum + (size_t)bh * P.N + (size_t)kb * P.BS;
+        const float* cs = P.colsum + (size_t)bh * P.L + (size_t)kb * P.BS;
+        const float* gs = P.diagsum + (size_t)bh * P.L + (size_t)kb * P.BS;
         float cm = 0.0f, dm = 0.0f;
         for (int r = 0; r < P.BS; ++r) {
             if (selc_s[r]) cm = cm + cs[r];
@@ -773,9 +797,9 @@ __global__ __launch_bounds__(64) void k_diag_mass(PlanDev P, const SelState* __r
     if (threadIdx.x != 0 || a == 0 || P.mode_all || P.pattern[bh] == kPatternQueryAware) return;
     const SelState sg = st[2 * bh + 1];
     const long long base = (long long)(a - 1) * P.BS;
-    const float* gs = P.diagsum + (size_t)bh * P.N;
+    const float* gs = P.diagsum + (size_t)bh * P.L;
     float dm = P.diagmass[(size_t)bh * P.nb + a];
-    for (int r = 1; r < P.BS; ++r) {
+    for (int r = 1; r < P.BS && base + r < P.L; ++r) {
         const float x = gs[base + r];
         if (sg.has && order_key(x, base + r, sg.ibits) <= sg.kstar) dm = dm + x;
     }
@@ -798,7 +822,8 @@ __device__ __forceinline__ bool member(const PlanDev& P, const SelState& s0, int
     if (qa) return s0.has && order_key(arow[kb], toff + kb, s0.ibits) <= s0.kstar;
     const size_t base = (size_t)bh * P.nb;
     const int a = qb - kb;
-    return P.colblk[base + kb] || P.diagA[base + a] || (a >= 1 && P.diagB[base + a - 1]);
+    const unsigned char* own = qb == P.nb - 1 ? P.diagT : P.diagA;
+    return P.colblk[base + kb] || own[base + a] || (a >= 1 && P.diagB[base + a - 1]);
 }
 
 __device__ __forceinline__ unsigned long long wave_sum_u64(unsigned long long v) {
@@ -995,24 +1020,23 @@ __global__ __launch_bounds__(256) void k_probe_sqrt(const double* x, double* y, 
 static inline unsigned grid1(long long n, int per = 256) { return (unsigned)((n + per - 1) / per); }
 
 hipError_t launch_plan(const PlanArgs& a, PlanDev& P, hipStream_t st) {
-    const int BS = P.BS, nb = P.nb, N = P.N, BH = P.BH;
-    const int bkv = a.B * a.Hkv;
-    const float inv_bs = 1.0f / (float)BS;
+    const int BS = P.BS, nb = P.nb, L = P.L, NS = P.NS, BH = P.BH;
+    const int bkv = a.nseq * a.Hkv;
     // K1
     const unsigned pg = (unsigned)((nb + 15) / 16);
     if (a.dtype_bf16) {
-        hipLaunchKernelGGL(k_pool<bf16_t>, dim3(pg, BH), dim3(256), 0, st, (const bf16_t*)a.q, P.qbar, N, BS, inv_bs);
-        hipLaunchKernelGGL(k_pool<bf16_t>, dim3(pg, bkv), dim3(256), 0, st, (const bf16_t*)a.k, P.kbar, N, BS, inv_bs);
+        hipLaunchKernelGGL(k_pool<bf16_t>, dim3(pg, BH), dim3(256), 0, st, (const bf16_t*)a.q, a.qs, a.Hq, P.qbar, L, BS);
+        hipLaunchKernelGGL(k_pool<bf16_t>, dim3(pg, bkv), dim3(256), 0, st, (const bf16_t*)a.k, a.ks, a.Hkv, P.kbar, L, BS);
     } else {
-        hipLaunchKernelGGL(k_pool<float>, dim3(pg, BH), dim3(256), 0, st, (const float*)a.q, P.qbar, N, BS, inv_bs);
-        hipLaunchKernelGGL(k_pool<float>, dim3(pg, bkv), dim3(256), 0, st, (const float*)a.k, P.kbar, N, BS, inv_bs);
+        hipLaunchKernelGGL(k_pool<float>, dim3(pg, BH), dim3(256), 0, st, (const float*)a.q, a.qs, a.Hq, P.qbar, L, BS);
+        hipLaunchKernelGGL(k_pool<float>, dim3(pg, bkv), dim3(256), 0, st, (const float*)a.k, a.ks, a.Hkv, P.kbar, L, BS);
     }
     // K2
-    const dim3 gs((N + kScoreTK - 1) / kScoreTK, BH);
+    const dim3 gs(NS / kScoreTK, BH);
     const int group = a.Hq / a.Hkv;
 #define FP_SCORES(T, B_)                                                                                   \
-    hipLaunchKernelGGL((k_scores<T, B_>), gs, dim3(256), 0, st, (const T*)a.q, (const T*)a.k, a.s2, a.pmax, \
-                       N, a.Hq, a.Hkv, group, a.canon.C)
+    hipLaunchKernelGGL((k_scores<T, B_>), gs, dim3(256), 0, st, (const T*)a.q, (const T*)a.k, a.qs, a.ks,   \
+                       a.s2, a.pmax, L, NS, a.Hq, group, a.canon.C)
     if (a.dtype_bf16) {
         if (BS == 128) FP_SCORES(bf16_t, 128); else FP_SCORES(bf16_t, 64);
     } else {
@@ -1021,18 +1045,24 @@ hipError_t launch_plan(const PlanArgs& a, PlanDev& P, hipStream_t st) {
 #undef FP_SCORES
     // K3
     if (BS == 128)
-        hipLaunchKernelGGL(k_rowexp<128>, dim3(BS, BH), dim3(256), 0, st, a.s2, a.pmax, P.rowmax, P.rowsum, a.rz, N, a.canon);
+        hipLaunchKernelGGL(k_rowexp<128>, dim3(BS, BH), dim3(256), 0, st, a.s2, a.pmax, P.rowmax, P.rowsum, a.rz, L,
+                           NS, a.canon);
     else
-        hipLaunchKernelGGL(k_rowexp<64>, dim3(BS, BH), dim3(256), 0, st, a.s2, a.pmax, P.rowmax, P.rowsum, a.rz, N, a.canon);
-    const dim3 gl((N + kLineW - 1) / kLineW, BH);
+        hipLaunchKernelGGL(k_rowexp<64>, dim3(BS, BH), dim3(256), 0, st, a.s2, a.pmax, P.rowmax, P.rowsum, a.rz, L,
+                           NS, a.canon);
+    const dim3 gl((L + kLineW - 1) / kLineW, BH);
     if (BS == 128) {
-        hipLaunchKernelGGL(k_linesums<128>, gl, dim3(256), 0, st, a.s2, P.rowmax, a.rz, P.colsum, P.diagsum, N, a.canon);
-        hipLaunchKernelGGL(k_diagtail<128>, dim3(BH), dim3(128), 0, st, a.s2, P.rowmax, a.rz, P.diagsum, N, a.canon);
+        hipLaunchKernelGGL(k_linesums<128>, gl, dim3(256), 0, st, a.s2, P.rowmax, a.rz, P.colsum, P.diagsum, L, NS,
+                           a.canon);
+        hipLaunchKernelGGL(k_diagtail<128>, dim3(BH), dim3(128), 0, st, a.s2, P.rowmax, a.rz, P.diagsum, L, NS,
+                           a.canon);
     } else {
-        hipLaunchKernelGGL(k_linesums<64>, gl, dim3(256), 0, st, a.s2, P.rowmax, a.rz, P.colsum, P.diagsum, N, a.canon);
-        hipLaunchKernelGGL(k_diagtail<64>, dim3(BH), dim3(64), 0, st, a.s2, P.rowmax, a.rz, P.diagsum, N, a.canon);
+        hipLaunchKernelGGL(k_linesums<64>, gl, dim3(256), 0, st, a.s2, P.rowmax, a.rz, P.colsum, P.diagsum, L, NS,
+                           a.canon);
+        hipLaunchKernelGGL(k_diagtail<64>, dim3(BH), dim3(64), 0, st, a.s2, P.rowmax, a.rz, P.diagsum, L, NS,
+                           a.canon);
     }
-    hipLaunchKernelGGL(k_atrue, dim3(BH), dim3(256), 0, st, P.colsum, P.atrue, N, BS);
+    hipLaunchKernelGGL(k_atrue, dim3(BH), dim3(256), 0, st, P.colsum, P.atrue, L, BS);
     // K4, K5
     if (nb <= 1024) {
         const size_t lds = (size_t)8 * nb * sizeof(float);
@@ -1048,7 +1078,7 @@ hipError_t launch_plan(const PlanArgs& a, PlanDev& P, hipStream_t st) {
     const int nlists = 2 * BH;
     if (!P.mode_all) {
         hipLaunchKernelGGL(k_sel_reset, dim3(grid1((long long)nlists * kRadixBins)), dim3(256), 0, st, P.sel, P.hist, nlists);
-        const long long maxlen = P.tri > N ? P.tri : N;
+        const long long maxlen = P.tri > L ? P.tri : L;
         const dim3 gc((unsigned)((maxlen + kSelChunk - 1) / kSelChunk), nlists);
         hipLaunchKernelGGL(k_sel_total, gc, dim3(256), 0, st, P, P.sel);
         hipLaunchKernelGGL(k_sel_init, dim3(grid1(nlists)), dim3(256), 0, st, P, P.sel, nlists, a.G);
@@ -1065,6 +1095,14 @@ hipError_t launch_plan(const PlanArgs& a, PlanDev& P, hipStream_t st) {
     hipLaunchKernelGGL(k_fill_u32, dim3(grid1(2LL * BH)), dim3(256), 0, st, (unsigned int*)P.total_blocks, 0u,
                        2LL * BH);
     hipLaunchKernelGGL(k_lists, dim3((nb + 3) / 4, BH), dim3(256), 0, st, P, P.sel);
+    return hipGetLastError();
+}
+
+hipError_t launch_fill_u32(unsigned int* p, unsigned int v, long long n, hipStream_t st) {
+    if (n > 0) {
+        const long long g = (n + 255) / 256;
+        hipLaunchKernelGGL(k_fill_u32, dim3((unsigned)(g < 65535 ? g : 65535)), dim3(256), 0, st, p, v, n);
+    }
     return hipGetLastError();
 }
 

@@ -60,7 +60,7 @@ def _plan(lib, dtype=0, B=1, Hq=4, Hkv=4, N=1024, d=128, block=128, gamma=0.95, 
 
 @pytest.mark.parametrize("kw,code", [
     (dict(d=64), -2), (dict(d=256), -2), (dict(block=32), -2), (dict(dtype=7), -2),
-    (dict(N=1000), -3), (dict(Hq=6, Hkv=4), -3), (dict(N=128 * 4097), -3), (dict(Hkv=0), -3),
+    (dict(Hq=6, Hkv=4), -3), (dict(N=128 * 4097), -3), (dict(N=128 * 4096 + 1), -3), (dict(Hkv=0), -3),
     (dict(gamma=0.0), -1), (dict(gamma=1.5), -1), (dict(gamma=float("nan")), -1),
     (dict(tau=-0.1), -1), (dict(tau=float("inf")), -1), (dict(min_budget=-1), -1),
     (dict(q=None), -1), (dict(k=None), -1), (dict(B=-1), -1), (dict(out=False), -1),
@@ -143,3 +143,39 @@ def test_plan_options_validation(lib):
         assert lib.fp_plan_info_get(h, C.byref(info)) == 0
         assert (info.max_budget, info.qa_selection) == ((8192, 1) if opt is not None else (0, 0))
         lib.fp_plan_destroy(h)
+
+
+def test_varlen_validation(lib):
+    from sparse_long_context_last_amd._lib import PlanInfo
+
+    def plan_v(cu, nseq=None, q=1, Hq=4, Hkv=4, block=128):
+        cu = np.asarray(cu, np.int32)
+        h = C.c_void_p()
+        st = lib.fp_prefill_plan_varlen(q, q, 0, len(cu) - 1 if nseq is None else nseq,
+                                        cu.ctypes.data if cu.size else None, Hq, Hkv, 128, block, 0.95, 0.1,
+                                        1024, None, None, C.byref(h))
+        return st, h
+    assert plan_v([1, 5])[0] == -1                        # cu[0] != 0
+    assert plan_v([0, 9, 5])[0] == -1                     # decreasing
+    assert "decreases" in lib.fp_last_error().decode()
+    assert plan_v([], nseq=2)[0] == -1                    # NULL cu_seqlens
+    assert plan_v([0, 128 * 4096 + 1])[0] == -3           # more than 4096 blocks
+    assert plan_v([0, 100], Hq=6)[0] == -3                # Hq % Hkv
+    assert plan_v([0, 100], nseq=-1)[0] == -1
+    # no tokens at all: valid, no device needed; every head reports pattern 0
+    for cu in ([0], [0, 0, 0]):
+        st, h = plan_v(cu, q=None)
+        assert st == 0, lib.fp_last_error()
+        info = PlanInfo()
+        assert lib.fp_plan_info_get(h, C.byref(info)) == 0
+        assert info.layout == 1 and info.rows == 0 and info.tokens == 0 and info.total_blocks == 0
+        pat = np.ones(max(1, info.B * info.Hq), np.uint8)
+        rp = np.ones(1, np.int32)
+        assert lib.fp_plan_copy_out(h, pat.ctypes.data, None, rp.ctypes.data, rp.ctypes.data, None) == 0
+        assert rp[0] == 0 and (info.B == 0 or not pat.any())
+        assert lib.fp_prefill_attend(h, None, None, None, None, None) == 0
+        lib.fp_plan_destroy(h)
+    cu = np.zeros(3, np.int32)
+    assert lib.fp_dense_attend_varlen(None, None, None, None, 0, 2, cu.ctypes.data, 4, 4, 128, 128, None) == 0
+    cu = np.array([0, 3], np.int32)
+    assert lib.fp_dense_attend_varlen(None, None, None, None, 0, 1, cu.ctypes.data, 4, 4, 128, 128, None) == -1
