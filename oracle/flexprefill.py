@@ -49,7 +49,10 @@ the design notes of the repository):
     estimate (query-aware) or selected line mass (vertical-slash), ties
     to the block nearest the diagonal;
   * the optional query-wise selection applies the same cumulative rule to
-    each estimated row on its own instead of to the flattened map.
+    each estimated row on its own instead of to the flattened map;
+  * the optional token-granular vertical-slash mode attends a vertical-slash
+    head's selected columns token by token and keeps only its slash blocks
+    and the minimum-budget fill (and cap) as whole blocks.
 
 Pins (tests in ``tests/test_oracle_*.py``): exp2_c / ln_c against libm
 within a few ulp; JSD against scipy and closed forms; canonical softmax
@@ -507,6 +510,7 @@ class HeadPlan:
     sel_s: Optional[np.ndarray]
     mask: np.ndarray             # [nb, nb] final block mask incl. the floor
     lists: List[np.ndarray] = field(default_factory=list)
+    cols: Optional[np.ndarray] = None   # [N] token-granular columns (vertical-slash, token mode)
 
     @property
     def counts(self) -> np.ndarray:
@@ -515,17 +519,29 @@ class HeadPlan:
 
 QA_FLATTENED = "flattened"
 QA_QUERYWISE = "querywise"
+VS_BLOCK = "block"
+VS_TOKEN = "token"
 
 
 def plan_head(q: np.ndarray, k: np.ndarray, bs: int, gamma: float, tau: float,
-              min_budget: int, max_budget: int = 0, qa_selection: str = QA_FLATTENED) -> HeadPlan:
+              min_budget: int, max_budget: int = 0, qa_selection: str = QA_FLATTENED,
+              vs_granularity: str = VS_BLOCK) -> HeadPlan:
     """Pattern determination and index selection for one query head q [N, d]
     against its key/value head's keys k [N, d]; max_budget > 0 caps every
     query-block row (applied after the minimum-budget fill); qa_selection
     picks the flattened (default) or the query-wise selection for a
-    query-aware head."""
+    query-aware head.
+
+    vs_granularity = "token" keeps a vertical-slash head's selected key
+    columns as single tokens instead of whole blocks: the block mask then
+    holds the blocks its slash lines touch plus the minimum-budget fill (and
+    the cap), and ``cols`` marks the columns every later query attends to
+    individually (the pages call the selections lines; the blocked kernel is
+    the default)."""
     if qa_selection not in (QA_FLATTENED, QA_QUERYWISE):
         raise ValueError(f"unknown qa_selection {qa_selection!r}")
+    if vs_granularity not in (VS_BLOCK, VS_TOKEN):
+        raise ValueError(f"unknown vs_granularity {vs_granularity!r}")
     q = np.asarray(q, dtype=F32)
     k = np.asarray(k, dtype=F32)
     N, d = q.shape
@@ -550,7 +566,10 @@ def plan_head(q: np.ndarray, k: np.ndarray, bs: int, gamma: float, tau: float,
     else:
         sel_v = select_cumulative(st.c, gamma)
         sel_s = select_cumulative(st.g, gamma)
-        mask = vs_block_mask(sel_v, sel_s, bs)
+        if vs_granularity == VS_TOKEN:
+            mask = vs_block_mask(np.zeros_like(sel_v), sel_s, bs)
+        else:
+            mask = vs_block_mask(sel_v, sel_s, bs)
     mask = apply_floor(mask, min_budget, bs)
     if cap_blocks(max_budget, bs):
         if pattern == QUERY_AWARE or sel_v is None:
@@ -559,7 +578,8 @@ def plan_head(q: np.ndarray, k: np.ndarray, bs: int, gamma: float, tau: float,
             scores = vs_block_scores(st.c, st.g, sel_v, sel_s, bs)
         mask = apply_cap(mask, scores, max_budget, bs)
     lists = [np.nonzero(mask[qb, : qb + 1])[0].astype(np.int32) for qb in range(nb)]
-    return HeadPlan(qbar, kbar, st, A, jsd, D, pattern, sel_qa, sel_v, sel_s, mask, lists)
+    cols = sel_v.copy() if (vs_granularity == VS_TOKEN and sel_v is not None) else None
+    return HeadPlan(qbar, kbar, st, A, jsd, D, pattern, sel_qa, sel_v, sel_s, mask, lists, cols)
 
 
 # --------------------------------------------------------------------------
@@ -568,11 +588,12 @@ def plan_head(q: np.ndarray, k: np.ndarray, bs: int, gamma: float, tau: float,
 
 
 def attend_rows(q: np.ndarray, k: np.ndarray, v: np.ndarray, mask: np.ndarray,
-                bs: int, qbs: Iterable[int]) -> Dict[int, np.ndarray]:
+                bs: int, qbs: Iterable[int], cols: Optional[np.ndarray] = None) -> Dict[int, np.ndarray]:
     """float64 attention outputs of the query blocks ``qbs``: for query i the
-    keys j <= i whose block (i // bs, j // bs) is in ``mask``; scores
-    q_i . k_j / sqrt(d); softmax; weighted sum of v_j.  A partial last block
-    (N not a multiple of bs) has N - qb bs rows."""
+    keys j <= i whose block (i // bs, j // bs) is in ``mask`` or, when given,
+    whose column is marked in ``cols``; scores q_i . k_j / sqrt(d); softmax;
+    weighted sum of v_j.  A partial last block (N not a multiple of bs) has
+    N - qb bs rows."""
     q = np.asarray(q, dtype=F64)
     k = np.asarray(k, dtype=F64)
     v = np.asarray(v, dtype=F64)
@@ -583,7 +604,10 @@ def attend_rows(q: np.ndarray, k: np.ndarray, v: np.ndarray, mask: np.ndarray,
         i = np.arange(qb * bs, end)
         s = (q[i] @ k[:end].T) / math.sqrt(d)
         j = np.arange(end)
-        keep = (j[None, :] <= i[:, None]) & mask[qb, j // bs][None, :]
+        sel = mask[qb, j // bs]
+        if cols is not None:
+            sel = sel | cols[:end]
+        keep = (j[None, :] <= i[:, None]) & sel[None, :]
         s = np.where(keep, s, -np.inf)
         mx = s.max(axis=1, keepdims=True)
         w = np.where(keep, np.exp(s - mx), 0.0)
@@ -592,9 +616,9 @@ def attend_rows(q: np.ndarray, k: np.ndarray, v: np.ndarray, mask: np.ndarray,
     return out
 
 
-def attend_head(q, k, v, mask, bs) -> np.ndarray:
+def attend_head(q, k, v, mask, bs, cols=None) -> np.ndarray:
     nb = -(-q.shape[0] // bs)
-    rows = attend_rows(q, k, v, mask, bs, range(nb))
+    rows = attend_rows(q, k, v, mask, bs, range(nb), cols)
     return np.concatenate([rows[qb] for qb in range(nb)], axis=0)
 
 

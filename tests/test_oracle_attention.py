@@ -152,3 +152,40 @@ def test_constant_inputs_tie_break():
     # single block: the whole plan degenerates to the one diagonal block
     P1 = O.plan_head(q[:bs], k[:bs], bs, 0.95, 0.1, 0)
     assert P1.D == 0.0 and [x.tolist() for x in P1.lists] == [[0]]
+
+
+def test_token_granular_vertical_slash():
+    """Token mode: block mask = slash blocks + floor; every selected column is
+    attended by every later query (token-level brute force), and the result
+    equals the block mode's whenever the columns' blocks are in the mask."""
+    rng = np.random.default_rng(31)
+    bs, N, d = 8, 61, 16
+    q = rng.standard_normal((N, d)).astype(F32)
+    k = rng.standard_normal((N, d)).astype(F32)
+    v = rng.standard_normal((N, d)).astype(F32)
+    k[[3, 20]] += 4.0                                   # two sink columns
+    P = O.plan_head(q, k, bs, 0.7, 0.0, bs, vs_granularity=O.VS_TOKEN)
+    B = O.plan_head(q, k, bs, 0.7, 0.0, bs)
+    assert P.pattern == O.VERTICAL_SLASH and P.cols is not None and P.cols.any()
+    assert np.array_equal(P.cols, B.sel_v) and B.cols is None
+    nb = -(-N // bs)
+    slash = O.apply_floor(O.vs_block_mask(np.zeros(N, bool), P.sel_s, bs), bs, bs)
+    assert np.array_equal(P.mask, slash)
+    assert not (P.mask & ~B.mask).any()               # never more blocks than block mode
+    # token-level definition
+    out = O.attend_head(q, k, v, P.mask, bs, P.cols)
+    ref = np.zeros((N, d))
+    for i in range(N):
+        keys = [j for j in range(i + 1) if P.mask[i // bs, j // bs] or P.cols[j]]
+        s = np.array([float(q[i].astype(np.float64) @ k[j].astype(np.float64)) for j in keys]) / math.sqrt(d)
+        w = np.exp(s - s.max())
+        ref[i] = (w / w.sum()) @ v[keys].astype(np.float64)
+    np.testing.assert_allclose(out, ref, rtol=0, atol=1e-12)
+    # marking every column of the block mode's column blocks reproduces block mode
+    colblk = np.zeros(N, bool)
+    for kb in np.unique(np.nonzero(B.sel_v)[0] // bs):
+        colblk[kb * bs: (kb + 1) * bs] = True
+    np.testing.assert_allclose(O.attend_head(q, k, v, P.mask, bs, colblk),
+                               O.attend_head(q, k, v, B.mask, bs), rtol=0, atol=1e-12)
+    with pytest.raises(ValueError):
+        O.plan_head(q, k, bs, 0.7, 0.0, bs, vs_granularity="lines")
