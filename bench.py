@@ -61,7 +61,7 @@ def read_traffic(workload: str, default_settings: bool):
 
 
 def cpu_baseline(cfg, total_blocks_by_head, sample_rows: int, budget_s: float, max_budget: int = 0,
-                 qa_selection: str = "flattened"):
+                 qa_selection: str = "flattened", vs_granularity: str = "block"):
     """The oracle as it stands on the host cores: one query head planned in
     full, float64 attention on a sample of that head's query blocks,
     extrapolated to the whole layer by head count and selected-block count."""
@@ -79,14 +79,15 @@ def cpu_baseline(cfg, total_blocks_by_head, sample_rows: int, budget_s: float, m
     k = gen.k_head(0, h // cfg.group)
     v = gen.v_head(0, h // cfg.group)
     t0 = time.perf_counter()
-    hp = O.plan_head(q, k, cfg.block, cfg.gamma, cfg.tau, cfg.min_budget, max_budget, qa_selection)
+    hp = O.plan_head(q, k, cfg.block, cfg.gamma, cfg.tau, cfg.min_budget, max_budget, qa_selection,
+                     vs_granularity)
     t_plan = time.perf_counter() - t0
     rng = np.random.default_rng(7)
     rows = sorted(set([0, cfg.nb - 1] + rng.choice(cfg.nb, size=min(cfg.nb, sample_rows), replace=False).tolist()))
     t0 = time.perf_counter()
     done_blocks = 0
     for r in rows:
-        O.attend_rows(q, k, v, hp.mask, cfg.block, [r])
+        O.attend_rows(q, k, v, hp.mask, cfg.block, [r], hp.cols)
         done_blocks += len(hp.lists[r])
         if time.perf_counter() - t0 > budget_s:
             break
@@ -115,6 +116,8 @@ def main() -> int:
                     help="cap every query-block row at this many keys (0: uncapped)")
     ap.add_argument("--qa-selection", default="flattened", choices=["flattened", "querywise"],
                     help="how query-aware heads select blocks from the estimated map")
+    ap.add_argument("--vs-granularity", default="block", choices=["block", "token"],
+                    help="vertical-slash columns as whole blocks or token by token")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -144,7 +147,8 @@ def main() -> int:
 
     def step():
         P = F.plan(q, k, block=cfg.block, gamma=cfg.gamma, tau=cfg.tau, min_budget=cfg.min_budget,
-                   max_budget=args.max_budget, qa_selection=args.qa_selection)
+                   max_budget=args.max_budget, qa_selection=args.qa_selection,
+                   vs_granularity=args.vs_granularity)
         F.attend(P, q, k, v, out=out)
         return P
 
@@ -162,7 +166,8 @@ def main() -> int:
     for i in range(args.steps):
         ev[i][0].record(stream)
         P = F.plan(q, k, block=cfg.block, gamma=cfg.gamma, tau=cfg.tau, min_budget=cfg.min_budget,
-                   max_budget=args.max_budget, qa_selection=args.qa_selection)
+                   max_budget=args.max_budget, qa_selection=args.qa_selection,
+                   vs_granularity=args.vs_granularity)
         ev[i][1].record(stream)
         F.attend(P, q, k, v, out=out)
         ev[i][2].record(stream)
@@ -176,12 +181,20 @@ def main() -> int:
     F.profile_enable(False)
     info = plans[-1].info()
     counts = plans[-1].debug("counts")
+    plans_last_colptr = plans[-1].debug("colptr") if args.vs_granularity == "token" else None
     pattern, djs, _, _ = plans[-1].copy_out()
     del plans
     blocks_by_head = counts.sum(axis=1).tolist()
 
     flop_per_block = 4.0 * cfg.block * cfg.block * cfg.d
     sparse_flop = info.total_blocks * flop_per_block
+    gathered_tiles = 0
+    if args.vs_granularity == "token":
+        # gathered-column tiles: ceil(columns before the row's end / 64) per row,
+        # each 64 keys x block queries x 4 d FLOP
+        cp = plans_last_colptr.astype(np.int64)[:, 1:]
+        gathered_tiles = int(((cp + 63) // 64).sum())
+        sparse_flop += gathered_tiles * 4.0 * 64 * cfg.block * cfg.d
     dense_flop = info.dense_blocks * flop_per_block
     kern_avg_ms = kern_ms / max(kern_n, 1)
     peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_FP32_TFLOPS
@@ -216,17 +229,19 @@ def main() -> int:
         torch.cuda.synchronize()
         del a, b
 
-    traffic = read_traffic(cfg.name, args.max_budget == 0 and args.qa_selection == "flattened")
+    traffic = read_traffic(cfg.name, args.max_budget == 0 and args.qa_selection == "flattened"
+                           and args.vs_granularity == "block")
     roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
             "frac": round(achieved / peak, 4), "traffic": traffic,
-            "kernel": f"fp::k_attn_{'bf16' if cfg.dtype == 'bf16' else 'f32'}<{cfg.block}, true>",
+            "kernel": (f"fp::k_attn_{'bf16' if cfg.dtype == 'bf16' else 'f32'}<{cfg.block}, true, "
+                       f"{'true' if args.vs_granularity == 'token' else 'false'}>"),
             "algorithmic_flop_per_launch": sparse_flop, "avg_kernel_ms": round(kern_avg_ms, 4),
             "launches": kern_n}
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
         cpu = cpu_baseline(cfg, blocks_by_head, args.cpu_rows, args.cpu_budget_s, args.max_budget,
-                           args.qa_selection)
+                           args.qa_selection, args.vs_granularity)
 
     rec = {
         "metric": METRIC,
@@ -244,7 +259,7 @@ def main() -> int:
         "config": {"workload": cfg.name, "B": cfg.B, "Hq": cfg.Hq, "Hkv": cfg.Hkv, "N": cfg.N,
                    "d": cfg.d, "block": cfg.block, "gamma": cfg.gamma, "tau": cfg.tau,
                    "min_budget": cfg.min_budget, "max_budget": args.max_budget,
-                   "qa_selection": args.qa_selection,
+                   "qa_selection": args.qa_selection, "vs_granularity": args.vs_granularity,
                    "parallelism": "single GPU"},
         "plan_ms": round(plan_ms, 3),
         "attend_ms": round(attend_ms, 3),
@@ -254,6 +269,7 @@ def main() -> int:
         "dense_kernel_ms": round(dense_kernel_ms, 3) if dense_ms is not None else None,
         "speedup_vs_dense": round(dense_ms / step_ms, 3) if dense_ms is not None else None,
         "computed_blocks": info.total_blocks,
+        "gathered_column_tiles": gathered_tiles,
         "dense_blocks": info.dense_blocks,
         "density": round(info.total_blocks / max(info.dense_blocks, 1), 5),
         "query_aware_heads": info.query_aware_heads,

@@ -85,6 +85,7 @@ typedef struct fp_plan_info {
     int max_budget;                    /* tokens, 0 = uncapped */
     int qa_selection;                  /* fp_qa_selection */
     int layout;                        /* fp_layout */
+    int vs_granularity;                /* fp_vs_granularity */
     long long tokens;                  /* B * N (BHND) or T (THD) */
     long long rows;                    /* query-block rows of all heads: sum over sequences of Hq * nb */
 } fp_plan_info;
@@ -95,10 +96,17 @@ typedef enum fp_qa_selection {
     FP_QA_QUERYWISE = 1    /* every query-block row selects from its own row */
 } fp_qa_selection;
 
+/* How a vertical-slash head's selected key columns are attended. */
+typedef enum fp_vs_granularity {
+    FP_VS_BLOCK = 0,       /* whole key blocks touched by a selected column (the method's blocked kernel) */
+    FP_VS_TOKEN = 1        /* each selected column on its own, gathered into dense key tiles */
+} fp_vs_granularity;
+
 /* Optional planning settings; a NULL pointer means all defaults (zeros). */
 typedef struct fp_plan_options {
     int max_budget;        /* tokens per query-block row, 0 = uncapped */
     int qa_selection;      /* fp_qa_selection */
+    int vs_granularity;    /* fp_vs_granularity */
 } fp_plan_options;
 
 /*
@@ -138,8 +146,17 @@ fp_status fp_prefill_plan(const void* q, const void* k, fp_dtype dtype,
  *   its own -- the minimal set of the row's key blocks, value descending
  *   then key block ascending, whose fixed-point mass reaches gamma of the
  *   row's total.  Vertical-slash heads are unaffected.
+ *   options->vs_granularity = FP_VS_TOKEN (the Approach paragraph calls a
+ *   vertical-slash selection a set of lines): a vertical-slash head attends
+ *   each selected key column token by token -- every query j >= column sees
+ *   it -- instead of computing every key block a column touches; the blocks
+ *   its slash lines touch, the minimum-budget fill and the cap stay whole
+ *   blocks (the block lists then hold only those).  fp_prefill_attend
+ *   gathers the columns' K and V rows into dense 64-key tiles (a workspace
+ *   of 2*B*Hq*nb*block*d elements).  Query-aware heads are unaffected.
  *   FP_ERR_INVALID_ARG if max_budget < 0, if it allows fewer blocks per row
- *   than min_budget asks for, or if qa_selection is not a listed value.
+ *   than min_budget asks for, or if qa_selection or vs_granularity is not a
+ *   listed value.
  */
 fp_status fp_prefill_plan_ex(const void* q, const void* k, fp_dtype dtype,
                              int B, int Hq, int Hkv, int N, int d, int block,
@@ -224,11 +241,16 @@ fp_status fp_plan_copy_out(const fp_plan* plan, unsigned char* pattern, double* 
  *   FP_DBG_ATRUE  float [B*Hq][nb]         block-pooled true distribution
  *   FP_DBG_AHAT   float [B*Hq][nb(nb+1)/2] estimated map, causal triangle row-major
  *   FP_DBG_COUNTS int   [B*Hq][nb]         selected blocks per row
+ *   FP_DBG_COLPTR int   [B*Hq][nb+1]       token-granular columns before each key
+ *                                          block (FP_VS_TOKEN plans; 0 bytes otherwise)
+ *   FP_DBG_COLIDX int   [B*Hq][N]          those columns ascending, the first
+ *                                          colptr[nb] entries of each head valid
+ *                                          (FP_VS_TOKEN plans; 0 bytes otherwise)
  */
 enum {
     FP_DBG_QBAR = 0, FP_DBG_KBAR = 1, FP_DBG_ROWMAX = 2, FP_DBG_ROWSUM = 3,
     FP_DBG_COLSUM = 4, FP_DBG_DIAGSUM = 5, FP_DBG_ATRUE = 6, FP_DBG_AHAT = 7,
-    FP_DBG_COUNTS = 8
+    FP_DBG_COUNTS = 8, FP_DBG_COLPTR = 9, FP_DBG_COLIDX = 10
 };
 fp_status fp_plan_copy_debug(const fp_plan* plan, int which, void* host_dst, size_t bytes);
 

@@ -127,7 +127,8 @@ class Plan:
                 "rowmax": ((self.Hq, bs), np.float32), "rowsum": ((self.Hq, bs), np.float32),
                 "colsum": ((self.Hq, L), np.float32), "diagsum": ((self.Hq, L), np.float32),
                 "atrue": ((self.Hq, nb), np.float32), "ahat": ((self.Hq, nb * (nb + 1) // 2), np.float32),
-                "counts": ((self.Hq, nb), np.int32)}[item]
+                "counts": ((self.Hq, nb), np.int32),
+                "colptr": ((self.Hq, nb + 1), np.int32), "colidx": ((self.Hq, L), np.int32)}[item]
 
     def debug_seqs(self, item: str):
         """An intermediate of steps 1-2 per sequence: a list over sequences of
@@ -173,18 +174,22 @@ class Plan:
             pass
 
 
-def _options(max_budget: int, qa_selection: str):
+def _options(max_budget: int, qa_selection: str, vs_granularity: str):
     if qa_selection not in _lib.QA_SELECTION:
         raise ValueError(f"qa_selection must be one of {sorted(_lib.QA_SELECTION)}")
-    return _lib.PlanOptions(int(max_budget), _lib.QA_SELECTION[qa_selection])
+    if vs_granularity not in _lib.VS_GRANULARITY:
+        raise ValueError(f"vs_granularity must be one of {sorted(_lib.VS_GRANULARITY)}")
+    return _lib.PlanOptions(int(max_budget), _lib.QA_SELECTION[qa_selection],
+                            _lib.VS_GRANULARITY[vs_granularity])
 
 
 def plan(q, k, block: int = 128, gamma: float = 0.95, tau: float = 0.1,
          min_budget: int = 1024, max_budget: int = 0, qa_selection: str = "flattened",
-         stream=None) -> Plan:
+         vs_granularity: str = "block", stream=None) -> Plan:
     """Pattern determination and index selection for q [B, Hq, N, d],
     k [B, Hkv, N, d] (fp_prefill_plan_ex; max_budget = 0 leaves rows
-    uncapped; qa_selection "flattened" or "querywise")."""
+    uncapped; qa_selection "flattened" or "querywise"; vs_granularity
+    "block" or "token")."""
     _check_tensor(q, "q")
     _check_tensor(k, "k")
     if q.dtype != k.dtype:
@@ -194,7 +199,7 @@ def plan(q, k, block: int = 128, gamma: float = 0.95, tau: float = 0.1,
     if tuple(k.shape) != (B, Hkv, N, d):
         raise ValueError("k must be [B, Hkv, N, d] with q's B, N and d")
     dt = _dtype_code(q)
-    opts = _options(max_budget, qa_selection)
+    opts = _options(max_budget, qa_selection, vs_granularity)
     h = C.c_void_p()
     _lib.check(_lib.load().fp_prefill_plan_ex(q.data_ptr(), k.data_ptr(), dt, B, Hq, Hkv, N, d, block,
                                               float(gamma), float(tau), int(min_budget), C.byref(opts),
@@ -204,7 +209,7 @@ def plan(q, k, block: int = 128, gamma: float = 0.95, tau: float = 0.1,
 
 def plan_varlen(q, k, cu_seqlens, block: int = 128, gamma: float = 0.95, tau: float = 0.1,
                 min_budget: int = 1024, max_budget: int = 0, qa_selection: str = "flattened",
-                stream=None) -> Plan:
+                vs_granularity: str = "block", stream=None) -> Plan:
     """The same for packed sequences: q [T, Hq, d], k [T, Hkv, d], sequence b
     at tokens cu_seqlens[b] .. cu_seqlens[b+1]-1 (fp_prefill_plan_varlen)."""
     _check_tensor(q, "q", 3)
@@ -217,7 +222,7 @@ def plan_varlen(q, k, cu_seqlens, block: int = 128, gamma: float = 0.95, tau: fl
     if tuple(k.shape) != (T, Hkv, d) or int(cu[-1]) != T:
         raise ValueError("k must be [T, Hkv, d] and cu_seqlens[-1] must equal T")
     dt = _dtype_code(q)
-    opts = _options(max_budget, qa_selection)
+    opts = _options(max_budget, qa_selection, vs_granularity)
     h = C.c_void_p()
     _lib.check(_lib.load().fp_prefill_plan_varlen(q.data_ptr(), k.data_ptr(), dt, cu.size - 1, cu.ctypes.data,
                                                   Hq, Hkv, d, block, float(gamma), float(tau), int(min_budget),

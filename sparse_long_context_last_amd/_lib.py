@@ -20,7 +20,8 @@ FP_PATTERN_QUERY_AWARE = 1
 FP_LAYOUT_BHND = 0
 FP_LAYOUT_THD = 1
 DEBUG_ITEMS = {"qbar": 0, "kbar": 1, "rowmax": 2, "rowsum": 3, "colsum": 4,
-               "diagsum": 5, "atrue": 6, "ahat": 7, "counts": 8}
+               "diagsum": 5, "atrue": 6, "ahat": 7, "counts": 8,
+               "colptr": 9, "colidx": 10}
 
 
 class PlanInfo(C.Structure):
@@ -29,15 +30,16 @@ class PlanInfo(C.Structure):
                 ("gamma", C.c_float), ("tau", C.c_float), ("min_budget", C.c_int),
                 ("total_blocks", C.c_longlong), ("dense_blocks", C.c_longlong),
                 ("query_aware_heads", C.c_int), ("max_budget", C.c_int),
-                ("qa_selection", C.c_int), ("layout", C.c_int), ("tokens", C.c_longlong),
-                ("rows", C.c_longlong)]
+                ("qa_selection", C.c_int), ("layout", C.c_int), ("vs_granularity", C.c_int),
+                ("tokens", C.c_longlong), ("rows", C.c_longlong)]
 
 
 class PlanOptions(C.Structure):
-    _fields_ = [("max_budget", C.c_int), ("qa_selection", C.c_int)]
+    _fields_ = [("max_budget", C.c_int), ("qa_selection", C.c_int), ("vs_granularity", C.c_int)]
 
 
 QA_SELECTION = {"flattened": 0, "querywise": 1}
+VS_GRANULARITY = {"block": 0, "token": 1}
 
 
 # name -> (restype, argtypes)

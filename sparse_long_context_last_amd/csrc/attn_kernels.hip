@@ -69,9 +69,12 @@ struct RowId {
     size_t q0, k0, vt0;     // element offsets: token 0 of the query head, of its kv head; its V^T rows
     int NT;                 // V^T row length
     const int* lst;
+    int ncol;               // token-granular columns below the row's end (gathered tiles)
+    const int* gidx;        // the head's selected columns, ascending
+    size_t g0;              // element offset of the head's gathered K / V^T
 };
 
-__device__ __forceinline__ RowId work_row(const AttnArgs& a, long long item, bool sparse) {
+__device__ __forceinline__ RowId work_row(const AttnArgs& a, long long item, bool sparse, bool gather = false) {
     int lo = 0, hi = a.nseg - 1;
     while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
@@ -97,13 +100,66 @@ __device__ __forceinline__ RowId work_row(const AttnArgs& a, long long item, boo
         r.cnt = r.qb + 1;
         r.lst = nullptr;
     }
+    r.ncol = 0;
+    r.gidx = nullptr;
+    r.g0 = 0;
+    if (gather) {
+        const int* cp = a.colptr + sg.cpoff + (long long)bh * (sg.nb + 1);
+        r.ncol = cp[r.qb + 1];
+        r.gidx = a.colidx + sg.cioff + (long long)bh * sg.L;
+        r.g0 = (size_t)sg.goff + (size_t)bh * kHeadDim * sg.NT;
+    }
     return r;
+}
+
+// Mask of a gathered-column tile (64 keys, one per lane: column c = 64 t +
+// lane of the head's ascending selected columns): a key is dropped when it
+// lies past the row's columns, inside one of the row's full blocks (those
+// are attended in full already) or, in the diagonal block, after the query.
+// Each wave writes the tile's additive bias (0 or -inf) and, for keys in the
+// diagonal block, their positions to its own LDS slot; every lane then adds
+// the biases of its 32 keys with 16-byte reads.
+template <int BS>
+__device__ __forceinline__ void gather_mask(f32x16_t (&st)[2], int t, const RowId& rid, const unsigned int* fbits,
+                                            float* gb, int* gj, int qb, int qrow, int lane, int hh) {
+    const int c = 64 * t + lane;
+    const int j = c < rid.ncol ? rid.gidx[c] : -1;
+    const int jb = j >= 0 ? j / BS : 0;
+    const bool valid = j >= 0 && !((fbits[jb >> 5] >> (jb & 31)) & 1u);
+    const bool diag = valid && jb == qb;
+    gb[lane] = valid ? 0.0f : -INFINITY;
+    gj[lane] = diag ? j : -1;
+    const bool anydiag = __ballot(diag) != 0;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const f32x4_t bv = *reinterpret_cast<const f32x4_t*>(&gb[32 * u + 8 * q + 4 * hh]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) st[u][4 * q + e] += bv[e];
+        }
+    if (anydiag) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int4 jv = *reinterpret_cast<const int4*>(&gj[32 * u + 8 * q + 4 * hh]);
+                if (jv.x > qrow) st[u][4 * q] = -INFINITY;
+                if (jv.y > qrow) st[u][4 * q + 1] = -INFINITY;
+                if (jv.z > qrow) st[u][4 * q + 2] = -INFINITY;
+                if (jv.w > qrow) st[u][4 * q + 3] = -INFINITY;
+            }
+    }
+    __builtin_amdgcn_wave_barrier();   // the slot is rewritten by the next tile
 }
 
 // ---------------------------------------------------------------------------
 // bf16 inputs, bf16 MFMA 32x32x16, fp32 accumulation and softmax
 // ---------------------------------------------------------------------------
-template <int BS, bool SPARSE>
+template <int BS, bool SPARSE, bool GATHER>
 __global__ __launch_bounds__(2 * BS, BS == 128 ? 2 : 1) void k_attn_bf16(AttnArgs a) {
     constexpr int D = kHeadDim, KT = kKT, NW = BS / 32, SPB = BS / KT;
     constexpr int TILE = KT * D * 2;            // bytes of one K (or V^T) tile
@@ -114,11 +170,14 @@ __global__ __launch_bounds__(2 * BS, BS == 128 ? 2 : 1) void k_attn_bf16(AttnArg
     // so that the MFMA fragment reads below hit distinct banks.
     __shared__ __attribute__((aligned(1024))) unsigned char Ks[2][TILE];
     __shared__ __attribute__((aligned(1024))) unsigned char Vs[2][TILE];
+    __shared__ unsigned int fbits[GATHER ? kMaxBlocks / 32 : 1];   // the row's full blocks
+    __shared__ __attribute__((aligned(16))) float gbias[GATHER ? NW : 1][64];
+    __shared__ __attribute__((aligned(16))) int gjpos[GATHER ? NW : 1][64];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index (uniform)
     const int l32 = lane & 31, hh = lane >> 5;
-    const RowId rid = work_row(a, blockIdx.x, SPARSE);
+    const RowId rid = work_row(a, blockIdx.x, SPARSE, GATHER);
     const int qb = rid.qb, L = rid.L;
     const unsigned char* K = (const unsigned char*)a.k + rid.k0 * 2;
     const unsigned char* VT = (const unsigned char*)a.vt + rid.vt0 * 2;
@@ -128,6 +187,17 @@ __global__ __launch_bounds__(2 * BS, BS == 128 ? 2 : 1) void k_attn_bf16(AttnArg
     const int cnt = rid.cnt;
     const int* lst = rid.lst;
     const int nsub = cnt * SPB;
+    // token-granular columns: 64-key tiles of the head's gathered K / V^T after the blocks
+    const int ngs = GATHER ? (rid.ncol + KT - 1) / KT : 0;
+    const int nstage = nsub + ngs;
+    const unsigned char* KG = GATHER ? (const unsigned char*)a.kg + rid.g0 * 2 : nullptr;
+    const unsigned char* VGT = GATHER ? (const unsigned char*)a.vgt + rid.g0 * 2 : nullptr;
+    if (GATHER && ngs > 0) {
+        for (int e = tid; e < kMaxBlocks / 32; e += 2 * BS) fbits[e] = 0u;
+        __syncthreads();
+        for (int e = tid; e < cnt; e += 2 * BS) atomicOr(&fbits[lst[e] >> 5], 1u << (lst[e] & 31));
+        __syncthreads();
+    }
 
     // Q fragments (B operand of S^T = K Q^T): query l32 of this wave, d = 16c + 8hh + [0, 8).
     // Rows past the sequence end (a partial last block) read its last row and are not stored.
@@ -166,7 +236,7 @@ __global__ __launch_bounds__(2 * BS, BS == 128 ? 2 : 1) void k_attn_bf16(AttnArg
     // the last key for the missing rows: finite values that the causal mask
     // removes; V^T is zero there.
 #define FP_FETCH_BF16(s_, buf_)                                                                          \
-    {                                                                                                    \
+    if (!GATHER || (s_) < nsub) {                                                                        \
         const int kb_ = SPARSE ? lst[(s_) / SPB] : (s_) / SPB;                                          \
         const int key0_ = kb_ * BS + ((s_) % SPB) * KT;                                                 \
         const unsigned char* kg_ = K + (size_t)key0_ * krs;                                             \
@@ -184,17 +254,30 @@ __global__ __launch_bounds__(2 * BS, BS == 128 ? 2 : 1) void k_attn_bf16(AttnArg
             __builtin_amdgcn_global_load_lds((const void*)(vg_ + voff[j]),                              \
                 (__attribute__((address_space(3))) void*)(&Vs[(buf_)][J * 1024]), 16, 0, 0);           \
         }                                                                                                \
+    } else {                                                                                             \
+        const int c0_ = ((s_) - nsub) * KT;                                                             \
+        const unsigned char* kg_ = KG + (size_t)c0_ * D * 2;                                            \
+        const unsigned char* vg_ = VGT + (size_t)c0_ * 2;                                               \
+        _Pragma("unroll") for (int j = 0; j < LOADS; ++j) {                                             \
+            const int J = w + NW * j;                                                                   \
+            const int kr_ = 4 * J + (lane >> 4);                                                        \
+            __builtin_amdgcn_global_load_lds((const void*)(kg_ + kr_ * D * 2 + 16 * ((lane & 15) ^ (kr_ & 15))), \
+                (__attribute__((address_space(3))) void*)(&Ks[(buf_)][J * 1024]), 16, 0, 0);           \
+            __builtin_amdgcn_global_load_lds((const void*)(vg_ + voff[j]),                              \
+                (__attribute__((address_space(3))) void*)(&Vs[(buf_)][J * 1024]), 16, 0, 0);           \
+        }                                                                                                \
     }
 
     FP_FETCH_BF16(0, 0);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
 
-    for (int s = 0; s < nsub; ++s) {
+    for (int s = 0; s < nstage; ++s) {
         const int buf = s & 1;
-        const int kb = SPARSE ? lst[s / SPB] : s / SPB;
+        const bool gst = GATHER && s >= nsub;
+        const int kb = gst ? -1 : (SPARSE ? lst[s / SPB] : s / SPB);
         const int sub = s % SPB;
-        if (s + 1 < nsub) FP_FETCH_BF16(s + 1, buf ^ 1);
+        if (s + 1 < nstage) FP_FETCH_BF16(s + 1, buf ^ 1);
 
         // Wave priority is raised while this wave issues MFMAs, so the other
         // resident wave on the SIMD fills the matrix unit's busy time with its
@@ -225,6 +308,7 @@ __global__ __launch_bounds__(2 * BS, BS == 128 ? 2 : 1) void k_attn_bf16(AttnArg
                     if (krel > qrel) st[t][r] = -INFINITY;
                 }
         }
+        if (GATHER && gst) gather_mask<BS>(st, s - nsub, rid, fbits, gbias[w], gjpos[w], qb, qrow, lane, hh);
         // online softmax (lane = one query; lane ^ 32 holds its other keys).
         // After a row's first stage the exp2 arguments use the reference
         // maximum of earlier stages; as long as every lane's sum of the new
@@ -304,7 +388,7 @@ __global__ __launch_bounds__(2 * BS, BS == 128 ? 2 : 1) void k_attn_bf16(AttnArg
 // lane pair (hh) maps to d = c + 64 hh (scores) and to key 32t + 8i + 4hh + j
 // (values), identically for both operands.
 // ---------------------------------------------------------------------------
-template <int BS, bool SPARSE>
+template <int BS, bool SPARSE, bool GATHER>
 __global__ __launch_bounds__(2 * BS) void k_attn_f32(AttnArgs a) {
     constexpr int D = kHeadDim, KT = kKT, NT = 2 * BS, SPB = BS / KT;
     constexpr int KP = D + 4;     // floats: 528 B
@@ -315,9 +399,12 @@ __global__ __launch_bounds__(2 * BS) void k_attn_f32(AttnArgs a) {
     float* Ks0 = smem_f32;
     float* Vs0 = smem_f32 + 2 * KT * KP;
 
+    __shared__ unsigned int fbits[GATHER ? kMaxBlocks / 32 : 1];   // the row's full blocks
+    __shared__ __attribute__((aligned(16))) float gbias[GATHER ? BS / 32 : 1][64];
+    __shared__ __attribute__((aligned(16))) int gjpos[GATHER ? BS / 32 : 1][64];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int l32 = lane & 31, hh = lane >> 5;
-    const RowId rid = work_row(a, blockIdx.x, SPARSE);
+    const RowId rid = work_row(a, blockIdx.x, SPARSE, GATHER);
     const int qb = rid.qb, L = rid.L;
     const float* K = (const float*)a.k + rid.k0;
     const float* VT = (const float*)a.vt + rid.vt0;
@@ -327,6 +414,16 @@ __global__ __launch_bounds__(2 * BS) void k_attn_f32(AttnArgs a) {
     const int cnt = rid.cnt;
     const int* lst = rid.lst;
     const int nsub = cnt * SPB;
+    const int ngs = GATHER ? (rid.ncol + KT - 1) / KT : 0;
+    const int nstage = nsub + ngs;
+    const float* KG = GATHER ? (const float*)a.kg + rid.g0 : nullptr;
+    const float* VGT = GATHER ? (const float*)a.vgt + rid.g0 : nullptr;
+    if (GATHER && ngs > 0) {
+        for (int e = tid; e < kMaxBlocks / 32; e += NT) fbits[e] = 0u;
+        __syncthreads();
+        for (int e = tid; e < cnt; e += NT) atomicOr(&fbits[lst[e] >> 5], 1u << (lst[e] & 31));
+        __syncthreads();
+    }
     const int qrel = 32 * w + l32;
     const int qrow = qb * BS + qrel;
     float qf[64];
@@ -348,7 +445,7 @@ __global__ __launch_bounds__(2 * BS) void k_attn_f32(AttnArgs a) {
 
     f32x4_t kreg[KCH], vreg[VCH];
 #define FP_FETCH_F32(s_)                                                                             \
-    {                                                                                                \
+    if (!GATHER || (s_) < nsub) {                                                                    \
         const int kb_ = SPARSE ? lst[(s_) / SPB] : (s_) / SPB;                                          \
         const int key0_ = kb_ * BS + ((s_) % SPB) * KT;                                              \
         _Pragma("unroll") for (int r = 0; r < KCH; ++r) {                                            \
@@ -358,6 +455,16 @@ __global__ __launch_bounds__(2 * BS) void k_attn_f32(AttnArgs a) {
         _Pragma("unroll") for (int r = 0; r < VCH; ++r) {                                            \
             const int e = tid + NT * r, dv = e >> 4, k4 = e & 15;                                    \
             vreg[r] = *reinterpret_cast<const f32x4_t*>(VT + (size_t)dv * NTv + key0_ + 4 * k4);      \
+        }                                                                                            \
+    } else {                                                                                         \
+        const int c0_ = ((s_) - nsub) * KT;                                                          \
+        _Pragma("unroll") for (int r = 0; r < KCH; ++r) {                                            \
+            const int e = tid + NT * r, key = e >> 5, d4 = e & 31;                                   \
+            kreg[r] = *reinterpret_cast<const f32x4_t*>(KG + (size_t)(c0_ + key) * D + 4 * d4);      \
+        }                                                                                            \
+        _Pragma("unroll") for (int r = 0; r < VCH; ++r) {                                            \
+            const int e = tid + NT * r, dv = e >> 4, k4 = e & 15;                                    \
+            vreg[r] = *reinterpret_cast<const f32x4_t*>(VGT + (size_t)dv * NTv + c0_ + 4 * k4);      \
         }                                                                                            \
     }
 #define FP_STASH_F32(buf_)                                                                           \
@@ -377,13 +484,14 @@ __global__ __launch_bounds__(2 * BS) void k_attn_f32(AttnArgs a) {
     FP_FETCH_F32(0);
     FP_STASH_F32(0);
     __syncthreads();
-    for (int s = 0; s < nsub; ++s) {
+    for (int s = 0; s < nstage; ++s) {
         const int buf = s & 1;
         const float* Ks = Ks0 + buf * KT * KP;
         const float* Vs = Vs0 + buf * D * VP;
-        const int kb = SPARSE ? lst[s / SPB] : s / SPB;
+        const bool gst = GATHER && s >= nsub;
+        const int kb = gst ? -1 : (SPARSE ? lst[s / SPB] : s / SPB);
         const int sub = s % SPB;
-        if (s + 1 < nsub) FP_FETCH_F32(s + 1);
+        if (s + 1 < nstage) FP_FETCH_F32(s + 1);
         f32x16_t st[2];
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
@@ -408,6 +516,7 @@ __global__ __launch_bounds__(2 * BS) void k_attn_f32(AttnArgs a) {
                     if (krel > qrel) st[t][r] = -INFINITY;
                 }
         }
+        if (GATHER && gst) gather_mask<BS>(st, s - nsub, rid, fbits, gbias[w], gjpos[w], qb, qrow, lane, hh);
         float mx = -INFINITY;
 #pragma unroll
         for (int t = 0; t < 2; ++t)
@@ -449,7 +558,7 @@ __global__ __launch_bounds__(2 * BS) void k_attn_f32(AttnArgs a) {
                     o[T] = __builtin_amdgcn_mfma_f32_32x32x2f32(vv.w, st[t][4 * i + 3], o[T], 0, 0, 0);
                 }
         }
-        if (s + 1 < nsub) FP_STASH_F32(buf ^ 1);
+        if (s + 1 < nstage) FP_STASH_F32(buf ^ 1);
         __syncthreads();
     }
 #undef FP_FETCH_F32
@@ -510,29 +619,81 @@ hipError_t launch_transpose_v(const void* v, const TokStride& vs, void* vt, int 
     return hipGetLastError();
 }
 
-template <bool SPARSE>
+template <bool SPARSE, bool GATHER>
 static void launch_attention_t(const AttnArgs& a, hipStream_t st) {
     const unsigned items = (unsigned)a.items;
     if (a.dtype_bf16) {
-        if (a.BS == 128) hipLaunchKernelGGL((k_attn_bf16<128, SPARSE>), dim3(items), dim3(256), 0, st, a);
-        else hipLaunchKernelGGL((k_attn_bf16<64, SPARSE>), dim3(items), dim3(128), 0, st, a);
+        if (a.BS == 128) hipLaunchKernelGGL((k_attn_bf16<128, SPARSE, GATHER>), dim3(items), dim3(256), 0, st, a);
+        else hipLaunchKernelGGL((k_attn_bf16<64, SPARSE, GATHER>), dim3(items), dim3(128), 0, st, a);
     } else {
         const size_t lds = (size_t)2 * (kKT * (kHeadDim + 4) + kHeadDim * (kKT + 4)) * sizeof(float);
         if (a.BS == 128) {
-            (void)hipFuncSetAttribute((const void*)k_attn_f32<128, SPARSE>,
+            (void)hipFuncSetAttribute((const void*)k_attn_f32<128, SPARSE, GATHER>,
                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-            hipLaunchKernelGGL((k_attn_f32<128, SPARSE>), dim3(items), dim3(256), lds, st, a);
+            hipLaunchKernelGGL((k_attn_f32<128, SPARSE, GATHER>), dim3(items), dim3(256), lds, st, a);
         } else {
-            (void)hipFuncSetAttribute((const void*)k_attn_f32<64, SPARSE>,
+            (void)hipFuncSetAttribute((const void*)k_attn_f32<64, SPARSE, GATHER>,
                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-            hipLaunchKernelGGL((k_attn_f32<64, SPARSE>), dim3(items), dim3(128), lds, st, a);
+            hipLaunchKernelGGL((k_attn_f32<64, SPARSE, GATHER>), dim3(items), dim3(128), lds, st, a);
         }
     }
 }
 
 hipError_t launch_attention(const AttnArgs& a, hipStream_t st) {
-    if (a.lists) launch_attention_t<true>(a, st);
-    else launch_attention_t<false>(a, st);
+    if (!a.lists) launch_attention_t<false, false>(a, st);
+    else if (a.colptr) launch_attention_t<true, true>(a, st);
+    else launch_attention_t<true, false>(a, st);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Token-granular columns: per query head, the K rows of its selected columns
+// (ascending) as Kg [NT][d] and their V values transposed as V^T [d][NT]
+// (same 16-key permutation as the main V^T for bf16), zero past the last
+// column of the 64-column tile.  grid (NT / 64, nseq * Hq); heads without
+// columns return at once.
+// ---------------------------------------------------------------------------
+template <typename T, bool PERMUTE>
+__global__ __launch_bounds__(256) void k_gather_cols(const T* __restrict__ k, const T* __restrict__ v, TokStride ks,
+                                                     int Hq, int Hkv, int L, int nb, int NT,
+                                                     const int* __restrict__ colptr, const int* __restrict__ colidx,
+                                                     T* __restrict__ kg, T* __restrict__ vgt) {
+    constexpr int D = kHeadDim, TK = 64;
+    __shared__ T tile[TK][D + 2];
+    __shared__ int js[TK];
+    const int bh = blockIdx.y, c0 = blockIdx.x * TK, tid = threadIdx.x;
+    const int ncol = colptr[(size_t)bh * (nb + 1) + nb];
+    if (c0 >= ncol) return;
+    const int b = bh / Hq, kvh = (bh % Hq) / (Hq / Hkv);
+    const size_t base = (size_t)b * ks.bst + (size_t)kvh * ks.hs;
+    if (tid < TK) js[tid] = c0 + tid < ncol ? colidx[(size_t)bh * L + c0 + tid] : -1;
+    __syncthreads();
+    T* kd = kg + ((size_t)bh * NT + c0) * D;
+    for (int e = tid; e < TK * D; e += 256) {
+        const int n = e / D, dd = e % D;
+        const int j = js[n];
+        kd[(size_t)n * D + dd] = j >= 0 ? k[base + (size_t)j * ks.rs + dd] : (T)0;
+        tile[n][dd] = j >= 0 ? v[base + (size_t)j * ks.rs + dd] : (T)0;
+    }
+    __syncthreads();
+    T* dst = vgt + (size_t)bh * D * NT + c0;
+    for (int e = tid; e < TK * D; e += 256) {
+        const int dd = e / TK, p = e % TK;
+        const int n = PERMUTE ? ((p & ~12) | ((p & 4) << 1) | ((p & 8) >> 1)) : p;
+        dst[(size_t)dd * NT + p] = tile[n][dd];
+    }
+}
+
+hipError_t launch_gather_cols(const void* k, const void* v, const TokStride& ks, int dtype_bf16, int nseq, int Hq,
+                              int Hkv, int L, int nb, int NT, const int* colptr, const int* colidx, void* kg,
+                              void* vgt, hipStream_t st) {
+    const dim3 g(NT / 64, nseq * Hq);
+    if (dtype_bf16)
+        hipLaunchKernelGGL((k_gather_cols<bf16_t, true>), g, dim3(256), 0, st, (const bf16_t*)k, (const bf16_t*)v,
+                           ks, Hq, Hkv, L, nb, NT, colptr, colidx, (bf16_t*)kg, (bf16_t*)vgt);
+    else
+        hipLaunchKernelGGL((k_gather_cols<float, false>), g, dim3(256), 0, st, (const float*)k, (const float*)v,
+                           ks, Hq, Hkv, L, nb, NT, colptr, colidx, (float*)kg, (float*)vgt);
     return hipGetLastError();
 }
 

@@ -31,7 +31,7 @@ struct fp_plan {
     int B, Hq, Hkv, N, d, bs, nb;     // N, nb: longest sequence
     fp_dtype dtype;
     float gamma, tau;
-    int min_budget, max_budget, qa_selection;
+    int min_budget, max_budget, qa_selection, vs_granularity;
     int layout;
     long long tokens, rows, dense_blocks;
     std::vector<int> seqlens;
@@ -46,8 +46,10 @@ struct fp_plan {
     unsigned long long* total_blocks;
     int* lists;
     int* counts;
+    int* colptr;                     // token-granular columns (vs_granularity = token), else null
+    int* colidx;
     float *qbar, *kbar, *rowmax, *rowsum, *colsum, *diagsum, *atrue, *ahat;
-    size_t n_qbar, n_kbar, n_rowmax, n_colsum, n_atrue, n_ahat, n_counts, n_lists;
+    size_t n_qbar, n_kbar, n_rowmax, n_colsum, n_atrue, n_ahat, n_counts, n_lists, n_colptr;
     int device;
     hipStream_t stream;
     std::vector<void*> allocs;
@@ -228,10 +230,10 @@ void free_plan(fp_plan* p) {
 
 // The attention segment table of a problem and the V^T workspace size.
 void attention_table(const std::vector<SegHost>& segs, int Hq, int Hkv, int bs, std::vector<AttnSeg>& t,
-                     long long& items, size_t& vt_elems) {
+                     long long& items, size_t& vt_elems, size_t& g_elems) {
     t.clear();
     items = 0;
-    long long vt = 0, loff = 0, coff = 0;
+    long long vt = 0, loff = 0, coff = 0, goff = 0, cpoff = 0, cioff = 0;
     for (const SegHost& g : segs) {
         AttnSeg a{};
         a.item0 = items;
@@ -240,6 +242,9 @@ void attention_table(const std::vector<SegHost>& segs, int Hq, int Hkv, int bs, 
         a.vtoff = vt;
         a.loff = loff;
         a.coff = coff;
+        a.goff = goff;
+        a.cpoff = cpoff;
+        a.cioff = cioff;
         a.nseq = g.nseq;
         a.L = g.L;
         a.nb = g.nb;
@@ -250,8 +255,12 @@ void attention_table(const std::vector<SegHost>& segs, int Hq, int Hkv, int bs, 
         vt += (long long)g.nseq * Hkv * kHeadDim * a.NT;
         loff += nbh * g.tri;
         coff += nbh * g.nb;
+        goff += nbh * kHeadDim * a.NT;
+        cpoff += nbh * (g.nb + 1);
+        cioff += nbh * g.L;
     }
     vt_elems = (size_t)vt;
+    g_elems = (size_t)goff;
 }
 
 fp_status attend_common(const void* q, const void* k, const void* v, void* o, fp_dtype dtype, int Hq, int Hkv,
@@ -263,13 +272,25 @@ fp_status attend_common(const void* q, const void* k, const void* v, void* o, fp
     set_pool_threshold(dev);
     std::vector<AttnSeg> table;
     long long items = 0;
-    size_t vt_elems = 0;
-    attention_table(segs, Hq, Hkv, block, table, items, vt_elems);
+    size_t vt_elems = 0, g_elems = 0;
+    attention_table(segs, Hq, Hkv, block, table, items, vt_elems, g_elems);
     if (items == 0) return FP_OK;
-    void* vt = nullptr;
+    void *vt = nullptr, *kg = nullptr, *vgt = nullptr;
     AttnSeg* dtab = plan ? plan->aseg : nullptr;
+    const bool gather = plan && plan->colptr;
     FP_HIP(hipMallocAsync(&vt, vt_elems * esz, st), "hipMallocAsync (V^T)");
     hipError_t e = hipSuccess;
+    if (gather) {
+        e = hipMallocAsync(&kg, g_elems * esz, st);
+        if (e == hipSuccess) e = hipMallocAsync(&vgt, g_elems * esz, st);
+        for (size_t i = 0; i < segs.size() && e == hipSuccess; ++i)
+            e = launch_gather_cols((const unsigned char*)k + (size_t)segs[i].koff * esz,
+                                   (const unsigned char*)v + (size_t)segs[i].koff * esz, ks, dtype == FP_BF16,
+                                   segs[i].nseq, Hq, Hkv, segs[i].L, segs[i].nb, table[i].NT,
+                                   plan->colptr + table[i].cpoff, plan->colidx + table[i].cioff,
+                                   (unsigned char*)kg + (size_t)table[i].goff * esz,
+                                   (unsigned char*)vgt + (size_t)table[i].goff * esz, st);
+    }
     if (!dtab) {
         e = hipMallocAsync((void**)&dtab, table.size() * sizeof(AttnSeg), st);
         if (e == hipSuccess)
@@ -298,6 +319,12 @@ fp_status attend_common(const void* q, const void* k, const void* v, void* o, fp
         a.lists = plan->lists;
         a.counts = plan->counts;
     }
+    if (gather) {
+        a.colptr = plan->colptr;
+        a.colidx = plan->colidx;
+        a.kg = kg;
+        a.vgt = vgt;
+    }
     EvPair ev{};
     bool prof;
     {
@@ -317,6 +344,8 @@ fp_status attend_common(const void* q, const void* k, const void* v, void* o, fp
         g_prof_events.push_back(ev);
     }
     (void)hipFreeAsync(vt, st);
+    if (kg) (void)hipFreeAsync(kg, st);
+    if (vgt) (void)hipFreeAsync(vgt, st);
     if (!plan && dtab) (void)hipFreeAsync(dtab, st);
     if (e != hipSuccess) return hip_fail(e, "attention");
     return FP_OK;
@@ -328,12 +357,15 @@ fp_status make_plan(const void* q, const void* k, fp_dtype dtype, int layout, in
                     const fp_plan_options* options, void* stream, fp_plan** out) {
     const int max_budget = options ? options->max_budget : 0;
     const int qa_selection = options ? options->qa_selection : FP_QA_FLATTENED;
+    const int vs_granularity = options ? options->vs_granularity : FP_VS_BLOCK;
     if (!(gamma > 0.0f && gamma <= 1.0f)) return fail(FP_ERR_INVALID_ARG, "gamma %g outside (0, 1]", (double)gamma);
     if (!(tau >= 0.0f) || std::isinf(tau)) return fail(FP_ERR_INVALID_ARG, "tau %g must be finite and >= 0", (double)tau);
     if (min_budget < 0) return fail(FP_ERR_INVALID_ARG, "min_budget %d < 0", min_budget);
     if (max_budget < 0) return fail(FP_ERR_INVALID_ARG, "max_budget %d < 0", max_budget);
     if (qa_selection != FP_QA_FLATTENED && qa_selection != FP_QA_QUERYWISE)
         return fail(FP_ERR_INVALID_ARG, "qa_selection %d is not FP_QA_FLATTENED or FP_QA_QUERYWISE", qa_selection);
+    if (vs_granularity != FP_VS_BLOCK && vs_granularity != FP_VS_TOKEN)
+        return fail(FP_ERR_INVALID_ARG, "vs_granularity %d is not FP_VS_BLOCK or FP_VS_TOKEN", vs_granularity);
     {
         const long long floor_b = std::max(1LL, ((long long)min_budget + block - 1) / block);
         const long long cap_b = ((long long)max_budget + block - 1) / block;
@@ -352,6 +384,7 @@ fp_status make_plan(const void* q, const void* k, fp_dtype dtype, int layout, in
     p->dtype = dtype; p->gamma = gamma; p->tau = tau; p->min_budget = min_budget;
     p->max_budget = max_budget;
     p->qa_selection = qa_selection;
+    p->vs_granularity = vs_granularity;
     p->layout = layout;
     p->stream = (hipStream_t)stream;
     p->qs = qs;
@@ -367,7 +400,7 @@ fp_status make_plan(const void* q, const void* k, fp_dtype dtype, int layout, in
     p->rows = 0;
     p->dense_blocks = 0;
     long long lists_n = 0;
-    size_t n_qbar = 0, n_kbar = 0, n_rowmax = 0, n_colsum = 0, n_atrue = 0, n_ahat = 0;
+    size_t n_qbar = 0, n_kbar = 0, n_rowmax = 0, n_colsum = 0, n_atrue = 0, n_ahat = 0, n_cp = 0;
     int max_bh = 0;
     size_t s2_max = 0, pmax_max = 0, rz_max = 0;
     for (const SegHost& g : segs) {
@@ -382,6 +415,7 @@ fp_status make_plan(const void* q, const void* k, fp_dtype dtype, int layout, in
         n_colsum += (size_t)nbh * g.L;
         n_atrue += (size_t)nbh * g.nb;
         n_ahat += (size_t)nbh * g.tri;
+        n_cp += (size_t)nbh * (g.nb + 1);
         max_bh = std::max(max_bh, (int)nbh);
         s2_max = std::max(s2_max, (size_t)nbh * block * NS);
         pmax_max = std::max(pmax_max, (size_t)nbh * (NS / 256) * block);
@@ -389,6 +423,8 @@ fp_status make_plan(const void* q, const void* k, fp_dtype dtype, int layout, in
     }
     p->n_qbar = n_qbar; p->n_kbar = n_kbar; p->n_rowmax = n_rowmax; p->n_colsum = n_colsum;
     p->n_atrue = n_atrue; p->n_ahat = n_ahat; p->n_counts = (size_t)p->rows; p->n_lists = (size_t)lists_n;
+    const bool token = vs_granularity == FP_VS_TOKEN;
+    p->n_colptr = token ? n_cp : 0;
     if (segs.empty()) {
         p->device = -1;
         *out = p;
@@ -415,6 +451,9 @@ fp_status make_plan(const void* q, const void* k, fp_dtype dtype, int layout, in
     } while (0)
     unsigned char *colblk, *diagA, *diagB, *diagT;
     float *colmass = nullptr, *diagmass = nullptr;
+    int* colcount = nullptr;
+    p->colptr = nullptr;
+    p->colidx = nullptr;
     SelState* sel;
     unsigned long long* hist;
     AttnSeg* aseg;
@@ -439,14 +478,19 @@ fp_status make_plan(const void* q, const void* k, fp_dtype dtype, int layout, in
         PALLOC(colmass, (size_t)p->rows);
         PALLOC(diagmass, (size_t)p->rows);
     }
+    if (token) {
+        PALLOC(colcount, (size_t)p->rows);
+        PALLOC(p->colptr, n_cp);
+        PALLOC(p->colidx, n_colsum);
+    }
     PALLOC(sel, (size_t)2 * max_bh);
     PALLOC(hist, (size_t)2 * max_bh * kRadixBins);
     PALLOC(aseg, segs.size());
 #undef PALLOC
     p->aseg = aseg;
     long long items = 0;
-    size_t vt_elems = 0;
-    attention_table(segs, Hq, Hkv, block, p->aseg_host, items, vt_elems);
+    size_t vt_elems = 0, g_elems = 0;
+    attention_table(segs, Hq, Hkv, block, p->aseg_host, items, vt_elems, g_elems);
     hipStream_t st = p->stream;
     he = hipMemcpyAsync(aseg, p->aseg_host.data(), segs.size() * sizeof(AttnSeg), hipMemcpyHostToDevice, st);
     // heads of empty sequences keep pattern 0, divergence 0 and no blocks
@@ -455,7 +499,7 @@ fp_status make_plan(const void* q, const void* k, fp_dtype dtype, int layout, in
     if (he == hipSuccess) he = launch_fill_u32((unsigned int*)p->total_blocks, 0u, 2LL * (long long)BHall, st);
 
     // per-segment views
-    size_t o_qbar = 0, o_kbar = 0, o_rowmax = 0, o_colsum = 0, o_atrue = 0, o_ahat = 0, o_rows = 0;
+    size_t o_qbar = 0, o_kbar = 0, o_rowmax = 0, o_colsum = 0, o_atrue = 0, o_ahat = 0, o_rows = 0, o_cp = 0;
     p->dev.resize(segs.size());
     for (size_t i = 0; i < segs.size(); ++i) {
         const SegHost& g = segs[i];
@@ -469,6 +513,7 @@ fp_status make_plan(const void* q, const void* k, fp_dtype dtype, int layout, in
         P.floor_blocks = std::max(1, (min_budget + block - 1) / block);
         P.cap_blocks = (int)(((long long)max_budget + block - 1) / block);
         P.qa_querywise = qa_selection == FP_QA_QUERYWISE;
+        P.vs_token = token;
         P.G = G;
         P.pattern = p->pattern + (size_t)g.b0 * Hq;
         P.djs = p->djs + (size_t)g.b0 * Hq;
@@ -491,6 +536,11 @@ fp_status make_plan(const void* q, const void* k, fp_dtype dtype, int layout, in
             P.colmass = colmass + o_rows;
             P.diagmass = diagmass + o_rows;
         }
+        if (token) {
+            P.colcount = colcount + o_rows;
+            P.colptr = p->colptr + o_cp;
+            P.colidx = p->colidx + o_colsum;
+        }
         P.sel = sel;
         P.hist = hist;
         o_qbar += (size_t)nbh * g.nb * kHeadDim;
@@ -500,6 +550,7 @@ fp_status make_plan(const void* q, const void* k, fp_dtype dtype, int layout, in
         o_atrue += (size_t)nbh * g.nb;
         o_ahat += (size_t)nbh * g.tri;
         o_rows += (size_t)nbh * g.nb;
+        o_cp += (size_t)nbh * (g.nb + 1);
     }
 
     // one transient score workspace, reused segment after segment (stream order)
@@ -634,6 +685,7 @@ fp_status fp_plan_info_get(const fp_plan* plan, fp_plan_info* out) {
     I.min_budget = plan->min_budget;
     I.max_budget = plan->max_budget;
     I.qa_selection = plan->qa_selection;
+    I.vs_granularity = plan->vs_granularity;
     I.layout = plan->layout;
     I.tokens = plan->tokens;
     I.rows = plan->rows;
@@ -711,6 +763,8 @@ fp_status fp_plan_copy_debug(const fp_plan* plan, int which, void* host_dst, siz
         case FP_DBG_ATRUE: src = plan->atrue; need = plan->n_atrue * 4; break;
         case FP_DBG_AHAT: src = plan->ahat; need = plan->n_ahat * 4; break;
         case FP_DBG_COUNTS: src = plan->counts; need = plan->n_counts * 4; break;
+        case FP_DBG_COLPTR: src = plan->colptr; need = plan->n_colptr * 4; break;
+        case FP_DBG_COLIDX: src = plan->colidx; need = plan->colidx ? plan->n_colsum * 4 : 0; break;
         default: return fail(FP_ERR_INVALID_ARG, "unknown debug item %d", which);
     }
     if (bytes != need) return fail(FP_ERR_INVALID_ARG, "item %d has %zu bytes, %zu given", which, need, bytes);

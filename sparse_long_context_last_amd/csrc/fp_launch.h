@@ -52,6 +52,7 @@ struct PlanDev {
     int floor_blocks;            // max(1, ceil(min_budget / BS))
     int cap_blocks;              // ceil(max_budget / BS), 0 = uncapped
     int qa_querywise;            // query-aware heads select row by row
+    int vs_token;                // vertical-slash columns attended token by token
     unsigned long long G;        // rint(gamma 2^24)
     unsigned char* pattern;      // [BH]
     double* djs;                 // [BH]
@@ -71,6 +72,9 @@ struct PlanDev {
     unsigned char* diagT;        // [BH][nb]
     float* colmass;              // [BH][nb]  selected column mass per key block (cap only)
     float* diagmass;             // [BH][nb]  selected diagonal mass per block diagonal (cap only)
+    int* colcount;               // [BH][nb]   selected columns per key block (token mode)
+    int* colptr;                 // [BH][nb+1] exclusive prefix of colcount (token mode)
+    int* colidx;                 // [BH][L]    selected columns ascending (token mode)
     int* lists;                  // [BH][tri]  row r's list at offset r (r + 1) / 2
     int* counts;                 // [BH][nb]
     unsigned long long* total_blocks;  // [BH] selected blocks per head
@@ -97,6 +101,8 @@ struct AttnSeg {
     long long qoff, koff; // element offsets of the segment base in Q/O and in K/V
     long long vtoff;      // element offset of the segment in the V^T workspace
     long long loff, coff; // offsets of the segment in the plan's lists and counts
+    long long goff;       // element offset of the segment in the gathered-column K and V^T buffers
+    long long cpoff, cioff; // offsets of the segment in colptr and colidx
     int nseq;             // sequences (query heads = nseq Hq)
     int L, nb, NT;        // tokens, blocks, V^T row length nb BS
 };
@@ -114,6 +120,10 @@ struct AttnArgs {
     long long items;
     const int* lists;    // nullptr: dense causal
     const int* counts;
+    const int* colptr;   // token-granular columns (nullptr: none)
+    const int* colidx;
+    const void* kg;      // gathered K rows     per head [NT][d]
+    const void* vgt;     // gathered V^T        per head [d][NT]
     float scale_log2;    // log2(e) / sqrt(d)
 };
 
@@ -125,5 +135,8 @@ hipError_t launch_probe_sqrt(const double* x, double* y, long long n, hipStream_
 hipError_t launch_transpose_v(const void* v, const TokStride& vs, void* vt, int dtype_bf16, int nseq, int Hkv,
                               int L, int NT, hipStream_t st);
 hipError_t launch_attention(const AttnArgs& a, hipStream_t st);
+hipError_t launch_gather_cols(const void* k, const void* v, const TokStride& ks, int dtype_bf16, int nseq, int Hq,
+                              int Hkv, int L, int nb, int NT, const int* colptr, const int* colidx, void* kg,
+                              void* vgt, hipStream_t st);
 
 }  // namespace fp

@@ -746,11 +746,11 @@ __global__ __launch_bounds__(256) void k_sel_scan(SelState* __restrict__ st, uns
 // the last block row) or diagB[qb-kb-1].  grid (nb, BH), BS threads.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(128) void k_vs_flags(PlanDev P, const SelState* __restrict__ st) {
-    __shared__ int f[4];
+    __shared__ int f[5];
     __shared__ unsigned char selc_s[kMaxBlock], selg_s[kMaxBlock];
     const int kb = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
     if (P.mode_all || P.pattern[bh] == kPatternQueryAware) return;
-    if (tid < 4) f[tid] = 0;
+    if (tid < 5) f[tid] = 0;
     __syncthreads();
     const SelState sc = st[2 * bh], sg = st[2 * bh + 1];
     const long long j = (long long)kb * P.BS + tid;
@@ -763,6 +763,7 @@ __global__ __launch_bounds__(128) void k_vs_flags(PlanDev P, const SelState* __r
     if (selg) f[1] = 1;
     if (selg && tid > 0) f[2] = 1;
     if (selg && tid < P.tail) f[3] = 1;
+    if (selc && P.vs_token) atomicAdd(&f[4], 1);
     selc_s[tid] = selc;
     selg_s[tid] = selg;
     __syncthreads();
@@ -772,6 +773,7 @@ __global__ __launch_bounds__(128) void k_vs_flags(PlanDev P, const SelState* __r
         P.diagA[o] = (unsigned char)f[1];
         P.diagB[o] = (unsigned char)f[2];
         P.diagT[o] = (unsigned char)f[3];
+        if (P.vs_token) P.colcount[o] = f[4];
     }
     if (P.cap_blocks > 0 && tid == 0) {
         // line mass for the per-row cap, float32 sums in ascending index:
@@ -807,6 +809,60 @@ __global__ __launch_bounds__(64) void k_diag_mass(PlanDev P, const SelState* __r
 }
 
 // ---------------------------------------------------------------------------
+// Token-granular columns: colptr[kb] = selected columns in key blocks < kb
+// (exclusive prefix over the head's blocks, colptr[nb] = all of them), then
+// colidx[colptr[kb] + rank] = the block's selected columns in ascending order.
+// Heads without token columns (query-aware, gamma = 1) get colptr = 0.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_col_scan(PlanDev P) {
+    constexpr int PER = kMaxBlocks / 256;
+    __shared__ int tot[256];
+    const int bh = blockIdx.x, tid = threadIdx.x, nb = P.nb;
+    const bool vs = !P.mode_all && P.pattern[bh] != kPatternQueryAware;
+    int v[PER];
+    int run = 0;
+#pragma unroll
+    for (int r = 0; r < PER; ++r) {
+        const int kb = tid * PER + r;
+        v[r] = (vs && kb < nb) ? P.colcount[(size_t)bh * nb + kb] : 0;
+        run += v[r];
+    }
+    tot[tid] = run;
+    __syncthreads();
+    for (int o = 1; o < 256; o <<= 1) {
+        const int add = tid >= o ? tot[tid - o] : 0;
+        __syncthreads();
+        tot[tid] += add;
+        __syncthreads();
+    }
+    int cum = tot[tid] - run;
+    int* cp = P.colptr + (size_t)bh * (nb + 1);
+#pragma unroll
+    for (int r = 0; r < PER; ++r) {
+        const int kb = tid * PER + r;
+        if (kb < nb) cp[kb] = cum;
+        cum += v[r];
+    }
+    if (tid == 255) cp[nb] = tot[255];
+}
+
+__global__ __launch_bounds__(128) void k_col_compact(PlanDev P, const SelState* __restrict__ st) {
+    __shared__ int wcount[2];
+    const int kb = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    if (P.mode_all || P.pattern[bh] == kPatternQueryAware) return;
+    const SelState sc = st[2 * bh];
+    const long long j = (long long)kb * P.BS + tid;
+    const bool in = j < P.L;
+    const float xc = in ? P.colsum[(size_t)bh * P.L + j] : 0.0f;
+    const bool selc = in && sc.has && order_key(xc, j, sc.ibits) <= sc.kstar;
+    const unsigned long long bal = __ballot(selc);
+    if (lane == 0) wcount[w] = __popcll(bal);
+    __syncthreads();
+    const int rank = (w == 1 ? wcount[0] : 0) + __popcll(bal & ((1ull << lane) - 1ull));
+    if (selc) P.colidx[(size_t)bh * P.L + P.colptr[(size_t)bh * (P.nb + 1) + kb] + rank] = (int)j;
+}
+
+// ---------------------------------------------------------------------------
 // K7b: per (head, query-block row) block list: selected blocks, topped up to
 // the minimum budget with unselected blocks nearest the diagonal first, in
 // ascending key-block order at lists[bh][row (row+1)/2 + ...].
@@ -823,7 +879,7 @@ __device__ __forceinline__ bool member(const PlanDev& P, const SelState& s0, int
     const size_t base = (size_t)bh * P.nb;
     const int a = qb - kb;
     const unsigned char* own = qb == P.nb - 1 ? P.diagT : P.diagA;
-    return P.colblk[base + kb] || own[base + a] || (a >= 1 && P.diagB[base + a - 1]);
+    return (!P.vs_token && P.colblk[base + kb]) || own[base + a] || (a >= 1 && P.diagB[base + a - 1]);
 }
 
 __device__ __forceinline__ unsigned long long wave_sum_u64(unsigned long long v) {
@@ -1090,6 +1146,10 @@ hipError_t launch_plan(const PlanArgs& a, PlanDev& P, hipStream_t st) {
         }
         hipLaunchKernelGGL(k_vs_flags, dim3(nb, BH), dim3(BS), 0, st, P, P.sel);
         if (P.cap_blocks > 0) hipLaunchKernelGGL(k_diag_mass, dim3(nb, BH), dim3(64), 0, st, P, P.sel);
+    }
+    if (P.vs_token) {
+        hipLaunchKernelGGL(k_col_scan, dim3(BH), dim3(256), 0, st, P);
+        if (!P.mode_all) hipLaunchKernelGGL(k_col_compact, dim3(nb, BH), dim3(BS), 0, st, P, P.sel);
     }
     // K7
     hipLaunchKernelGGL(k_fill_u32, dim3(grid1(2LL * BH)), dim3(256), 0, st, (unsigned int*)P.total_blocks, 0u,

@@ -133,6 +133,14 @@ def test_plan_options_validation(lib):
     assert plan_ex(qa_selection=2) == -1
     assert "qa_selection" in lib.fp_last_error().decode()
     assert plan_ex(qa_selection=-1) == -1
+
+    def plan_vs(g):
+        h = C.c_void_p()
+        opt = PlanOptions(0, 0, g)
+        return lib.fp_prefill_plan_ex(1, 1, 0, 1, 4, 4, 1024, 128, 128, 0.95, 0.1, 1024, C.byref(opt),
+                                      None, C.byref(h))
+    assert plan_vs(2) == -1 and "vs_granularity" in lib.fp_last_error().decode()
+    assert plan_vs(-1) == -1
     from sparse_long_context_last_amd._lib import PlanInfo
     for opt in (None, PlanOptions(8192, 1)):
         # valid settings on an empty problem need no device
