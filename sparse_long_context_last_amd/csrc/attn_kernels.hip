@@ -168,8 +168,15 @@ __global__ __launch_bounds__(2 * BS, BS == 128 ? 2 : 1) void k_attn_bf16(AttnArg
     //   K   [64 keys][256 B]: chunk c of row r at chunk c ^ (r & 15)
     //   V^T [128 dv][128 B]:  chunk c of row r at chunk c ^ gray(r) & 7
     // so that the MFMA fragment reads below hit distinct banks.
-    __shared__ __attribute__((aligned(1024))) unsigned char Ks[2][TILE];
-    __shared__ __attribute__((aligned(1024))) unsigned char Vs[2][TILE];
+    // The two stages' tiles are four separate LDS objects and the stage loop
+    // is unrolled by two, so every access names its buffer at compile time:
+    // the compiler can then tell that the direct loads filling one buffer do
+    // not alias the reads of the other, and the tile loads stay in flight
+    // during the whole stage instead of being waited for before its softmax.
+    __shared__ __attribute__((aligned(1024))) unsigned char Ks0[TILE];
+    __shared__ __attribute__((aligned(1024))) unsigned char Ks1[TILE];
+    __shared__ __attribute__((aligned(1024))) unsigned char Vs0[TILE];
+    __shared__ __attribute__((aligned(1024))) unsigned char Vs1[TILE];
     __shared__ unsigned int fbits[GATHER ? kMaxBlocks / 32 : 1];   // the row's full blocks
     __shared__ __attribute__((aligned(16))) float gbias[GATHER ? NW : 1][64];
     __shared__ __attribute__((aligned(16))) int gjpos[GATHER ? NW : 1][64];
@@ -185,7 +192,10 @@ __global__ __launch_bounds__(2 * BS, BS == 128 ? 2 : 1) void k_attn_bf16(AttnArg
     const size_t krs = (size_t)a.ks.rs * 2;      // bytes per key row
 
     const int cnt = rid.cnt;
-    const int* lst = rid.lst;
+    // the row's list is read with scalar loads (uniform addresses, counted
+    // apart from the vector-memory tile loads)
+    typedef const __attribute__((address_space(4))) int* cint_p;
+    const cint_p lst = (cint_p)rid.lst;
     const int nsub = cnt * SPB;
     // token-granular columns: 64-key tiles of the head's gathered K / V^T after the blocks
     const int ngs = GATHER ? (rid.ncol + KT - 1) / KT : 0;
@@ -235,7 +245,7 @@ __global__ __launch_bounds__(2 * BS, BS == 128 ? 2 : 1) void k_attn_bf16(AttnArg
     // A tile reaching past the sequence end (only in the last key block) reads
     // the last key for the missing rows: finite values that the causal mask
     // removes; V^T is zero there.
-#define FP_FETCH_BF16(s_, buf_)                                                                          \
+#define FP_FETCH_BF16(s_, KD_, VD_)                                                                          \
     if (!GATHER || (s_) < nsub) {                                                                        \
         const int kb_ = SPARSE ? lst[(s_) / SPB] : (s_) / SPB;                                          \
         const int key0_ = kb_ * BS + ((s_) % SPB) * KT;                                                 \
@@ -250,9 +260,9 @@ __global__ __launch_bounds__(2 * BS, BS == 128 ? 2 : 1) void k_attn_bf16(AttnArg
                 ka_ = K + (size_t)min(key0_ + kr_, L - 1) * krs + 16 * ((lane & 15) ^ (kr_ & 15));      \
             }                                                                                           \
             __builtin_amdgcn_global_load_lds((const void*)ka_,                                          \
-                (__attribute__((address_space(3))) void*)(&Ks[(buf_)][J * 1024]), 16, 0, 0);           \
+                (__attribute__((address_space(3))) void*)(&KD_[J * 1024]), 16, 0, 0);           \
             __builtin_amdgcn_global_load_lds((const void*)(vg_ + voff[j]),                              \
-                (__attribute__((address_space(3))) void*)(&Vs[(buf_)][J * 1024]), 16, 0, 0);           \
+                (__attribute__((address_space(3))) void*)(&VD_[J * 1024]), 16, 0, 0);           \
         }                                                                                                \
     } else {                                                                                             \
         const int c0_ = ((s_) - nsub) * KT;                                                             \
@@ -262,107 +272,99 @@ __global__ __launch_bounds__(2 * BS, BS == 128 ? 2 : 1) void k_attn_bf16(AttnArg
             const int J = w + NW * j;                                                                   \
             const int kr_ = 4 * J + (lane >> 4);                                                        \
             __builtin_amdgcn_global_load_lds((const void*)(kg_ + kr_ * D * 2 + 16 * ((lane & 15) ^ (kr_ & 15))), \
-                (__attribute__((address_space(3))) void*)(&Ks[(buf_)][J * 1024]), 16, 0, 0);           \
+                (__attribute__((address_space(3))) void*)(&KD_[J * 1024]), 16, 0, 0);           \
             __builtin_amdgcn_global_load_lds((const void*)(vg_ + voff[j]),                              \
-                (__attribute__((address_space(3))) void*)(&Vs[(buf_)][J * 1024]), 16, 0, 0);           \
+                (__attribute__((address_space(3))) void*)(&VD_[J * 1024]), 16, 0, 0);           \
         }                                                                                                \
     }
 
-    FP_FETCH_BF16(0, 0);
+    FP_FETCH_BF16(0, Ks0, Vs0);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
 
-    for (int s = 0; s < nstage; ++s) {
-        const int buf = s & 1;
-        const bool gst = GATHER && s >= nsub;
-        const int kb = gst ? -1 : (SPARSE ? lst[s / SPB] : s / SPB);
-        const int sub = s % SPB;
-        if (s + 1 < nstage) FP_FETCH_BF16(s + 1, buf ^ 1);
-
-        // Wave priority is raised while this wave issues MFMAs, so the other
-        // resident wave on the SIMD fills the matrix unit's busy time with its
-        // softmax VALU work instead of competing for issue slots.
-        __builtin_amdgcn_s_setprio(1);
-        // S^T tile: keys (rows) x queries (cols)
-        f32x16_t st[2];
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) st[t][r] = 0.0f;
-            const int row = 32 * t + l32;
-            const unsigned char* kr = &Ks[buf][row * D * 2];
-#pragma unroll
-            for (int c = 0; c < 8; ++c) {
-                const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(kr + 16 * ((2 * c + hh) ^ (row & 15)));
-                st[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[c], st[t], 0, 0, 0);
-            }
-        }
-        __builtin_amdgcn_s_setprio(0);
-        // causal mask inside the diagonal block
-        if (kb == qb) {
-#pragma unroll
-            for (int t = 0; t < 2; ++t)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int krel = sub * KT + 32 * t + 8 * (r >> 2) + 4 * hh + (r & 3);
-                    if (krel > qrel) st[t][r] = -INFINITY;
-                }
-        }
-        if (GATHER && gst) gather_mask<BS>(st, s - nsub, rid, fbits, gbias[w], gjpos[w], qb, qrow, lane, hh);
-        // online softmax (lane = one query; lane ^ 32 holds its other keys).
-        // After a row's first stage the exp2 arguments use the reference
-        // maximum of earlier stages; as long as every lane's sum of the new
-        // probabilities stays <= kSumLimit (so each is <= kSumLimit) that
-        // reference is kept and no maximum is formed at all.  Otherwise (and
-        // on the first stage) the exact maximum becomes the reference, the
-        // accumulators are rescaled and the probabilities recomputed.  The
-        // final division by the row sum makes the result independent of the
-        // reference chosen.
-        bf16x8_t pf[4];
-        float ls = 0.0f;
-        bool exact = s == 0;
-        if (!exact) {
-            ls = exp_pack(st, sl, m_run * sl, pf);
-            exact = __ballot(!(ls <= kSumLimit)) != 0;
-        }
-        if (exact) {
-            float mx = -INFINITY;
-#pragma unroll
-            for (int t = 0; t < 2; ++t)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, st[t][r]);
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
-            const float m_new = fmaxf(m_run, mx);
-            const float alpha = fast_exp2((m_run - m_new) * sl);   // 0 while m_run = -inf
-            l_run *= alpha;
-#pragma unroll
-            for (int T = 0; T < 4; ++T)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) o[T][r] *= alpha;
-            m_run = m_new;
-            ls = exp_pack(st, sl, m_run * sl, pf);
-        }
-        l_run += ls;
-
-        __builtin_amdgcn_s_setprio(1);
-        // O^T += V^T P^T; key order of the B operand: kc*16 + 8*(e/4) + 4*hh + e%4.
-        // V^T rows store each 16-key chunk as key groups [0-3, 8-11, 4-7, 12-15],
-        // so those 8 keys are one contiguous 16-byte chunk (logical chunk 2kc + hh).
-#pragma unroll
-        for (int T = 0; T < 4; ++T) {
-            const int row = 32 * T + l32;
-            const int g = (row ^ (row >> 1)) & 7;
-            const unsigned char* vr = &Vs[buf][row * KT * 2];
-#pragma unroll
-            for (int kc = 0; kc < 4; ++kc) {
-                const bf16x8_t vf = *reinterpret_cast<const bf16x8_t*>(vr + 16 * ((2 * kc + hh) ^ g));
-                o[T] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[kc], o[T], 0, 0, 0);
-            }
-        }
-        __builtin_amdgcn_s_setprio(0);
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
+    // One stage: scores and softmax of the tile in (KC_, VC_) while the next
+    // stage's tile streams into (KN_, VN_).
+#define FP_STAGE_BF16(s, KC_, VC_, KN_, VN_)                                                             \
+    {                                                                                                    \
+        const bool gst = GATHER && (s) >= nsub;                                                          \
+        const int kb = gst ? -1 : (SPARSE ? lst[(s) / SPB] : (s) / SPB);                                 \
+        const int sub = (s) % SPB;                                                                       \
+        if ((s) + 1 < nstage) FP_FETCH_BF16((s) + 1, KN_, VN_);                                          \
+        /* Wave priority is raised while this wave issues MFMAs, so the other                       */  \
+        /* resident wave on the SIMD fills the matrix unit's busy time with its softmax.            */  \
+        __builtin_amdgcn_s_setprio(1);                                                                   \
+        f32x16_t st[2];                                                                                  \
+        _Pragma("unroll") for (int t = 0; t < 2; ++t) {                                                  \
+            _Pragma("unroll") for (int r = 0; r < 16; ++r) st[t][r] = 0.0f;                              \
+            const int row = 32 * t + l32;                                                                \
+            const unsigned char* kr = &KC_[row * D * 2];                                                 \
+            _Pragma("unroll") for (int c = 0; c < 8; ++c) {                                              \
+                const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(kr + 16 * ((2 * c + hh) ^ (row & 15))); \
+                st[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[c], st[t], 0, 0, 0);              \
+            }                                                                                            \
+        }                                                                                                \
+        __builtin_amdgcn_s_setprio(0);                                                                   \
+        if (kb == qb) {                                                                                  \
+            _Pragma("unroll") for (int t = 0; t < 2; ++t)                                                \
+            _Pragma("unroll") for (int r = 0; r < 16; ++r) {                                             \
+                const int krel = sub * KT + 32 * t + 8 * (r >> 2) + 4 * hh + (r & 3);                   \
+                if (krel > qrel) st[t][r] = -INFINITY;                                                   \
+            }                                                                                            \
+        }                                                                                                \
+        if (GATHER && gst) gather_mask<BS>(st, (s) - nsub, rid, fbits, gbias[w], gjpos[w], qb, qrow, lane, hh); \
+        bf16x8_t pf[4];                                                                                  \
+        float ls = 0.0f;                                                                                 \
+        bool exact = (s) == 0;                                                                           \
+        if (!exact) {                                                                                    \
+            ls = exp_pack(st, sl, m_run * sl, pf);                                                       \
+            exact = __ballot(!(ls <= kSumLimit)) != 0;                                                   \
+        }                                                                                                \
+        if (exact) {                                                                                     \
+            float mx = -INFINITY;                                                                        \
+            _Pragma("unroll") for (int t = 0; t < 2; ++t)                                                \
+            _Pragma("unroll") for (int r = 0; r < 16; ++r) mx = fmaxf(mx, st[t][r]);                     \
+            mx = fmaxf(mx, __shfl_xor(mx, 32));                                                          \
+            const float m_new = fmaxf(m_run, mx);                                                        \
+            const float alpha = fast_exp2((m_run - m_new) * sl);                                         \
+            l_run *= alpha;                                                                              \
+            _Pragma("unroll") for (int T = 0; T < 4; ++T)                                                \
+            _Pragma("unroll") for (int r = 0; r < 16; ++r) o[T][r] *= alpha;                             \
+            m_run = m_new;                                                                               \
+            ls = exp_pack(st, sl, m_run * sl, pf);                                                       \
+        }                                                                                                \
+        l_run += ls;                                                                                     \
+        __builtin_amdgcn_s_setprio(1);                                                                   \
+        _Pragma("unroll") for (int T = 0; T < 4; ++T) {                                                  \
+            const int row = 32 * T + l32;                                                                \
+            const int g = (row ^ (row >> 1)) & 7;                                                        \
+            const unsigned char* vr = &VC_[row * KT * 2];                                                \
+            _Pragma("unroll") for (int kc = 0; kc < 4; ++kc) {                                           \
+                const bf16x8_t vf = *reinterpret_cast<const bf16x8_t*>(vr + 16 * ((2 * kc + hh) ^ g));   \
+                o[T] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[kc], o[T], 0, 0, 0);               \
+            }                                                                                            \
+        }                                                                                                \
+        __builtin_amdgcn_s_setprio(0);                                                                   \
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");                                                 \
+        __syncthreads();                                                                                 \
     }
+
+    // online softmax (lane = one query; lane ^ 32 holds its other keys).
+    // After a row's first stage the exp2 arguments use the reference
+    // maximum of earlier stages; as long as every lane's sum of the new
+    // probabilities stays <= kSumLimit (so each is <= kSumLimit) that
+    // reference is kept and no maximum is formed at all.  Otherwise (and
+    // on the first stage) the exact maximum becomes the reference, the
+    // accumulators are rescaled and the probabilities recomputed.  The
+    // final division by the row sum makes the result independent of the
+    // reference chosen.  O^T += V^T P^T uses the key order kc*16 + 8*(e/4) +
+    // 4*hh + e%4 of the B operand; V^T rows store each 16-key chunk as key
+    // groups [0-3, 8-11, 4-7, 12-15], so those 8 keys are one contiguous
+    // 16-byte chunk (logical chunk 2kc + hh).
+    for (int s = 0; s < nstage; s += 2) {
+        FP_STAGE_BF16(s, Ks0, Vs0, Ks1, Vs1);
+        if (s + 1 < nstage) FP_STAGE_BF16(s + 1, Ks1, Vs1, Ks0, Vs0);
+    }
+#undef FP_STAGE_BF16
 #undef FP_FETCH_BF16
 
     const float l_tot = l_run + __shfl_xor(l_run, 32);
