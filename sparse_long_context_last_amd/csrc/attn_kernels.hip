@@ -592,20 +592,33 @@ __global__ __launch_bounds__(2 * BS) void k_attn_f32(AttnArgs a) {
 template <typename T, bool PERMUTE>
 __global__ __launch_bounds__(256) void k_transpose_v(const T* __restrict__ v, TokStride vs, int Hkv,
                                                      T* __restrict__ vt, int L, int NT) {
-    constexpr int D = kHeadDim, TK = 64;
-    __shared__ T tile[TK][D + 2];
+    constexpr int D = kHeadDim, TK = 64, VEC = 16 / (int)sizeof(T);   // elements per 16-byte access
+    __shared__ __attribute__((aligned(16))) T tile[TK][D + VEC];
     const int head = blockIdx.y, n0 = blockIdx.x * TK, tid = threadIdx.x;
     const T* src = v + (size_t)(head / Hkv) * vs.bst + (size_t)(head % Hkv) * vs.hs;
-    for (int e = tid; e < TK * D; e += 256) {
-        const int n = e / D, dd = e % D;
-        tile[n][dd] = n0 + n < L ? src[(size_t)(n0 + n) * vs.rs + dd] : (T)0;
+    // 16-byte row pieces in, one row of the tile per key (zero past L)
+    for (int e = tid; e < TK * D / VEC; e += 256) {
+        const int n = e / (D / VEC), c = e % (D / VEC);
+        uint4 w = make_uint4(0u, 0u, 0u, 0u);
+        if (n0 + n < L) w = *reinterpret_cast<const uint4*>(src + (size_t)(n0 + n) * vs.rs + c * VEC);
+        *reinterpret_cast<uint4*>(&tile[n][c * VEC]) = w;
     }
     __syncthreads();
+    // 16-byte pieces out: VEC consecutive key positions of one V^T row
     T* dst = vt + (size_t)head * D * NT + n0;
-    for (int e = tid; e < TK * D; e += 256) {
-        const int dd = e / TK, p = e % TK;
-        const int n = PERMUTE ? ((p & ~12) | ((p & 4) << 1) | ((p & 8) >> 1)) : p;
-        dst[(size_t)dd * NT + p] = tile[n][dd];
+    for (int e = tid; e < D * TK / VEC; e += 256) {
+        const int dd = e / (TK / VEC), p0 = (e % (TK / VEC)) * VEC;
+        union {
+            uint4 w;
+            T x[VEC];
+        } u;
+#pragma unroll
+        for (int k = 0; k < VEC; ++k) {
+            const int p = p0 + k;
+            const int n = PERMUTE ? ((p & ~12) | ((p & 4) << 1) | ((p & 8) >> 1)) : p;
+            u.x[k] = tile[n][dd];
+        }
+        *reinterpret_cast<uint4*>(dst + (size_t)dd * NT + p0) = u.w;
     }
 }
 
