@@ -12,7 +12,9 @@
 // O^T = V^T P^T.  V is transposed once per call ([d][N]) so that the V^T
 // A-operand reads are contiguous in LDS.  Key tiles of 64 keys are staged
 // through double-buffered LDS; grouped-query heads map to kv head
-// h / (Hq / Hkv).
+// h / (Hq / Hkv).  The stage loop is software-pipelined: the score MFMAs of
+// the next tile are interleaved with the exponentials of the current one, so
+// a wave keeps the matrix unit and the vector ALU busy at the same time.
 #include "fp_common.h"
 #include "fp_launch.h"
 
@@ -49,6 +51,15 @@ __device__ __forceinline__ float exp_pack(const f32x16_t (&st)[2], float sl, flo
         ls = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf[kc], pf[kc], 6, 7), ones, ls, false);
     }
     return ls;
+}
+
+// 16 bytes per lane from global memory straight into LDS: a buffer load
+// whose resource starts at the (uniform) tile base, plus the lane's 32-bit
+// offset.  Lane i's bytes land at dst + 16 i.
+__device__ __forceinline__ void lds_load16(const void* base, unsigned voff, void* dst) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7fffffff, 0x00020000),
+        (__attribute__((address_space(3))) void*)dst, 16, voff, 0, 0, 0);
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -163,16 +174,18 @@ template <int BS, bool SPARSE, bool GATHER>
 __global__ __launch_bounds__(2 * BS, BS == 128 ? 2 : 1) void k_attn_bf16(AttnArgs a) {
     constexpr int D = kHeadDim, KT = kKT, NW = BS / 32, SPB = BS / KT;
     constexpr int TILE = KT * D * 2;            // bytes of one K (or V^T) tile
-    constexpr int LOADS = TILE / 1024 / NW;     // 1 KB direct loads per wave per tile
+    constexpr int LOADS = TILE / 1024 / NW;     // 1 KB loads into LDS per wave per tile
     // Tiles are unpadded and XOR-swizzled at 16-byte granularity:
     //   K   [64 keys][256 B]: chunk c of row r at chunk c ^ (r & 15)
     //   V^T [128 dv][128 B]:  chunk c of row r at chunk c ^ gray(r) & 7
     // so that the MFMA fragment reads below hit distinct banks.
-    // The two stages' tiles are four separate LDS objects and the stage loop
-    // is unrolled by two, so every access names its buffer at compile time:
-    // the compiler can then tell that the direct loads filling one buffer do
-    // not alias the reads of the other, and the tile loads stay in flight
-    // during the whole stage instead of being waited for before its softmax.
+    // The tiles are four separate LDS objects and the stage loop is unrolled
+    // by two, so every access names its buffer at compile time: the compiler
+    // can then tell that the loads filling one buffer do not alias the reads
+    // of another, and the tile loads stay in flight during the whole stage.
+    // The loads are buffer loads (not global ones): with a global load into
+    // LDS in flight the compiler waits for every outstanding LDS read instead
+    // of only the one an MFMA needs.
     __shared__ __attribute__((aligned(1024))) unsigned char Ks0[TILE];
     __shared__ __attribute__((aligned(1024))) unsigned char Ks1[TILE];
     __shared__ __attribute__((aligned(1024))) unsigned char Vs0[TILE];
@@ -228,7 +241,7 @@ __global__ __launch_bounds__(2 * BS, BS == 128 ? 2 : 1) void k_attn_bf16(AttnArg
     float m_run = -INFINITY, l_run = 0.0f;
     const float sl = a.scale_log2;
 
-    // Per-lane source offsets of the direct loads (independent of the stage).
+    // Per-lane source offsets of the tile loads (independent of the stage).
     // K load j of wave w covers rows 4J..4J+3 (J = w + NW j); lane -> row 4J + lane/16,
     // stored chunk lane%16 holds logical chunk (lane%16) ^ (row & 15).
     // V^T load j covers rows 8J..8J+7; lane -> row 8J + lane/8, stored chunk lane%8
@@ -242,87 +255,120 @@ __global__ __launch_bounds__(2 * BS, BS == 128 ? 2 : 1) void k_attn_bf16(AttnArg
         const int vr = 8 * J + (lane >> 3);
         voff[j] = (unsigned)((size_t)vr * vrow + 16 * ((lane & 7) ^ ((vr ^ (vr >> 1)) & 7)));
     }
+    // Tiles go straight from global memory to LDS (buffer loads with the
+    // tile's first byte as the uniform base and the offsets above per lane).
     // A tile reaching past the sequence end (only in the last key block) reads
     // the last key for the missing rows: finite values that the causal mask
     // removes; V^T is zero there.
-#define FP_FETCH_BF16(s_, KD_, VD_)                                                                          \
-    if (!GATHER || (s_) < nsub) {                                                                        \
-        const int kb_ = SPARSE ? lst[(s_) / SPB] : (s_) / SPB;                                          \
-        const int key0_ = kb_ * BS + ((s_) % SPB) * KT;                                                 \
-        const unsigned char* kg_ = K + (size_t)key0_ * krs;                                             \
-        const unsigned char* vg_ = VT + (size_t)key0_ * 2;                                              \
-        const bool full_ = key0_ + KT <= L;                                                             \
-        _Pragma("unroll") for (int j = 0; j < LOADS; ++j) {                                             \
-            const int J = w + NW * j;                                                                   \
-            const unsigned char* ka_ = kg_ + koff[j];                                                   \
-            if (!full_) {                                                                               \
-                const int kr_ = 4 * J + (lane >> 4);                                                    \
-                ka_ = K + (size_t)min(key0_ + kr_, L - 1) * krs + 16 * ((lane & 15) ^ (kr_ & 15));      \
+#define FP_FETCH_K(s_, KD_)                                                                              \
+    {                                                                                                    \
+        if (!GATHER || (s_) < nsub) {                                                                    \
+            const int kb_ = SPARSE ? lst[(s_) / SPB] : (s_) / SPB;                                      \
+            const int key0_ = kb_ * BS + ((s_) % SPB) * KT;                                             \
+            const unsigned char* kg_ = K + (size_t)key0_ * krs;                                         \
+            if (key0_ + KT <= L) {                                                                      \
+                _Pragma("unroll") for (int j = 0; j < LOADS; ++j)                                       \
+                    lds_load16(kg_, koff[j], &KD_[(w + NW * j) * 1024]);                               \
+            } else {                                                                                    \
+                _Pragma("unroll") for (int j = 0; j < LOADS; ++j) {                                     \
+                    const int kr_ = 4 * (w + NW * j) + (lane >> 4);                                     \
+                    const unsigned o_ = (unsigned)((min(key0_ + kr_, L - 1) - key0_) * krs) +           \
+                                        16u * ((lane & 15) ^ (kr_ & 15));                               \
+                    lds_load16(kg_, o_, &KD_[(w + NW * j) * 1024]);                                    \
+                }                                                                                       \
             }                                                                                           \
-            __builtin_amdgcn_global_load_lds((const void*)ka_,                                          \
-                (__attribute__((address_space(3))) void*)(&KD_[J * 1024]), 16, 0, 0);           \
-            __builtin_amdgcn_global_load_lds((const void*)(vg_ + voff[j]),                              \
-                (__attribute__((address_space(3))) void*)(&VD_[J * 1024]), 16, 0, 0);           \
-        }                                                                                                \
-    } else {                                                                                             \
-        const int c0_ = ((s_) - nsub) * KT;                                                             \
-        const unsigned char* kg_ = KG + (size_t)c0_ * D * 2;                                            \
-        const unsigned char* vg_ = VGT + (size_t)c0_ * 2;                                               \
-        _Pragma("unroll") for (int j = 0; j < LOADS; ++j) {                                             \
-            const int J = w + NW * j;                                                                   \
-            const int kr_ = 4 * J + (lane >> 4);                                                        \
-            __builtin_amdgcn_global_load_lds((const void*)(kg_ + kr_ * D * 2 + 16 * ((lane & 15) ^ (kr_ & 15))), \
-                (__attribute__((address_space(3))) void*)(&KD_[J * 1024]), 16, 0, 0);           \
-            __builtin_amdgcn_global_load_lds((const void*)(vg_ + voff[j]),                              \
-                (__attribute__((address_space(3))) void*)(&VD_[J * 1024]), 16, 0, 0);           \
+        } else {                                                                                         \
+            const unsigned char* kg_ = KG + (size_t)((s_) - nsub) * KT * D * 2;                         \
+            _Pragma("unroll") for (int j = 0; j < LOADS; ++j) {                                         \
+                const int kr_ = 4 * (w + NW * j) + (lane >> 4);                                         \
+                lds_load16(kg_, (unsigned)(kr_ * D * 2 + 16 * ((lane & 15) ^ (kr_ & 15))),             \
+                            &KD_[(w + NW * j) * 1024]);                                                 \
+            }                                                                                           \
         }                                                                                                \
     }
+#define FP_FETCH_V(s_, VD_)                                                                              \
+    {                                                                                                    \
+        const unsigned char* vg_;                                                                        \
+        if (!GATHER || (s_) < nsub) {                                                                    \
+            const int kb_ = SPARSE ? lst[(s_) / SPB] : (s_) / SPB;                                      \
+            vg_ = VT + (size_t)(kb_ * BS + ((s_) % SPB) * KT) * 2;                                      \
+        } else {                                                                                         \
+            vg_ = VGT + (size_t)(((s_) - nsub) * KT) * 2;                                               \
+        }                                                                                                \
+        _Pragma("unroll") for (int j = 0; j < LOADS; ++j)                                               \
+            lds_load16(vg_, voff[j], &VD_[(w + NW * j) * 1024]);                                       \
+    }
+    // Operand fragments in LDS: K rows (S^T = K Q^T) and V^T rows (O^T += V^T P^T).
+#define FP_KFRAG(B_, t_, c_) (*reinterpret_cast<const bf16x8_t*>(&B_[kfa[(c_)] + (t_) * 32 * D * 2]))
+#define FP_VFRAG(B_, T_, kc_) (*reinterpret_cast<const bf16x8_t*>(                                       \
+        &B_[(32 * (T_) + l32) * KT * 2 +                                                                \
+             16 * ((2 * (kc_) + hh) ^ (((32 * (T_) + l32) ^ ((32 * (T_) + l32) >> 1)) & 7))]))
+    // byte offset of K fragment c (contraction chunk c) of key row l32 within a
+    // 32-row half tile; the half (t) and the buffer are immediate offsets
+    unsigned kfa[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) kfa[c] = (unsigned)(l32 * D * 2 + 16 * ((2 * c + hh) ^ (l32 & 15)));
+    constexpr int RING = 4;   // LDS operand reads in flight ahead of the MFMAs
+    const f32x16_t zero16 = {};
 
-    FP_FETCH_BF16(0, Ks0, Vs0);
+    // Software pipeline: stage s runs the softmax of tile s while the matrix
+    // unit computes the scores of tile s + 1, then O^T += V^T P^T of tile s.
+    // K tiles are fetched two stages ahead, V^T tiles one stage ahead.
+    f32x16_t scA[2], scB[2];
+    FP_FETCH_K(0, Ks0);
+    FP_FETCH_V(0, Vs0);
+    if (nstage > 1) { FP_FETCH_K(1, Ks1); }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+        scA[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(FP_KFRAG(Ks0, i & 1, i >> 1), qf[i >> 1],
+                                                             i < 2 ? zero16 : scA[i & 1], 0, 0, 0);
+    __syncthreads();
 
-    // One stage: scores and softmax of the tile in (KC_, VC_) while the next
-    // stage's tile streams into (KN_, VN_).
-#define FP_STAGE_BF16(s, KC_, VC_, KN_, VN_)                                                             \
+    // One stage.  The 16 score MFMAs of the next tile are interleaved with
+    // the exponentials of this tile (two scores per MFMA); scheduling fences
+    // keep that order, so each MFMA runs while the vector ALU works.
+#define FP_STAGE_BF16(s, KC_, VC_, KN_, VN_, SC_, SN_)                                                   \
     {                                                                                                    \
         const bool gst = GATHER && (s) >= nsub;                                                          \
         const int kb = gst ? -1 : (SPARSE ? lst[(s) / SPB] : (s) / SPB);                                 \
         const int sub = (s) % SPB;                                                                       \
-        if ((s) + 1 < nstage) FP_FETCH_BF16((s) + 1, KN_, VN_);                                          \
-        /* Wave priority is raised while this wave issues MFMAs, so the other                       */  \
-        /* resident wave on the SIMD fills the matrix unit's busy time with its softmax.            */  \
-        __builtin_amdgcn_s_setprio(1);                                                                   \
-        f32x16_t st[2];                                                                                  \
-        _Pragma("unroll") for (int t = 0; t < 2; ++t) {                                                  \
-            _Pragma("unroll") for (int r = 0; r < 16; ++r) st[t][r] = 0.0f;                              \
-            const int row = 32 * t + l32;                                                                \
-            const unsigned char* kr = &KC_[row * D * 2];                                                 \
-            _Pragma("unroll") for (int c = 0; c < 8; ++c) {                                              \
-                const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(kr + 16 * ((2 * c + hh) ^ (row & 15))); \
-                st[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[c], st[t], 0, 0, 0);              \
-            }                                                                                            \
-        }                                                                                                \
-        __builtin_amdgcn_s_setprio(0);                                                                   \
+        if ((s) + 2 < nstage) { FP_FETCH_K((s) + 2, KN_); }                                              \
+        if ((s) + 1 < nstage) { FP_FETCH_V((s) + 1, VN_); }                                              \
         if (kb == qb) {                                                                                  \
             _Pragma("unroll") for (int t = 0; t < 2; ++t)                                                \
             _Pragma("unroll") for (int r = 0; r < 16; ++r) {                                             \
                 const int krel = sub * KT + 32 * t + 8 * (r >> 2) + 4 * hh + (r & 3);                   \
-                if (krel > qrel) st[t][r] = -INFINITY;                                                   \
+                if (krel > qrel) SC_[t][r] = -INFINITY;                                                  \
             }                                                                                            \
         }                                                                                                \
-        if (GATHER && gst) gather_mask<BS>(st, (s) - nsub, rid, fbits, gbias[w], gjpos[w], qb, qrow, lane, hh); \
+        if (GATHER && gst) gather_mask<BS>(SC_, (s) - nsub, rid, fbits, gbias[w], gjpos[w], qb, qrow, lane, hh); \
         bf16x8_t pf[4];                                                                                  \
         float ls = 0.0f;                                                                                 \
-        bool exact = (s) == 0;                                                                           \
-        if (!exact) {                                                                                    \
-            ls = exp_pack(st, sl, m_run * sl, pf);                                                       \
-            exact = __ballot(!(ls <= kSumLimit)) != 0;                                                   \
+        const float mb = m_run * sl;                                                                     \
+        {                                                                                                \
+            bf16x8_t fr[RING];                                                                           \
+            _Pragma("unroll") for (int i = 0; i < RING; ++i) fr[i] = FP_KFRAG(KC_, i & 1, i >> 1);       \
+            __builtin_amdgcn_sched_barrier(0);                                                           \
+            _Pragma("unroll") for (int i = 0; i < 16; ++i) {                                             \
+                SN_[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[i % RING], qf[i >> 1],           \
+                                                                     i < 2 ? zero16 : SN_[i & 1], 0, 0, 0); \
+                if (i + RING < 16) fr[i % RING] = FP_KFRAG(KC_, (i + RING) & 1, (i + RING) >> 1);        \
+                const int t_ = i >> 3, r_ = 2 * (i & 7);                                                 \
+                const float e0_ = __builtin_amdgcn_exp2f(__builtin_fmaf(SC_[t_][r_], sl, -mb));          \
+                const float e1_ = __builtin_amdgcn_exp2f(__builtin_fmaf(SC_[t_][r_ + 1], sl, -mb));      \
+                const bf16x2_t p2_ = {(__bf16)e0_, (__bf16)e1_};                                         \
+                pf[2 * t_ + (r_ >> 3)][r_ & 7] = p2_[0];                                                 \
+                pf[2 * t_ + (r_ >> 3)][(r_ & 7) + 1] = p2_[1];                                           \
+                ls = __builtin_amdgcn_fdot2_f32_bf16(p2_, ones2, ls, false);                              \
+                __builtin_amdgcn_sched_barrier(0);                                                       \
+            }                                                                                            \
         }                                                                                                \
-        if (exact) {                                                                                     \
+        if (__ballot(!(ls <= kSumLimit)) != 0) {                                                         \
             float mx = -INFINITY;                                                                        \
             _Pragma("unroll") for (int t = 0; t < 2; ++t)                                                \
-            _Pragma("unroll") for (int r = 0; r < 16; ++r) mx = fmaxf(mx, st[t][r]);                     \
+            _Pragma("unroll") for (int r = 0; r < 16; ++r) mx = fmaxf(mx, SC_[t][r]);                    \
             mx = fmaxf(mx, __shfl_xor(mx, 32));                                                          \
             const float m_new = fmaxf(m_run, mx);                                                        \
             const float alpha = fast_exp2((m_run - m_new) * sl);                                         \
@@ -330,42 +376,48 @@ __global__ __launch_bounds__(2 * BS, BS == 128 ? 2 : 1) void k_attn_bf16(AttnArg
             _Pragma("unroll") for (int T = 0; T < 4; ++T)                                                \
             _Pragma("unroll") for (int r = 0; r < 16; ++r) o[T][r] *= alpha;                             \
             m_run = m_new;                                                                               \
-            ls = exp_pack(st, sl, m_run * sl, pf);                                                       \
+            ls = exp_pack(SC_, sl, m_run * sl, pf);                                                      \
         }                                                                                                \
         l_run += ls;                                                                                     \
-        __builtin_amdgcn_s_setprio(1);                                                                   \
-        _Pragma("unroll") for (int T = 0; T < 4; ++T) {                                                  \
-            const int row = 32 * T + l32;                                                                \
-            const int g = (row ^ (row >> 1)) & 7;                                                        \
-            const unsigned char* vr = &VC_[row * KT * 2];                                                \
-            _Pragma("unroll") for (int kc = 0; kc < 4; ++kc) {                                           \
-                const bf16x8_t vf = *reinterpret_cast<const bf16x8_t*>(vr + 16 * ((2 * kc + hh) ^ g));   \
-                o[T] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[kc], o[T], 0, 0, 0);               \
+        {                                                                                                \
+            bf16x8_t fr[RING];                                                                           \
+            _Pragma("unroll") for (int i = 0; i < RING; ++i) fr[i] = FP_VFRAG(VC_, i & 3, i >> 2);       \
+            __builtin_amdgcn_sched_barrier(0);                                                           \
+            _Pragma("unroll") for (int i = 0; i < 16; ++i) {                                             \
+                o[i & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[i % RING], pf[i >> 2], o[i & 3], 0, 0, 0); \
+                if (i + RING < 16) fr[i % RING] = FP_VFRAG(VC_, (i + RING) & 3, (i + RING) >> 2);        \
+                __builtin_amdgcn_sched_barrier(0);                                                       \
             }                                                                                            \
         }                                                                                                \
-        __builtin_amdgcn_s_setprio(0);                                                                   \
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");                                                 \
         __syncthreads();                                                                                 \
     }
 
     // online softmax (lane = one query; lane ^ 32 holds its other keys).
-    // After a row's first stage the exp2 arguments use the reference
-    // maximum of earlier stages; as long as every lane's sum of the new
-    // probabilities stays <= kSumLimit (so each is <= kSumLimit) that
-    // reference is kept and no maximum is formed at all.  Otherwise (and
-    // on the first stage) the exact maximum becomes the reference, the
-    // accumulators are rescaled and the probabilities recomputed.  The
-    // final division by the row sum makes the result independent of the
-    // reference chosen.  O^T += V^T P^T uses the key order kc*16 + 8*(e/4) +
-    // 4*hh + e%4 of the B operand; V^T rows store each 16-key chunk as key
-    // groups [0-3, 8-11, 4-7, 12-15], so those 8 keys are one contiguous
-    // 16-byte chunk (logical chunk 2kc + hh).
+    // The exp2 arguments use the reference maximum of earlier stages; as
+    // long as every lane's sum of the new probabilities stays <= kSumLimit
+    // (so each is <= kSumLimit) that reference is kept and no maximum is
+    // formed at all.  Otherwise (always on the first stage, whose reference
+    // -inf makes every sum infinite or NaN) the exact maximum becomes the
+    // reference, the accumulators are rescaled and the probabilities
+    // recomputed.  The final division by the row sum makes the result
+    // independent of the reference chosen.  O^T += V^T P^T uses the key order
+    // kc*16 + 8*(e/4) + 4*hh + e%4 of the B operand; V^T rows store each
+    // 16-key chunk as key groups [0-3, 8-11, 4-7, 12-15], so those 8 keys are
+    // one contiguous 16-byte chunk (logical chunk 2kc + hh).
+    // Stage s reads K(s+1) from buffer (s+1)%2 and V(s) from buffer s%2, and
+    // fills K(s+2) into buffer s%2 and V(s+1) into buffer (s+1)%2; on the
+    // last stage the score MFMAs read a stale tile and their result is unused.
+    const bf16x2_t ones2 = {(__bf16)1.0f, (__bf16)1.0f};
     for (int s = 0; s < nstage; s += 2) {
-        FP_STAGE_BF16(s, Ks0, Vs0, Ks1, Vs1);
-        if (s + 1 < nstage) FP_STAGE_BF16(s + 1, Ks1, Vs1, Ks0, Vs0);
+        FP_STAGE_BF16(s, Ks1, Vs0, Ks0, Vs1, scA, scB);
+        if (s + 1 < nstage) FP_STAGE_BF16(s + 1, Ks0, Vs1, Ks1, Vs0, scB, scA);
     }
 #undef FP_STAGE_BF16
-#undef FP_FETCH_BF16
+#undef FP_KFRAG
+#undef FP_VFRAG
+#undef FP_FETCH_K
+#undef FP_FETCH_V
 
     const float l_tot = l_run + __shfl_xor(l_run, 32);
     const float inv = 1.0f / l_tot;
@@ -493,7 +545,7 @@ __global__ __launch_bounds__(2 * BS) void k_attn_f32(AttnArgs a) {
         const bool gst = GATHER && s >= nsub;
         const int kb = gst ? -1 : (SPARSE ? lst[s / SPB] : s / SPB);
         const int sub = s % SPB;
-        if (s + 1 < nstage) FP_FETCH_F32(s + 1);
+        if (s + 1 < nstage) { FP_FETCH_F32(s + 1); }
         f32x16_t st[2];
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
@@ -699,26 +751,23 @@ __device__ __forceinline__ void pp_group(PPState& S, const AttnArgs& a, const Ro
     {                                                                                                    \
         const int key0_ = PP_KEY0(t_);                                                                   \
         const unsigned char* kg_ = K + (size_t)key0_ * krs;                                             \
-        const bool full_ = key0_ + KT <= L;                                                             \
-        _Pragma("unroll") for (int j = 0; j < LOADS; ++j) {                                             \
-            const int J = qw + 4 * j;                                                                   \
-            const unsigned char* ka_ = kg_ + koff[j];                                                   \
-            if (!full_) {                                                                               \
-                const int kr_ = 4 * J + (lane >> 4);                                                    \
-                ka_ = K + (size_t)min(key0_ + kr_, L - 1) * krs + 16 * ((lane & 15) ^ (kr_ & 15));      \
+        if (key0_ + KT <= L) {                                                                          \
+            _Pragma("unroll") for (int j = 0; j < LOADS; ++j)                                           \
+                lds_load16(kg_, koff[j], &KD_[(qw + 4 * j) * 1024]);                                    \
+        } else {                                                                                        \
+            _Pragma("unroll") for (int j = 0; j < LOADS; ++j) {                                         \
+                const int kr_ = 4 * (qw + 4 * j) + (lane >> 4);                                         \
+                const unsigned o_ = (unsigned)((min(key0_ + kr_, L - 1) - key0_) * krs) +               \
+                                    16u * ((lane & 15) ^ (kr_ & 15));                                   \
+                lds_load16(kg_, o_, &KD_[(qw + 4 * j) * 1024]);                                         \
             }                                                                                           \
-            __builtin_amdgcn_global_load_lds((const void*)ka_,                                          \
-                (__attribute__((address_space(3))) void*)(&KD_[J * 1024]), 16, 0, 0);                  \
         }                                                                                                \
     }
 #define PP_FETCH_V(t_, VD_)                                                                              \
     {                                                                                                    \
         const unsigned char* vg_ = VT + (size_t)PP_KEY0(t_) * 2;                                        \
-        _Pragma("unroll") for (int j = 0; j < LOADS; ++j) {                                             \
-            const int J = qw + 4 * j;                                                                   \
-            __builtin_amdgcn_global_load_lds((const void*)(vg_ + voff[j]),                              \
-                (__attribute__((address_space(3))) void*)(&VD_[J * 1024]), 16, 0, 0);                  \
-        }                                                                                                \
+        _Pragma("unroll") for (int j = 0; j < LOADS; ++j)                                               \
+            lds_load16(vg_, voff[j], &VD_[(qw + 4 * j) * 1024]);                                        \
     }
     // An MFMA block reads 16 operand fragments from LDS and issues 16 MFMAs.
     // The reads run kPPRing ahead of the MFMAs through a ring of fragment
@@ -762,9 +811,10 @@ __device__ __forceinline__ void pp_group(PPState& S, const AttnArgs& a, const Ro
     // softmax of S(t_) into P(t_); then waits for the tiles the next M phase reads
 #define PP_PHASE_V(t_, KN_, VN_)                                                                         \
     {                                                                                                    \
-        const bool lk_ = (t_) + 2 < n, lv_ = (t_) + 1 < n;                                               \
-        if (lk_) PP_FETCH_K((t_) + 2, KN_);                                                              \
-        if (lv_) PP_FETCH_V((t_) + 1, VN_);                                                              \
+        /* past the row's end the last tile is loaded again (unused): every V */                        \
+        /* phase issues the same loads, so every wait count is fixed           */                        \
+        PP_FETCH_K(min((t_) + 2, n - 1), KN_);                                                           \
+        PP_FETCH_V(min((t_) + 1, n - 1), VN_);                                                           \
         const int kb_ = SPARSE ? lst[(t_)] : (t_);                                                       \
         if (kb_ == qb) {                                                                                 \
             _Pragma("unroll") for (int t = 0; t < 2; ++t)                                                \
@@ -794,9 +844,7 @@ __device__ __forceinline__ void pp_group(PPState& S, const AttnArgs& a, const Ro
             ls = exp_pack(S.st, sl, none_ ? 0.0f : m_new * sl, S.pf);                                    \
         }                                                                                                \
         S.l_run += ls;                                                                                   \
-        if (lk_ && lv_) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");                                 \
-        else if (lk_ || lv_) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");                            \
-        else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");                                            \
+        asm volatile("s_waitcnt vmcnt(8)" ::: "memory");                                                 \
     }
     static_assert(LOADS == 4, "the V-phase waits count 4 loads per tile");
 
