@@ -402,7 +402,7 @@ fp_status make_plan(const void* q, const void* k, fp_dtype dtype, int layout, in
     long long lists_n = 0;
     size_t n_qbar = 0, n_kbar = 0, n_rowmax = 0, n_colsum = 0, n_atrue = 0, n_ahat = 0, n_cp = 0;
     int max_bh = 0;
-    size_t s2_max = 0, pmax_max = 0, rz_max = 0;
+    size_t s2_max = 0, pmax_max = 0, rz_max = 0, qt_max = 0;
     for (const SegHost& g : segs) {
         const long long nbh = (long long)g.nseq * Hq;
         const int NS = (g.L + 255) / 256 * 256;
@@ -420,6 +420,7 @@ fp_status make_plan(const void* q, const void* k, fp_dtype dtype, int layout, in
         s2_max = std::max(s2_max, (size_t)nbh * block * NS);
         pmax_max = std::max(pmax_max, (size_t)nbh * (NS / 256) * block);
         rz_max = std::max(rz_max, (size_t)nbh * block);
+        qt_max = std::max(qt_max, (size_t)nbh * kHeadDim * block);
     }
     p->n_qbar = n_qbar; p->n_kbar = n_kbar; p->n_rowmax = n_rowmax; p->n_colsum = n_colsum;
     p->n_atrue = n_atrue; p->n_ahat = n_ahat; p->n_counts = (size_t)p->rows; p->n_lists = (size_t)lists_n;
@@ -554,10 +555,11 @@ fp_status make_plan(const void* q, const void* k, fp_dtype dtype, int layout, in
     }
 
     // one transient score workspace, reused segment after segment (stream order)
-    void *s2 = nullptr, *pmax = nullptr, *rz = nullptr;
+    void *s2 = nullptr, *pmax = nullptr, *rz = nullptr, *qt = nullptr;
     if (he == hipSuccess) he = hipMallocAsync(&s2, s2_max * sizeof(float), st);
     if (he == hipSuccess) he = hipMallocAsync(&pmax, pmax_max * sizeof(float), st);
     if (he == hipSuccess) he = hipMallocAsync(&rz, rz_max * sizeof(float), st);
+    if (he == hipSuccess) he = hipMallocAsync(&qt, qt_max * sizeof(float), st);
     const size_t esz = dtype == FP_BF16 ? 2 : 4;
     const Canon canon = make_canon(d);
     for (size_t i = 0; i < segs.size() && he == hipSuccess; ++i) {
@@ -576,11 +578,13 @@ fp_status make_plan(const void* q, const void* k, fp_dtype dtype, int layout, in
         a.s2 = (float*)s2;
         a.pmax = (float*)pmax;
         a.rz = (float*)rz;
+        a.qt = (float*)qt;
         he = launch_plan(a, p->dev[i], st);
     }
     if (s2) (void)hipFreeAsync(s2, st);
     if (pmax) (void)hipFreeAsync(pmax, st);
     if (rz) (void)hipFreeAsync(rz, st);
+    if (qt) (void)hipFreeAsync(qt, st);
     if (he != hipSuccess) {
         free_plan(p);
         return hip_fail(he, "planning");

@@ -93,6 +93,7 @@ struct PlanArgs {
     float* s2;        // [BH][BS][NS] transient
     float* pmax;      // [BH][NS/256][BS] transient
     float* rz;        // [BH][BS] transient
+    float* qt;        // [BH][d][BS] transient: the last block's queries, fp32, transposed
 };
 
 // One segment of the attention work (device table, one entry per segment).

@@ -173,14 +173,31 @@ __global__ __launch_bounds__(256) void k_pool(const T* __restrict__ x, TokStride
 // L-BS+i < 0 (a sequence shorter than one block) do not exist: their maxima
 // stay -inf and later kernels skip them.
 // Register-blocked VALU product: 256 threads, tile BS queries x 256 keys, each
-// thread owns BS/16 queries x 16 keys; d staged through LDS in slices of 32.
+// thread owns BS/16 queries x 16 keys; d staged through LDS in slices of 32
+// (the query slices from the transposed copy k_qt writes).
 // ---------------------------------------------------------------------------
 constexpr int kScoreTK = 256;
 constexpr int kScoreDS = kScoreDSConst;
 
+// The last block's queries, widened to fp32 and transposed once per call:
+// qt[bh][t][i] = q[L-BS+i][t] (0 for rows that do not exist), so that every
+// score workgroup stages its query slices with contiguous 16-byte loads.
 template <typename T, int BS>
-__global__ __launch_bounds__(256) void k_scores(const T* __restrict__ q, const T* __restrict__ k,
-                                                TokStride qs, TokStride ks, float* __restrict__ s2,
+__global__ __launch_bounds__(256) void k_qt(const T* __restrict__ q, TokStride qs, float* __restrict__ qt, int L,
+                                            int Hq) {
+    constexpr int D = kHeadDim;
+    const int bh = blockIdx.x, b = bh / Hq, h = bh % Hq;
+    const T* qhead = q + (size_t)b * qs.bst + (size_t)h * qs.hs;
+    for (int e = threadIdx.x; e < D * BS; e += 256) {
+        const int t = e % D, i = e / D;       // reads run along t (contiguous in q)
+        const int pos = L - BS + i;
+        qt[((size_t)bh * D + t) * BS + i] = pos >= 0 ? load_f32(qhead + (size_t)pos * qs.rs + t) : 0.0f;
+    }
+}
+
+template <typename T, int BS>
+__global__ __launch_bounds__(256) void k_scores(const float* __restrict__ qt, const T* __restrict__ k,
+                                                TokStride ks, float* __restrict__ s2,
                                                 float* __restrict__ pmax, int L, int NS, int Hq, int group,
                                                 float C) {
     constexpr int D = kHeadDim, TK = kScoreTK, DS = kScoreDS, MR = BS / 16;
@@ -189,7 +206,7 @@ __global__ __launch_bounds__(256) void k_scores(const T* __restrict__ q, const T
     const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
     const int chunk = blockIdx.x, bh = blockIdx.y;
     const int b = bh / Hq, h = bh % Hq;
-    const T* qhead = q + (size_t)b * qs.bst + (size_t)h * qs.hs;
+    const float* qth = qt + (size_t)bh * D * BS;
     const int j0 = chunk * TK;
     const T* kbase = k + (size_t)b * ks.bst + (size_t)(h / group) * ks.hs;
     const bool key_ok = (j0 + tid) < L;
@@ -202,10 +219,9 @@ __global__ __launch_bounds__(256) void k_scores(const T* __restrict__ q, const T
 
     for (int t0 = 0; t0 < D; t0 += DS) {
         // Q slice, transposed: Qs[tt][i]
-        for (int e = tid; e < BS * DS; e += 256) {
-            int i = e / DS, tt = e % DS;
-            const int pos = L - BS + i;
-            Qs[tt][i] = pos >= 0 ? load_f32(qhead + (size_t)pos * qs.rs + t0 + tt) : 0.0f;
+        for (int e4 = tid; e4 < BS * DS / 4; e4 += 256) {
+            const int tt = e4 / (BS / 4), i = 4 * (e4 % (BS / 4));
+            *reinterpret_cast<float4*>(&Qs[tt][i]) = *reinterpret_cast<const float4*>(qth + (size_t)(t0 + tt) * BS + i);
         }
         // K slice, transposed: thread tid owns key j0 + tid
         {
@@ -1091,8 +1107,11 @@ hipError_t launch_plan(const PlanArgs& a, PlanDev& P, hipStream_t st) {
     const dim3 gs(NS / kScoreTK, BH);
     const int group = a.Hq / a.Hkv;
 #define FP_SCORES(T, B_)                                                                                   \
-    hipLaunchKernelGGL((k_scores<T, B_>), gs, dim3(256), 0, st, (const T*)a.q, (const T*)a.k, a.qs, a.ks,   \
-                       a.s2, a.pmax, L, NS, a.Hq, group, a.canon.C)
+    do {                                                                                                   \
+        hipLaunchKernelGGL((k_qt<T, B_>), dim3(BH), dim3(256), 0, st, (const T*)a.q, a.qs, a.qt, L, a.Hq);  \
+        hipLaunchKernelGGL((k_scores<T, B_>), gs, dim3(256), 0, st, (const float*)a.qt, (const T*)a.k, a.ks, \
+                           a.s2, a.pmax, L, NS, a.Hq, group, a.canon.C);                                   \
+    } while (0)
     if (a.dtype_bf16) {
         if (BS == 128) FP_SCORES(bf16_t, 128); else FP_SCORES(bf16_t, 64);
     } else {
