@@ -118,6 +118,9 @@ def main() -> int:
                     help="how query-aware heads select blocks from the estimated map")
     ap.add_argument("--vs-granularity", default="block", choices=["block", "token"],
                     help="vertical-slash columns as whole blocks or token by token")
+    ap.add_argument("--varlen", default="",
+                    help="comma-separated sequence lengths: time a packed [T, H, d] batch of sequences of "
+                         "these lengths (the --config head shape) instead of the batched layer")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -138,17 +141,39 @@ def main() -> int:
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     t0 = time.perf_counter()
-    q, k, v = LayerGen(cfg).torch_layer(dev)
+    lens = [int(x) for x in args.varlen.split(",") if x.strip()] if args.varlen else None
+    if lens:
+        # packed batch: each sequence generated with its own seed at the config's head shape
+        if min(lens) < 1:
+            print(json.dumps({"error": "--varlen lengths must be positive"}))
+            return 2
+        parts = []
+        for b, n in enumerate(lens):
+            n_gen = -(-n // 128) * 128
+            qs_, ks_, vs_ = LayerGen(cfg.with_(B=1, N=n_gen, seed=cfg.seed + 7 * b)).torch_layer(dev)
+            parts.append([t[0, :, :n].transpose(0, 1) for t in (qs_, ks_, vs_)])
+            del qs_, ks_, vs_
+        q, k, v = (torch.cat([pt[i] for pt in parts]).contiguous() for i in range(3))
+        del parts
+        cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+        workload = f"{cfg.name}_varlen_{len(lens)}seq_{int(cu[-1])}tok"
+    else:
+        q, k, v = LayerGen(cfg).torch_layer(dev)
+        workload = cfg.name
     torch.cuda.synchronize()
     gen_s = time.perf_counter() - t0
-    print(f"[bench] inputs {cfg.name} generated in {gen_s:.1f}s", file=sys.stderr, flush=True)
+    print(f"[bench] inputs {workload} generated in {gen_s:.1f}s", file=sys.stderr, flush=True)
     out = torch.empty_like(q)
     stream = torch.cuda.current_stream()
 
+    def make_plan():
+        kw = dict(block=cfg.block, gamma=cfg.gamma, tau=cfg.tau, min_budget=cfg.min_budget,
+                  max_budget=args.max_budget, qa_selection=args.qa_selection,
+                  vs_granularity=args.vs_granularity)
+        return F.plan_varlen(q, k, cu, **kw) if lens else F.plan(q, k, **kw)
+
     def step():
-        P = F.plan(q, k, block=cfg.block, gamma=cfg.gamma, tau=cfg.tau, min_budget=cfg.min_budget,
-                   max_budget=args.max_budget, qa_selection=args.qa_selection,
-                   vs_granularity=args.vs_granularity)
+        P = make_plan()
         F.attend(P, q, k, v, out=out)
         return P
 
@@ -165,9 +190,7 @@ def main() -> int:
     t_wall = time.perf_counter()
     for i in range(args.steps):
         ev[i][0].record(stream)
-        P = F.plan(q, k, block=cfg.block, gamma=cfg.gamma, tau=cfg.tau, min_budget=cfg.min_budget,
-                   max_budget=args.max_budget, qa_selection=args.qa_selection,
-                   vs_granularity=args.vs_granularity)
+        P = make_plan()
         ev[i][1].record(stream)
         F.attend(P, q, k, v, out=out)
         ev[i][2].record(stream)
@@ -180,11 +203,12 @@ def main() -> int:
     kern_ms, kern_n, _, _ = F.profile_read(reset=True)
     F.profile_enable(False)
     info = plans[-1].info()
-    counts = plans[-1].debug("counts")
-    plans_last_colptr = plans[-1].debug("colptr") if args.vs_granularity == "token" else None
+    counts = [c for c in plans[-1].debug_seqs("counts") if c is not None]
+    colptrs = ([c for c in plans[-1].debug_seqs("colptr") if c is not None]
+               if args.vs_granularity == "token" else None)
     pattern, djs, _, _ = plans[-1].copy_out()
     del plans
-    blocks_by_head = counts.sum(axis=1).tolist()
+    blocks_by_head = np.concatenate([c.sum(axis=1) for c in counts]).tolist()
 
     flop_per_block = 4.0 * cfg.block * cfg.block * cfg.d
     sparse_flop = info.total_blocks * flop_per_block
@@ -192,8 +216,7 @@ def main() -> int:
     if args.vs_granularity == "token":
         # gathered-column tiles: ceil(columns before the row's end / 64) per row,
         # each 64 keys x block queries x 4 d FLOP
-        cp = plans_last_colptr.astype(np.int64)[:, 1:]
-        gathered_tiles = int(((cp + 63) // 64).sum())
+        gathered_tiles = sum(int(((c.astype(np.int64)[:, 1:] + 63) // 64).sum()) for c in colptrs)
         sparse_flop += gathered_tiles * 4.0 * 64 * cfg.block * cfg.d
     dense_flop = info.dense_blocks * flop_per_block
     kern_avg_ms = kern_ms / max(kern_n, 1)
@@ -205,13 +228,18 @@ def main() -> int:
         F.profile_enable(True)
         F.profile_read(reset=True)
         outd = torch.empty_like(q)
-        F.dense_attend(q, k, v, block=cfg.block, out=outd)      # warm-up
+        def dense():
+            if lens:
+                F.dense_attend_varlen(q, k, v, cu, block=cfg.block, out=outd)
+            else:
+                F.dense_attend(q, k, v, block=cfg.block, out=outd)
+        dense()      # warm-up
         torch.cuda.synchronize()
         F.profile_read(reset=True)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         for _ in range(args.dense_reps):
-            F.dense_attend(q, k, v, block=cfg.block, out=outd)
+            dense()
         e1.record(stream)
         torch.cuda.synchronize()
         dense_ms = e0.elapsed_time(e1) / args.dense_reps
@@ -229,7 +257,7 @@ def main() -> int:
         torch.cuda.synchronize()
         del a, b
 
-    traffic = read_traffic(cfg.name, args.max_budget == 0 and args.qa_selection == "flattened"
+    traffic = read_traffic(workload, args.max_budget == 0 and args.qa_selection == "flattened"
                            and args.vs_granularity == "block")
     roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
             "frac": round(achieved / peak, 4), "traffic": traffic,
@@ -238,7 +266,7 @@ def main() -> int:
             "algorithmic_flop_per_launch": sparse_flop, "avg_kernel_ms": round(kern_avg_ms, 4),
             "launches": kern_n}
     cpu = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not lens:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
         cpu = cpu_baseline(cfg, blocks_by_head, args.cpu_rows, args.cpu_budget_s, args.max_budget,
                            args.qa_selection, args.vs_granularity)
@@ -256,7 +284,8 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": cfg.dtype,
         "data": "synthetic (seeded planted head types; no datasets or weights)",
-        "config": {"workload": cfg.name, "B": cfg.B, "Hq": cfg.Hq, "Hkv": cfg.Hkv, "N": cfg.N,
+        "config": {"workload": workload, "B": len(lens) if lens else cfg.B, "Hq": cfg.Hq, "Hkv": cfg.Hkv,
+                   "N": None if lens else cfg.N, "seqlens": lens,
                    "d": cfg.d, "block": cfg.block, "gamma": cfg.gamma, "tau": cfg.tau,
                    "min_budget": cfg.min_budget, "max_budget": args.max_budget,
                    "qa_selection": args.qa_selection, "vs_granularity": args.vs_granularity,
