@@ -339,7 +339,13 @@ __global__ __launch_bounds__(256) void k_rowexp(const float* __restrict__ s2, co
         __syncthreads();
         if (tid < kSegBlocks && seg0 + tid * BS < L) {
             float z = 0.0f;
-            for (int jj = 0; jj < BS; ++jj) z = z + es[tid][jj];
+            for (int jj = 0; jj < BS; jj += 16) {
+                float v[16];
+#pragma unroll
+                for (int u = 0; u < 16; ++u) v[u] = es[tid][jj + u];
+#pragma unroll
+                for (int u = 0; u < 16; ++u) z = z + v[u];
+            }
             zp[seg0 / BS + tid] = z;
         }
         __syncthreads();
@@ -347,7 +353,15 @@ __global__ __launch_bounds__(256) void k_rowexp(const float* __restrict__ s2, co
     if (tid == 0) {
         const int nb = (L + BS - 1) / BS;
         float Z = 0.0f;
-        for (int kb = 0; kb < nb; ++kb) Z = Z + zp[kb];
+        int kb = 0;
+        for (; kb + 16 <= nb; kb += 16) {
+            float v[16];
+#pragma unroll
+            for (int u = 0; u < 16; ++u) v[u] = zp[kb + u];
+#pragma unroll
+            for (int u = 0; u < 16; ++u) Z = Z + v[u];
+        }
+        for (; kb < nb; ++kb) Z = Z + zp[kb];
         rowmax[(size_t)bh * BS + row] = M;
         rowsum[(size_t)bh * BS + row] = Z;
         rz[(size_t)bh * BS + row] = 1.0f / Z;
@@ -455,17 +469,34 @@ __global__ __launch_bounds__(256) void k_atrue(const float* __restrict__ colsum,
     __shared__ float ts[kMaxBlocks];
     __shared__ float Tsh;
     const int tid = threadIdx.x, bh = blockIdx.x, nb = (L + BS - 1) / BS;
+    // sequential sums; the reads go out 16 at a time ahead of the adds
     for (int kb = tid; kb < nb; kb += 256) {
         const float* c = colsum + (size_t)bh * L + (size_t)kb * BS;
         const int n = min(BS, L - kb * BS);
         float t = 0.0f;
-        for (int jj = 0; jj < n; ++jj) t = t + c[jj];
+        int jj = 0;
+        for (; jj + 16 <= n; jj += 16) {
+            float v[16];
+#pragma unroll
+            for (int u = 0; u < 16; ++u) v[u] = c[jj + u];
+#pragma unroll
+            for (int u = 0; u < 16; ++u) t = t + v[u];
+        }
+        for (; jj < n; ++jj) t = t + c[jj];
         ts[kb] = t;
     }
     __syncthreads();
     if (tid == 0) {
         float T = 0.0f;
-        for (int kb = 0; kb < nb; ++kb) T = T + ts[kb];
+        int kb = 0;
+        for (; kb + 16 <= nb; kb += 16) {
+            float v[16];
+#pragma unroll
+            for (int u = 0; u < 16; ++u) v[u] = ts[kb + u];
+#pragma unroll
+            for (int u = 0; u < 16; ++u) T = T + v[u];
+        }
+        for (; kb < nb; ++kb) T = T + ts[kb];
         Tsh = T;
     }
     __syncthreads();
@@ -545,8 +576,19 @@ __global__ __launch_bounds__(256) void k_estimate(const float* __restrict__ qbar
             if (kb <= q0 + r) sc[r * nb + kb] = exp2_c(sc[r * nb + kb] - Mr[r], K);
     __syncthreads();
     if (tid < R && q0 + tid < nb) {
+        // sequential sum; the LDS reads go out 16 at a time ahead of the adds
+        const float* zr = sc + tid * nb;
+        const int n = q0 + tid + 1;
         float Z = 0.0f;
-        for (int kb = 0; kb <= q0 + tid; ++kb) Z = Z + sc[tid * nb + kb];
+        int kb = 0;
+        for (; kb + 16 <= n; kb += 16) {
+            float v[16];
+#pragma unroll
+            for (int u = 0; u < 16; ++u) v[u] = zr[kb + u];
+#pragma unroll
+            for (int u = 0; u < 16; ++u) Z = Z + v[u];
+        }
+        for (; kb < n; ++kb) Z = Z + zr[kb];
         Zr[tid] = Z;
     }
     __syncthreads();
