@@ -228,6 +228,31 @@ void free_plan(fp_plan* p) {
     delete p;
 }
 
+// Sequences of a packed batch are planned concurrently on up to kPlanLanes
+// streams (segment i on lane i % lanes), each lane with its own transient
+// workspace and selection state; the caller's stream forks to the lanes and
+// joins them with events.  The lane streams are created once per device and
+// kept; they have the default priority.
+constexpr int kPlanLanes = 4;
+
+hipError_t lane_streams(hipStream_t* out) {
+    static std::mutex mu;
+    static std::vector<std::vector<hipStream_t>> pool;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    std::lock_guard<std::mutex> lock(mu);
+    if ((int)pool.size() <= dev) pool.resize(dev + 1);
+    while ((int)pool[dev].size() < kPlanLanes) {
+        hipStream_t s;
+        e = hipStreamCreateWithFlags(&s, hipStreamNonBlocking);
+        if (e != hipSuccess) return e;
+        pool[dev].push_back(s);
+    }
+    for (int i = 0; i < kPlanLanes; ++i) out[i] = pool[dev][i];
+    return hipSuccess;
+}
+
 // The attention segment table of a problem and the V^T workspace size.
 void attention_table(const std::vector<SegHost>& segs, int Hq, int Hkv, int bs, std::vector<AttnSeg>& t,
                      long long& items, size_t& vt_elems, size_t& g_elems) {
@@ -402,8 +427,11 @@ fp_status make_plan(const void* q, const void* k, fp_dtype dtype, int layout, in
     long long lists_n = 0;
     size_t n_qbar = 0, n_kbar = 0, n_rowmax = 0, n_colsum = 0, n_atrue = 0, n_ahat = 0, n_cp = 0;
     int max_bh = 0;
-    size_t s2_max = 0, pmax_max = 0, rz_max = 0, qt_max = 0;
-    for (const SegHost& g : segs) {
+    const int lanes = (int)std::min<size_t>(segs.size(), kPlanLanes);
+    size_t s2_max[kPlanLanes] = {}, pmax_max[kPlanLanes] = {}, rz_max[kPlanLanes] = {}, qt_max[kPlanLanes] = {};
+    for (size_t si = 0; si < segs.size(); ++si) {
+        const SegHost& g = segs[si];
+        const int ln = (int)(si % kPlanLanes);
         const long long nbh = (long long)g.nseq * Hq;
         const int NS = (g.L + 255) / 256 * 256;
         p->rows += nbh * g.nb;
@@ -417,10 +445,10 @@ fp_status make_plan(const void* q, const void* k, fp_dtype dtype, int layout, in
         n_ahat += (size_t)nbh * g.tri;
         n_cp += (size_t)nbh * (g.nb + 1);
         max_bh = std::max(max_bh, (int)nbh);
-        s2_max = std::max(s2_max, (size_t)nbh * block * NS);
-        pmax_max = std::max(pmax_max, (size_t)nbh * (NS / 256) * block);
-        rz_max = std::max(rz_max, (size_t)nbh * block);
-        qt_max = std::max(qt_max, (size_t)nbh * kHeadDim * block);
+        s2_max[ln] = std::max(s2_max[ln], (size_t)nbh * block * NS);
+        pmax_max[ln] = std::max(pmax_max[ln], (size_t)nbh * (NS / 256) * block);
+        rz_max[ln] = std::max(rz_max[ln], (size_t)nbh * block);
+        qt_max[ln] = std::max(qt_max[ln], (size_t)nbh * kHeadDim * block);
     }
     p->n_qbar = n_qbar; p->n_kbar = n_kbar; p->n_rowmax = n_rowmax; p->n_colsum = n_colsum;
     p->n_atrue = n_atrue; p->n_ahat = n_ahat; p->n_counts = (size_t)p->rows; p->n_lists = (size_t)lists_n;
@@ -484,8 +512,8 @@ fp_status make_plan(const void* q, const void* k, fp_dtype dtype, int layout, in
         PALLOC(p->colptr, n_cp);
         PALLOC(p->colidx, n_colsum);
     }
-    PALLOC(sel, (size_t)2 * max_bh);
-    PALLOC(hist, (size_t)2 * max_bh * kRadixBins);
+    PALLOC(sel, (size_t)2 * max_bh * lanes);
+    PALLOC(hist, (size_t)2 * max_bh * kRadixBins * lanes);
     PALLOC(aseg, segs.size());
 #undef PALLOC
     p->aseg = aseg;
@@ -542,8 +570,8 @@ fp_status make_plan(const void* q, const void* k, fp_dtype dtype, int layout, in
             P.colptr = p->colptr + o_cp;
             P.colidx = p->colidx + o_colsum;
         }
-        P.sel = sel;
-        P.hist = hist;
+        P.sel = sel + (size_t)2 * max_bh * (i % kPlanLanes);
+        P.hist = hist + (size_t)2 * max_bh * kRadixBins * (i % kPlanLanes);
         o_qbar += (size_t)nbh * g.nb * kHeadDim;
         o_kbar += (size_t)g.nseq * Hkv * g.nb * kHeadDim;
         o_rowmax += (size_t)nbh * block;
@@ -554,15 +582,32 @@ fp_status make_plan(const void* q, const void* k, fp_dtype dtype, int layout, in
         o_cp += (size_t)nbh * (g.nb + 1);
     }
 
-    // one transient score workspace, reused segment after segment (stream order)
+    // transient score workspace per lane, reused by the lane's segments in its stream order
+    size_t o_s2[kPlanLanes + 1] = {}, o_pm[kPlanLanes + 1] = {}, o_rz[kPlanLanes + 1] = {}, o_qt[kPlanLanes + 1] = {};
+    for (int j = 0; j < lanes; ++j) {
+        o_s2[j + 1] = o_s2[j] + s2_max[j];
+        o_pm[j + 1] = o_pm[j] + pmax_max[j];
+        o_rz[j + 1] = o_rz[j] + rz_max[j];
+        o_qt[j + 1] = o_qt[j] + qt_max[j];
+    }
     void *s2 = nullptr, *pmax = nullptr, *rz = nullptr, *qt = nullptr;
-    if (he == hipSuccess) he = hipMallocAsync(&s2, s2_max * sizeof(float), st);
-    if (he == hipSuccess) he = hipMallocAsync(&pmax, pmax_max * sizeof(float), st);
-    if (he == hipSuccess) he = hipMallocAsync(&rz, rz_max * sizeof(float), st);
-    if (he == hipSuccess) he = hipMallocAsync(&qt, qt_max * sizeof(float), st);
+    if (he == hipSuccess) he = hipMallocAsync(&s2, o_s2[lanes] * sizeof(float), st);
+    if (he == hipSuccess) he = hipMallocAsync(&pmax, o_pm[lanes] * sizeof(float), st);
+    if (he == hipSuccess) he = hipMallocAsync(&rz, o_rz[lanes] * sizeof(float), st);
+    if (he == hipSuccess) he = hipMallocAsync(&qt, o_qt[lanes] * sizeof(float), st);
+    hipStream_t ls[kPlanLanes];
+    hipEvent_t ev[kPlanLanes + 1] = {};
+    for (int j = 0; j < kPlanLanes; ++j) ls[j] = st;
+    if (lanes > 1 && he == hipSuccess) {
+        he = lane_streams(ls);
+        for (int j = 0; j <= lanes && he == hipSuccess; ++j) he = hipEventCreateWithFlags(&ev[j], hipEventDisableTiming);
+        if (he == hipSuccess) he = hipEventRecord(ev[lanes], st);     // fork
+        for (int j = 0; j < lanes && he == hipSuccess; ++j) he = hipStreamWaitEvent(ls[j], ev[lanes], 0);
+    }
     const size_t esz = dtype == FP_BF16 ? 2 : 4;
     const Canon canon = make_canon(d);
     for (size_t i = 0; i < segs.size() && he == hipSuccess; ++i) {
+        const int ln = (int)(i % kPlanLanes);
         PlanArgs a{};
         a.q = (const unsigned char*)q + (size_t)segs[i].qoff * esz;
         a.k = (const unsigned char*)k + (size_t)segs[i].koff * esz;
@@ -575,11 +620,20 @@ fp_status make_plan(const void* q, const void* k, fp_dtype dtype, int layout, in
         a.tau = (double)tau;
         a.G = G;
         a.canon = canon;
-        a.s2 = (float*)s2;
-        a.pmax = (float*)pmax;
-        a.rz = (float*)rz;
-        a.qt = (float*)qt;
-        he = launch_plan(a, p->dev[i], st);
+        a.s2 = (float*)s2 + o_s2[ln];
+        a.pmax = (float*)pmax + o_pm[ln];
+        a.rz = (float*)rz + o_rz[ln];
+        a.qt = (float*)qt + o_qt[ln];
+        he = launch_plan(a, p->dev[i], ls[ln]);
+    }
+    if (lanes > 1) {
+        // join: the caller's stream waits for every lane (also after a failure,
+        // so the workspace is not freed under running kernels)
+        for (int j = 0; j < lanes; ++j) {
+            if (ev[j] && hipEventRecord(ev[j], ls[j]) == hipSuccess) (void)hipStreamWaitEvent(st, ev[j], 0);
+        }
+        for (int j = 0; j <= lanes; ++j)
+            if (ev[j]) (void)hipEventDestroy(ev[j]);
     }
     if (s2) (void)hipFreeAsync(s2, st);
     if (pmax) (void)hipFreeAsync(pmax, st);
