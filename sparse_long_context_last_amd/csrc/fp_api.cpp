@@ -597,9 +597,13 @@ fp_status make_plan(const void* q, const void* k, fp_dtype dtype, int layout, in
     if (he == hipSuccess) he = hipMallocAsync(&qt, o_qt[lanes] * sizeof(float), st);
     hipStream_t ls[kPlanLanes];
     hipEvent_t ev[kPlanLanes + 1] = {};
+    hipStream_t pool_streams[kPlanLanes];
     for (int j = 0; j < kPlanLanes; ++j) ls[j] = st;
+    if (he == hipSuccess) he = lane_streams(pool_streams);
+    // one segment: a lane stream carries its pooling kernels
+    hipStream_t aux = lanes == 1 && he == hipSuccess ? pool_streams[0] : nullptr;
     if (lanes > 1 && he == hipSuccess) {
-        he = lane_streams(ls);
+        for (int j = 0; j < kPlanLanes; ++j) ls[j] = pool_streams[j];
         for (int j = 0; j <= lanes && he == hipSuccess; ++j) he = hipEventCreateWithFlags(&ev[j], hipEventDisableTiming);
         if (he == hipSuccess) he = hipEventRecord(ev[lanes], st);     // fork
         for (int j = 0; j < lanes && he == hipSuccess; ++j) he = hipStreamWaitEvent(ls[j], ev[lanes], 0);
@@ -624,6 +628,7 @@ fp_status make_plan(const void* q, const void* k, fp_dtype dtype, int layout, in
         a.pmax = (float*)pmax + o_pm[ln];
         a.rz = (float*)rz + o_rz[ln];
         a.qt = (float*)qt + o_qt[ln];
+        a.aux = aux;
         he = launch_plan(a, p->dev[i], ls[ln]);
     }
     if (lanes > 1) {

@@ -94,6 +94,7 @@ struct PlanArgs {
     float* pmax;      // [BH][NS/256][BS] transient
     float* rz;        // [BH][BS] transient
     float* qt;        // [BH][d][BS] transient: the last block's queries, fp32, transposed
+    hipStream_t aux;  // second stream for the pooling kernels (nullptr: all on the call's stream)
 };
 
 // One segment of the attention work (device table, one entry per segment).

@@ -1136,14 +1136,38 @@ static inline unsigned grid1(long long n, int per = 256) { return (unsigned)((n 
 hipError_t launch_plan(const PlanArgs& a, PlanDev& P, hipStream_t st) {
     const int BS = P.BS, nb = P.nb, L = P.L, NS = P.NS, BH = P.BH;
     const int bkv = a.nseq * a.Hkv;
-    // K1
+    // K1 (pooling reads Q and K from HBM) runs on the auxiliary stream, when
+    // there is one, next to the VALU-bound score kernels; K4 joins it.
+    hipStream_t ps = st;
+    hipEvent_t fork = nullptr, join = nullptr;
+    hipError_t he = hipSuccess;
+    if (a.aux) {
+        he = hipEventCreateWithFlags(&fork, hipEventDisableTiming);
+        if (he == hipSuccess) he = hipEventCreateWithFlags(&join, hipEventDisableTiming);
+        if (he == hipSuccess) he = hipEventRecord(fork, st);
+        if (he == hipSuccess) he = hipStreamWaitEvent(a.aux, fork, 0);
+        if (he != hipSuccess) {
+            if (fork) (void)hipEventDestroy(fork);
+            if (join) (void)hipEventDestroy(join);
+            return he;
+        }
+        ps = a.aux;
+    }
     const unsigned pg = (unsigned)((nb + 15) / 16);
     if (a.dtype_bf16) {
-        hipLaunchKernelGGL(k_pool<bf16_t>, dim3(pg, BH), dim3(256), 0, st, (const bf16_t*)a.q, a.qs, a.Hq, P.qbar, L, BS);
-        hipLaunchKernelGGL(k_pool<bf16_t>, dim3(pg, bkv), dim3(256), 0, st, (const bf16_t*)a.k, a.ks, a.Hkv, P.kbar, L, BS);
+        hipLaunchKernelGGL(k_pool<bf16_t>, dim3(pg, BH), dim3(256), 0, ps, (const bf16_t*)a.q, a.qs, a.Hq, P.qbar, L, BS);
+        hipLaunchKernelGGL(k_pool<bf16_t>, dim3(pg, bkv), dim3(256), 0, ps, (const bf16_t*)a.k, a.ks, a.Hkv, P.kbar, L, BS);
     } else {
-        hipLaunchKernelGGL(k_pool<float>, dim3(pg, BH), dim3(256), 0, st, (const float*)a.q, a.qs, a.Hq, P.qbar, L, BS);
-        hipLaunchKernelGGL(k_pool<float>, dim3(pg, bkv), dim3(256), 0, st, (const float*)a.k, a.ks, a.Hkv, P.kbar, L, BS);
+        hipLaunchKernelGGL(k_pool<float>, dim3(pg, BH), dim3(256), 0, ps, (const float*)a.q, a.qs, a.Hq, P.qbar, L, BS);
+        hipLaunchKernelGGL(k_pool<float>, dim3(pg, bkv), dim3(256), 0, ps, (const float*)a.k, a.ks, a.Hkv, P.kbar, L, BS);
+    }
+    if (a.aux) {
+        he = hipEventRecord(join, ps);
+        (void)hipEventDestroy(fork);
+        if (he != hipSuccess) {
+            (void)hipEventDestroy(join);
+            return he;
+        }
     }
     // K2
     const dim3 gs(NS / kScoreTK, BH);
@@ -1181,6 +1205,11 @@ hipError_t launch_plan(const PlanArgs& a, PlanDev& P, hipStream_t st) {
     }
     hipLaunchKernelGGL(k_atrue, dim3(BH), dim3(256), 0, st, P.colsum, P.atrue, L, BS);
     // K4, K5
+    if (a.aux) {
+        he = hipStreamWaitEvent(st, join, 0);
+        (void)hipEventDestroy(join);
+        if (he != hipSuccess) return he;
+    }
     if (nb <= 1024) {
         const size_t lds = (size_t)8 * nb * sizeof(float);
         hipLaunchKernelGGL(k_estimate<8>, dim3((nb + 7) / 8, BH), dim3(256), lds, st, P.qbar, P.kbar, P.ahat, nb,
