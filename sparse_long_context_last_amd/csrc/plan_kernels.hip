@@ -1136,8 +1136,10 @@ static inline unsigned grid1(long long n, int per = 256) { return (unsigned)((n 
 hipError_t launch_plan(const PlanArgs& a, PlanDev& P, hipStream_t st) {
     const int BS = P.BS, nb = P.nb, L = P.L, NS = P.NS, BH = P.BH;
     const int bkv = a.nseq * a.Hkv;
-    // K1 (pooling reads Q and K from HBM) runs on the auxiliary stream, when
-    // there is one, next to the VALU-bound score kernels; K4 joins it.
+    const int group = a.Hq / a.Hkv;
+    // K1 (pooling reads Q and K from HBM) and K4 (the estimated map from the
+    // pooled vectors) run on the auxiliary stream, when there is one, next to
+    // the VALU-bound score kernels; K5 joins them.
     hipStream_t ps = st;
     hipEvent_t fork = nullptr, join = nullptr;
     hipError_t he = hipSuccess;
@@ -1161,6 +1163,16 @@ hipError_t launch_plan(const PlanArgs& a, PlanDev& P, hipStream_t st) {
         hipLaunchKernelGGL(k_pool<float>, dim3(pg, BH), dim3(256), 0, ps, (const float*)a.q, a.qs, a.Hq, P.qbar, L, BS);
         hipLaunchKernelGGL(k_pool<float>, dim3(pg, bkv), dim3(256), 0, ps, (const float*)a.k, a.ks, a.Hkv, P.kbar, L, BS);
     }
+    // K4: the estimated block map needs only the pooled vectors
+    if (nb <= 1024) {
+        const size_t lds = (size_t)8 * nb * sizeof(float);
+        hipLaunchKernelGGL(k_estimate<8>, dim3((nb + 7) / 8, BH), dim3(256), lds, ps, P.qbar, P.kbar, P.ahat, nb,
+                           a.Hq, a.Hkv, group, a.canon);
+    } else {
+        const size_t lds = (size_t)2 * nb * sizeof(float);
+        hipLaunchKernelGGL(k_estimate<2>, dim3((nb + 1) / 2, BH), dim3(256), lds, ps, P.qbar, P.kbar, P.ahat, nb,
+                           a.Hq, a.Hkv, group, a.canon);
+    }
     if (a.aux) {
         he = hipEventRecord(join, ps);
         (void)hipEventDestroy(fork);
@@ -1171,7 +1183,6 @@ hipError_t launch_plan(const PlanArgs& a, PlanDev& P, hipStream_t st) {
     }
     // K2
     const dim3 gs(NS / kScoreTK, BH);
-    const int group = a.Hq / a.Hkv;
 #define FP_SCORES(T, B_)                                                                                   \
     do {                                                                                                   \
         hipLaunchKernelGGL((k_qt<T, B_>), dim3(BH), dim3(256), 0, st, (const T*)a.q, a.qs, a.qt, L, a.Hq);  \
@@ -1204,20 +1215,11 @@ hipError_t launch_plan(const PlanArgs& a, PlanDev& P, hipStream_t st) {
                            a.canon);
     }
     hipLaunchKernelGGL(k_atrue, dim3(BH), dim3(256), 0, st, P.colsum, P.atrue, L, BS);
-    // K4, K5
+    // K5
     if (a.aux) {
         he = hipStreamWaitEvent(st, join, 0);
         (void)hipEventDestroy(join);
         if (he != hipSuccess) return he;
-    }
-    if (nb <= 1024) {
-        const size_t lds = (size_t)8 * nb * sizeof(float);
-        hipLaunchKernelGGL(k_estimate<8>, dim3((nb + 7) / 8, BH), dim3(256), lds, st, P.qbar, P.kbar, P.ahat, nb,
-                           a.Hq, a.Hkv, group, a.canon);
-    } else {
-        const size_t lds = (size_t)2 * nb * sizeof(float);
-        hipLaunchKernelGGL(k_estimate<2>, dim3((nb + 1) / 2, BH), dim3(256), lds, st, P.qbar, P.kbar, P.ahat, nb,
-                           a.Hq, a.Hkv, group, a.canon);
     }
     hipLaunchKernelGGL(k_jsd, dim3(BH), dim3(256), 0, st, P.ahat, P.atrue, P.djs, P.pattern, nb, a.tau, a.canon);
     // K6
