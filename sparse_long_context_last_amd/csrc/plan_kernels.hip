@@ -321,22 +321,32 @@ __global__ __launch_bounds__(256) void k_rowexp(const float* __restrict__ s2, co
     }
     const float M = red[0];
     const float* srow = s2 + ((size_t)bh * BS + row) * NS;
+    // the next segment's loads are in flight while the current one is summed;
+    // keys at or past L read key 0 and count as 0
+    constexpr int NU = SEG / 1024;
+    float4 buf[NU];
+#define FP_LOAD_SEG(seg_)                                                                                  \
+    _Pragma("unroll") for (int u = 0; u < NU; ++u) {                                                     \
+        const int j = (seg_) + u * 1024 + 4 * tid;                                                       \
+        buf[u] = *reinterpret_cast<const float4*>(srow + (j < L ? j : 0));                               \
+    }
+    FP_LOAD_SEG(0);
     for (int seg0 = 0; seg0 < L; seg0 += SEG) {
-#pragma unroll 4
-        for (int u = 0; u < SEG / 1024; ++u) {
+#pragma unroll
+        for (int u = 0; u < NU; ++u) {
             const int jl = u * 1024 + 4 * tid;      // 4 consecutive keys, coalesced
             const int j = seg0 + jl;
-            {
-                float4 v = j < L ? *reinterpret_cast<const float4*>(srow + j) : make_float4(0.f, 0.f, 0.f, 0.f);
-                v.x = j <= pos ? exp2_c(v.x - M, K) : 0.0f;
-                v.y = j + 1 <= pos ? exp2_c(v.y - M, K) : 0.0f;
-                v.z = j + 2 <= pos ? exp2_c(v.z - M, K) : 0.0f;
-                v.w = j + 3 <= pos ? exp2_c(v.w - M, K) : 0.0f;
-                float* e = &es[jl / BS][jl % BS];
-                e[0] = v.x; e[1] = v.y; e[2] = v.z; e[3] = v.w;
-            }
+            float4 v = buf[u];
+            const bool in = j < L;
+            v.x = in && j <= pos ? exp2_c(v.x - M, K) : 0.0f;
+            v.y = in && j + 1 <= pos ? exp2_c(v.y - M, K) : 0.0f;
+            v.z = in && j + 2 <= pos ? exp2_c(v.z - M, K) : 0.0f;
+            v.w = in && j + 3 <= pos ? exp2_c(v.w - M, K) : 0.0f;
+            float* e = &es[jl / BS][jl % BS];
+            e[0] = v.x; e[1] = v.y; e[2] = v.z; e[3] = v.w;
         }
         __syncthreads();
+        if (seg0 + SEG < L) { FP_LOAD_SEG(seg0 + SEG); }
         if (tid < kSegBlocks && seg0 + tid * BS < L) {
             float z = 0.0f;
             for (int jj = 0; jj < BS; jj += 16) {
@@ -350,6 +360,7 @@ __global__ __launch_bounds__(256) void k_rowexp(const float* __restrict__ s2, co
         }
         __syncthreads();
     }
+#undef FP_LOAD_SEG
     if (tid == 0) {
         const int nb = (L + BS - 1) / BS;
         float Z = 0.0f;
@@ -400,22 +411,39 @@ __global__ __launch_bounds__(256) void k_linesums(const float* __restrict__ s2, 
 #pragma unroll
     for (int q = 0; q < W / 256; ++q) cacc[q] = gacc[q] = 0.0f;
     const float* S = s2 + (size_t)bh * BS * NS;
+    // Each thread loads NL float4 of a chunk; the next chunk's loads are in
+    // flight while the current one is summed.  Columns at or past L read
+    // column 0 of their row and count as 0.
+    constexpr int NL = RC * TW / 4 / 256;
+    static_assert(NL * 256 * 4 == RC * TW, "chunk tiling");
+    float4 buf[NL];
+#define FP_LOAD_CHUNK(i0_)                                                                                 \
+    _Pragma("unroll") for (int n = 0; n < NL; ++n) {                                                     \
+        const int e4 = tid + 256 * n;                                                                    \
+        const int ii = e4 / (TW / 4), cc = 4 * (e4 % (TW / 4));                                          \
+        const int j = j0 + cc;                                                                           \
+        buf[n] = *reinterpret_cast<const float4*>(S + (size_t)((i0_) + ii) * NS + (j < L ? j : 0));       \
+    }
+    FP_LOAD_CHUNK(0);
     __syncthreads();
     for (int i0 = 0; i0 < BS; i0 += RC) {
-        for (int e4 = tid; e4 < RC * TW / 4; e4 += 256) {
+#pragma unroll
+        for (int n = 0; n < NL; ++n) {
+            const int e4 = tid + 256 * n;
             const int ii = e4 / (TW / 4), cc = 4 * (e4 % (TW / 4));
             const int i = i0 + ii, j = j0 + cc, pos = L - BS + i;
-            float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (j < L) v = *reinterpret_cast<const float4*>(S + (size_t)i * NS + j);
+            const float4 v = buf[n];
             const float M = sM[i];
+            const bool in = j < L;
             float4 x;
-            x.x = j <= pos ? exp2_c(v.x - M, K) : 0.0f;
-            x.y = j + 1 <= pos ? exp2_c(v.y - M, K) : 0.0f;
-            x.z = j + 2 <= pos ? exp2_c(v.z - M, K) : 0.0f;
-            x.w = j + 3 <= pos ? exp2_c(v.w - M, K) : 0.0f;
+            x.x = in && j <= pos ? exp2_c(v.x - M, K) : 0.0f;
+            x.y = in && j + 1 <= pos ? exp2_c(v.y - M, K) : 0.0f;
+            x.z = in && j + 2 <= pos ? exp2_c(v.z - M, K) : 0.0f;
+            x.w = in && j + 3 <= pos ? exp2_c(v.w - M, K) : 0.0f;
             *reinterpret_cast<float4*>(&es[ii][cc]) = x;
         }
         __syncthreads();
+        if (i0 + RC < BS) { FP_LOAD_CHUNK(i0 + RC); }
 #pragma unroll 4
         for (int ii = 0; ii < RC; ++ii) {
             const int i = i0 + ii;
@@ -431,6 +459,7 @@ __global__ __launch_bounds__(256) void k_linesums(const float* __restrict__ s2, 
         }
         __syncthreads();
     }
+#undef FP_LOAD_CHUNK
 #pragma unroll
     for (int q = 0; q < W / 256; ++q) {
         const int t = tid + 256 * q;
