@@ -10,8 +10,8 @@
 // for half of a 32-key tile, so the row softmax needs a single cross-lane
 // exchange, and the probabilities already sit in the B-operand layout of
 // O^T = V^T P^T.  V is transposed once per call ([d][N]) so that the V^T
-// A-operand reads are contiguous in LDS.  Key tiles of 64 keys are staged
-// through double-buffered LDS; grouped-query heads map to kv head
+// A-operand reads are contiguous in LDS.  Key tiles of 64 keys (32 for
+// block 64) are staged through double-buffered LDS; grouped-query heads map to kv head
 // h / (Hq / Hkv).  The stage loop is software-pipelined: the score MFMAs of
 // the next tile are interleaved with the exponentials of the current one, so
 // a wave keeps the matrix unit and the vector ALU busy at the same time.
@@ -35,16 +35,17 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 // p = exp2(s * sl - mb) for the 32 scores a lane holds, packed as bf16 in
 // the B-operand order of O^T += V^T P^T; returns the lane's sum of the
 // bf16-rounded values (the same values the numerator uses).
-__device__ __forceinline__ float exp_pack(const f32x16_t (&st)[2], float sl, float mb, bf16x8_t (&pf)[4]) {
+template <int NT>
+__device__ __forceinline__ float exp_pack(const f32x16_t (&st)[NT], float sl, float mb, bf16x8_t (&pf)[2 * NT]) {
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+    for (int t = 0; t < NT; ++t)
 #pragma unroll
         for (int r = 0; r < 16; ++r)
             pf[2 * t + (r >> 3)][r & 7] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(st[t][r], sl, -mb));
     const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
     float ls = 0.0f;
 #pragma unroll
-    for (int kc = 0; kc < 4; ++kc) {
+    for (int kc = 0; kc < 2 * NT; ++kc) {
         ls = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf[kc], pf[kc], 0, 1), ones, ls, false);
         ls = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf[kc], pf[kc], 2, 3), ones, ls, false);
         ls = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf[kc], pf[kc], 4, 5), ones, ls, false);
@@ -170,14 +171,27 @@ __device__ __forceinline__ void gather_mask(f32x16_t (&st)[2], int t, const RowI
 // ---------------------------------------------------------------------------
 // bf16 inputs, bf16 MFMA 32x32x16, fp32 accumulation and softmax
 // ---------------------------------------------------------------------------
+// Stages of KT keys: 64, except 32 for block 64 without gathered columns,
+// whose tiles then take 32 KB of LDS per workgroup, so that four two-wave
+// workgroups (two waves per SIMD) share a CU instead of two.
+template <int BS, bool GATHER>
+constexpr int attn_kt() { return BS == 64 && !GATHER ? 32 : kKT; }
+template <int BS, bool GATHER>
+constexpr int attn_wg_per_cu() { return BS == 128 || !GATHER ? 2 : 1; }
+
 template <int BS, bool SPARSE, bool GATHER>
-__global__ __launch_bounds__(2 * BS, BS == 128 ? 2 : 1) void k_attn_bf16(AttnArgs a) {
-    constexpr int D = kHeadDim, KT = kKT, NW = BS / 32, SPB = BS / KT;
+__global__ __launch_bounds__(2 * BS, (attn_wg_per_cu<BS, GATHER>())) void k_attn_bf16(AttnArgs a) {
+    constexpr int D = kHeadDim, KT = attn_kt<BS, GATHER>(), NW = BS / 32, SPB = BS / KT;
+    constexpr int NT = KT / 32;                 // 32-key score tiles per stage
+    constexpr int NMS = 8 * NT;                 // score MFMAs per stage (= exponential pairs)
+    constexpr int NMV = 4 * 2 * NT;             // P V MFMAs per stage
+    constexpr int CPR = KT / 8;                 // 16-byte chunks per V^T row
     constexpr int TILE = KT * D * 2;            // bytes of one K (or V^T) tile
     constexpr int LOADS = TILE / 1024 / NW;     // 1 KB loads into LDS per wave per tile
+    static_assert(LOADS >= 1 && TILE % (1024 * NW) == 0, "tile loads");
     // Tiles are unpadded and XOR-swizzled at 16-byte granularity:
-    //   K   [64 keys][256 B]: chunk c of row r at chunk c ^ (r & 15)
-    //   V^T [128 dv][128 B]:  chunk c of row r at chunk c ^ gray(r) & 7
+    //   K   [KT keys][256 B]:      chunk c of row r at chunk c ^ (r & 15)
+    //   V^T [128 dv][2 KT bytes]:  chunk c of row r at chunk c ^ gray(r) & (CPR - 1)
     // so that the MFMA fragment reads below hit distinct banks.
     // The tiles are four separate LDS objects and the stage loop is unrolled
     // by two, so every access names its buffer at compile time: the compiler
@@ -244,16 +258,16 @@ __global__ __launch_bounds__(2 * BS, BS == 128 ? 2 : 1) void k_attn_bf16(AttnArg
     // Per-lane source offsets of the tile loads (independent of the stage).
     // K load j of wave w covers rows 4J..4J+3 (J = w + NW j); lane -> row 4J + lane/16,
     // stored chunk lane%16 holds logical chunk (lane%16) ^ (row & 15).
-    // V^T load j covers rows 8J..8J+7; lane -> row 8J + lane/8, stored chunk lane%8
-    // holds logical chunk (lane%8) ^ gray(row) & 7.
+    // V^T load j covers rows (64/CPR) J ..; lane -> row (64/CPR) J + lane/CPR, stored
+    // chunk lane%CPR holds logical chunk (lane%CPR) ^ gray(row) & (CPR-1).
     unsigned koff[LOADS], voff[LOADS];
 #pragma unroll
     for (int j = 0; j < LOADS; ++j) {
         const int J = w + NW * j;
         const int kr = 4 * J + (lane >> 4);
         koff[j] = (unsigned)(kr * krs + 16 * ((lane & 15) ^ (kr & 15)));
-        const int vr = 8 * J + (lane >> 3);
-        voff[j] = (unsigned)((size_t)vr * vrow + 16 * ((lane & 7) ^ ((vr ^ (vr >> 1)) & 7)));
+        const int vr = (64 / CPR) * J + lane / CPR;
+        voff[j] = (unsigned)((size_t)vr * vrow + 16 * ((lane % CPR) ^ ((vr ^ (vr >> 1)) & (CPR - 1))));
     }
     // Tiles go straight from global memory to LDS (buffer loads with the
     // tile's first byte as the uniform base and the offsets above per lane).
@@ -302,7 +316,7 @@ __global__ __launch_bounds__(2 * BS, BS == 128 ? 2 : 1) void k_attn_bf16(AttnArg
 #define FP_KFRAG(B_, t_, c_) (*reinterpret_cast<const bf16x8_t*>(&B_[kfa[(c_)] + (t_) * 32 * D * 2]))
 #define FP_VFRAG(B_, T_, kc_) (*reinterpret_cast<const bf16x8_t*>(                                       \
         &B_[(32 * (T_) + l32) * KT * 2 +                                                                \
-             16 * ((2 * (kc_) + hh) ^ (((32 * (T_) + l32) ^ ((32 * (T_) + l32) >> 1)) & 7))]))
+             16 * ((2 * (kc_) + hh) ^ (((32 * (T_) + l32) ^ ((32 * (T_) + l32) >> 1)) & (CPR - 1)))]))
     // byte offset of K fragment c (contraction chunk c) of key row l32 within a
     // 32-row half tile; the half (t) and the buffer are immediate offsets
     unsigned kfa[8];
@@ -314,16 +328,16 @@ __global__ __launch_bounds__(2 * BS, BS == 128 ? 2 : 1) void k_attn_bf16(AttnArg
     // Software pipeline: stage s runs the softmax of tile s while the matrix
     // unit computes the scores of tile s + 1, then O^T += V^T P^T of tile s.
     // K tiles are fetched two stages ahead, V^T tiles one stage ahead.
-    f32x16_t scA[2], scB[2];
+    f32x16_t scA[NT], scB[NT];
     FP_FETCH_K(0, Ks0);
     FP_FETCH_V(0, Vs0);
     if (nstage > 1) { FP_FETCH_K(1, Ks1); }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
 #pragma unroll
-    for (int i = 0; i < 16; ++i)
-        scA[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(FP_KFRAG(Ks0, i & 1, i >> 1), qf[i >> 1],
-                                                             i < 2 ? zero16 : scA[i & 1], 0, 0, 0);
+    for (int i = 0; i < NMS; ++i)
+        scA[i % NT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(FP_KFRAG(Ks0, i % NT, i / NT), qf[i / NT],
+                                                              i < NT ? zero16 : scA[i % NT], 0, 0, 0);
     __syncthreads();
 
     // One stage.  The 16 score MFMAs of the next tile are interleaved with
@@ -337,24 +351,26 @@ __global__ __launch_bounds__(2 * BS, BS == 128 ? 2 : 1) void k_attn_bf16(AttnArg
         if ((s) + 2 < nstage) { FP_FETCH_K((s) + 2, KN_); }                                              \
         if ((s) + 1 < nstage) { FP_FETCH_V((s) + 1, VN_); }                                              \
         if (kb == qb) {                                                                                  \
-            _Pragma("unroll") for (int t = 0; t < 2; ++t)                                                \
+            _Pragma("unroll") for (int t = 0; t < NT; ++t)                                               \
             _Pragma("unroll") for (int r = 0; r < 16; ++r) {                                             \
                 const int krel = sub * KT + 32 * t + 8 * (r >> 2) + 4 * hh + (r & 3);                   \
                 if (krel > qrel) SC_[t][r] = -INFINITY;                                                  \
             }                                                                                            \
         }                                                                                                \
-        if (GATHER && gst) gather_mask<BS>(SC_, (s) - nsub, rid, fbits, gbias[w], gjpos[w], qb, qrow, lane, hh); \
-        bf16x8_t pf[4];                                                                                  \
+        if constexpr (GATHER) {                                                                          \
+            if (gst) gather_mask<BS>(SC_, (s) - nsub, rid, fbits, gbias[w], gjpos[w], qb, qrow, lane, hh); \
+        }                                                                                                \
+        bf16x8_t pf[2 * NT];                                                                             \
         float ls = 0.0f;                                                                                 \
         const float mb = m_run * sl;                                                                     \
         {                                                                                                \
             bf16x8_t fr[RING];                                                                           \
-            _Pragma("unroll") for (int i = 0; i < RING; ++i) fr[i] = FP_KFRAG(KC_, i & 1, i >> 1);       \
+            _Pragma("unroll") for (int i = 0; i < RING; ++i) fr[i] = FP_KFRAG(KC_, i % NT, i / NT);      \
             __builtin_amdgcn_sched_barrier(0);                                                           \
-            _Pragma("unroll") for (int i = 0; i < 16; ++i) {                                             \
-                SN_[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[i % RING], qf[i >> 1],           \
-                                                                     i < 2 ? zero16 : SN_[i & 1], 0, 0, 0); \
-                if (i + RING < 16) fr[i % RING] = FP_KFRAG(KC_, (i + RING) & 1, (i + RING) >> 1);        \
+            _Pragma("unroll") for (int i = 0; i < NMS; ++i) {                                            \
+                SN_[i % NT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[i % RING], qf[i / NT],          \
+                                                                      i < NT ? zero16 : SN_[i % NT], 0, 0, 0); \
+                if (i + RING < NMS) fr[i % RING] = FP_KFRAG(KC_, (i + RING) % NT, (i + RING) / NT);     \
                 const int t_ = i >> 3, r_ = 2 * (i & 7);                                                 \
                 const float e0_ = __builtin_amdgcn_exp2f(__builtin_fmaf(SC_[t_][r_], sl, -mb));          \
                 const float e1_ = __builtin_amdgcn_exp2f(__builtin_fmaf(SC_[t_][r_ + 1], sl, -mb));      \
@@ -367,7 +383,7 @@ __global__ __launch_bounds__(2 * BS, BS == 128 ? 2 : 1) void k_attn_bf16(AttnArg
         }                                                                                                \
         if (__ballot(!(ls <= kSumLimit)) != 0) {                                                         \
             float mx = -INFINITY;                                                                        \
-            _Pragma("unroll") for (int t = 0; t < 2; ++t)                                                \
+            _Pragma("unroll") for (int t = 0; t < NT; ++t)                                               \
             _Pragma("unroll") for (int r = 0; r < 16; ++r) mx = fmaxf(mx, SC_[t][r]);                    \
             mx = fmaxf(mx, __shfl_xor(mx, 32));                                                          \
             const float m_new = fmaxf(m_run, mx);                                                        \
@@ -383,9 +399,9 @@ __global__ __launch_bounds__(2 * BS, BS == 128 ? 2 : 1) void k_attn_bf16(AttnArg
             bf16x8_t fr[RING];                                                                           \
             _Pragma("unroll") for (int i = 0; i < RING; ++i) fr[i] = FP_VFRAG(VC_, i & 3, i >> 2);       \
             __builtin_amdgcn_sched_barrier(0);                                                           \
-            _Pragma("unroll") for (int i = 0; i < 16; ++i) {                                             \
+            _Pragma("unroll") for (int i = 0; i < NMV; ++i) {                                            \
                 o[i & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[i % RING], pf[i >> 2], o[i & 3], 0, 0, 0); \
-                if (i + RING < 16) fr[i % RING] = FP_VFRAG(VC_, (i + RING) & 3, (i + RING) >> 2);        \
+                if (i + RING < NMV) fr[i % RING] = FP_VFRAG(VC_, (i + RING) & 3, (i + RING) >> 2);       \
                 __builtin_amdgcn_sched_barrier(0);                                                       \
             }                                                                                            \
         }                                                                                                \
