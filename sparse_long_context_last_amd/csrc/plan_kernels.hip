@@ -183,16 +183,21 @@ constexpr int kScoreDS = kScoreDSConst;
 // qt[bh][t][i] = q[L-BS+i][t] (0 for rows that do not exist), so that every
 // score workgroup stages its query slices with contiguous 16-byte loads.
 template <typename T, int BS>
-__global__ __launch_bounds__(256) void k_qt(const T* __restrict__ q, TokStride qs, float* __restrict__ qt, int L,
-                                            int Hq) {
+__global__ __launch_bounds__(BS) void k_qt(const T* __restrict__ q, TokStride qs, float* __restrict__ qt, int L,
+                                           int Hq) {
     constexpr int D = kHeadDim;
-    const int bh = blockIdx.x, b = bh / Hq, h = bh % Hq;
-    const T* qhead = q + (size_t)b * qs.bst + (size_t)h * qs.hs;
-    for (int e = threadIdx.x; e < D * BS; e += 256) {
-        const int t = e % D, i = e / D;       // reads run along t (contiguous in q)
-        const int pos = L - BS + i;
-        qt[((size_t)bh * D + t) * BS + i] = pos >= 0 ? load_f32(qhead + (size_t)pos * qs.rs + t) : 0.0f;
+    const int i = threadIdx.x, t0 = 8 * blockIdx.x, bh = blockIdx.y;
+    const int b = bh / Hq, h = bh % Hq;
+    const int pos = L - BS + i;
+    float v[8];
+    if (pos >= 0) {
+        load8_f32<T>(q + (size_t)b * qs.bst + (size_t)h * qs.hs + (size_t)pos * qs.rs + t0, v);
+    } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = 0.0f;
     }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) qt[((size_t)bh * D + t0 + e) * BS + i] = v[e];
 }
 
 // Built for three waves per SIMD (at most 168 registers), which measured
@@ -1216,7 +1221,7 @@ hipError_t launch_plan(const PlanArgs& a, PlanDev& P, hipStream_t st) {
     const dim3 gs(NS / kScoreTK, BH);
 #define FP_SCORES(T, B_)                                                                                   \
     do {                                                                                                   \
-        hipLaunchKernelGGL((k_qt<T, B_>), dim3(BH), dim3(256), 0, st, (const T*)a.q, a.qs, a.qt, L, a.Hq);  \
+        hipLaunchKernelGGL((k_qt<T, B_>), dim3(kHeadDim / 8, BH), dim3(B_), 0, st, (const T*)a.q, a.qs, a.qt, L, a.Hq); \
         hipLaunchKernelGGL((k_scores<T, B_>), gs, dim3(256), 0, st, (const float*)a.qt, (const T*)a.k, a.ks, \
                            a.s2, a.pmax, L, NS, a.Hq, group, a.canon.C);                                   \
     } while (0)
