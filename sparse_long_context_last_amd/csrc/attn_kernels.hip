@@ -65,17 +65,29 @@ __device__ __forceinline__ void lds_load16(const void* base, unsigned voff, void
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Row of the work handled by workgroup `item`: head-major, query blocks
-// descending (the longest causal rows of a head first).  Workgroups are
-// dealt to the 8 XCDs round-robin by id, so every XCD works on neighbouring
-// rows of the same head at a time (their key/value tiles overlap and stay in
-// that XCD's L2) and every head's work is spread evenly over the XCDs.
-// (Grouping the query heads of one key/value head per XCD, or interleaving
-// all heads per query block, measured 1.6x-4.6x slower on the sparse 128k
-// layer: head-to-head density differences then unbalance the XCDs.)
+// Row of the work handled by workgroup `item`.  Workgroup i of a launch runs
+// on XCD i mod 8 whatever the durations (measured with the XCC_ID hardware
+// register), so the item order fixes which rows share an XCD's L2 and how
+// evenly the XCDs are loaded.
+//  - Sparse rows: head after head in the plan's head order (within every
+//    group of query heads sharing a key/value head, the heads with the most
+//    blocks first, so the launch ends on light heads, and heads reading the
+//    same key/value tiles stay adjacent); a head's query blocks descending
+//    (longest causal rows first), dealt to the XCDs in chunks of kRowChunk
+//    consecutive blocks, so the rows on one XCD share their diagonal and
+//    near-diagonal tiles.  Measured on the sparse 128k layer (block 128) and
+//    the 64k layer (block 64, 16 query heads per key/value head): chunks of 4
+//    take 1 % and 9 % off the attention time against chunks of 1.
+//  - Dense rows: the query heads of a key/value group interleaved per query
+//    block (with a rotation so every XCD sees every head), so each key/value
+//    tile is read by all heads of its group on the same XCD at about the same
+//    time (17 % faster at block 64, 1 % at block 128).
+//    Interleaving the heads of sparse rows instead measured 2x slower at 128k:
+//    heads of different patterns then compete for the L2.
 // With several segments (sequences of different lengths) the items of each
 // segment follow one another; a workgroup finds its segment by binary
 // search in the segment table.
+constexpr int kRowChunk = 4;
 struct RowId {
     int qb, L, cnt;
     size_t q0, k0, vt0;     // element offsets: token 0 of the query head, of its kv head; its V^T rows
@@ -95,9 +107,23 @@ __device__ __forceinline__ RowId work_row(const AttnArgs& a, long long item, boo
     }
     const AttnSeg sg = a.segs[lo];
     const long long local = item - sg.item0;
-    const int bh = (int)(local / sg.nb);
+    int bh, pos;
+    if (sparse) {
+        const int slot = (int)(local / sg.nb), rr = (int)(local % sg.nb);
+        bh = a.hperm ? a.hperm[sg.hoff + slot] - (int)sg.hoff : slot;
+        constexpr int C8 = 8 * kRowChunk;
+        const int blk = rr / C8, within = rr % C8;
+        pos = (blk + 1) * C8 <= sg.nb ? blk * C8 + (within % 8) * kRowChunk + within / 8 : rr;
+    } else {
+        const int G = a.Hq / a.Hkv;
+        const long long gsz = (long long)G * sg.nb;
+        const int grp = (int)(local / gsz), u = (int)(local % gsz);
+        pos = u / G;
+        const int rot = pos / (G >= 8 ? 1 : 8 / G);
+        bh = (grp / a.Hkv) * a.Hq + (grp % a.Hkv) * G + (u % G + rot) % G;
+    }
     RowId r;
-    r.qb = sg.nb - 1 - (int)(local % sg.nb);
+    r.qb = sg.nb - 1 - pos;
     r.L = sg.L;
     r.NT = sg.NT;
     const int bl = bh / a.Hq, h = bh % a.Hq, kvh = h / (a.Hq / a.Hkv);
@@ -688,6 +714,30 @@ __global__ __launch_bounds__(256) void k_transpose_v(const T* __restrict__ v, To
         }
         *reinterpret_cast<uint4*>(dst + (size_t)dd * NT + p0) = u.w;
     }
+}
+
+// Attention order of the heads: within each run of `group` consecutive heads
+// (the query heads of one key/value head of one sequence) the heads sorted by
+// their block count, most first, ties by index.  hperm[grp * group + rank] = head.
+__global__ __launch_bounds__(64) void k_head_order(const unsigned long long* __restrict__ tot, int* __restrict__ hperm,
+                                                   int group) {
+    const int base = blockIdx.x * group;
+    for (int g = threadIdx.x; g < group; g += 64) {
+        const unsigned long long t = tot[base + g];
+        int rank = 0;
+        for (int j = 0; j < group; ++j) {
+            const unsigned long long u = tot[base + j];
+            rank += (u > t || (u == t && j < g)) ? 1 : 0;
+        }
+        hperm[base + rank] = base + g;
+    }
+}
+
+hipError_t launch_head_order(const unsigned long long* total_blocks, int* hperm, int nheads, int group,
+                             hipStream_t st) {
+    if (nheads <= 0 || group <= 0 || nheads % group != 0) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(k_head_order, dim3(nheads / group), dim3(64), 0, st, total_blocks, hperm, group);
+    return hipGetLastError();
 }
 
 hipError_t launch_transpose_v(const void* v, const TokStride& vs, void* vt, int dtype_bf16, int nseq, int Hkv,

@@ -44,6 +44,7 @@ struct fp_plan {
     unsigned char* pattern;
     double* djs;
     unsigned long long* total_blocks;
+    int* hperm;                      // attention order of the heads (see launch_head_order)
     int* lists;
     int* counts;
     int* colptr;                     // token-granular columns (vs_granularity = token), else null
@@ -270,6 +271,7 @@ void attention_table(const std::vector<SegHost>& segs, int Hq, int Hkv, int bs, 
         a.goff = goff;
         a.cpoff = cpoff;
         a.cioff = cioff;
+        a.hoff = (long long)g.b0 * Hq;
         a.nseq = g.nseq;
         a.L = g.L;
         a.nb = g.nb;
@@ -343,6 +345,7 @@ fp_status attend_common(const void* q, const void* k, const void* v, void* o, fp
     if (plan) {
         a.lists = plan->lists;
         a.counts = plan->counts;
+        a.hperm = plan->hperm;
     }
     if (gather) {
         a.colptr = plan->colptr;
@@ -489,6 +492,7 @@ fp_status make_plan(const void* q, const void* k, fp_dtype dtype, int layout, in
     PALLOC(p->pattern, (BHall + 3) / 4 * 4);
     PALLOC(p->djs, BHall);
     PALLOC(p->total_blocks, BHall);
+    PALLOC(p->hperm, BHall);
     PALLOC(p->qbar, n_qbar);
     PALLOC(p->kbar, n_kbar);
     PALLOC(p->rowmax, n_rowmax);
@@ -640,6 +644,7 @@ fp_status make_plan(const void* q, const void* k, fp_dtype dtype, int layout, in
         for (int j = 0; j <= lanes; ++j)
             if (ev[j]) (void)hipEventDestroy(ev[j]);
     }
+    if (he == hipSuccess) he = launch_head_order(p->total_blocks, p->hperm, (int)BHall, Hq / Hkv, st);
     if (s2) (void)hipFreeAsync(s2, st);
     if (pmax) (void)hipFreeAsync(pmax, st);
     if (rz) (void)hipFreeAsync(rz, st);

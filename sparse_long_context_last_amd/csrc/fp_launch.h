@@ -105,6 +105,7 @@ struct AttnSeg {
     long long loff, coff; // offsets of the segment in the plan's lists and counts
     long long goff;       // element offset of the segment in the gathered-column K and V^T buffers
     long long cpoff, cioff; // offsets of the segment in colptr and colidx
+    long long hoff;       // global index (sequence * Hq + head) of the segment's first head
     int nseq;             // sequences (query heads = nseq Hq)
     int L, nb, NT;        // tokens, blocks, V^T row length nb BS
 };
@@ -122,6 +123,7 @@ struct AttnArgs {
     long long items;
     const int* lists;    // nullptr: dense causal
     const int* counts;
+    const int* hperm;    // sparse: global head order (heads of each kv group, most blocks first); nullptr: identity
     const int* colptr;   // token-granular columns (nullptr: none)
     const int* colidx;
     const void* kg;      // gathered K rows     per head [NT][d]
@@ -137,6 +139,8 @@ hipError_t launch_probe_sqrt(const double* x, double* y, long long n, hipStream_
 hipError_t launch_transpose_v(const void* v, const TokStride& vs, void* vt, int dtype_bf16, int nseq, int Hkv,
                               int L, int NT, hipStream_t st);
 hipError_t launch_attention(const AttnArgs& a, hipStream_t st);
+hipError_t launch_head_order(const unsigned long long* total_blocks, int* hperm, int nheads, int group,
+                             hipStream_t st);
 hipError_t launch_gather_cols(const void* k, const void* v, const TokStride& ks, int dtype_bf16, int nseq, int Hq,
                               int Hkv, int L, int nb, int NT, const int* colptr, const int* colidx, void* kg,
                               void* vgt, hipStream_t st);
