@@ -93,12 +93,15 @@ struct RowId {
     size_t q0, k0, vt0;     // element offsets: token 0 of the query head, of its kv head; its V^T rows
     int NT;                 // V^T row length
     const int* lst;
+    int cntB;               // two query blocks per workgroup: the block below qb (count, list)
+    const int* lstB;
     int ncol;               // token-granular columns below the row's end (gathered tiles)
     const int* gidx;        // the head's selected columns, ascending
     size_t g0;              // element offset of the head's gathered K / V^T
 };
 
-__device__ __forceinline__ RowId work_row(const AttnArgs& a, long long item, bool sparse, bool gather = false) {
+__device__ __forceinline__ RowId work_row(const AttnArgs& a, long long item, bool sparse, bool gather = false,
+                                          bool pair = false) {
     int lo = 0, hi = a.nseg - 1;
     while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
@@ -107,23 +110,25 @@ __device__ __forceinline__ RowId work_row(const AttnArgs& a, long long item, boo
     }
     const AttnSeg sg = a.segs[lo];
     const long long local = item - sg.item0;
+    // items per head: one per query block, or one per pair of query blocks
+    const int npi = sg.npi;
     int bh, pos;
     if (sparse) {
-        const int slot = (int)(local / sg.nb), rr = (int)(local % sg.nb);
+        const int slot = (int)(local / npi), rr = (int)(local % npi);
         bh = a.hperm ? a.hperm[sg.hoff + slot] - (int)sg.hoff : slot;
         constexpr int C8 = 8 * kRowChunk;
         const int blk = rr / C8, within = rr % C8;
-        pos = (blk + 1) * C8 <= sg.nb ? blk * C8 + (within % 8) * kRowChunk + within / 8 : rr;
+        pos = (blk + 1) * C8 <= npi ? blk * C8 + (within % 8) * kRowChunk + within / 8 : rr;
     } else {
         const int G = a.Hq / a.Hkv;
-        const long long gsz = (long long)G * sg.nb;
+        const long long gsz = (long long)G * npi;
         const int grp = (int)(local / gsz), u = (int)(local % gsz);
         pos = u / G;
         const int rot = pos / (G >= 8 ? 1 : 8 / G);
         bh = (grp / a.Hkv) * a.Hq + (grp % a.Hkv) * G + (u % G + rot) % G;
     }
     RowId r;
-    r.qb = sg.nb - 1 - pos;
+    r.qb = sg.nb - 1 - (pair ? 2 * pos : pos);
     r.L = sg.L;
     r.NT = sg.NT;
     const int bl = bh / a.Hq, h = bh % a.Hq, kvh = h / (a.Hq / a.Hkv);
@@ -134,9 +139,14 @@ __device__ __forceinline__ RowId work_row(const AttnArgs& a, long long item, boo
         const long long tri = (long long)sg.nb * (sg.nb + 1) / 2;
         r.cnt = a.counts[sg.coff + (long long)bh * sg.nb + r.qb];
         r.lst = a.lists + sg.loff + (long long)bh * tri + (long long)r.qb * (r.qb + 1) / 2;
+        const int qbB = r.qb - 1;
+        r.cntB = pair && qbB >= 0 ? a.counts[sg.coff + (long long)bh * sg.nb + qbB] : 0;
+        r.lstB = pair && qbB >= 0 ? a.lists + sg.loff + (long long)bh * tri + (long long)qbB * (qbB + 1) / 2 : r.lst;
     } else {
         r.cnt = r.qb + 1;
         r.lst = nullptr;
+        r.cntB = r.qb;
+        r.lstB = nullptr;
     }
     r.ncol = 0;
     r.gidx = nullptr;
@@ -200,14 +210,21 @@ __device__ __forceinline__ void gather_mask(f32x16_t (&st)[2], int t, const RowI
 // Stages of KT keys: 64, except 32 for block 64 without gathered columns,
 // whose tiles then take 32 KB of LDS per workgroup, so that four two-wave
 // workgroups (two waves per SIMD) share a CU instead of two.
-template <int BS, bool GATHER>
-constexpr int attn_kt() { return BS == 64 && !GATHER ? 32 : kKT; }
+// PAIR (block 64): one four-wave workgroup takes two neighbouring query
+// blocks of a head (waves 0-1 block qb, waves 2-3 block qb - 1) and walks the
+// union of their lists in 64-key stages: each key/value tile is loaded once
+// for 128 queries, as at block 128, and a wave pair skips the work of the
+// tiles its own list lacks.
+template <int BS, bool GATHER, bool PAIR = false>
+constexpr int attn_kt() { return BS == 64 && !GATHER && !PAIR ? 32 : kKT; }
 template <int BS, bool GATHER>
 constexpr int attn_wg_per_cu() { return BS == 128 || !GATHER ? 2 : 1; }
 
-template <int BS, bool SPARSE, bool GATHER>
-__global__ __launch_bounds__(2 * BS, (attn_wg_per_cu<BS, GATHER>())) void k_attn_bf16(AttnArgs a) {
-    constexpr int D = kHeadDim, KT = attn_kt<BS, GATHER>(), NW = BS / 32, SPB = BS / KT;
+template <int BS, bool SPARSE, bool GATHER, bool PAIR = false>
+__global__ __launch_bounds__(PAIR ? 256 : 2 * BS, (attn_wg_per_cu<BS, GATHER>())) void k_attn_bf16(AttnArgs a) {
+    static_assert(!PAIR || (BS == 64 && !GATHER), "query-block pairs: block 64, no gathered columns");
+    constexpr int D = kHeadDim, KT = attn_kt<BS, GATHER, PAIR>(), NW = PAIR ? 4 : BS / 32, SPB = BS / KT;
+    constexpr int NTH = 64 * NW;                // threads
     constexpr int NT = KT / 32;                 // 32-key score tiles per stage
     constexpr int NMS = 8 * NT;                 // score MFMAs per stage (= exponential pairs)
     constexpr int NMV = 4 * 2 * NT;             // P V MFMAs per stage
@@ -233,12 +250,20 @@ __global__ __launch_bounds__(2 * BS, (attn_wg_per_cu<BS, GATHER>())) void k_attn
     __shared__ unsigned int fbits[GATHER ? kMaxBlocks / 32 : 1];   // the row's full blocks
     __shared__ __attribute__((aligned(16))) float gbias[GATHER ? NW : 1][64];
     __shared__ __attribute__((aligned(16))) int gjpos[GATHER ? NW : 1][64];
+    // PAIR, sparse: each row's blocks as bits, the union of the two lists ascending
+    constexpr bool UNION = PAIR && SPARSE;
+    static_assert(!UNION || kMaxBlocks == 64 * 64, "one wave scans the block bitmaps");
+    __shared__ unsigned int pbits[UNION ? 2 : 1][UNION ? kMaxBlocks / 32 : 1];
+    __shared__ unsigned short ulist[UNION ? kMaxBlocks : 1];
+    __shared__ int ucnt[1];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index (uniform)
     const int l32 = lane & 31, hh = lane >> 5;
-    const RowId rid = work_row(a, blockIdx.x, SPARSE, GATHER);
-    const int qb = rid.qb, L = rid.L;
+    const RowId rid = work_row(a, blockIdx.x, SPARSE, GATHER, PAIR);
+    // PAIR: the wave's query block, -1 for the missing partner of block 0
+    const int prow = PAIR ? (w >> 1) : 0;
+    const int qb = rid.qb - prow, L = rid.L;
     const unsigned char* K = (const unsigned char*)a.k + rid.k0 * 2;
     const unsigned char* VT = (const unsigned char*)a.vt + rid.vt0 * 2;
     const size_t vrow = (size_t)rid.NT * 2;      // bytes per V^T row
@@ -252,23 +277,56 @@ __global__ __launch_bounds__(2 * BS, (attn_wg_per_cu<BS, GATHER>())) void k_attn
     const int nsub = cnt * SPB;
     // token-granular columns: 64-key tiles of the head's gathered K / V^T after the blocks
     const int ngs = GATHER ? (rid.ncol + KT - 1) / KT : 0;
-    const int nstage = nsub + ngs;
+    int nstage = nsub + ngs;
+    if constexpr (UNION) {
+        const cint_p lstB = (cint_p)rid.lstB;
+        for (int e = tid; e < 2 * kMaxBlocks / 32; e += NTH) (&pbits[0][0])[e] = 0u;
+        __syncthreads();
+        for (int e = tid; e < cnt; e += NTH) atomicOr(&pbits[0][lst[e] >> 5], 1u << (lst[e] & 31));
+        for (int e = tid; e < rid.cntB; e += NTH) atomicOr(&pbits[1][lstB[e] >> 5], 1u << (lstB[e] & 31));
+        __syncthreads();
+        if (w == 0) {
+            // lane l: blocks 64 l .. 64 l + 63; exclusive scan of the union counts
+            const unsigned u0 = pbits[0][2 * lane] | pbits[1][2 * lane];
+            const unsigned u1 = pbits[0][2 * lane + 1] | pbits[1][2 * lane + 1];
+            const int c = __popc(u0) + __popc(u1);
+            int incl = c;
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const int t = __shfl_up(incl, o);
+                if (lane >= o) incl += t;
+            }
+            int at = incl - c;
+            for (unsigned m = u0; m; m &= m - 1) ulist[at++] = (unsigned short)(64 * lane + __builtin_ctz(m));
+            for (unsigned m = u1; m; m &= m - 1) ulist[at++] = (unsigned short)(64 * lane + 32 + __builtin_ctz(m));
+            if (lane == 63) ucnt[0] = incl;
+        }
+        __syncthreads();
+        nstage = __builtin_amdgcn_readfirstlane(ucnt[0]);
+    } else if constexpr (PAIR) {
+        nstage = rid.qb + 1;
+    }
+    // key block of stage s, and whether it is in this wave's own list
+#define FP_KB(s_) (UNION ? (int)__builtin_amdgcn_readfirstlane((int)ulist[(s_)])                          \
+                         : (PAIR ? (s_) : (SPARSE ? lst[(s_) / SPB] : (s_) / SPB)))
+#define FP_MINE(kb_) (!PAIR || (UNION ? ((__builtin_amdgcn_readfirstlane(pbits[prow][(kb_) >> 5]) >> ((kb_) & 31)) & 1u) != 0 \
+                                      : (kb_) <= qb))
     const unsigned char* KG = GATHER ? (const unsigned char*)a.kg + rid.g0 * 2 : nullptr;
     const unsigned char* VGT = GATHER ? (const unsigned char*)a.vgt + rid.g0 * 2 : nullptr;
     if (GATHER && ngs > 0) {
-        for (int e = tid; e < kMaxBlocks / 32; e += 2 * BS) fbits[e] = 0u;
+        for (int e = tid; e < kMaxBlocks / 32; e += NTH) fbits[e] = 0u;
         __syncthreads();
-        for (int e = tid; e < cnt; e += 2 * BS) atomicOr(&fbits[lst[e] >> 5], 1u << (lst[e] & 31));
+        for (int e = tid; e < cnt; e += NTH) atomicOr(&fbits[lst[e] >> 5], 1u << (lst[e] & 31));
         __syncthreads();
     }
 
     // Q fragments (B operand of S^T = K Q^T): query l32 of this wave, d = 16c + 8hh + [0, 8).
     // Rows past the sequence end (a partial last block) read its last row and are not stored.
-    const int qrel = 32 * w + l32;
+    const int qrel = 32 * (PAIR ? (w & 1) : w) + l32;
     const int qrow = qb * BS + qrel;
     bf16x8_t qf[8];
     {
-        const bf16_t* qp = (const bf16_t*)a.q + rid.q0 + (size_t)min(qrow, L - 1) * a.qs.rs + 8 * hh;
+        const bf16_t* qp = (const bf16_t*)a.q + rid.q0 + (size_t)max(min(qrow, L - 1), 0) * a.qs.rs + 8 * hh;
 #pragma unroll
         for (int c = 0; c < 8; ++c) qf[c] = *reinterpret_cast<const bf16x8_t*>(qp + 16 * c);
     }
@@ -303,7 +361,7 @@ __global__ __launch_bounds__(2 * BS, (attn_wg_per_cu<BS, GATHER>())) void k_attn
 #define FP_FETCH_K(s_, KD_)                                                                              \
     {                                                                                                    \
         if (!GATHER || (s_) < nsub) {                                                                    \
-            const int kb_ = SPARSE ? lst[(s_) / SPB] : (s_) / SPB;                                      \
+            const int kb_ = FP_KB(s_);                                                                  \
             const int key0_ = kb_ * BS + ((s_) % SPB) * KT;                                             \
             const unsigned char* kg_ = K + (size_t)key0_ * krs;                                         \
             if (key0_ + KT <= L) {                                                                      \
@@ -330,7 +388,7 @@ __global__ __launch_bounds__(2 * BS, (attn_wg_per_cu<BS, GATHER>())) void k_attn
     {                                                                                                    \
         const unsigned char* vg_;                                                                        \
         if (!GATHER || (s_) < nsub) {                                                                    \
-            const int kb_ = SPARSE ? lst[(s_) / SPB] : (s_) / SPB;                                      \
+            const int kb_ = FP_KB(s_);                                                                  \
             vg_ = VT + (size_t)(kb_ * BS + ((s_) % SPB) * KT) * 2;                                      \
         } else {                                                                                         \
             vg_ = VGT + (size_t)(((s_) - nsub) * KT) * 2;                                               \
@@ -372,10 +430,13 @@ __global__ __launch_bounds__(2 * BS, (attn_wg_per_cu<BS, GATHER>())) void k_attn
 #define FP_STAGE_BF16(s, KC_, VC_, KN_, VN_, SC_, SN_)                                                   \
     {                                                                                                    \
         const bool gst = GATHER && (s) >= nsub;                                                          \
-        const int kb = gst ? -1 : (SPARSE ? lst[(s) / SPB] : (s) / SPB);                                 \
+        const int kb = gst ? -1 : FP_KB(s);                                                              \
         const int sub = (s) % SPB;                                                                       \
         if ((s) + 2 < nstage) { FP_FETCH_K((s) + 2, KN_); }                                              \
         if ((s) + 1 < nstage) { FP_FETCH_V((s) + 1, VN_); }                                              \
+        /* PAIR: a tile outside the wave's own list gets scores and exponentials */                     \
+        /* (cheap: the union exceeds each list by a few tiles) but no P V and no row sum */              \
+        const bool mS = gst || FP_MINE(kb);                                                              \
         if (kb == qb) {                                                                                  \
             _Pragma("unroll") for (int t = 0; t < NT; ++t)                                               \
             _Pragma("unroll") for (int r = 0; r < 16; ++r) {                                             \
@@ -407,21 +468,21 @@ __global__ __launch_bounds__(2 * BS, (attn_wg_per_cu<BS, GATHER>())) void k_attn
                 __builtin_amdgcn_sched_barrier(0);                                                       \
             }                                                                                            \
         }                                                                                                \
-        if (__ballot(!(ls <= kSumLimit)) != 0) {                                                         \
-            float mx = -INFINITY;                                                                        \
-            _Pragma("unroll") for (int t = 0; t < NT; ++t)                                               \
-            _Pragma("unroll") for (int r = 0; r < 16; ++r) mx = fmaxf(mx, SC_[t][r]);                    \
-            mx = fmaxf(mx, __shfl_xor(mx, 32));                                                          \
-            const float m_new = fmaxf(m_run, mx);                                                        \
-            const float alpha = fast_exp2((m_run - m_new) * sl);                                         \
-            l_run *= alpha;                                                                              \
-            _Pragma("unroll") for (int T = 0; T < 4; ++T)                                                \
-            _Pragma("unroll") for (int r = 0; r < 16; ++r) o[T][r] *= alpha;                             \
-            m_run = m_new;                                                                               \
-            ls = exp_pack(SC_, sl, m_run * sl, pf);                                                      \
-        }                                                                                                \
-        l_run += ls;                                                                                     \
-        {                                                                                                \
+        if (mS) {                                                                                        \
+            if (__ballot(!(ls <= kSumLimit)) != 0) {                                                     \
+                float mx = -INFINITY;                                                                    \
+                _Pragma("unroll") for (int t = 0; t < NT; ++t)                                           \
+                _Pragma("unroll") for (int r = 0; r < 16; ++r) mx = fmaxf(mx, SC_[t][r]);                \
+                mx = fmaxf(mx, __shfl_xor(mx, 32));                                                      \
+                const float m_new = fmaxf(m_run, mx);                                                    \
+                const float alpha = fast_exp2((m_run - m_new) * sl);                                     \
+                l_run *= alpha;                                                                          \
+                _Pragma("unroll") for (int T = 0; T < 4; ++T)                                            \
+                _Pragma("unroll") for (int r = 0; r < 16; ++r) o[T][r] *= alpha;                         \
+                m_run = m_new;                                                                           \
+                ls = exp_pack(SC_, sl, m_run * sl, pf);                                                  \
+            }                                                                                            \
+            l_run += ls;                                                                                 \
             bf16x8_t fr[RING];                                                                           \
             _Pragma("unroll") for (int i = 0; i < RING; ++i) fr[i] = FP_VFRAG(VC_, i & 3, i >> 2);       \
             __builtin_amdgcn_sched_barrier(0);                                                           \
@@ -456,6 +517,8 @@ __global__ __launch_bounds__(2 * BS, (attn_wg_per_cu<BS, GATHER>())) void k_attn
         if (s + 1 < nstage) FP_STAGE_BF16(s + 1, Ks0, Vs1, Ks1, Vs0, scB, scA);
     }
 #undef FP_STAGE_BF16
+#undef FP_KB
+#undef FP_MINE
 #undef FP_KFRAG
 #undef FP_VFRAG
 #undef FP_FETCH_K
@@ -463,7 +526,7 @@ __global__ __launch_bounds__(2 * BS, (attn_wg_per_cu<BS, GATHER>())) void k_attn
 
     const float l_tot = l_run + __shfl_xor(l_run, 32);
     const float inv = 1.0f / l_tot;
-    if (qrow >= L) return;
+    if (qb < 0 || qrow >= L) return;
     bf16_t* op = (bf16_t*)a.o + rid.q0 + (size_t)qrow * a.qs.rs;
 #pragma unroll
     for (int T = 0; T < 4; ++T)
@@ -1023,7 +1086,8 @@ static void launch_attention_t(const AttnArgs& a, hipStream_t st) {
         // workgroup per CU each row's start is not hidden), so it serves the dense path.
         if (a.BS == 128 && !SPARSE) hipLaunchKernelGGL((k_attn_pp<false>), dim3(items), dim3(512), 0, st, a);
         else if (a.BS == 128) hipLaunchKernelGGL((k_attn_bf16<128, SPARSE, GATHER>), dim3(items), dim3(256), 0, st, a);
-        else hipLaunchKernelGGL((k_attn_bf16<64, SPARSE, GATHER>), dim3(items), dim3(128), 0, st, a);
+        else if (GATHER || !a.pair) hipLaunchKernelGGL((k_attn_bf16<64, SPARSE, GATHER>), dim3(items), dim3(128), 0, st, a);
+        else hipLaunchKernelGGL((k_attn_bf16<64, SPARSE, false, true>), dim3(items), dim3(256), 0, st, a);
     } else {
         const size_t lds = (size_t)2 * (kKT * (kHeadDim + 4) + kHeadDim * (kKT + 4)) * sizeof(float);
         if (a.BS == 128) {

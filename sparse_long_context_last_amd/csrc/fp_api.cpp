@@ -254,8 +254,12 @@ hipError_t lane_streams(hipStream_t* out) {
     return hipSuccess;
 }
 
+// Whether the bf16 kernel at block 64 takes two query blocks per workgroup
+// (not with gathered token-granular columns).
+bool attention_pairs(int bs, fp_dtype dtype, bool gather) { return bs == 64 && dtype == FP_BF16 && !gather; }
+
 // The attention segment table of a problem and the V^T workspace size.
-void attention_table(const std::vector<SegHost>& segs, int Hq, int Hkv, int bs, std::vector<AttnSeg>& t,
+void attention_table(const std::vector<SegHost>& segs, int Hq, int Hkv, int bs, bool pair, std::vector<AttnSeg>& t,
                      long long& items, size_t& vt_elems, size_t& g_elems) {
     t.clear();
     items = 0;
@@ -276,9 +280,10 @@ void attention_table(const std::vector<SegHost>& segs, int Hq, int Hkv, int bs, 
         a.L = g.L;
         a.nb = g.nb;
         a.NT = g.nb * bs;
+        a.npi = pair ? (g.nb + 1) / 2 : g.nb;
         t.push_back(a);
         const long long nbh = (long long)g.nseq * Hq;
-        items += nbh * g.nb;
+        items += nbh * a.npi;
         vt += (long long)g.nseq * Hkv * kHeadDim * a.NT;
         loff += nbh * g.tri;
         coff += nbh * g.nb;
@@ -300,11 +305,12 @@ fp_status attend_common(const void* q, const void* k, const void* v, void* o, fp
     std::vector<AttnSeg> table;
     long long items = 0;
     size_t vt_elems = 0, g_elems = 0;
-    attention_table(segs, Hq, Hkv, block, table, items, vt_elems, g_elems);
+    const bool gather = plan && plan->colptr;
+    const bool pair = attention_pairs(block, dtype, gather);
+    attention_table(segs, Hq, Hkv, block, pair, table, items, vt_elems, g_elems);
     if (items == 0) return FP_OK;
     void *vt = nullptr, *kg = nullptr, *vgt = nullptr;
     AttnSeg* dtab = plan ? plan->aseg : nullptr;
-    const bool gather = plan && plan->colptr;
     FP_HIP(hipMallocAsync(&vt, vt_elems * esz, st), "hipMallocAsync (V^T)");
     hipError_t e = hipSuccess;
     if (gather) {
@@ -336,6 +342,7 @@ fp_status attend_common(const void* q, const void* k, const void* v, void* o, fp
     a.Hq = Hq;
     a.Hkv = Hkv;
     a.BS = block;
+    a.pair = pair;
     a.qs = qs;
     a.ks = ks;
     a.segs = dtab;
@@ -523,7 +530,8 @@ fp_status make_plan(const void* q, const void* k, fp_dtype dtype, int layout, in
     p->aseg = aseg;
     long long items = 0;
     size_t vt_elems = 0, g_elems = 0;
-    attention_table(segs, Hq, Hkv, block, p->aseg_host, items, vt_elems, g_elems);
+    attention_table(segs, Hq, Hkv, block, attention_pairs(block, dtype, token), p->aseg_host, items, vt_elems,
+                    g_elems);
     hipStream_t st = p->stream;
     he = hipMemcpyAsync(aseg, p->aseg_host.data(), segs.size() * sizeof(AttnSeg), hipMemcpyHostToDevice, st);
     // heads of empty sequences keep pattern 0, divergence 0 and no blocks

@@ -108,6 +108,7 @@ struct AttnSeg {
     long long hoff;       // global index (sequence * Hq + head) of the segment's first head
     int nseq;             // sequences (query heads = nseq Hq)
     int L, nb, NT;        // tokens, blocks, V^T row length nb BS
+    int npi;              // work items per head: nb, or (nb + 1) / 2 with two query blocks per item
 };
 
 struct AttnArgs {
@@ -117,6 +118,7 @@ struct AttnArgs {
     void* o;
     int dtype_bf16;
     int Hq, Hkv, BS;
+    int pair;            // two query blocks per workgroup (block 64, bf16, no gathered columns)
     TokStride qs, ks;
     const AttnSeg* segs; // device
     int nseg;
