@@ -74,10 +74,12 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 //    blocks first, so the launch ends on light heads, and heads reading the
 //    same key/value tiles stay adjacent); a head's query blocks descending
 //    (longest causal rows first), dealt to the XCDs in chunks of kRowChunk
-//    consecutive blocks, so the rows on one XCD share their diagonal and
+//    consecutive blocks (kRowChunk / 2 items when a workgroup takes a pair
+//    of blocks), so the rows on one XCD share their diagonal and
 //    near-diagonal tiles.  Measured on the sparse 128k layer (block 128) and
 //    the 64k layer (block 64, 16 query heads per key/value head): chunks of 4
-//    take 1 % and 9 % off the attention time against chunks of 1.
+//    blocks take 1 % and 9 % off the attention time against chunks of 1;
+//    chunks of 2 or 8 blocks were slower.
 //  - Dense rows: the query heads of a key/value group interleaved per query
 //    block (with a rotation so every XCD sees every head), so each key/value
 //    tile is read by all heads of its group on the same XCD at about the same
@@ -116,9 +118,9 @@ __device__ __forceinline__ RowId work_row(const AttnArgs& a, long long item, boo
     if (sparse) {
         const int slot = (int)(local / npi), rr = (int)(local % npi);
         bh = a.hperm ? a.hperm[sg.hoff + slot] - (int)sg.hoff : slot;
-        constexpr int C8 = 8 * kRowChunk;
+        const int C = pair ? kRowChunk / 2 : kRowChunk, C8 = 8 * C;   // items per chunk
         const int blk = rr / C8, within = rr % C8;
-        pos = (blk + 1) * C8 <= npi ? blk * C8 + (within % 8) * kRowChunk + within / 8 : rr;
+        pos = (blk + 1) * C8 <= npi ? blk * C8 + (within % 8) * C + within / 8 : rr;
     } else {
         const int G = a.Hq / a.Hkv;
         const long long gsz = (long long)G * npi;
