@@ -209,23 +209,20 @@ __device__ __forceinline__ void gather_mask(f32x16_t (&st)[2], int t, const RowI
 // ---------------------------------------------------------------------------
 // bf16 inputs, bf16 MFMA 32x32x16, fp32 accumulation and softmax
 // ---------------------------------------------------------------------------
-// Stages of KT keys: 64, except 32 for block 64 without gathered columns,
-// whose tiles then take 32 KB of LDS per workgroup, so that four two-wave
-// workgroups (two waves per SIMD) share a CU instead of two.
-// PAIR (block 64): one four-wave workgroup takes two neighbouring query
-// blocks of a head (waves 0-1 block qb, waves 2-3 block qb - 1) and walks the
-// union of their lists in 64-key stages: each key/value tile is loaded once
-// for 128 queries, as at block 128, and a wave pair skips the work of the
-// tiles its own list lacks.
-template <int BS, bool GATHER, bool PAIR = false>
-constexpr int attn_kt() { return BS == 64 && !GATHER && !PAIR ? 32 : kKT; }
+// Stages of 64 keys.  Block 128: one four-wave workgroup per query block, two
+// workgroups per CU.  Block 64 (PAIR): one four-wave workgroup takes two
+// neighbouring query blocks of a head (waves 0-1 block qb, waves 2-3 block
+// qb - 1) and walks the union of their lists: each key/value tile is loaded
+// once for 128 queries, as at block 128, and a wave pair skips the P V work of
+// the tiles its own list lacks.  Block 64 with gathered token columns: one
+// two-wave workgroup per query block.
 template <int BS, bool GATHER>
 constexpr int attn_wg_per_cu() { return BS == 128 || !GATHER ? 2 : 1; }
 
 template <int BS, bool SPARSE, bool GATHER, bool PAIR = false>
 __global__ __launch_bounds__(PAIR ? 256 : 2 * BS, (attn_wg_per_cu<BS, GATHER>())) void k_attn_bf16(AttnArgs a) {
     static_assert(!PAIR || (BS == 64 && !GATHER), "query-block pairs: block 64, no gathered columns");
-    constexpr int D = kHeadDim, KT = attn_kt<BS, GATHER, PAIR>(), NW = PAIR ? 4 : BS / 32, SPB = BS / KT;
+    constexpr int D = kHeadDim, KT = kKT, NW = PAIR ? 4 : BS / 32, SPB = BS / KT;
     constexpr int NTH = 64 * NW;                // threads
     constexpr int NT = KT / 32;                 // 32-key score tiles per stage
     constexpr int NMS = 8 * NT;                 // score MFMAs per stage (= exponential pairs)
@@ -1088,7 +1085,7 @@ static void launch_attention_t(const AttnArgs& a, hipStream_t st) {
         // workgroup per CU each row's start is not hidden), so it serves the dense path.
         if (a.BS == 128 && !SPARSE) hipLaunchKernelGGL((k_attn_pp<false>), dim3(items), dim3(512), 0, st, a);
         else if (a.BS == 128) hipLaunchKernelGGL((k_attn_bf16<128, SPARSE, GATHER>), dim3(items), dim3(256), 0, st, a);
-        else if (GATHER || !a.pair) hipLaunchKernelGGL((k_attn_bf16<64, SPARSE, GATHER>), dim3(items), dim3(128), 0, st, a);
+        else if constexpr (GATHER) hipLaunchKernelGGL((k_attn_bf16<64, SPARSE, true>), dim3(items), dim3(128), 0, st, a);
         else hipLaunchKernelGGL((k_attn_bf16<64, SPARSE, false, true>), dim3(items), dim3(256), 0, st, a);
     } else {
         const size_t lds = (size_t)2 * (kKT * (kHeadDim + 4) + kHeadDim * (kKT + 4)) * sizeof(float);
@@ -1105,6 +1102,9 @@ static void launch_attention_t(const AttnArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_attention(const AttnArgs& a, hipStream_t st) {
+    // bf16 at block 64 without gathered columns always runs query-block pairs;
+    // the work items must have been counted that way
+    if (a.dtype_bf16 && a.BS == 64 && !a.colptr && !a.pair) return hipErrorInvalidValue;
     if (!a.lists) launch_attention_t<false, false>(a, st);
     else if (a.colptr) launch_attention_t<true, true>(a, st);
     else launch_attention_t<true, false>(a, st);
