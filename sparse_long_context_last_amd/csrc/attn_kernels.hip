@@ -98,6 +98,7 @@ struct RowId {
     int cntB;               // two query blocks per workgroup: the block below qb (count, list)
     const int* lstB;
     int ncol;               // token-granular columns below the row's end (gathered tiles)
+    int ncolB;              // ... below the end of the block under qb (pairs)
     const int* gidx;        // the head's selected columns, ascending
     size_t g0;              // element offset of the head's gathered K / V^T
 };
@@ -151,11 +152,13 @@ __device__ __forceinline__ RowId work_row(const AttnArgs& a, long long item, boo
         r.lstB = nullptr;
     }
     r.ncol = 0;
+    r.ncolB = 0;
     r.gidx = nullptr;
     r.g0 = 0;
     if (gather) {
         const int* cp = a.colptr + sg.cpoff + (long long)bh * (sg.nb + 1);
         r.ncol = cp[r.qb + 1];
+        r.ncolB = pair && r.qb >= 1 ? cp[r.qb] : 0;
         r.gidx = a.colidx + sg.cioff + (long long)bh * sg.L;
         r.g0 = (size_t)sg.goff + (size_t)bh * kHeadDim * sg.NT;
     }
@@ -170,10 +173,11 @@ __device__ __forceinline__ RowId work_row(const AttnArgs& a, long long item, boo
 // diagonal block, their positions to its own LDS slot; every lane then adds
 // the biases of its 32 keys with 16-byte reads.
 template <int BS>
-__device__ __forceinline__ void gather_mask(f32x16_t (&st)[2], int t, const RowId& rid, const unsigned int* fbits,
-                                            float* gb, int* gj, int qb, int qrow, int lane, int hh) {
+__device__ __forceinline__ void gather_mask(f32x16_t (&st)[2], int t, const RowId& rid, int ncol,
+                                            const unsigned int* fbits, float* gb, int* gj, int qb, int qrow, int lane,
+                                            int hh) {
     const int c = 64 * t + lane;
-    const int j = c < rid.ncol ? rid.gidx[c] : -1;
+    const int j = c < ncol ? rid.gidx[c] : -1;
     const int jb = j >= 0 ? j / BS : 0;
     const bool valid = j >= 0 && !((fbits[jb >> 5] >> (jb & 31)) & 1u);
     const bool diag = valid && jb == qb;
@@ -214,14 +218,12 @@ __device__ __forceinline__ void gather_mask(f32x16_t (&st)[2], int t, const RowI
 // neighbouring query blocks of a head (waves 0-1 block qb, waves 2-3 block
 // qb - 1) and walks the union of their lists: each key/value tile is loaded
 // once for 128 queries, as at block 128, and a wave pair skips the P V work of
-// the tiles its own list lacks.  Block 64 with gathered token columns: one
-// two-wave workgroup per query block.
-template <int BS, bool GATHER>
-constexpr int attn_wg_per_cu() { return BS == 128 || !GATHER ? 2 : 1; }
-
+// the tiles its own list lacks.  With gathered token columns the pair walks
+// the column tiles of block qb and each wave masks the columns past its own
+// row.  Two workgroups per CU either way.
 template <int BS, bool SPARSE, bool GATHER, bool PAIR = false>
-__global__ __launch_bounds__(PAIR ? 256 : 2 * BS, (attn_wg_per_cu<BS, GATHER>())) void k_attn_bf16(AttnArgs a) {
-    static_assert(!PAIR || (BS == 64 && !GATHER), "query-block pairs: block 64, no gathered columns");
+__global__ __launch_bounds__(PAIR ? 256 : 2 * BS, 2) void k_attn_bf16(AttnArgs a) {
+    static_assert(!PAIR || BS == 64, "query-block pairs: block 64");
     constexpr int D = kHeadDim, KT = kKT, NW = PAIR ? 4 : BS / 32, SPB = BS / KT;
     constexpr int NTH = 64 * NW;                // threads
     constexpr int NT = KT / 32;                 // 32-key score tiles per stage
@@ -246,7 +248,7 @@ __global__ __launch_bounds__(PAIR ? 256 : 2 * BS, (attn_wg_per_cu<BS, GATHER>())
     __shared__ __attribute__((aligned(1024))) unsigned char Ks1[TILE];
     __shared__ __attribute__((aligned(1024))) unsigned char Vs0[TILE];
     __shared__ __attribute__((aligned(1024))) unsigned char Vs1[TILE];
-    __shared__ unsigned int fbits[GATHER ? kMaxBlocks / 32 : 1];   // the row's full blocks
+    __shared__ unsigned int fbits[GATHER && !PAIR ? kMaxBlocks / 32 : 1];   // the row's full blocks
     __shared__ __attribute__((aligned(16))) float gbias[GATHER ? NW : 1][64];
     __shared__ __attribute__((aligned(16))) int gjpos[GATHER ? NW : 1][64];
     // PAIR, sparse: each row's blocks as bits, the union of the two lists ascending
@@ -273,9 +275,13 @@ __global__ __launch_bounds__(PAIR ? 256 : 2 * BS, (attn_wg_per_cu<BS, GATHER>())
     // apart from the vector-memory tile loads)
     typedef const __attribute__((address_space(4))) int* cint_p;
     const cint_p lst = (cint_p)rid.lst;
-    const int nsub = cnt * SPB;
-    // token-granular columns: 64-key tiles of the head's gathered K / V^T after the blocks
+    int nsub = cnt * SPB;
+    // token-granular columns: 64-key tiles of the head's gathered K / V^T after
+    // the blocks (a pair walks those of block qb, whose columns include those
+    // of qb - 1; each wave masks the columns past its own row)
     const int ngs = GATHER ? (rid.ncol + KT - 1) / KT : 0;
+    const int ncolW = prow ? rid.ncolB : rid.ncol;
+    (void)ncolW;
     int nstage = nsub + ngs;
     if constexpr (UNION) {
         const cint_p lstB = (cint_p)rid.lstB;
@@ -301,9 +307,10 @@ __global__ __launch_bounds__(PAIR ? 256 : 2 * BS, (attn_wg_per_cu<BS, GATHER>())
             if (lane == 63) ucnt[0] = incl;
         }
         __syncthreads();
-        nstage = __builtin_amdgcn_readfirstlane(ucnt[0]);
+        nsub = __builtin_amdgcn_readfirstlane(ucnt[0]);
+        nstage = nsub + ngs;
     } else if constexpr (PAIR) {
-        nstage = rid.qb + 1;
+        nsub = nstage = rid.qb + 1;
     }
     // key block of stage s, and whether it is in this wave's own list
 #define FP_KB(s_) (UNION ? (int)__builtin_amdgcn_readfirstlane((int)ulist[(s_)])                          \
@@ -312,7 +319,7 @@ __global__ __launch_bounds__(PAIR ? 256 : 2 * BS, (attn_wg_per_cu<BS, GATHER>())
                                       : (kb_) <= qb))
     const unsigned char* KG = GATHER ? (const unsigned char*)a.kg + rid.g0 * 2 : nullptr;
     const unsigned char* VGT = GATHER ? (const unsigned char*)a.vgt + rid.g0 * 2 : nullptr;
-    if (GATHER && ngs > 0) {
+    if (GATHER && !PAIR && ngs > 0) {
         for (int e = tid; e < kMaxBlocks / 32; e += NTH) fbits[e] = 0u;
         __syncthreads();
         for (int e = tid; e < cnt; e += NTH) atomicOr(&fbits[lst[e] >> 5], 1u << (lst[e] & 31));
@@ -444,7 +451,8 @@ __global__ __launch_bounds__(PAIR ? 256 : 2 * BS, (attn_wg_per_cu<BS, GATHER>())
             }                                                                                            \
         }                                                                                                \
         if constexpr (GATHER) {                                                                          \
-            if (gst) gather_mask<BS>(SC_, (s) - nsub, rid, fbits, gbias[w], gjpos[w], qb, qrow, lane, hh); \
+            if (gst) gather_mask<BS>(SC_, (s) - nsub, rid, PAIR ? ncolW : rid.ncol, PAIR ? pbits[prow] : fbits, \
+                                     gbias[w], gjpos[w], qb, qrow, lane, hh);                            \
         }                                                                                                \
         bf16x8_t pf[2 * NT];                                                                             \
         float ls = 0.0f;                                                                                 \
@@ -674,7 +682,7 @@ __global__ __launch_bounds__(2 * BS) void k_attn_f32(AttnArgs a) {
                     if (krel > qrel) st[t][r] = -INFINITY;
                 }
         }
-        if (GATHER && gst) gather_mask<BS>(st, s - nsub, rid, fbits, gbias[w], gjpos[w], qb, qrow, lane, hh);
+        if (GATHER && gst) gather_mask<BS>(st, s - nsub, rid, rid.ncol, fbits, gbias[w], gjpos[w], qb, qrow, lane, hh);
         float mx = -INFINITY;
 #pragma unroll
         for (int t = 0; t < 2; ++t)
@@ -1085,8 +1093,7 @@ static void launch_attention_t(const AttnArgs& a, hipStream_t st) {
         // workgroup per CU each row's start is not hidden), so it serves the dense path.
         if (a.BS == 128 && !SPARSE) hipLaunchKernelGGL((k_attn_pp<false>), dim3(items), dim3(512), 0, st, a);
         else if (a.BS == 128) hipLaunchKernelGGL((k_attn_bf16<128, SPARSE, GATHER>), dim3(items), dim3(256), 0, st, a);
-        else if constexpr (GATHER) hipLaunchKernelGGL((k_attn_bf16<64, SPARSE, true>), dim3(items), dim3(128), 0, st, a);
-        else hipLaunchKernelGGL((k_attn_bf16<64, SPARSE, false, true>), dim3(items), dim3(256), 0, st, a);
+        else hipLaunchKernelGGL((k_attn_bf16<64, SPARSE, GATHER, true>), dim3(items), dim3(256), 0, st, a);
     } else {
         const size_t lds = (size_t)2 * (kKT * (kHeadDim + 4) + kHeadDim * (kKT + 4)) * sizeof(float);
         if (a.BS == 128) {
@@ -1102,9 +1109,9 @@ static void launch_attention_t(const AttnArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_attention(const AttnArgs& a, hipStream_t st) {
-    // bf16 at block 64 without gathered columns always runs query-block pairs;
-    // the work items must have been counted that way
-    if (a.dtype_bf16 && a.BS == 64 && !a.colptr && !a.pair) return hipErrorInvalidValue;
+    // bf16 at block 64 always runs query-block pairs; the work items must have
+    // been counted that way
+    if (a.dtype_bf16 && a.BS == 64 && !a.pair) return hipErrorInvalidValue;
     if (!a.lists) launch_attention_t<false, false>(a, st);
     else if (a.colptr) launch_attention_t<true, true>(a, st);
     else launch_attention_t<true, false>(a, st);
