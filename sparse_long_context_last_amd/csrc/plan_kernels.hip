@@ -172,6 +172,7 @@ __global__ __launch_bounds__(256) void k_pool(const T* __restrict__ x, TokStride
 // per-(row, 256-key chunk) maxima over causal keys (j <= L-BS+i).  Rows with
 // L-BS+i < 0 (a sequence shorter than one block) do not exist: their maxima
 // stay -inf and later kernels skip them.
+// (fp32 inputs and block 64; bf16 at block 128 runs k_scores_mfma below.)
 // Register-blocked VALU product: 256 threads, tile BS queries x 256 keys, each
 // thread owns BS/16 queries x 16 keys; d staged through LDS in slices of 32
 // (the query slices from the transposed copy k_qt writes).
@@ -286,6 +287,166 @@ __global__ __launch_bounds__(256, 3) void k_scores(const float* __restrict__ qt,
         for (int o = 8; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
         if (tx == 0) pmax[((size_t)bh * nchunks + chunk) * BS + i] = mx;
     }
+}
+
+// ---------------------------------------------------------------------------
+// K2 for bf16 inputs on the matrix unit.  v_mfma_f32_32x32x2_f32 adds its two
+// products to the accumulator one after the other, each add rounded to fp32
+// (k index 0 first): measured bit-identical to two fused multiply-adds, k = 0
+// then k = 1, over 16.8 M outputs including denormal and signed-zero cases.
+// Products of bf16 values are exact in fp32, so a chain of these MFMAs over
+// d = (0, 1), (2, 3), ... computes exactly the sequential sum of the
+// definition, at twice the fp32 rate of the vector ALU.
+// Persistent over key chunks: workgroup g of a head takes the 256-key chunks
+// g, g + P, ... (P = gridDim.x), so the block's queries are loaded into
+// registers once (wave w: 32 queries, lane l holds q[l % 32][2 t + l / 32],
+// t = 0..63).  A step covers 128 keys per wave: four 32-key tiles, four
+// independent accumulator chains.  Key tiles go from global memory straight
+// into LDS (buffer loads, 16-byte chunks XOR-swizzled by row), double
+// buffered: the next step's tile loads while this step computes.  Built for
+// two waves per SIMD.  Used at block 128 (the block-64 layers keep k_scores).
+// Same outputs as k_scores: s2 (0 past L) and the per-chunk causal row maxima.
+// Measured on the 128k layer: 1.6 ms against 1.9 ms for k_scores.  Storing a
+// step's scores during the next step's MFMAs, or two tiles per step at three
+// waves per SIMD, ran out of registers (spills) and measured slower.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void lds_copy16(const void* base, unsigned voff, void* dst) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7fffffff, 0x00020000),
+        (__attribute__((address_space(3))) void*)dst, 16, voff, 0, 0, 0);
+}
+
+template <int BS>
+__global__ __launch_bounds__(256, 2) void k_scores_mfma(const float* __restrict__ qt, const bf16_t* __restrict__ k,
+                                                        TokStride ks, float* __restrict__ s2,
+                                                        float* __restrict__ pmax, int L, int NS, int Hq, int group,
+                                                        float C) {
+    typedef float f32x16_t __attribute__((ext_vector_type(16)));
+    constexpr int D = kHeadDim, TK = kScoreTK, QG = BS / 32, KG = 4 / QG;
+    constexpr int KP = 128 * KG;                 // keys per step (all waves)
+    constexpr int SPC = TK / KP;                 // steps per 256-key chunk
+    constexpr int TILE = KP * D * 2;             // bytes of one step's keys
+    constexpr int LOADS = TILE / 1024 / 4;       // 1 KB buffer loads per wave per step
+    static_assert(QG * KG == 4 && TK % KP == 0 && LOADS >= 1, "wave layout");
+    __shared__ __attribute__((aligned(1024))) unsigned char Kb0[TILE];
+    __shared__ __attribute__((aligned(1024))) unsigned char Kb1[TILE];
+    __shared__ float red[KG][BS];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int qg = w % QG, kg = w / QG;
+    const int l32 = lane & 31, par = lane >> 5;
+    const int bh = blockIdx.y, g = blockIdx.x, P = gridDim.x;
+    const int b = bh / Hq, h = bh % Hq;
+    const int nchunks = NS / TK;
+    const int mych = g < nchunks ? (nchunks - 1 - g) / P + 1 : 0;
+    const int nst = mych * SPC;
+    if (nst == 0) return;
+    const unsigned char* kbase = (const unsigned char*)(k + (size_t)b * ks.bst + (size_t)(h / group) * ks.hs);
+    const size_t krs = (size_t)ks.rs * 2;       // bytes per key row
+
+    // queries of this wave: A operand of step t = q[i][2 t + par]
+    float qa[D / 2];
+    {
+        const float* qp = qt + (size_t)bh * D * BS + qg * 32 + l32;
+#pragma unroll
+        for (int t = 0; t < D / 2; ++t) qa[t] = qp[(size_t)(2 * t + par) * BS];
+    }
+    // key tile loads: load j of wave w covers rows 4 (w + 4 j) + lane / 16; stored
+    // 16-byte chunk lane % 16 of a row holds chunk (lane % 16) ^ (row & 15).
+    // Rows past L read row L - 1 (finite; their scores are stored as 0).
+#define FP_KLOAD(st_, KD_)                                                                                 \
+    {                                                                                                      \
+        const int key0_ = (g + P * ((st_) / SPC)) * TK + ((st_) % SPC) * KP;                               \
+        _Pragma("unroll") for (int j = 0; j < LOADS; ++j) {                                                \
+            const int r_ = 4 * (w + 4 * j) + (lane >> 4);                                                 \
+            const int kr_ = min(key0_ + r_, L - 1);                                                        \
+            lds_copy16(kbase, (unsigned)((size_t)kr_ * krs + 16 * ((lane & 15) ^ (r_ & 15))),              \
+                       &KD_[(w + 4 * j) * 1024]);                                                          \
+        }                                                                                                  \
+    }
+    // this lane's key row within the step: kg 128 + 32 q + l32; its 16-byte chunk c sits at c ^ (row & 15)
+    const int krow0 = kg * 128 + l32;
+    float mx[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx[r] = -INFINITY;
+    f32x16_t acc[4];
+
+    // one step: MFMAs over the tile in KB_ (keys key0_ ..), then the scores
+    // stored and their causal row maxima
+#define FP_SSTEP(st_, KB_, KN_)                                                                            \
+    {                                                                                                      \
+        if ((st_) + 1 < nst) { FP_KLOAD((st_) + 1, KN_); }                                                 \
+        const int key0_ = (g + P * ((st_) / SPC)) * TK + ((st_) % SPC) * KP;                               \
+        _Pragma("unroll") for (int q = 0; q < 4; ++q)                                                      \
+        _Pragma("unroll") for (int r = 0; r < 16; ++r) acc[q][r] = 0.0f;                                   \
+        _Pragma("unroll") for (int c = 0; c < D / 8; ++c) {                                                \
+            uint4 bv[4];                                                                                   \
+            _Pragma("unroll") for (int q = 0; q < 4; ++q) {                                                \
+                const int row = krow0 + 32 * q;                                                            \
+                bv[q] = *reinterpret_cast<const uint4*>(&KB_[row * 256 + 16 * (c ^ (row & 15))]);          \
+            }                                                                                              \
+            _Pragma("unroll") for (int u = 0; u < 4; ++u)                                                  \
+            _Pragma("unroll") for (int q = 0; q < 4; ++q) {                                                \
+                const unsigned wd = u == 0 ? bv[q].x : u == 1 ? bv[q].y : u == 2 ? bv[q].z : bv[q].w;      \
+                const float kb = __uint_as_float(par ? (wd & 0xffff0000u) : (wd << 16));                  \
+                acc[q] = __builtin_amdgcn_mfma_f32_32x32x2f32(qa[4 * c + u], kb, acc[q], 0, 0, 0);         \
+            }                                                                                              \
+        }                                                                                                  \
+        _Pragma("unroll") for (int q = 0; q < 4; ++q) {                                                    \
+            const int j = key0_ + kg * 128 + 32 * q + l32;                                                 \
+            _Pragma("unroll") for (int r = 0; r < 16; ++r) {                                               \
+                const int i = qg * 32 + 8 * (r >> 2) + 4 * par + (r & 3);                                  \
+                const float v_ = acc[q][r] * C;                                                            \
+                s2[((size_t)bh * BS + i) * NS + j] = j < L ? v_ : 0.0f;                                    \
+                if (j <= L - BS + i) mx[r] = fmaxf(mx[r], v_);                                             \
+            }                                                                                              \
+        }                                                                                                  \
+        if ((st_) % SPC == SPC - 1) {                                                                      \
+            /* chunk done: its row maxima */                                                               \
+            const int chunk_ = g + P * ((st_) / SPC);                                                      \
+            _Pragma("unroll") for (int r = 0; r < 16; ++r) {                                               \
+                float m_ = mx[r];                                                                          \
+                _Pragma("unroll") for (int o = 16; o >= 1; o >>= 1) m_ = fmaxf(m_, __shfl_xor(m_, o));     \
+                mx[r] = m_;                                                                                \
+            }                                                                                              \
+            if (KG == 1) {                                                                                 \
+                if (l32 == 0) {                                                                            \
+                    _Pragma("unroll") for (int r = 0; r < 16; ++r)                                         \
+                        pmax[((size_t)bh * nchunks + chunk_) * BS + qg * 32 + 8 * (r >> 2) + 4 * par + (r & 3)] = mx[r]; \
+                }                                                                                          \
+            } else {                                                                                       \
+                if (l32 == 0) {                                                                            \
+                    _Pragma("unroll") for (int r = 0; r < 16; ++r)                                         \
+                        red[kg][qg * 32 + 8 * (r >> 2) + 4 * par + (r & 3)] = mx[r];                       \
+                }                                                                                          \
+                __syncthreads();                                                                           \
+                for (int i_ = tid; i_ < BS; i_ += 256) {                                                   \
+                    float m_ = red[0][i_];                                                                 \
+                    _Pragma("unroll") for (int g2 = 1; g2 < KG; ++g2) m_ = fmaxf(m_, red[g2][i_]);         \
+                    pmax[((size_t)bh * nchunks + chunk_) * BS + i_] = m_;                                  \
+                }                                                                                          \
+            }                                                                                              \
+            _Pragma("unroll") for (int r = 0; r < 16; ++r) mx[r] = -INFINITY;                              \
+        }                                                                                                  \
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");                                                   \
+        __syncthreads();                                                                                   \
+    }
+
+    FP_KLOAD(0, Kb0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    for (int st = 0; st < nst; st += 2) {
+        FP_SSTEP(st, Kb0, Kb1);
+        if (st + 1 < nst) FP_SSTEP(st + 1, Kb1, Kb0);
+    }
+#undef FP_SSTEP
+#undef FP_KLOAD
+}
+
+// Workgroups per head for k_scores_mfma: about two per CU in all, at most one per chunk.
+inline int scores_mfma_groups(int BH, int nchunks) {
+    const int want = (2 * 256 + BH - 1) / BH;
+    return want < nchunks ? want : nchunks;
 }
 
 // ---------------------------------------------------------------------------
@@ -1222,8 +1383,13 @@ hipError_t launch_plan(const PlanArgs& a, PlanDev& P, hipStream_t st) {
 #define FP_SCORES(T, B_)                                                                                   \
     do {                                                                                                   \
         hipLaunchKernelGGL((k_qt<T, B_>), dim3(kHeadDim / 8, BH), dim3(B_), 0, st, (const T*)a.q, a.qs, a.qt, L, a.Hq); \
-        hipLaunchKernelGGL((k_scores<T, B_>), gs, dim3(256), 0, st, (const float*)a.qt, (const T*)a.k, a.ks, \
-                           a.s2, a.pmax, L, NS, a.Hq, group, a.canon.C);                                   \
+        if constexpr (sizeof(T) == 2 && B_ == 128)                                                         \
+            hipLaunchKernelGGL((k_scores_mfma<B_>), dim3(scores_mfma_groups(BH, NS / kScoreTK), BH), dim3(256), 0, \
+                               st, (const float*)a.qt, (const bf16_t*)a.k, a.ks, a.s2, a.pmax, L, NS, a.Hq, group, \
+                               a.canon.C);                                                                 \
+        else                                                                                               \
+            hipLaunchKernelGGL((k_scores<T, B_>), gs, dim3(256), 0, st, (const float*)a.qt, (const T*)a.k, a.ks, \
+                               a.s2, a.pmax, L, NS, a.Hq, group, a.canon.C);                               \
     } while (0)
     if (a.dtype_bf16) {
         if (BS == 128) FP_SCORES(bf16_t, 128); else FP_SCORES(bf16_t, 64);
