@@ -172,7 +172,7 @@ __global__ __launch_bounds__(256) void k_pool(const T* __restrict__ x, TokStride
 // per-(row, 256-key chunk) maxima over causal keys (j <= L-BS+i).  Rows with
 // L-BS+i < 0 (a sequence shorter than one block) do not exist: their maxima
 // stay -inf and later kernels skip them.
-// (fp32 inputs and block 64; bf16 at block 128 runs k_scores_mfma below.)
+// (fp32 inputs; bf16 ones run k_scores_mfma below.)
 // Register-blocked VALU product: 256 threads, tile BS queries x 256 keys, each
 // thread owns BS/16 queries x 16 keys; d staged through LDS in slices of 32
 // (the query slices from the transposed copy k_qt writes).
@@ -300,11 +300,12 @@ __global__ __launch_bounds__(256, 3) void k_scores(const float* __restrict__ qt,
 // Persistent over key chunks: workgroup g of a head takes the 256-key chunks
 // g, g + P, ... (P = gridDim.x), so the block's queries are loaded into
 // registers once (wave w: 32 queries, lane l holds q[l % 32][2 t + l / 32],
-// t = 0..63).  A step covers 128 keys per wave: four 32-key tiles, four
-// independent accumulator chains.  Key tiles go from global memory straight
+// t = 0..63).  A step covers 128 keys: at block 128 each wave takes all of
+// them (four 32-key tiles, four independent accumulator chains), at block 64
+// two waves share the queries and each takes 64 keys.  Key tiles go from global memory straight
 // into LDS (buffer loads, 16-byte chunks XOR-swizzled by row), double
 // buffered: the next step's tile loads while this step computes.  Built for
-// two waves per SIMD.  Used at block 128 (the block-64 layers keep k_scores).
+// two waves per SIMD.  Used for bf16 inputs (fp32 ones keep k_scores).
 // Same outputs as k_scores: s2 (0 past L) and the per-chunk causal row maxima.
 // Measured on the 128k layer: 1.6 ms against 1.9 ms for k_scores.  Storing a
 // step's scores during the next step's MFMAs, or two tiles per step at three
@@ -323,7 +324,8 @@ __global__ __launch_bounds__(256, 2) void k_scores_mfma(const float* __restrict_
                                                         float C) {
     typedef float f32x16_t __attribute__((ext_vector_type(16)));
     constexpr int D = kHeadDim, TK = kScoreTK, QG = BS / 32, KG = 4 / QG;
-    constexpr int KP = 128 * KG;                 // keys per step (all waves)
+    constexpr int NQ = 4 / KG;                   // 32-key tiles per wave per step
+    constexpr int KP = 32 * NQ * KG;             // keys per step (all waves): 128
     constexpr int SPC = TK / KP;                 // steps per 256-key chunk
     constexpr int TILE = KP * D * 2;             // bytes of one step's keys
     constexpr int LOADS = TILE / 1024 / 4;       // 1 KB buffer loads per wave per step
@@ -365,11 +367,11 @@ __global__ __launch_bounds__(256, 2) void k_scores_mfma(const float* __restrict_
         }                                                                                                  \
     }
     // this lane's key row within the step: kg 128 + 32 q + l32; its 16-byte chunk c sits at c ^ (row & 15)
-    const int krow0 = kg * 128 + l32;
+    const int krow0 = kg * 32 * NQ + l32;
     float mx[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) mx[r] = -INFINITY;
-    f32x16_t acc[4];
+    f32x16_t acc[NQ];
 
     // one step: MFMAs over the tile in KB_ (keys key0_ ..), then the scores
     // stored and their causal row maxima
@@ -377,23 +379,23 @@ __global__ __launch_bounds__(256, 2) void k_scores_mfma(const float* __restrict_
     {                                                                                                      \
         if ((st_) + 1 < nst) { FP_KLOAD((st_) + 1, KN_); }                                                 \
         const int key0_ = (g + P * ((st_) / SPC)) * TK + ((st_) % SPC) * KP;                               \
-        _Pragma("unroll") for (int q = 0; q < 4; ++q)                                                      \
+        _Pragma("unroll") for (int q = 0; q < NQ; ++q)                                                     \
         _Pragma("unroll") for (int r = 0; r < 16; ++r) acc[q][r] = 0.0f;                                   \
         _Pragma("unroll") for (int c = 0; c < D / 8; ++c) {                                                \
-            uint4 bv[4];                                                                                   \
-            _Pragma("unroll") for (int q = 0; q < 4; ++q) {                                                \
+            uint4 bv[NQ];                                                                                  \
+            _Pragma("unroll") for (int q = 0; q < NQ; ++q) {                                               \
                 const int row = krow0 + 32 * q;                                                            \
                 bv[q] = *reinterpret_cast<const uint4*>(&KB_[row * 256 + 16 * (c ^ (row & 15))]);          \
             }                                                                                              \
             _Pragma("unroll") for (int u = 0; u < 4; ++u)                                                  \
-            _Pragma("unroll") for (int q = 0; q < 4; ++q) {                                                \
+            _Pragma("unroll") for (int q = 0; q < NQ; ++q) {                                               \
                 const unsigned wd = u == 0 ? bv[q].x : u == 1 ? bv[q].y : u == 2 ? bv[q].z : bv[q].w;      \
                 const float kb = __uint_as_float(par ? (wd & 0xffff0000u) : (wd << 16));                  \
                 acc[q] = __builtin_amdgcn_mfma_f32_32x32x2f32(qa[4 * c + u], kb, acc[q], 0, 0, 0);         \
             }                                                                                              \
         }                                                                                                  \
-        _Pragma("unroll") for (int q = 0; q < 4; ++q) {                                                    \
-            const int j = key0_ + kg * 128 + 32 * q + l32;                                                 \
+        _Pragma("unroll") for (int q = 0; q < NQ; ++q) {                                                   \
+            const int j = key0_ + kg * 32 * NQ + 32 * q + l32;                                             \
             _Pragma("unroll") for (int r = 0; r < 16; ++r) {                                               \
                 const int i = qg * 32 + 8 * (r >> 2) + 4 * par + (r & 3);                                  \
                 const float v_ = acc[q][r] * C;                                                            \
@@ -1383,7 +1385,7 @@ hipError_t launch_plan(const PlanArgs& a, PlanDev& P, hipStream_t st) {
 #define FP_SCORES(T, B_)                                                                                   \
     do {                                                                                                   \
         hipLaunchKernelGGL((k_qt<T, B_>), dim3(kHeadDim / 8, BH), dim3(B_), 0, st, (const T*)a.q, a.qs, a.qt, L, a.Hq); \
-        if constexpr (sizeof(T) == 2 && B_ == 128)                                                         \
+        if constexpr (sizeof(T) == 2)                                                                      \
             hipLaunchKernelGGL((k_scores_mfma<B_>), dim3(scores_mfma_groups(BH, NS / kScoreTK), BH), dim3(256), 0, \
                                st, (const float*)a.qt, (const bf16_t*)a.k, a.ks, a.s2, a.pmax, L, NS, a.Hq, group, \
                                a.canon.C);                                                                 \
