@@ -243,3 +243,28 @@ def test_querywise_all_query_aware_and_ties(F):
     z = np.zeros((1, cfg.Hq, cfg.N, cfg.d), np.float32)            # uniform rows: pure tie-break
     zk = np.zeros((1, cfg.Hkv, cfg.N, cfg.d), np.float32)
     run_capped(F, cfg, z, zk, LayerGen(cfg).numpy_layer()[2], 0, qa_selection="querywise")
+
+
+def _wide_bf16(rng, shape, emin, emax):
+    """bf16-representable values with random signs, 7-bit mantissas and
+    exponents uniform in [emin, emax], as float32."""
+    e = rng.integers(emin, emax + 1, size=shape)
+    m = rng.integers(0, 128, size=shape)
+    s = np.where(rng.integers(0, 2, size=shape) == 1, -1.0, 1.0)
+    return (s * (1.0 + m / 128.0) * np.exp2(e.astype(np.float64))).astype(np.float32)
+
+
+@pytest.mark.parametrize("block", [128, 64])
+def test_wide_range_bf16_scores(F, block):
+    """bf16 inputs over a wide exponent range (every third query row and every
+    fifth key row with exponents in [-75, -64], so about 5 % of the last-block
+    dot products are denormal): the last-block statistics, divergences and
+    lists stay bit-exact."""
+    cfg = BY_NAME["llama8b_32k"].with_(Hq=2, Hkv=1, N=640, block=block, min_budget=256, gamma=0.9)
+    rng = np.random.default_rng(7)
+    q = _wide_bf16(rng, (1, cfg.Hq, cfg.N, cfg.d), -40, 6)
+    k = _wide_bf16(rng, (1, cfg.Hkv, cfg.N, cfg.d), -40, 6)
+    q[:, :, ::3, :] = _wide_bf16(rng, q[:, :, ::3, :].shape, -75, -64)
+    k[:, :, ::5, :] = _wide_bf16(rng, k[:, :, ::5, :].shape, -75, -64)
+    v = rng.standard_normal((1, cfg.Hkv, cfg.N, cfg.d)).astype(np.float32)
+    run_and_compare(F, cfg, q, k, v, attention=False, dense=False)
