@@ -4,17 +4,18 @@
 // of the atlas.scime.ai summary page).  The dense causal variant (every key
 // block 0..row) shares the kernel and is the speedup baseline.
 //
-// Layout of the work: one workgroup per (head, query block) row, BS / 32
-// waves, each wave owns 32 query rows.  Scores are computed transposed,
-// S^T = K Q^T, with the 32x32 MFMA: every lane then holds one query's scores
-// for half of a 32-key tile, so the row softmax needs a single cross-lane
-// exchange, and the probabilities already sit in the B-operand layout of
-// O^T = V^T P^T.  V is transposed once per call ([d][N]) so that the V^T
-// A-operand reads are contiguous in LDS.  Key tiles of 64 keys (32 for
-// block 64) are staged through double-buffered LDS; grouped-query heads map to kv head
-// h / (Hq / Hkv).  The stage loop is software-pipelined: the score MFMAs of
-// the next tile are interleaved with the exponentials of the current one, so
-// a wave keeps the matrix unit and the vector ALU busy at the same time.
+// Layout of the work: one four-wave workgroup per (head, query block) row at
+// block 128, per pair of neighbouring query blocks at block 64; each wave owns
+// 32 query rows.  Scores are computed transposed, S^T = K Q^T, with the 32x32
+// MFMA: every lane then holds one query's scores for half of a 32-key tile,
+// so the row softmax needs a single cross-lane exchange, and the
+// probabilities already sit in the B-operand layout of O^T = V^T P^T.  V is
+// transposed once per call ([d][N]) so that the V^T A-operand reads are
+// contiguous in LDS.  Key tiles of 64 keys are staged through double-buffered
+// LDS; grouped-query heads map to kv head h / (Hq / Hkv).  The stage loop is
+// software-pipelined: the score MFMAs of the next tile are interleaved with
+// the exponentials of the current one, so a wave keeps the matrix unit and
+// the vector ALU busy at the same time.
 #include "fp_common.h"
 #include "fp_launch.h"
 
