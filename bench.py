@@ -38,10 +38,15 @@ COUNTERS_FILE = os.path.join(ROOT, "profiles", "attention_counters_llama8b_128k.
 
 
 def kernel_source_hash() -> str:
+    """Hash of the attention kernel source without its // comments and blank
+    lines (a comment edit does not change the kernel the counters measured)."""
     h = hashlib.sha256()
     for s in ATTN_SOURCES:
-        with open(os.path.join(ROOT, "sparse_long_context_last_amd", "csrc", s), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "sparse_long_context_last_amd", "csrc", s), encoding="utf-8") as f:
+            for line in f:
+                code = line.split("//", 1)[0].rstrip()
+                if code:
+                    h.update(code.encode() + b"\n")
     return h.hexdigest()[:16]
 
 
