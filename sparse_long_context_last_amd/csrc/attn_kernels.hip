@@ -215,17 +215,17 @@ __device__ __forceinline__ void gather_mask(f32x16_t (&st)[2], int t, const RowI
 // bf16 inputs, bf16 MFMA 32x32x16, fp32 accumulation and softmax
 // ---------------------------------------------------------------------------
 // Stages of 64 keys.  Block 128: one four-wave workgroup per query block, two
-// workgroups per CU.  Block 64 (PAIR): one four-wave workgroup takes two
-// neighbouring query blocks of a head (waves 0-1 block qb, waves 2-3 block
-// qb - 1) and walks the union of their lists: each key/value tile is loaded
-// once for 128 queries, as at block 128, and a wave pair skips the P V work of
-// the tiles its own list lacks.  With gathered token columns the pair walks
-// the column tiles of block qb and each wave masks the columns past its own
-// row.  Two workgroups per CU either way.
+// workgroups per CU.  PAIR (block 64; dense rows at block 128): one workgroup
+// takes two neighbouring query blocks of a head (the first half of its waves
+// block qb, the second half block qb - 1) and walks the union of their lists:
+// each key/value tile is loaded once for twice the queries, and a wave skips
+// the P V work of the tiles its own row's list lacks.  With gathered token
+// columns the pair walks the column tiles of block qb and each wave masks the
+// columns past its own row.  Two workgroups per CU, one for the eight-wave
+// block-128 pairs.
 template <int BS, bool SPARSE, bool GATHER, bool PAIR = false>
-__global__ __launch_bounds__(PAIR ? 256 : 2 * BS, 2) void k_attn_bf16(AttnArgs a) {
-    static_assert(!PAIR || BS == 64, "query-block pairs: block 64");
-    constexpr int D = kHeadDim, KT = kKT, NW = PAIR ? 4 : BS / 32, SPB = BS / KT;
+__global__ __launch_bounds__(PAIR ? 2 * 2 * BS : 2 * BS, (PAIR && BS == 128) ? 1 : 2) void k_attn_bf16(AttnArgs a) {
+    constexpr int D = kHeadDim, KT = kKT, NW = PAIR ? 2 * (BS / 32) : BS / 32, SPB = BS / KT;
     constexpr int NTH = 64 * NW;                // threads
     constexpr int NT = KT / 32;                 // 32-key score tiles per stage
     constexpr int NMS = 8 * NT;                 // score MFMAs per stage (= exponential pairs)
@@ -264,7 +264,7 @@ __global__ __launch_bounds__(PAIR ? 256 : 2 * BS, 2) void k_attn_bf16(AttnArgs a
     const int l32 = lane & 31, hh = lane >> 5;
     const RowId rid = work_row(a, blockIdx.x, SPARSE, GATHER, PAIR);
     // PAIR: the wave's query block, -1 for the missing partner of block 0
-    const int prow = PAIR ? (w >> 1) : 0;
+    const int prow = PAIR ? (w / (BS / 32)) : 0;
     const int qb = rid.qb - prow, L = rid.L;
     const unsigned char* K = (const unsigned char*)a.k + rid.k0 * 2;
     const unsigned char* VT = (const unsigned char*)a.vt + rid.vt0 * 2;
@@ -308,14 +308,14 @@ __global__ __launch_bounds__(PAIR ? 256 : 2 * BS, 2) void k_attn_bf16(AttnArgs a
             if (lane == 63) ucnt[0] = incl;
         }
         __syncthreads();
-        nsub = __builtin_amdgcn_readfirstlane(ucnt[0]);
+        nsub = __builtin_amdgcn_readfirstlane(ucnt[0]) * SPB;
         nstage = nsub + ngs;
     } else if constexpr (PAIR) {
-        nsub = nstage = rid.qb + 1;
+        nsub = nstage = (rid.qb + 1) * SPB;
     }
     // key block of stage s, and whether it is in this wave's own list
-#define FP_KB(s_) (UNION ? (int)__builtin_amdgcn_readfirstlane((int)ulist[(s_)])                          \
-                         : (PAIR ? (s_) : (SPARSE ? lst[(s_) / SPB] : (s_) / SPB)))
+#define FP_KB(s_) (UNION ? (int)__builtin_amdgcn_readfirstlane((int)ulist[(s_) / SPB])                    \
+                         : (PAIR ? (s_) / SPB : (SPARSE ? lst[(s_) / SPB] : (s_) / SPB)))
 #define FP_MINE(kb_) (!PAIR || (UNION ? ((__builtin_amdgcn_readfirstlane(pbits[prow][(kb_) >> 5]) >> ((kb_) & 31)) & 1u) != 0 \
                                       : (kb_) <= qb))
     const unsigned char* KG = GATHER ? (const unsigned char*)a.kg + rid.g0 * 2 : nullptr;
@@ -329,7 +329,7 @@ __global__ __launch_bounds__(PAIR ? 256 : 2 * BS, 2) void k_attn_bf16(AttnArgs a
 
     // Q fragments (B operand of S^T = K Q^T): query l32 of this wave, d = 16c + 8hh + [0, 8).
     // Rows past the sequence end (a partial last block) read its last row and are not stored.
-    const int qrel = 32 * (PAIR ? (w & 1) : w) + l32;
+    const int qrel = 32 * (PAIR ? (w % (BS / 32)) : w) + l32;
     const int qrow = qb * BS + qrel;
     bf16x8_t qf[8];
     {
@@ -823,276 +823,15 @@ hipError_t launch_transpose_v(const void* v, const TokStride& vs, void* vt, int 
     return hipGetLastError();
 }
 
-// ---------------------------------------------------------------------------
-// bf16, block 128: two-group ("ping-pong") variant.  One workgroup of 8 waves
-// per (head, query block): group G = wave / 4 handles key half G (keys
-// 64G .. 64G+63) of every selected block for all 128 queries (wave w % 4
-// owns 32 of them), with its own online-softmax state; the halves are merged
-// at the end.  Workgroup barriers hold the two groups half a stage apart:
-// while one group's waves issue the MFMAs of a stage (P V of the previous
-// tile and S of the current one), the other group's waves -- one per SIMD,
-// next to them -- run the softmax of their tile, so the matrix cores and the
-// vector ALUs work at the same time.  Each group double-buffers K and V^T in
-// its own four named LDS tiles (128 KB per workgroup, one workgroup per CU);
-// a K tile is loaded two stages and a V^T tile one stage before use.
-// ---------------------------------------------------------------------------
-constexpr int kPPTile = kKT * kHeadDim * 2;   // 16 KB
-constexpr int kPPRing = 4;                    // LDS operand reads in flight ahead of the MFMAs
-__shared__ __attribute__((aligned(1024))) unsigned char pp_k00[kPPTile];
-__shared__ __attribute__((aligned(1024))) unsigned char pp_k01[kPPTile];
-__shared__ __attribute__((aligned(1024))) unsigned char pp_k10[kPPTile];
-__shared__ __attribute__((aligned(1024))) unsigned char pp_k11[kPPTile];
-__shared__ __attribute__((aligned(1024))) unsigned char pp_v00[kPPTile];
-__shared__ __attribute__((aligned(1024))) unsigned char pp_v01[kPPTile];
-__shared__ __attribute__((aligned(1024))) unsigned char pp_v10[kPPTile];
-__shared__ __attribute__((aligned(1024))) unsigned char pp_v11[kPPTile];
-__shared__ __attribute__((aligned(16))) float pp_ml[4][64][2];
-
-__device__ __forceinline__ void pp_barrier() { asm volatile("s_barrier" ::: "memory"); }
-
-struct PPState {
-    bf16x8_t qf[8];
-    f32x16_t o[4];
-    f32x16_t st[2];
-    bf16x8_t pf[4];
-    float m_run, l_run;
-};
-
-template <int G, bool SPARSE>
-__device__ __forceinline__ void pp_group(PPState& S, const AttnArgs& a, const RowId& rid,
-                                         const __attribute__((address_space(4))) int* lst, int n, int qw, int lane) {
-    constexpr int D = kHeadDim, KT = kKT, BS = 128, LOADS = kPPTile / 1024 / 4;
-    unsigned char* const Kb0 = G ? pp_k10 : pp_k00;
-    unsigned char* const Kb1 = G ? pp_k11 : pp_k01;
-    unsigned char* const Vb0 = G ? pp_v10 : pp_v00;
-    unsigned char* const Vb1 = G ? pp_v11 : pp_v01;
-    const int l32 = lane & 31, hh = lane >> 5;
-    const int qb = rid.qb, L = rid.L;
-    const int qrel = 32 * qw + l32;
-    const unsigned char* K = (const unsigned char*)a.k + rid.k0 * 2;
-    const unsigned char* VT = (const unsigned char*)a.vt + rid.vt0 * 2;
-    const size_t vrow = (size_t)rid.NT * 2;
-    const size_t krs = (size_t)a.ks.rs * 2;
-    const float sl = a.scale_log2;
-    unsigned koff[LOADS], voff[LOADS];
-#pragma unroll
-    for (int j = 0; j < LOADS; ++j) {
-        const int J = qw + 4 * j;
-        const int kr = 4 * J + (lane >> 4);
-        koff[j] = (unsigned)(kr * krs + 16 * ((lane & 15) ^ (kr & 15)));
-        const int vr = 8 * J + (lane >> 3);
-        voff[j] = (unsigned)((size_t)vr * vrow + 16 * ((lane & 7) ^ ((vr ^ (vr >> 1)) & 7)));
-    }
-#define PP_KEY0(t_) ((SPARSE ? lst[(t_)] : (t_)) * BS + 64 * G)
-#define PP_FETCH_K(t_, KD_)                                                                              \
-    {                                                                                                    \
-        const int key0_ = PP_KEY0(t_);                                                                   \
-        const unsigned char* kg_ = K + (size_t)key0_ * krs;                                             \
-        if (key0_ + KT <= L) {                                                                          \
-            _Pragma("unroll") for (int j = 0; j < LOADS; ++j)                                           \
-                lds_load16(kg_, koff[j], &KD_[(qw + 4 * j) * 1024]);                                    \
-        } else {                                                                                        \
-            _Pragma("unroll") for (int j = 0; j < LOADS; ++j) {                                         \
-                const int kr_ = 4 * (qw + 4 * j) + (lane >> 4);                                         \
-                const unsigned o_ = (unsigned)((min(key0_ + kr_, L - 1) - key0_) * krs) +               \
-                                    16u * ((lane & 15) ^ (kr_ & 15));                                   \
-                lds_load16(kg_, o_, &KD_[(qw + 4 * j) * 1024]);                                         \
-            }                                                                                           \
-        }                                                                                                \
-    }
-#define PP_FETCH_V(t_, VD_)                                                                              \
-    {                                                                                                    \
-        const unsigned char* vg_ = VT + (size_t)PP_KEY0(t_) * 2;                                        \
-        _Pragma("unroll") for (int j = 0; j < LOADS; ++j)                                               \
-            lds_load16(vg_, voff[j], &VD_[(qw + 4 * j) * 1024]);                                        \
-    }
-    // An MFMA block reads 16 operand fragments from LDS and issues 16 MFMAs.
-    // The reads run kPPRing ahead of the MFMAs through a ring of fragment
-    // registers (scheduling fences keep that order), so each MFMA finds its
-    // operand loaded instead of waiting for a read issued just before it.
-#define PP_VFRAG(B_, i_) (*reinterpret_cast<const bf16x8_t*>(                                           \
-        &B_[(32 * ((i_) >> 2) + l32) * KT * 2 +                                                         \
-             16 * ((2 * ((i_) & 3) + hh) ^ (((32 * ((i_) >> 2) + l32) ^ ((32 * ((i_) >> 2) + l32) >> 1)) & 7))]))
-#define PP_KFRAG(B_, i_) (*reinterpret_cast<const bf16x8_t*>(                                           \
-        &B_[(32 * ((i_) >> 3) + l32) * D * 2 + 16 * ((2 * ((i_) & 7) + hh) ^ ((32 * ((i_) >> 3) + l32) & 15))]))
-    // M phase of stage t_: S^T(t_) = K(t_) Q^T, then O^T += V^T(t_-1) P^T(t_-1)
-#define PP_PHASE_M(t_, KC_, VP_)                                                                         \
-    {                                                                                                    \
-        __builtin_amdgcn_s_setprio(1);                                                                   \
-        bf16x8_t fr_[kPPRing];                                                                           \
-        /* S first: the softmax of the next phase reads it, while the P V            */                  \
-        /* accumulation issued after it completes underneath that softmax.           */                  \
-        if ((t_) < n) {                                                                                  \
-            _Pragma("unroll") for (int t = 0; t < 2; ++t)                                                \
-            _Pragma("unroll") for (int r = 0; r < 16; ++r) S.st[t][r] = 0.0f;                            \
-            _Pragma("unroll") for (int i = 0; i < kPPRing; ++i) fr_[i] = PP_KFRAG(KC_, i);               \
-            __builtin_amdgcn_sched_barrier(0);                                                           \
-            _Pragma("unroll") for (int i = 0; i < 16; ++i) {                                             \
-                S.st[i >> 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr_[i % kPPRing], S.qf[i & 7], S.st[i >> 3], 0, 0, 0); \
-                if (i + kPPRing < 16) fr_[i % kPPRing] = PP_KFRAG(KC_, i + kPPRing);                     \
-                __builtin_amdgcn_sched_barrier(0);                                                       \
-            }                                                                                            \
-        }                                                                                                \
-        if ((t_) >= 1) {                                                                                 \
-            _Pragma("unroll") for (int i = 0; i < kPPRing; ++i) fr_[i] = PP_VFRAG(VP_, i);               \
-            __builtin_amdgcn_sched_barrier(0);                                                           \
-            _Pragma("unroll") for (int i = 0; i < 16; ++i) {                                             \
-                S.o[i >> 2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr_[i % kPPRing], S.pf[i & 3], S.o[i >> 2], 0, 0, 0); \
-                if (i + kPPRing < 16) fr_[i % kPPRing] = PP_VFRAG(VP_, i + kPPRing);                     \
-                __builtin_amdgcn_sched_barrier(0);                                                       \
-            }                                                                                            \
-        }                                                                                                \
-        __builtin_amdgcn_s_setprio(0);                                                                   \
-    }
-    // V phase of stage t_: loads of K(t_+2) into KN_ and V^T(t_+1) into VN_,
-    // softmax of S(t_) into P(t_); then waits for the tiles the next M phase reads
-#define PP_PHASE_V(t_, KN_, VN_)                                                                         \
-    {                                                                                                    \
-        /* past the row's end the last tile is loaded again (unused): every V */                        \
-        /* phase issues the same loads, so every wait count is fixed           */                        \
-        PP_FETCH_K(min((t_) + 2, n - 1), KN_);                                                           \
-        PP_FETCH_V(min((t_) + 1, n - 1), VN_);                                                           \
-        const int kb_ = SPARSE ? lst[(t_)] : (t_);                                                       \
-        if (kb_ == qb) {                                                                                 \
-            _Pragma("unroll") for (int t = 0; t < 2; ++t)                                                \
-            _Pragma("unroll") for (int r = 0; r < 16; ++r) {                                             \
-                const int krel = 64 * G + 32 * t + 8 * (r >> 2) + 4 * hh + (r & 3);                      \
-                if (krel > qrel) S.st[t][r] = -INFINITY;                                                 \
-            }                                                                                            \
-        }                                                                                                \
-        float ls = 0.0f;                                                                                 \
-        bool exact = (t_) == 0;                                                                          \
-        if (!exact) {                                                                                    \
-            ls = exp_pack(S.st, sl, S.m_run * sl, S.pf);                                                 \
-            exact = __ballot(!(ls <= kSumLimit)) != 0;                                                   \
-        }                                                                                                \
-        if (exact) {                                                                                     \
-            float mx = -INFINITY;                                                                        \
-            _Pragma("unroll") for (int t = 0; t < 2; ++t)                                                \
-            _Pragma("unroll") for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S.st[t][r]);                   \
-            mx = fmaxf(mx, __shfl_xor(mx, 32));                                                          \
-            const float m_new = fmaxf(S.m_run, mx);                                                      \
-            const bool none_ = m_new == -INFINITY;   /* every key of this half masked so far */         \
-            const float alpha = none_ ? 1.0f : fast_exp2((S.m_run - m_new) * sl);                        \
-            S.l_run *= alpha;                                                                            \
-            _Pragma("unroll") for (int T = 0; T < 4; ++T)                                                \
-            _Pragma("unroll") for (int r = 0; r < 16; ++r) S.o[T][r] *= alpha;                           \
-            S.m_run = m_new;                                                                             \
-            ls = exp_pack(S.st, sl, none_ ? 0.0f : m_new * sl, S.pf);                                    \
-        }                                                                                                \
-        S.l_run += ls;                                                                                   \
-        asm volatile("s_waitcnt vmcnt(8)" ::: "memory");                                                 \
-    }
-    static_assert(LOADS == 4, "the V-phase waits count 4 loads per tile");
-
-    // prologue: K(0), K(1), V^T(0)
-    PP_FETCH_K(0, Kb0);
-    if (n > 1) PP_FETCH_K(1, Kb1);
-    PP_FETCH_V(0, Vb0);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    // Phase barriers are bare s_barrier: every wave has already waited for
-    // the loads the next phase reads (the V-phase waits above), and a
-    // workgroup fence here would also wait for the tiles still in flight.
-    // The memory clobber keeps the compiler from moving LDS accesses across.
-    if (G == 1) pp_barrier();             // group 1 starts half a stage later
-    for (int t = 0;; t += 2) {
-        PP_PHASE_M(t, Kb0, Vb1);
-        pp_barrier();
-        if (t == n) break;
-        PP_PHASE_V(t, Kb0, Vb1);
-        pp_barrier();
-        PP_PHASE_M(t + 1, Kb1, Vb0);
-        pp_barrier();
-        if (t + 1 == n) break;
-        PP_PHASE_V(t + 1, Kb1, Vb0);
-        pp_barrier();
-    }
-    if (G == 0) pp_barrier();             // ... and group 0 ends half a stage earlier
-#undef PP_KEY0
-#undef PP_FETCH_K
-#undef PP_FETCH_V
-#undef PP_PHASE_M
-#undef PP_PHASE_V
-#undef PP_VFRAG
-#undef PP_KFRAG
-}
-
-template <bool SPARSE>
-__global__ __launch_bounds__(512, 1) void k_attn_pp(AttnArgs a) {
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int G = w >> 2, qw = w & 3;
-    const int l32 = lane & 31, hh = lane >> 5;
-    const RowId rid = work_row(a, blockIdx.x, SPARSE);
-    const int qb = rid.qb, L = rid.L;
-    typedef const __attribute__((address_space(4))) int* cint_p;
-    const cint_p lst = (cint_p)rid.lst;
-    const int n = rid.cnt;             // stages per group: one key half of every block
-    const int qrow = qb * 128 + 32 * qw + l32;
-
-    PPState S;
-    {
-        const bf16_t* qp = (const bf16_t*)a.q + rid.q0 + (size_t)min(qrow, L - 1) * a.qs.rs + 8 * hh;
-#pragma unroll
-        for (int c = 0; c < 8; ++c) S.qf[c] = *reinterpret_cast<const bf16x8_t*>(qp + 16 * c);
-    }
-#pragma unroll
-    for (int T = 0; T < 4; ++T)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) S.o[T][r] = 0.0f;
-    S.m_run = -INFINITY;
-    S.l_run = 0.0f;
-    if (G == 0) pp_group<0, SPARSE>(S, a, rid, lst, n, qw, lane);
-    else pp_group<1, SPARSE>(S, a, rid, lst, n, qw, lane);
-
-    // merge the two key halves: group 1 hands its partial state over LDS
-    // (its O^T into one of the K tiles per wave, 16 KB each)
-    unsigned char* xo = qw == 0 ? pp_k00 : qw == 1 ? pp_k01 : qw == 2 ? pp_k10 : pp_k11;
-    if (G == 1) {
-#pragma unroll
-        for (int T = 0; T < 4; ++T)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                f32x4_t v = {S.o[T][4 * i], S.o[T][4 * i + 1], S.o[T][4 * i + 2], S.o[T][4 * i + 3]};
-                *reinterpret_cast<f32x4_t*>(xo + ((4 * T + i) * 64 + lane) * 16) = v;
-            }
-        pp_ml[qw][lane][0] = S.m_run;
-        pp_ml[qw][lane][1] = S.l_run;
-    }
-    __syncthreads();
-    if (G == 1 || qrow >= L) return;
-    const float sl = a.scale_log2;
-    const float m1 = pp_ml[qw][lane][0], l1 = pp_ml[qw][lane][1];
-    const float m = fmaxf(S.m_run, m1);
-    const float a0 = fast_exp2((S.m_run - m) * sl);
-    const float a1 = m1 == -INFINITY ? 0.0f : fast_exp2((m1 - m) * sl);
-    const float lsum = S.l_run * a0 + l1 * a1;
-    const float inv = 1.0f / (lsum + __shfl_xor(lsum, 32));
-    bf16_t* op = (bf16_t*)a.o + rid.q0 + (size_t)qrow * a.qs.rs;
-#pragma unroll
-    for (int T = 0; T < 4; ++T)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const f32x4_t v1 = *reinterpret_cast<const f32x4_t*>(xo + ((4 * T + i) * 64 + lane) * 16);
-            const int dv = 32 * T + 8 * i + 4 * hh;
-            ushort4 pk;
-            pk.x = f32_to_bf16((S.o[T][4 * i] * a0 + v1[0] * a1) * inv);
-            pk.y = f32_to_bf16((S.o[T][4 * i + 1] * a0 + v1[1] * a1) * inv);
-            pk.z = f32_to_bf16((S.o[T][4 * i + 2] * a0 + v1[2] * a1) * inv);
-            pk.w = f32_to_bf16((S.o[T][4 * i + 3] * a0 + v1[3] * a1) * inv);
-            *reinterpret_cast<ushort4*>(op + dv) = pk;
-        }
-}
-
 template <bool SPARSE, bool GATHER>
 static void launch_attention_t(const AttnArgs& a, hipStream_t st) {
     const unsigned items = (unsigned)a.items;
     if (a.dtype_bf16) {
-        // The two-group kernel measured faster on dense causal rows (long, contiguous key
-        // ranges) and slower on the sparse selections (shorter, scattered rows: with one
-        // workgroup per CU each row's start is not hidden), so it serves the dense path.
-        if (a.BS == 128 && !SPARSE) hipLaunchKernelGGL((k_attn_pp<false>), dim3(items), dim3(512), 0, st, a);
+        // Dense rows at block 128 also run in pairs (an eight-wave workgroup, one
+        // per CU): 4-5 % faster than one row per workgroup there, while on the
+        // sparse selections the pairs' list unions cost more than the shared
+        // tile loads save.
+        if (a.BS == 128 && !SPARSE) hipLaunchKernelGGL((k_attn_bf16<128, false, false, true>), dim3(items), dim3(512), 0, st, a);
         else if (a.BS == 128) hipLaunchKernelGGL((k_attn_bf16<128, SPARSE, GATHER>), dim3(items), dim3(256), 0, st, a);
         else hipLaunchKernelGGL((k_attn_bf16<64, SPARSE, GATHER, true>), dim3(items), dim3(256), 0, st, a);
     } else {
@@ -1110,9 +849,9 @@ static void launch_attention_t(const AttnArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_attention(const AttnArgs& a, hipStream_t st) {
-    // bf16 at block 64 always runs query-block pairs; the work items must have
-    // been counted that way
-    if (a.dtype_bf16 && a.BS == 64 && !a.pair) return hipErrorInvalidValue;
+    // bf16 at block 64, and bf16 dense rows, run query-block pairs; the work
+    // items must have been counted that way
+    if (a.dtype_bf16 && (a.BS == 64 || !a.lists) && !a.pair) return hipErrorInvalidValue;
     if (!a.lists) launch_attention_t<false, false>(a, st);
     else if (a.colptr) launch_attention_t<true, true>(a, st);
     else launch_attention_t<true, false>(a, st);

@@ -254,8 +254,9 @@ hipError_t lane_streams(hipStream_t* out) {
     return hipSuccess;
 }
 
-// Whether the attention kernel takes two query blocks per workgroup (bf16 at block 64).
-bool attention_pairs(int bs, fp_dtype dtype) { return bs == 64 && dtype == FP_BF16; }
+// Whether the attention kernel takes two query blocks per workgroup: bf16 at
+// block 64, and bf16 dense causal rows at any block.
+bool attention_pairs(int bs, fp_dtype dtype, bool dense) { return dtype == FP_BF16 && (bs == 64 || dense); }
 
 // The attention segment table of a problem and the V^T workspace size.
 void attention_table(const std::vector<SegHost>& segs, int Hq, int Hkv, int bs, bool pair, std::vector<AttnSeg>& t,
@@ -305,7 +306,7 @@ fp_status attend_common(const void* q, const void* k, const void* v, void* o, fp
     long long items = 0;
     size_t vt_elems = 0, g_elems = 0;
     const bool gather = plan && plan->colptr;
-    const bool pair = attention_pairs(block, dtype);
+    const bool pair = attention_pairs(block, dtype, plan == nullptr);
     attention_table(segs, Hq, Hkv, block, pair, table, items, vt_elems, g_elems);
     if (items == 0) return FP_OK;
     void *vt = nullptr, *kg = nullptr, *vgt = nullptr;
@@ -529,7 +530,8 @@ fp_status make_plan(const void* q, const void* k, fp_dtype dtype, int layout, in
     p->aseg = aseg;
     long long items = 0;
     size_t vt_elems = 0, g_elems = 0;
-    attention_table(segs, Hq, Hkv, block, attention_pairs(block, dtype), p->aseg_host, items, vt_elems, g_elems);
+    attention_table(segs, Hq, Hkv, block, attention_pairs(block, dtype, false), p->aseg_host, items, vt_elems,
+                    g_elems);
     hipStream_t st = p->stream;
     he = hipMemcpyAsync(aseg, p->aseg_host.data(), segs.size() * sizeof(AttnSeg), hipMemcpyHostToDevice, st);
     // heads of empty sequences keep pattern 0, divergence 0 and no blocks

@@ -118,7 +118,7 @@ struct AttnArgs {
     void* o;
     int dtype_bf16;
     int Hq, Hkv, BS;
-    int pair;            // two query blocks per workgroup (block 64, bf16)
+    int pair;            // two query blocks per workgroup (bf16: block 64, and dense rows)
     TokStride qs, ks;
     const AttnSeg* segs; // device
     int nseg;
