@@ -59,7 +59,9 @@ within a few ulp; JSD against scipy and closed forms; canonical softmax
 statistics, pooling and the estimate against float64 library computations;
 selection against brute force over all subsets; the block conversion
 against a token-level mask; attention against torch's scaled-dot-product
-attention (gamma = 1) and a per-token brute force.  Parity unpinned: that
+attention (gamma = 1) and a per-token brute force; hand-worked selections,
+line-to-block conversions and divergences stored under ``tests/golden/``.
+Parity unpinned: that
 the conventions above are the authors' own rules -- the pages print no
 formulas, listings or intermediate values to check them against.
 """
