@@ -1303,10 +1303,25 @@ __global__ __launch_bounds__(256) void k_lists(PlanDev P, const SelState* __rest
         if (f) out[written + __popcll(m & ((1ull << lane) - 1ull))] = kb;
         written += __popcll(m);
     }
-    if (lane == 0) {
-        P.counts[(size_t)bh * P.nb + qb] = written;
-        atomicAdd(&P.total_blocks[bh], (unsigned long long)written);
+    if (lane == 0) P.counts[(size_t)bh * P.nb + qb] = written;
+}
+
+// Per-head block totals from the rows' counts, one workgroup per head (a
+// per-row atomic add into one counter per head serialised about 1000 adds
+// on each address).
+__global__ __launch_bounds__(256) void k_head_totals(const int* __restrict__ counts,
+                                                     unsigned long long* __restrict__ tot, int nb) {
+    __shared__ unsigned long long red[256];
+    const int bh = blockIdx.x, tid = threadIdx.x;
+    unsigned long long s = 0ull;
+    for (int r = tid; r < nb; r += 256) s += (unsigned long long)counts[(size_t)bh * nb + r];
+    red[tid] = s;
+    __syncthreads();
+    for (int o = 128; o > 0; o >>= 1) {
+        if (tid < o) red[tid] += red[tid + o];
+        __syncthreads();
     }
+    if (tid == 0) tot[bh] = red[0];
 }
 
 __global__ __launch_bounds__(256) void k_fill_u32(unsigned int* __restrict__ p, unsigned int v, long long n) {
@@ -1448,9 +1463,8 @@ hipError_t launch_plan(const PlanArgs& a, PlanDev& P, hipStream_t st) {
         if (!P.mode_all) hipLaunchKernelGGL(k_col_compact, dim3(nb, BH), dim3(BS), 0, st, P, P.sel);
     }
     // K7
-    hipLaunchKernelGGL(k_fill_u32, dim3(grid1(2LL * BH)), dim3(256), 0, st, (unsigned int*)P.total_blocks, 0u,
-                       2LL * BH);
     hipLaunchKernelGGL(k_lists, dim3((nb + 3) / 4, BH), dim3(256), 0, st, P, P.sel);
+    hipLaunchKernelGGL(k_head_totals, dim3(BH), dim3(256), 0, st, P.counts, P.total_blocks, nb);
     return hipGetLastError();
 }
 
