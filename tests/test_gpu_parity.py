@@ -73,6 +73,9 @@ SMALL = {
     # 9 blocks: the score kernel's last 256-key chunk is half full
     "ragged_bf16_1152": BY_NAME["llama8b_32k"].with_(Hq=4, Hkv=1, N=1152, min_budget=256,
                                                       explicit_types=("V", "S", "QA", "N")),
+    # block 128, 9 blocks, two batches of GQA 2:1 (head orders and row pairs across sequences)
+    "gqa_bf16_1152_b2": BY_NAME["llama8b_32k"].with_(B=2, Hq=4, Hkv=2, N=1152, min_budget=256,
+                                                      explicit_types=("N", "QA", "V", "S")),
     # block 64, 17 blocks, two batches
     "bs64_bf16_1088_b2": BY_NAME["glm9b_64k_bs64"].with_(B=2, Hq=4, Hkv=2, N=1088, min_budget=256,
                                                           explicit_types=("QA", "V", "S", "N")),
