@@ -300,12 +300,16 @@ __global__ __launch_bounds__(256, 3) void k_scores(const float* __restrict__ qt,
 // Persistent over key chunks: workgroup g of a head takes the 256-key chunks
 // g, g + P, ... (P = gridDim.x), so the block's queries are loaded into
 // registers once (wave w: 32 queries, lane l holds q[l % 32][2 t + l / 32],
-// t = 0..63).  A step covers 128 keys: at block 128 each wave takes all of
-// them (four 32-key tiles, four independent accumulator chains), at block 64
-// two waves share the queries and each takes 64 keys.  Key tiles go from global memory straight
-// into LDS (buffer loads, 16-byte chunks XOR-swizzled by row), double
-// buffered: the next step's tile loads while this step computes.  Built for
-// two waves per SIMD.  Used for bf16 inputs (fp32 ones keep k_scores).
+// t = 0..63).  They are the B operand of the transposed product
+// S^T = K Q^T, so every lane ends up with one query's scores, four
+// consecutive keys per register group, stored with 16-byte writes.  A step
+// covers 128 keys: at block 128 each wave takes all of them (four 32-key
+// tiles, four independent accumulator chains), at block 64 two waves share
+// the queries and each takes 64 keys.  Key tiles go from global memory
+// straight into LDS (buffer loads, 16-byte chunks XOR-swizzled by row),
+// double buffered: the next step's tile loads while this step computes.
+// Built for two waves per SIMD.  Used for bf16 inputs (fp32 ones keep
+// k_scores).
 // Same outputs as k_scores: s2 (0 past L) and the per-chunk causal row maxima.
 // Measured on the 128k layer: 1.6 ms against 1.9 ms for k_scores.  Storing a
 // step's scores during the next step's MFMAs, or two tiles per step at three
@@ -368,9 +372,10 @@ __global__ __launch_bounds__(256, 2) void k_scores_mfma(const float* __restrict_
     }
     // this lane's key row within the step: kg 128 + 32 q + l32; its 16-byte chunk c sits at c ^ (row & 15)
     const int krow0 = kg * 32 * NQ + l32;
-    float mx[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) mx[r] = -INFINITY;
+    // this lane's query of the transposed product S^T = K Q^T, and its position
+    const int qi = qg * 32 + l32, qpos = L - BS + qi;
+    float* const srow = s2 + ((size_t)bh * BS + qi) * NS;
+    float mx = -INFINITY;
     f32x16_t acc[NQ];
 
     // one step: MFMAs over the tile in KB_ (keys key0_ ..), then the scores
@@ -391,44 +396,44 @@ __global__ __launch_bounds__(256, 2) void k_scores_mfma(const float* __restrict_
             _Pragma("unroll") for (int q = 0; q < NQ; ++q) {                                               \
                 const unsigned wd = u == 0 ? bv[q].x : u == 1 ? bv[q].y : u == 2 ? bv[q].z : bv[q].w;      \
                 const float kb = __uint_as_float(par ? (wd & 0xffff0000u) : (wd << 16));                  \
-                acc[q] = __builtin_amdgcn_mfma_f32_32x32x2f32(qa[4 * c + u], kb, acc[q], 0, 0, 0);         \
+                acc[q] = __builtin_amdgcn_mfma_f32_32x32x2f32(kb, qa[4 * c + u], acc[q], 0, 0, 0);         \
             }                                                                                              \
         }                                                                                                  \
-        _Pragma("unroll") for (int q = 0; q < NQ; ++q) {                                                   \
-            const int j = key0_ + kg * 32 * NQ + 32 * q + l32;                                             \
-            _Pragma("unroll") for (int r = 0; r < 16; ++r) {                                               \
-                const int i = qg * 32 + 8 * (r >> 2) + 4 * par + (r & 3);                                  \
-                const float v_ = acc[q][r] * C;                                                            \
-                s2[((size_t)bh * BS + i) * NS + j] = j < L ? v_ : 0.0f;                                    \
-                if (j <= L - BS + i) mx[r] = fmaxf(mx[r], v_);                                             \
-            }                                                                                              \
+        /* lane: query qi, keys .. + 32 q + 8 (r / 4) + 4 par + r % 4: four consecutive per store */     \
+        _Pragma("unroll") for (int q = 0; q < NQ; ++q)                                                     \
+        _Pragma("unroll") for (int g4 = 0; g4 < 4; ++g4) {                                                 \
+            const int j = key0_ + kg * 32 * NQ + 32 * q + 8 * g4 + 4 * par;                                \
+            float4 v_;                                                                                     \
+            v_.x = acc[q][4 * g4] * C;                                                                     \
+            v_.y = acc[q][4 * g4 + 1] * C;                                                                 \
+            v_.z = acc[q][4 * g4 + 2] * C;                                                                 \
+            v_.w = acc[q][4 * g4 + 3] * C;                                                                 \
+            if (j <= qpos) mx = fmaxf(mx, v_.x);                                                           \
+            if (j + 1 <= qpos) mx = fmaxf(mx, v_.y);                                                       \
+            if (j + 2 <= qpos) mx = fmaxf(mx, v_.z);                                                       \
+            if (j + 3 <= qpos) mx = fmaxf(mx, v_.w);                                                       \
+            if (j >= L) v_.x = 0.0f;                                                                       \
+            if (j + 1 >= L) v_.y = 0.0f;                                                                   \
+            if (j + 2 >= L) v_.z = 0.0f;                                                                   \
+            if (j + 3 >= L) v_.w = 0.0f;                                                                   \
+            *reinterpret_cast<float4*>(srow + j) = v_;                                                     \
         }                                                                                                  \
         if ((st_) % SPC == SPC - 1) {                                                                      \
-            /* chunk done: its row maxima */                                                               \
+            /* chunk done: its row maxima (the other half of the keys sits in lane ^ 32) */                \
             const int chunk_ = g + P * ((st_) / SPC);                                                      \
-            _Pragma("unroll") for (int r = 0; r < 16; ++r) {                                               \
-                float m_ = mx[r];                                                                          \
-                _Pragma("unroll") for (int o = 16; o >= 1; o >>= 1) m_ = fmaxf(m_, __shfl_xor(m_, o));     \
-                mx[r] = m_;                                                                                \
-            }                                                                                              \
+            const float m_ = fmaxf(mx, __shfl_xor(mx, 32));                                                \
             if (KG == 1) {                                                                                 \
-                if (l32 == 0) {                                                                            \
-                    _Pragma("unroll") for (int r = 0; r < 16; ++r)                                         \
-                        pmax[((size_t)bh * nchunks + chunk_) * BS + qg * 32 + 8 * (r >> 2) + 4 * par + (r & 3)] = mx[r]; \
-                }                                                                                          \
+                if (par == 0) pmax[((size_t)bh * nchunks + chunk_) * BS + qi] = m_;                        \
             } else {                                                                                       \
-                if (l32 == 0) {                                                                            \
-                    _Pragma("unroll") for (int r = 0; r < 16; ++r)                                         \
-                        red[kg][qg * 32 + 8 * (r >> 2) + 4 * par + (r & 3)] = mx[r];                       \
-                }                                                                                          \
+                if (par == 0) red[kg][qi] = m_;                                                            \
                 __syncthreads();                                                                           \
                 for (int i_ = tid; i_ < BS; i_ += 256) {                                                   \
-                    float m_ = red[0][i_];                                                                 \
-                    _Pragma("unroll") for (int g2 = 1; g2 < KG; ++g2) m_ = fmaxf(m_, red[g2][i_]);         \
-                    pmax[((size_t)bh * nchunks + chunk_) * BS + i_] = m_;                                  \
+                    float mm_ = red[0][i_];                                                                \
+                    _Pragma("unroll") for (int g2 = 1; g2 < KG; ++g2) mm_ = fmaxf(mm_, red[g2][i_]);       \
+                    pmax[((size_t)bh * nchunks + chunk_) * BS + i_] = mm_;                                 \
                 }                                                                                          \
             }                                                                                              \
-            _Pragma("unroll") for (int r = 0; r < 16; ++r) mx[r] = -INFINITY;                              \
+            mx = -INFINITY;                                                                                \
         }                                                                                                  \
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");                                                   \
         __syncthreads();                                                                                   \
