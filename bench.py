@@ -130,7 +130,8 @@ def main() -> int:
                     help="also run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+        print(json.dumps({"error": "the benchmark runs on one GPU; --gpus must be 1 (heads shard across "
+                                   "GPUs with no exchange, each GPU running the layer on its share of heads)",
                           "n_gpus": args.gpus}))
         return 2
 
