@@ -311,7 +311,7 @@ __global__ __launch_bounds__(256, 3) void k_scores(const float* __restrict__ qt,
 // Built for two waves per SIMD.  Used for bf16 inputs (fp32 ones keep
 // k_scores).
 // Same outputs as k_scores: s2 (0 past L) and the per-chunk causal row maxima.
-// Measured on the 128k layer: 1.6 ms against 1.9 ms for k_scores.  Storing a
+// Measured on the 128k layer: 1.54 ms against 1.9 ms for k_scores.  Storing a
 // step's scores during the next step's MFMAs, or two tiles per step at three
 // waves per SIMD, ran out of registers (spills) and measured slower.
 // ---------------------------------------------------------------------------
