@@ -460,19 +460,20 @@ inline int scores_mfma_groups(int BH, int nchunks) {
 // K3a: per last-block row: M = max, e = exp2_c(s - M) (0 for j > pos);
 // zpart[kb] = sum over the block's keys ascending; Z = sum of zpart
 // over kb ascending; rz = 1 / Z.  One workgroup per (bh, row); the row is
-// walked in segments of 64 key blocks staged through LDS, where one thread
-// per key block forms its sequential sum.  A row that does not exist
+// walked in segments of 32 key blocks staged through LDS (17 KB, so several
+// rows share a CU and one row's loads overlap another's arithmetic), where
+// one thread per key block forms its sequential sum.  A row that does not exist
 // (pos < 0) gets M = Z = rz = 0, so it adds exact zeros downstream.
 // ---------------------------------------------------------------------------
-constexpr int kSegBlocks = 64;
+constexpr int kRowSeg = 32;
 
 template <int BS>
 __global__ __launch_bounds__(256) void k_rowexp(const float* __restrict__ s2, const float* __restrict__ pmax,
                                                 float* __restrict__ rowmax, float* __restrict__ rowsum,
                                                 float* __restrict__ rz, int L, int NS, Canon K) {
-    constexpr int SEG = kSegBlocks * BS;
-    __shared__ float es[kSegBlocks][BS + 1];
-    __shared__ float zp[kMaxBlocks];
+    constexpr int SEG = kRowSeg * BS;
+    __shared__ float es[kRowSeg][BS + 1];
+    __shared__ float zs[kRowSeg];
     __shared__ float red[256];
     const int tid = threadIdx.x;
     const int row = blockIdx.x, bh = blockIdx.y;
@@ -506,6 +507,10 @@ __global__ __launch_bounds__(256) void k_rowexp(const float* __restrict__ s2, co
         buf[u] = *reinterpret_cast<const float4*>(srow + (j < L ? j : 0));                               \
     }
     FP_LOAD_SEG(0);
+    // thread 0 adds the previous segment's block sums (ascending) while the
+    // current segment's exponentials are formed
+    float Z = 0.0f;
+    int zn = 0;
     for (int seg0 = 0; seg0 < L; seg0 += SEG) {
 #pragma unroll
         for (int u = 0; u < NU; ++u) {
@@ -520,9 +525,12 @@ __global__ __launch_bounds__(256) void k_rowexp(const float* __restrict__ s2, co
             float* e = &es[jl / BS][jl % BS];
             e[0] = v.x; e[1] = v.y; e[2] = v.z; e[3] = v.w;
         }
+        if (tid == 0)
+            for (int i = 0; i < zn; ++i) Z = Z + zs[i];
         __syncthreads();
         if (seg0 + SEG < L) { FP_LOAD_SEG(seg0 + SEG); }
-        if (tid < kSegBlocks && seg0 + tid * BS < L) {
+        const int nbs = min(kRowSeg, (L - seg0 + BS - 1) / BS);
+        if (tid < nbs) {
             float z = 0.0f;
             for (int jj = 0; jj < BS; jj += 16) {
                 float v[16];
@@ -531,23 +539,14 @@ __global__ __launch_bounds__(256) void k_rowexp(const float* __restrict__ s2, co
 #pragma unroll
                 for (int u = 0; u < 16; ++u) z = z + v[u];
             }
-            zp[seg0 / BS + tid] = z;
+            zs[tid] = z;
         }
+        zn = nbs;
         __syncthreads();
     }
 #undef FP_LOAD_SEG
     if (tid == 0) {
-        const int nb = (L + BS - 1) / BS;
-        float Z = 0.0f;
-        int kb = 0;
-        for (; kb + 16 <= nb; kb += 16) {
-            float v[16];
-#pragma unroll
-            for (int u = 0; u < 16; ++u) v[u] = zp[kb + u];
-#pragma unroll
-            for (int u = 0; u < 16; ++u) Z = Z + v[u];
-        }
-        for (; kb < nb; ++kb) Z = Z + zp[kb];
+        for (int i = 0; i < zn; ++i) Z = Z + zs[i];
         rowmax[(size_t)bh * BS + row] = M;
         rowsum[(size_t)bh * BS + row] = Z;
         rz[(size_t)bh * BS + row] = 1.0f / Z;
@@ -561,19 +560,20 @@ __global__ __launch_bounds__(256) void k_rowexp(const float* __restrict__ s2, co
 //   diagsum[o] = sum_{i: pos_i >= o} p[i][pos_i - o],  i ascending.
 // Workgroup x owns columns j0 .. j0+W-1 and the offsets o = L - BS - j0 - t,
 // t in [0, W): row i of such an offset reads column j0 + t + i, so one LDS
-// tile of W + BS columns per row serves both sums.  Rows are staged 16 at a
-// time; every thread keeps its sums in registers across the chunks.
+// tile of W + BS columns per row serves both sums.  Rows are staged RC at a
+// time (8 at block 128: a 20 KB tile, several workgroups per CU; 16 at block
+// 64, where RC (W + BS) must stay a multiple of 1024 for the float4 tiling);
+// every thread keeps its sums in registers across the chunks.
 // Offsets above L - BS are done by k_diagtail.  grid (ceil(L / W), BH).
 // Rows that do not exist (L < BS) have M = rz = 0 and contribute zeros.
 // ---------------------------------------------------------------------------
 constexpr int kLineW = 512;
-constexpr int kLineRC = 16;
 
 template <int BS>
 __global__ __launch_bounds__(256) void k_linesums(const float* __restrict__ s2, const float* __restrict__ rowmax,
                                                   const float* __restrict__ rz, float* __restrict__ colsum,
                                                   float* __restrict__ diagsum, int L, int NS, Canon K) {
-    constexpr int W = kLineW, RC = kLineRC, TW = W + BS;
+    constexpr int W = kLineW, RC = BS == 128 ? 8 : 16, TW = W + BS;
     __shared__ __attribute__((aligned(16))) float es[RC][TW];
     __shared__ float sM[BS], sR[BS];
     const int tid = threadIdx.x, bh = blockIdx.y;
