@@ -65,45 +65,69 @@ def read_traffic(workload: str, default_settings: bool):
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(cfg, total_blocks_by_head, sample_rows: int, budget_s: float, max_budget: int = 0,
+def cpu_baseline(cfg, sample_rows: int, budget_s: float, max_budget: int = 0,
                  qa_selection: str = "flattened", vs_granularity: str = "block"):
-    """The oracle as it stands on the host cores: one query head planned in
-    full, float64 attention on a sample of that head's query blocks,
-    extrapolated to the whole layer by head count and selected-block count."""
+    """The oracle as it stands on the host cores, on a bounded sample of the
+    layer, extrapolated by the oracle's own cost model.
+
+    Selection: one query head of every planted type is planned in full; a
+    head's planning cost is taken as that of the head of its type.
+    Attention: the oracle computes a query-block row r from its full causal
+    prefix (a dense [block, (r + 1) block] score matrix, masked afterwards),
+    so a row costs in proportion to r + 1 "prefix blocks" whatever the
+    selection; sampled rows of those heads give seconds per prefix block,
+    scaled to the layer's Hq nb (nb + 1) / 2 prefix blocks."""
     import numpy as np
     import oracle as O
     from synth import LayerGen
+    cores = len(os.sched_getaffinity(0))
     try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+        from threadpoolctl import threadpool_limits, threadpool_info
+        threadpool_limits(cores)
+        blas = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
     except Exception:
-        threads = 1
+        blas = None
     gen = LayerGen(cfg)
-    h = 0
-    q = gen.q_head(0, h)
-    k = gen.k_head(0, h // cfg.group)
-    v = gen.v_head(0, h // cfg.group)
-    t0 = time.perf_counter()
-    hp = O.plan_head(q, k, cfg.block, cfg.gamma, cfg.tau, cfg.min_budget, max_budget, qa_selection,
-                     vs_granularity)
-    t_plan = time.perf_counter() - t0
+    types = [t for t in ("V", "S", "QA", "N") if t in gen.types]
+    heads = {t: gen.types.index(t) for t in types}
+    count = {t: gen.types.count(t) for t in types}
+    plan_s, plans, inputs = {}, {}, {}
+    for t in types:
+        h = heads[t]
+        q, k, v = gen.q_head(0, h), gen.k_head(0, h // cfg.group), gen.v_head(0, h // cfg.group)
+        t0 = time.perf_counter()
+        plans[t] = O.plan_head(q, k, cfg.block, cfg.gamma, cfg.tau, cfg.min_budget, max_budget, qa_selection,
+                               vs_granularity)
+        plan_s[t] = time.perf_counter() - t0
+        inputs[t] = (q, k, v)
     rng = np.random.default_rng(7)
-    rows = sorted(set([0, cfg.nb - 1] + rng.choice(cfg.nb, size=min(cfg.nb, sample_rows), replace=False).tolist()))
+    per_head = max(1, sample_rows // len(types))
+    work = []
+    for t in types:
+        rows = {cfg.nb - 1} | set(rng.choice(cfg.nb, size=min(cfg.nb, per_head - 1), replace=False).tolist())
+        work += [(t, int(r)) for r in sorted(rows)]
+    order = rng.permutation(len(work))
     t0 = time.perf_counter()
-    done_blocks = 0
-    for r in rows:
-        O.attend_rows(q, k, v, hp.mask, cfg.block, [r], hp.cols)
-        done_blocks += len(hp.lists[r])
+    prefix_done, rows_done = 0, 0
+    for i in order:
+        t, r = work[i]
+        q, k, v = inputs[t]
+        O.attend_rows(q, k, v, plans[t].mask, cfg.block, [r], plans[t].cols)
+        prefix_done += r + 1
+        rows_done += 1
         if time.perf_counter() - t0 > budget_s:
             break
     t_attn = time.perf_counter() - t0
-    per_block = t_attn / max(done_blocks, 1)
-    total_blocks = sum(total_blocks_by_head)
-    est_s = t_plan * cfg.B * cfg.Hq + per_block * total_blocks
-    return {"value": round(est_s * 1e3, 1), "unit": "ms/layer", "cores": threads, "kind": "oracle",
-            "sample": (f"query head {h} planned in full (N={cfg.N}, {t_plan:.1f} s) and float64 "
-                       f"attention on {done_blocks} selected blocks of that head ({t_attn:.1f} s); "
-                       f"extrapolated to {cfg.B * cfg.Hq} heads and {total_blocks} selected blocks")}
+    prefix_total = cfg.B * cfg.Hq * cfg.nb * (cfg.nb + 1) // 2
+    sel_s = cfg.B * sum(plan_s[t] * count[t] for t in types)
+    attn_s = t_attn * prefix_total / max(prefix_done, 1)
+    return {"value": round((sel_s + attn_s) * 1e3, 1), "unit": "ms/layer", "cores": cores, "kind": "oracle",
+            "sample": ("selection: one head per planted type planned in full ("
+                       + ", ".join(f"{t} {plan_s[t]:.2f} s x {count[t]} heads" for t in types)
+                       + f" = {sel_s:.1f} s per layer); float64 attention: {rows_done} query-block rows of those "
+                       f"heads covering {prefix_done} causal prefix blocks in {t_attn:.1f} s, scaled to the "
+                       f"layer's {prefix_total} prefix blocks = {attn_s:.0f} s (the oracle builds each row's "
+                       f"full causal prefix); host cores {cores}, BLAS threads {blas}")}
 
 
 def main() -> int:
@@ -209,12 +233,10 @@ def main() -> int:
     kern_ms, kern_n, _, _ = F.profile_read(reset=True)
     F.profile_enable(False)
     info = plans[-1].info()
-    counts = [c for c in plans[-1].debug_seqs("counts") if c is not None]
     colptrs = ([c for c in plans[-1].debug_seqs("colptr") if c is not None]
                if args.vs_granularity == "token" else None)
     pattern, djs, _, _ = plans[-1].copy_out()
     del plans
-    blocks_by_head = np.concatenate([c.sum(axis=1) for c in counts]).tolist()
 
     flop_per_block = 4.0 * cfg.block * cfg.block * cfg.d
     sparse_flop = info.total_blocks * flop_per_block
@@ -274,7 +296,7 @@ def main() -> int:
     cpu = None
     if not args.no_cpu_baseline and not lens:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(cfg, blocks_by_head, args.cpu_rows, args.cpu_budget_s, args.max_budget,
+        cpu = cpu_baseline(cfg, args.cpu_rows, args.cpu_budget_s, args.max_budget,
                            args.qa_selection, args.vs_granularity)
 
     rec = {

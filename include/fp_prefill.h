@@ -170,7 +170,10 @@ fp_status fp_prefill_plan_ex(const void* q, const void* k, fp_dtype dtype,
  *   q must be the tensor the plan was built from (the plan stores lists,
  *   not values); k and v of the plan's shape and layout.  Every token row
  *   of o is written.  Uses a stream-ordered workspace of V transposed, per
- *   sequence Hkv*d*nb*block elements.
+ *   sequence Hkv*d*nb*block elements.  `stream` may differ from the plan's
+ *   stream: the call then waits for the planning kernels, and the plan's
+ *   stream waits for this call's kernels (so fp_plan_destroy, ordered on the
+ *   plan's stream, cannot free the lists under them).
  */
 fp_status fp_prefill_attend(const fp_plan* plan, const void* q, const void* k,
                             const void* v, void* o, void* stream);

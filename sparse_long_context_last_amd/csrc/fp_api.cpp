@@ -53,6 +53,8 @@ struct fp_plan {
     size_t n_qbar, n_kbar, n_rowmax, n_colsum, n_atrue, n_ahat, n_counts, n_lists, n_colptr;
     int device;
     hipStream_t stream;
+    hipEvent_t ready;                // recorded on `stream` when planning is enqueued
+    hipEvent_t used;                 // recorded after an attend on another stream
     std::vector<void*> allocs;
 };
 
@@ -226,6 +228,8 @@ fp_status palloc(fp_plan* p, T** ptr, size_t count) {
 void free_plan(fp_plan* p) {
     for (void* q : p->allocs) (void)hipFreeAsync(q, p->stream);
     p->allocs.clear();
+    if (p->ready) (void)hipEventDestroy(p->ready);
+    if (p->used) (void)hipEventDestroy(p->used);
     delete p;
 }
 
@@ -295,13 +299,19 @@ void attention_table(const std::vector<SegHost>& segs, int Hq, int Hkv, int bs, 
     g_elems = (size_t)goff;
 }
 
+// Device workspace of one attention call: V^T and, for token-granular
+// plans, the gathered K rows and V^T columns.
+struct AttendWork {
+    void *vt = nullptr, *kg = nullptr, *vgt = nullptr;
+    AttnSeg* dtab = nullptr;     // segment table allocated by the call (dense calls)
+};
+
+// Attention over the segments of a validated problem; `plan` is null for the
+// dense baseline.
 fp_status attend_common(const void* q, const void* k, const void* v, void* o, fp_dtype dtype, int Hq, int Hkv,
                         int block, const std::vector<SegHost>& segs, const TokStride& qs, const TokStride& ks,
                         const fp_plan* plan, hipStream_t st) {
     const size_t esz = dtype == FP_BF16 ? 2 : 4;
-    int dev = 0;
-    FP_HIP(hipGetDevice(&dev), "hipGetDevice");
-    set_pool_threshold(dev);
     std::vector<AttnSeg> table;
     long long items = 0;
     size_t vt_elems = 0, g_elems = 0;
@@ -309,34 +319,41 @@ fp_status attend_common(const void* q, const void* k, const void* v, void* o, fp
     const bool pair = attention_pairs(block, dtype, plan == nullptr);
     attention_table(segs, Hq, Hkv, block, pair, table, items, vt_elems, g_elems);
     if (items == 0) return FP_OK;
-    void *vt = nullptr, *kg = nullptr, *vgt = nullptr;
+    AttendWork w;
     AttnSeg* dtab = plan ? plan->aseg : nullptr;
-    FP_HIP(hipMallocAsync(&vt, vt_elems * esz, st), "hipMallocAsync (V^T)");
     hipError_t e = hipSuccess;
-    if (gather) {
-        e = hipMallocAsync(&kg, g_elems * esz, st);
-        if (e == hipSuccess) e = hipMallocAsync(&vgt, g_elems * esz, st);
-        for (size_t i = 0; i < segs.size() && e == hipSuccess; ++i)
-            e = launch_gather_cols((const unsigned char*)k + (size_t)segs[i].koff * esz,
-                                   (const unsigned char*)v + (size_t)segs[i].koff * esz, ks, dtype == FP_BF16,
-                                   segs[i].nseq, Hq, Hkv, segs[i].L, segs[i].nb, table[i].NT,
-                                   plan->colptr + table[i].cpoff, plan->colidx + table[i].cioff,
-                                   (unsigned char*)kg + (size_t)table[i].goff * esz,
-                                   (unsigned char*)vgt + (size_t)table[i].goff * esz, st);
+    {
+        int dev = 0;
+        FP_HIP(hipGetDevice(&dev), "hipGetDevice");
+        set_pool_threshold(dev);
+        e = hipMallocAsync(&w.vt, vt_elems * esz, st);
+        if (e == hipSuccess && gather) e = hipMallocAsync(&w.kg, g_elems * esz, st);
+        if (e == hipSuccess && gather) e = hipMallocAsync(&w.vgt, g_elems * esz, st);
+        if (e == hipSuccess && !dtab) {
+            e = hipMallocAsync((void**)&w.dtab, table.size() * sizeof(AttnSeg), st);
+            dtab = w.dtab;
+        }
     }
-    if (!dtab) {
-        e = hipMallocAsync((void**)&dtab, table.size() * sizeof(AttnSeg), st);
-        if (e == hipSuccess)
-            e = hipMemcpyAsync(dtab, table.data(), table.size() * sizeof(AttnSeg), hipMemcpyHostToDevice, st);
-    }
+    // a plan made on another stream: wait for its kernels
+    const bool cross = plan && plan->ready && st != plan->stream;
+    if (e == hipSuccess && cross) e = hipStreamWaitEvent(st, plan->ready, 0);
+    if (e == hipSuccess && dtab != (plan ? plan->aseg : nullptr))
+        e = hipMemcpyAsync(dtab, table.data(), table.size() * sizeof(AttnSeg), hipMemcpyHostToDevice, st);
+    for (size_t i = 0; gather && i < segs.size() && e == hipSuccess; ++i)
+        e = launch_gather_cols((const unsigned char*)k + (size_t)segs[i].koff * esz,
+                               (const unsigned char*)v + (size_t)segs[i].koff * esz, ks, dtype == FP_BF16,
+                               segs[i].nseq, Hq, Hkv, segs[i].L, segs[i].nb, table[i].NT,
+                               plan->colptr + table[i].cpoff, plan->colidx + table[i].cioff,
+                               (unsigned char*)w.kg + (size_t)table[i].goff * esz,
+                               (unsigned char*)w.vgt + (size_t)table[i].goff * esz, st);
     for (size_t i = 0; i < segs.size() && e == hipSuccess; ++i)
         e = launch_transpose_v((const unsigned char*)v + (size_t)segs[i].koff * esz, ks,
-                               (unsigned char*)vt + (size_t)table[i].vtoff * esz, dtype == FP_BF16, segs[i].nseq,
+                               (unsigned char*)w.vt + (size_t)table[i].vtoff * esz, dtype == FP_BF16, segs[i].nseq,
                                Hkv, segs[i].L, table[i].NT, st);
     AttnArgs a{};
     a.q = q;
     a.k = k;
-    a.vt = vt;
+    a.vt = w.vt;
     a.o = o;
     a.dtype_bf16 = dtype == FP_BF16;
     a.Hq = Hq;
@@ -357,31 +374,38 @@ fp_status attend_common(const void* q, const void* k, const void* v, void* o, fp
     if (gather) {
         a.colptr = plan->colptr;
         a.colidx = plan->colidx;
-        a.kg = kg;
-        a.vgt = vgt;
+        a.kg = w.kg;
+        a.vgt = w.vgt;
     }
-    EvPair ev{};
-    bool prof;
+    bool prof = false;
     {
         std::lock_guard<std::mutex> g(g_prof_mu);
         prof = g_prof_on;
     }
+    EvPair ev{};
     if (e == hipSuccess && prof) {
-        FP_HIP(hipEventCreate(&ev.a), "hipEventCreate");
-        FP_HIP(hipEventCreate(&ev.b), "hipEventCreate");
         ev.dense = plan == nullptr;
-        FP_HIP(hipEventRecord(ev.a, st), "hipEventRecord");
+        e = hipEventCreate(&ev.a);
+        if (e == hipSuccess) e = hipEventCreate(&ev.b);
+        if (e == hipSuccess) e = hipEventRecord(ev.a, st);
     }
     if (e == hipSuccess) e = launch_attention(a, st);
+    if (e == hipSuccess && prof) e = hipEventRecord(ev.b, st);
     if (e == hipSuccess && prof) {
-        FP_HIP(hipEventRecord(ev.b, st), "hipEventRecord");
         std::lock_guard<std::mutex> g(g_prof_mu);
         g_prof_events.push_back(ev);
+    } else {
+        if (ev.a) (void)hipEventDestroy(ev.a);
+        if (ev.b) (void)hipEventDestroy(ev.b);
     }
-    (void)hipFreeAsync(vt, st);
-    if (kg) (void)hipFreeAsync(kg, st);
-    if (vgt) (void)hipFreeAsync(vgt, st);
-    if (!plan && dtab) (void)hipFreeAsync(dtab, st);
+    // a plan made on another stream: its buffers are released on its own
+    // stream, so that stream waits for this call's kernels
+    if (e == hipSuccess && cross) e = hipEventRecord(plan->used, st);
+    if (e == hipSuccess && cross) e = hipStreamWaitEvent(plan->stream, plan->used, 0);
+    if (w.vt) (void)hipFreeAsync(w.vt, st);
+    if (w.kg) (void)hipFreeAsync(w.kg, st);
+    if (w.vgt) (void)hipFreeAsync(w.vgt, st);
+    if (w.dtab) (void)hipFreeAsync(w.dtab, st);
     if (e != hipSuccess) return hip_fail(e, "attention");
     return FP_OK;
 }
@@ -551,8 +575,8 @@ fp_status make_plan(const void* q, const void* k, fp_dtype dtype, int layout, in
         P.tail = g.L - (g.nb - 1) * block;
         P.tri = g.tri;
         P.mode_all = G >= (1ull << kGammaShift);
-        P.floor_blocks = std::max(1, (min_budget + block - 1) / block);
-        P.cap_blocks = (int)(((long long)max_budget + block - 1) / block);
+        P.floor_blocks = (int)std::min<long long>(kMaxBlocks, std::max(1LL, ((long long)min_budget + block - 1) / block));
+        P.cap_blocks = (int)std::min<long long>(kMaxBlocks, ((long long)max_budget + block - 1) / block);
         P.qa_querywise = qa_selection == FP_QA_QUERYWISE;
         P.vs_token = token;
         P.G = G;
@@ -653,6 +677,9 @@ fp_status make_plan(const void* q, const void* k, fp_dtype dtype, int layout, in
             if (ev[j]) (void)hipEventDestroy(ev[j]);
     }
     if (he == hipSuccess) he = launch_head_order(p->total_blocks, p->hperm, (int)BHall, Hq / Hkv, st);
+    if (he == hipSuccess) he = hipEventCreateWithFlags(&p->ready, hipEventDisableTiming);
+    if (he == hipSuccess) he = hipEventCreateWithFlags(&p->used, hipEventDisableTiming);
+    if (he == hipSuccess) he = hipEventRecord(p->ready, st);
     if (s2) (void)hipFreeAsync(s2, st);
     if (pmax) (void)hipFreeAsync(pmax, st);
     if (rz) (void)hipFreeAsync(rz, st);
