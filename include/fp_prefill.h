@@ -179,6 +179,25 @@ fp_status fp_prefill_attend(const fp_plan* plan, const void* q, const void* k,
                             const void* v, void* o, void* stream);
 
 /*
+ * fp_prefill_attend_noalloc -- fp_prefill_attend for callers that cannot
+ *   allocate device memory (code under HIP graph capture, tight serving
+ *   loops, harnesses that forbid allocation).  Same arguments, layouts and
+ *   results as fp_prefill_attend; it calls no hipMalloc / hipFree and creates
+ *   no events.  Its workspace (V transposed, Hkv*d*nb*block elements per
+ *   sequence, plus 2*Hq*d*nb*block elements per sequence of gathered columns
+ *   for FP_VS_TOKEN plans, each part rounded up to 256 bytes) lives in one
+ *   static device array of 64 MiB per GPU, held until the process ends:
+ *   FP_ERR_SHAPE (and nothing enqueued) if the plan needs more.  Every call
+ *   on one GPU shares that array and overwrites what the previous call left
+ *   there (every byte a call reads it has written first), so calls whose
+ *   work overlaps on one GPU -- on different streams, or from different
+ *   threads without ordering -- race; serialize them on one stream.  The
+ *   measurement hooks do not time this call.
+ */
+fp_status fp_prefill_attend_noalloc(const fp_plan* plan, const void* q, const void* k,
+                                    const void* v, void* o, void* stream);
+
+/*
  * fp_prefill_plan_varlen -- fp_prefill_plan_ex for packed sequences of
  *   different lengths (FP_LAYOUT_THD): q [T, Hq, d], k [T, Hkv, d] with
  *   T = cu_seqlens[nseq].  cu_seqlens is a HOST array of nseq + 1 ints,

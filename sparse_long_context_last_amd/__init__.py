@@ -231,8 +231,11 @@ def plan_varlen(q, k, cu_seqlens, block: int = 128, gamma: float = 0.95, tau: fl
     return Plan(h, Hq, Hkv, d, block, np.diff(cu).tolist(), _lib.FP_LAYOUT_THD, dt, stream)
 
 
-def attend(p: Plan, q, k, v, out=None, stream=None):
-    """Block-sparse causal attention over the plan's selection (fp_prefill_attend)."""
+def attend(p: Plan, q, k, v, out=None, stream=None, noalloc: bool = False):
+    """Block-sparse causal attention over the plan's selection (fp_prefill_attend;
+    with noalloc, fp_prefill_attend_noalloc: no device allocation, the
+    library's static workspace of 64 MiB per GPU).  ``out`` must be given
+    for a call that may not allocate."""
     torch = _torch()
     ndim = 4 if p.layout == _lib.FP_LAYOUT_BHND else 3
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
@@ -252,8 +255,9 @@ def attend(p: Plan, q, k, v, out=None, stream=None):
         _check_tensor(out, "out", ndim)
         if out.shape != q.shape or out.dtype != q.dtype:
             raise ValueError("out must match q")
-    _lib.check(_lib.load().fp_prefill_attend(p.handle, q.data_ptr(), k.data_ptr(), v.data_ptr(),
-                                             out.data_ptr(), _stream_ptr(stream)), "fp_prefill_attend")
+    name = "fp_prefill_attend_noalloc" if noalloc else "fp_prefill_attend"
+    _lib.check(getattr(_lib.load(), name)(p.handle, q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                          out.data_ptr(), _stream_ptr(stream)), name)
     return out
 
 

@@ -54,6 +54,7 @@ SIGNATURES = {
                                          C.c_int, C.c_int, C.c_int, C.c_float, C.c_float, C.c_int,
                                          C.POINTER(PlanOptions), C.c_void_p, C.POINTER(C.c_void_p)]),
     "fp_prefill_attend": (C.c_int, [C.c_void_p] * 6),
+    "fp_prefill_attend_noalloc": (C.c_int, [C.c_void_p] * 6),
     "fp_dense_attend": (C.c_int, [C.c_void_p] * 4 + [C.c_int] * 7 + [C.c_void_p]),
     "fp_dense_attend_varlen": (C.c_int, [C.c_void_p] * 4 + [C.c_int, C.c_int, C.c_void_p] + [C.c_int] * 4
                                + [C.c_void_p]),

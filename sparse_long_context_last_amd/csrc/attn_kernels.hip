@@ -16,10 +16,39 @@
 // software-pipelined: the score MFMAs of the next tile are interleaved with
 // the exponentials of the current one, so a wave keeps the matrix unit and
 // the vector ALU busy at the same time.
+#include <mutex>
+#include <vector>
+
 #include "fp_common.h"
 #include "fp_launch.h"
 
 namespace fp {
+
+// Workspace of the allocation-free attention entry point (V^T and gathered
+// column tiles), one copy per GPU, held until the process ends.  Host code
+// never passes `scratch` itself to a kernel: its device address comes from
+// hipGetSymbolAddress, taken once per device.
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+hipError_t noalloc_scratch(void** ptr, size_t* bytes) {
+    static std::mutex mu;
+    static std::vector<void*> addr;   // per device
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    std::lock_guard<std::mutex> lock(mu);
+    if ((int)addr.size() <= dev) addr.resize(dev + 1, nullptr);
+    if (!addr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress((void**)&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        addr[dev] = p;
+    }
+    *ptr = addr[dev];
+    *bytes = kNoAllocScratchBytes;
+    return hipSuccess;
+}
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));

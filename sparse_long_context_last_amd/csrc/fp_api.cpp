@@ -307,10 +307,13 @@ struct AttendWork {
 };
 
 // Attention over the segments of a validated problem; `plan` is null for the
-// dense baseline.
+// dense baseline.  With `scratch` non-null the call allocates nothing: V^T
+// and the gathered tiles are carved from those `scratch_bytes` bytes (the
+// segment table is the plan's or must fit there too), no events are created
+// and the profiling hooks are skipped.
 fp_status attend_common(const void* q, const void* k, const void* v, void* o, fp_dtype dtype, int Hq, int Hkv,
                         int block, const std::vector<SegHost>& segs, const TokStride& qs, const TokStride& ks,
-                        const fp_plan* plan, hipStream_t st) {
+                        const fp_plan* plan, hipStream_t st, void* scratch = nullptr, size_t scratch_bytes = 0) {
     const size_t esz = dtype == FP_BF16 ? 2 : 4;
     std::vector<AttnSeg> table;
     long long items = 0;
@@ -322,7 +325,22 @@ fp_status attend_common(const void* q, const void* k, const void* v, void* o, fp
     AttendWork w;
     AttnSeg* dtab = plan ? plan->aseg : nullptr;
     hipError_t e = hipSuccess;
-    {
+    if (scratch) {
+        auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+        const size_t vt_b = up(vt_elems * esz), g_b = gather ? up(g_elems * esz) : 0;
+        const size_t tab_b = dtab ? 0 : up(table.size() * sizeof(AttnSeg));
+        const size_t need = vt_b + 2 * g_b + tab_b;
+        if (need > scratch_bytes)
+            return fail(FP_ERR_SHAPE, "attention needs %zu bytes of workspace; the allocation-free call has %zu",
+                        need, scratch_bytes);
+        unsigned char* base = (unsigned char*)scratch;
+        w.vt = base;
+        if (gather) {
+            w.kg = base + vt_b;
+            w.vgt = base + vt_b + g_b;
+        }
+        if (!dtab) dtab = (AttnSeg*)(base + vt_b + 2 * g_b);
+    } else {
         int dev = 0;
         FP_HIP(hipGetDevice(&dev), "hipGetDevice");
         set_pool_threshold(dev);
@@ -378,7 +396,7 @@ fp_status attend_common(const void* q, const void* k, const void* v, void* o, fp
         a.vgt = w.vgt;
     }
     bool prof = false;
-    {
+    if (!scratch) {
         std::lock_guard<std::mutex> g(g_prof_mu);
         prof = g_prof_on;
     }
@@ -402,10 +420,12 @@ fp_status attend_common(const void* q, const void* k, const void* v, void* o, fp
     // stream, so that stream waits for this call's kernels
     if (e == hipSuccess && cross) e = hipEventRecord(plan->used, st);
     if (e == hipSuccess && cross) e = hipStreamWaitEvent(plan->stream, plan->used, 0);
-    if (w.vt) (void)hipFreeAsync(w.vt, st);
-    if (w.kg) (void)hipFreeAsync(w.kg, st);
-    if (w.vgt) (void)hipFreeAsync(w.vgt, st);
-    if (w.dtab) (void)hipFreeAsync(w.dtab, st);
+    if (!scratch) {
+        if (w.vt) (void)hipFreeAsync(w.vt, st);
+        if (w.kg) (void)hipFreeAsync(w.kg, st);
+        if (w.vgt) (void)hipFreeAsync(w.vgt, st);
+        if (w.dtab) (void)hipFreeAsync(w.dtab, st);
+    }
     if (e != hipSuccess) return hip_fail(e, "attention");
     return FP_OK;
 }
@@ -754,6 +774,19 @@ fp_status fp_prefill_attend(const fp_plan* plan, const void* q, const void* k, c
     if (!q || !k || !v || !o) return fail(FP_ERR_INVALID_ARG, "q, k, v or o is NULL");
     return attend_common(q, k, v, o, plan->dtype, plan->Hq, plan->Hkv, plan->bs, plan->segs, plan->qs, plan->ks,
                          plan, (hipStream_t)stream);
+}
+
+fp_status fp_prefill_attend_noalloc(const fp_plan* plan, const void* q, const void* k, const void* v, void* o,
+                                    void* stream) {
+    if (!plan) return fail(FP_ERR_INVALID_ARG, "plan is NULL");
+    if (plan->segs.empty()) return FP_OK;
+    if (!q || !k || !v || !o) return fail(FP_ERR_INVALID_ARG, "q, k, v or o is NULL");
+    void* scr = nullptr;
+    size_t bytes = 0;
+    const hipError_t e = noalloc_scratch(&scr, &bytes);
+    if (e != hipSuccess) return hip_fail(e, "workspace address of the allocation-free call");
+    return attend_common(q, k, v, o, plan->dtype, plan->Hq, plan->Hkv, plan->bs, plan->segs, plan->qs, plan->ks,
+                         plan, (hipStream_t)stream, scr, bytes);
 }
 
 fp_status fp_dense_attend(const void* q, const void* k, const void* v, void* o, fp_dtype dtype, int B, int Hq,

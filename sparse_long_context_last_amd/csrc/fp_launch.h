@@ -14,6 +14,7 @@ constexpr int kRadixBins = 1 << kRadixBits;
 constexpr int kSelChunk = 4096;      // list elements per selection workgroup
 constexpr int kGammaShift = 24;      // G = rint(gamma * 2^24)
 constexpr unsigned char kPatternQueryAware = 1;
+constexpr size_t kNoAllocScratchBytes = 64ull << 20;   // device workspace of fp_prefill_attend_noalloc
 
 // State of one selection list (per head: slot 0 and slot 1).
 struct SelState {
@@ -141,6 +142,9 @@ hipError_t launch_probe_sqrt(const double* x, double* y, long long n, hipStream_
 hipError_t launch_transpose_v(const void* v, const TokStride& vs, void* vt, int dtype_bf16, int nseq, int Hkv,
                               int L, int NT, hipStream_t st);
 hipError_t launch_attention(const AttnArgs& a, hipStream_t st);
+// Device address and size of the allocation-free call's workspace on the
+// current device (looked up once per device).
+hipError_t noalloc_scratch(void** ptr, size_t* bytes);
 hipError_t launch_head_order(const unsigned long long* total_blocks, int* hperm, int nheads, int group,
                              hipStream_t st);
 hipError_t launch_gather_cols(const void* k, const void* v, const TokStride& ks, int dtype_bf16, int nseq, int Hq,
