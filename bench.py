@@ -50,6 +50,15 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
+def attention_kernel_name(cfg, token: bool) -> str:
+    """The template instance of the sparse attention kernel the library runs
+    for this workload (bf16: query-block pairs at block 64)."""
+    g = "true" if token else "false"
+    if cfg.dtype == "bf16":
+        return f"fp::k_attn_bf16<{cfg.block}, true, {g}, {'true' if cfg.block == 64 else 'false'}, {cfg.d}>"
+    return f"fp::k_attn_f32<{cfg.block}, true, {g}, {cfg.d}>"
+
+
 def read_traffic(workload: str, default_settings: bool):
     """HBM bytes per attention launch from the committed counter summary, if
     it was taken on the current attention kernel source and this workload
@@ -289,8 +298,7 @@ def main() -> int:
                            and args.vs_granularity == "block")
     roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
             "frac": round(achieved / peak, 4), "traffic": traffic,
-            "kernel": (f"fp::k_attn_{'bf16' if cfg.dtype == 'bf16' else 'f32'}<{cfg.block}, true, "
-                       f"{'true' if args.vs_granularity == 'token' else 'false'}>"),
+            "kernel": attention_kernel_name(cfg, args.vs_granularity == "token"),
             "algorithmic_flop_per_launch": sparse_flop, "avg_kernel_ms": round(kern_avg_ms, 4),
             "launches": kern_n}
     cpu = None

@@ -33,7 +33,7 @@
  *     holds the remaining L - (nb - 1) block tokens (its block mean averages
  *     those rows; the representative queries of step 1 are the last
  *     min(block, L) tokens).
- *   Supported shapes: d = 128; block in {64, 128}; nb <= 4096 per sequence;
+ *   Supported shapes: d in {64, 128}; block in {64, 128}; nb <= 4096 per sequence;
  *     Hq a multiple of Hkv.  A problem without tokens or heads is empty:
  *     FP_OK, nothing is launched.
  *   Streams: `stream` is a hipStream_t (NULL = the legacy default stream).
@@ -59,7 +59,7 @@ extern "C" {
 typedef enum fp_status {
     FP_OK = 0,
     FP_ERR_INVALID_ARG = -1,   /* null pointer, gamma outside (0,1], tau < 0, ... */
-    FP_ERR_UNSUPPORTED = -2,   /* d != 128, block not 64/128, unknown dtype */
+    FP_ERR_UNSUPPORTED = -2,   /* d not 64/128, block not 64/128, unknown dtype */
     FP_ERR_SHAPE = -3,         /* Hq % Hkv != 0, more than 4096 blocks, sizes too large */
     FP_ERR_OOM = -4,           /* device allocation failed */
     FP_ERR_HIP = -5            /* a HIP runtime call failed */

@@ -167,7 +167,7 @@ __device__ __forceinline__ RowId work_row(const AttnArgs& a, long long item, boo
     const int bl = bh / a.Hq, h = bh % a.Hq, kvh = h / (a.Hq / a.Hkv);
     r.q0 = (size_t)sg.qoff + (size_t)bl * a.qs.bst + (size_t)h * a.qs.hs;
     r.k0 = (size_t)sg.koff + (size_t)bl * a.ks.bst + (size_t)kvh * a.ks.hs;
-    r.vt0 = (size_t)sg.vtoff + (size_t)(bl * a.Hkv + kvh) * kHeadDim * sg.NT;
+    r.vt0 = (size_t)sg.vtoff + (size_t)(bl * a.Hkv + kvh) * a.d * sg.NT;
     if (sparse) {
         const long long tri = (long long)sg.nb * (sg.nb + 1) / 2;
         r.cnt = a.counts[sg.coff + (long long)bh * sg.nb + r.qb];
@@ -190,7 +190,7 @@ __device__ __forceinline__ RowId work_row(const AttnArgs& a, long long item, boo
         r.ncol = cp[r.qb + 1];
         r.ncolB = pair && r.qb >= 1 ? cp[r.qb] : 0;
         r.gidx = a.colidx + sg.cioff + (long long)bh * sg.L;
-        r.g0 = (size_t)sg.goff + (size_t)bh * kHeadDim * sg.NT;
+        r.g0 = (size_t)sg.goff + (size_t)bh * a.d * sg.NT;
     }
     return r;
 }
@@ -252,19 +252,25 @@ __device__ __forceinline__ void gather_mask(f32x16_t (&st)[2], int t, const RowI
 // columns the pair walks the column tiles of block qb and each wave masks the
 // columns past its own row.  Two workgroups per CU, one for the eight-wave
 // block-128 pairs.
-template <int BS, bool SPARSE, bool GATHER, bool PAIR = false>
+template <int BS, bool SPARSE, bool GATHER, bool PAIR, int D>
 __global__ __launch_bounds__(PAIR ? 2 * 2 * BS : 2 * BS, (PAIR && BS == 128) ? 1 : 2) void k_attn_bf16(AttnArgs a) {
-    constexpr int D = kHeadDim, KT = kKT, NW = PAIR ? 2 * (BS / 32) : BS / 32, SPB = BS / KT;
+    constexpr int KT = kKT, NW = PAIR ? 2 * (BS / 32) : BS / 32, SPB = BS / KT;
     constexpr int NTH = 64 * NW;                // threads
     constexpr int NT = KT / 32;                 // 32-key score tiles per stage
-    constexpr int NMS = 8 * NT;                 // score MFMAs per stage (= exponential pairs)
-    constexpr int NMV = 4 * 2 * NT;             // P V MFMAs per stage
+    constexpr int QC = D / 16;                  // 16-wide contraction chunks of a score tile
+    constexpr int TDV = D / 32;                 // 32-row dv tiles of O^T
+    constexpr int NMS = QC * NT;                // score MFMAs per stage
+    constexpr int EPS = 16 * NT / NMS;          // exponentials per score MFMA (32 per lane per stage)
+    constexpr int NMV = TDV * 2 * NT;           // P V MFMAs per stage
+    constexpr int KCH = D / 8;                  // 16-byte chunks per K row
+    constexpr int RPL = 1024 / (2 * D);         // K rows per 1 KB load
+    static_assert(EPS % 2 == 0 && 32 % KCH == 0, "tile layout");
     constexpr int CPR = KT / 8;                 // 16-byte chunks per V^T row
     constexpr int TILE = KT * D * 2;            // bytes of one K (or V^T) tile
     constexpr int LOADS = TILE / 1024 / NW;     // 1 KB loads into LDS per wave per tile
     static_assert(LOADS >= 1 && TILE % (1024 * NW) == 0, "tile loads");
     // Tiles are unpadded and XOR-swizzled at 16-byte granularity:
-    //   K   [KT keys][256 B]:      chunk c of row r at chunk c ^ (r & 15)
+    //   K   [KT keys][2 D bytes]:  chunk c of row r at chunk c ^ (r & (KCH - 1))
     //   V^T [128 dv][2 KT bytes]:  chunk c of row r at chunk c ^ gray(r) & (CPR - 1)
     // so that the MFMA fragment reads below hit distinct banks.
     // The tiles are four separate LDS objects and the stage loop is unrolled
@@ -360,32 +366,32 @@ __global__ __launch_bounds__(PAIR ? 2 * 2 * BS : 2 * BS, (PAIR && BS == 128) ? 1
     // Rows past the sequence end (a partial last block) read its last row and are not stored.
     const int qrel = 32 * (PAIR ? (w % (BS / 32)) : w) + l32;
     const int qrow = qb * BS + qrel;
-    bf16x8_t qf[8];
+    bf16x8_t qf[QC];
     {
         const bf16_t* qp = (const bf16_t*)a.q + rid.q0 + (size_t)max(min(qrow, L - 1), 0) * a.qs.rs + 8 * hh;
 #pragma unroll
-        for (int c = 0; c < 8; ++c) qf[c] = *reinterpret_cast<const bf16x8_t*>(qp + 16 * c);
+        for (int c = 0; c < QC; ++c) qf[c] = *reinterpret_cast<const bf16x8_t*>(qp + 16 * c);
     }
 
-    f32x16_t o[4];
+    f32x16_t o[TDV];
 #pragma unroll
-    for (int T = 0; T < 4; ++T)
+    for (int T = 0; T < TDV; ++T)
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[T][r] = 0.0f;
     float m_run = -INFINITY, l_run = 0.0f;
     const float sl = a.scale_log2;
 
     // Per-lane source offsets of the tile loads (independent of the stage).
-    // K load j of wave w covers rows 4J..4J+3 (J = w + NW j); lane -> row 4J + lane/16,
-    // stored chunk lane%16 holds logical chunk (lane%16) ^ (row & 15).
+    // K load j of wave w covers rows RPL J .. RPL J + RPL - 1 (J = w + NW j); lane -> row
+    // RPL J + lane / KCH, stored chunk lane % KCH holds logical chunk (lane % KCH) ^ (row % KCH).
     // V^T load j covers rows (64/CPR) J ..; lane -> row (64/CPR) J + lane/CPR, stored
     // chunk lane%CPR holds logical chunk (lane%CPR) ^ gray(row) & (CPR-1).
     unsigned koff[LOADS], voff[LOADS];
 #pragma unroll
     for (int j = 0; j < LOADS; ++j) {
         const int J = w + NW * j;
-        const int kr = 4 * J + (lane >> 4);
-        koff[j] = (unsigned)(kr * krs + 16 * ((lane & 15) ^ (kr & 15)));
+        const int kr = RPL * J + lane / KCH;
+        koff[j] = (unsigned)(kr * krs + 16 * ((lane % KCH) ^ (kr & (KCH - 1))));
         const int vr = (64 / CPR) * J + lane / CPR;
         voff[j] = (unsigned)((size_t)vr * vrow + 16 * ((lane % CPR) ^ ((vr ^ (vr >> 1)) & (CPR - 1))));
     }
@@ -405,17 +411,17 @@ __global__ __launch_bounds__(PAIR ? 2 * 2 * BS : 2 * BS, (PAIR && BS == 128) ? 1
                     lds_load16(kg_, koff[j], &KD_[(w + NW * j) * 1024]);                               \
             } else {                                                                                    \
                 _Pragma("unroll") for (int j = 0; j < LOADS; ++j) {                                     \
-                    const int kr_ = 4 * (w + NW * j) + (lane >> 4);                                     \
+                    const int kr_ = RPL * (w + NW * j) + lane / KCH;                                    \
                     const unsigned o_ = (unsigned)((min(key0_ + kr_, L - 1) - key0_) * krs) +           \
-                                        16u * ((lane & 15) ^ (kr_ & 15));                               \
+                                        16u * ((lane % KCH) ^ (kr_ & (KCH - 1)));                       \
                     lds_load16(kg_, o_, &KD_[(w + NW * j) * 1024]);                                    \
                 }                                                                                       \
             }                                                                                           \
         } else {                                                                                         \
             const unsigned char* kg_ = KG + (size_t)((s_) - nsub) * KT * D * 2;                         \
             _Pragma("unroll") for (int j = 0; j < LOADS; ++j) {                                         \
-                const int kr_ = 4 * (w + NW * j) + (lane >> 4);                                         \
-                lds_load16(kg_, (unsigned)(kr_ * D * 2 + 16 * ((lane & 15) ^ (kr_ & 15))),             \
+                const int kr_ = RPL * (w + NW * j) + lane / KCH;                                        \
+                lds_load16(kg_, (unsigned)(kr_ * D * 2 + 16 * ((lane % KCH) ^ (kr_ & (KCH - 1)))),     \
                             &KD_[(w + NW * j) * 1024]);                                                 \
             }                                                                                           \
         }                                                                                                \
@@ -439,9 +445,9 @@ __global__ __launch_bounds__(PAIR ? 2 * 2 * BS : 2 * BS, (PAIR && BS == 128) ? 1
              16 * ((2 * (kc_) + hh) ^ (((32 * (T_) + l32) ^ ((32 * (T_) + l32) >> 1)) & (CPR - 1)))]))
     // byte offset of K fragment c (contraction chunk c) of key row l32 within a
     // 32-row half tile; the half (t) and the buffer are immediate offsets
-    unsigned kfa[8];
+    unsigned kfa[QC];
 #pragma unroll
-    for (int c = 0; c < 8; ++c) kfa[c] = (unsigned)(l32 * D * 2 + 16 * ((2 * c + hh) ^ (l32 & 15)));
+    for (int c = 0; c < QC; ++c) kfa[c] = (unsigned)(l32 * D * 2 + 16 * ((2 * c + hh) ^ (l32 & (KCH - 1))));
     constexpr int RING = 4;   // LDS operand reads in flight ahead of the MFMAs
     const f32x16_t zero16 = {};
 
@@ -495,13 +501,15 @@ __global__ __launch_bounds__(PAIR ? 2 * 2 * BS : 2 * BS, (PAIR && BS == 128) ? 1
                 SN_[i % NT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[i % RING], qf[i / NT],          \
                                                                       i < NT ? zero16 : SN_[i % NT], 0, 0, 0); \
                 if (i + RING < NMS) fr[i % RING] = FP_KFRAG(KC_, (i + RING) % NT, (i + RING) / NT);     \
-                const int t_ = i >> 3, r_ = 2 * (i & 7);                                                 \
-                const float e0_ = __builtin_amdgcn_exp2f(__builtin_fmaf(SC_[t_][r_], sl, -mb));          \
-                const float e1_ = __builtin_amdgcn_exp2f(__builtin_fmaf(SC_[t_][r_ + 1], sl, -mb));      \
-                const bf16x2_t p2_ = {(__bf16)e0_, (__bf16)e1_};                                         \
-                pf[2 * t_ + (r_ >> 3)][r_ & 7] = p2_[0];                                                 \
-                pf[2 * t_ + (r_ >> 3)][(r_ & 7) + 1] = p2_[1];                                           \
-                ls = __builtin_amdgcn_fdot2_f32_bf16(p2_, ones2, ls, false);                              \
+                _Pragma("unroll") for (int u_ = 0; u_ < EPS / 2; ++u_) {                                 \
+                    const int x_ = EPS * i + 2 * u_, t_ = x_ >> 4, r_ = x_ & 15;                         \
+                    const float e0_ = __builtin_amdgcn_exp2f(__builtin_fmaf(SC_[t_][r_], sl, -mb));      \
+                    const float e1_ = __builtin_amdgcn_exp2f(__builtin_fmaf(SC_[t_][r_ + 1], sl, -mb));  \
+                    const bf16x2_t p2_ = {(__bf16)e0_, (__bf16)e1_};                                     \
+                    pf[2 * t_ + (r_ >> 3)][r_ & 7] = p2_[0];                                             \
+                    pf[2 * t_ + (r_ >> 3)][(r_ & 7) + 1] = p2_[1];                                       \
+                    ls = __builtin_amdgcn_fdot2_f32_bf16(p2_, ones2, ls, false);                          \
+                }                                                                                        \
                 __builtin_amdgcn_sched_barrier(0);                                                       \
             }                                                                                            \
         }                                                                                                \
@@ -514,18 +522,18 @@ __global__ __launch_bounds__(PAIR ? 2 * 2 * BS : 2 * BS, (PAIR && BS == 128) ? 1
                 const float m_new = fmaxf(m_run, mx);                                                    \
                 const float alpha = fast_exp2((m_run - m_new) * sl);                                     \
                 l_run *= alpha;                                                                          \
-                _Pragma("unroll") for (int T = 0; T < 4; ++T)                                            \
+                _Pragma("unroll") for (int T = 0; T < TDV; ++T)                                          \
                 _Pragma("unroll") for (int r = 0; r < 16; ++r) o[T][r] *= alpha;                         \
                 m_run = m_new;                                                                           \
                 ls = exp_pack(SC_, sl, m_run * sl, pf);                                                  \
             }                                                                                            \
             l_run += ls;                                                                                 \
             bf16x8_t fr[RING];                                                                           \
-            _Pragma("unroll") for (int i = 0; i < RING; ++i) fr[i] = FP_VFRAG(VC_, i & 3, i >> 2);       \
+            _Pragma("unroll") for (int i = 0; i < RING; ++i) fr[i] = FP_VFRAG(VC_, i % TDV, i / TDV);    \
             __builtin_amdgcn_sched_barrier(0);                                                           \
             _Pragma("unroll") for (int i = 0; i < NMV; ++i) {                                            \
-                o[i & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[i % RING], pf[i >> 2], o[i & 3], 0, 0, 0); \
-                if (i + RING < NMV) fr[i % RING] = FP_VFRAG(VC_, (i + RING) & 3, (i + RING) >> 2);       \
+                o[i % TDV] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[i % RING], pf[i / TDV], o[i % TDV], 0, 0, 0); \
+                if (i + RING < NMV) fr[i % RING] = FP_VFRAG(VC_, (i + RING) % TDV, (i + RING) / TDV);    \
                 __builtin_amdgcn_sched_barrier(0);                                                       \
             }                                                                                            \
         }                                                                                                \
@@ -566,7 +574,7 @@ __global__ __launch_bounds__(PAIR ? 2 * 2 * BS : 2 * BS, (PAIR && BS == 128) ? 1
     if (qb < 0 || qrow >= L) return;
     bf16_t* op = (bf16_t*)a.o + rid.q0 + (size_t)qrow * a.qs.rs;
 #pragma unroll
-    for (int T = 0; T < 4; ++T)
+    for (int T = 0; T < TDV; ++T)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int dv = 32 * T + 8 * i + 4 * hh;
@@ -581,12 +589,12 @@ __global__ __launch_bounds__(PAIR ? 2 * 2 * BS : 2 * BS, (PAIR && BS == 128) ? 1
 
 // ---------------------------------------------------------------------------
 // fp32 inputs: fp32 MFMA 32x32x2, same structure.  Contraction index e of a
-// lane pair (hh) maps to d = c + 64 hh (scores) and to key 32t + 8i + 4hh + j
+// lane pair (hh) maps to d = c + (D / 2) hh (scores) and to key 32t + 8i + 4hh + j
 // (values), identically for both operands.
 // ---------------------------------------------------------------------------
-template <int BS, bool SPARSE, bool GATHER>
+template <int BS, bool SPARSE, bool GATHER, int D>
 __global__ __launch_bounds__(2 * BS) void k_attn_f32(AttnArgs a) {
-    constexpr int D = kHeadDim, KT = kKT, NT = 2 * BS, SPB = BS / KT;
+    constexpr int KT = kKT, NT = 2 * BS, SPB = BS / KT, HD = D / 2, TDV = D / 32, D4 = D / 4;
     constexpr int KP = D + 4;     // floats: 528 B
     constexpr int VP = KT + 4;    // floats: 272 B
     constexpr int KCH = KT * D / 4 / NT;
@@ -622,18 +630,18 @@ __global__ __launch_bounds__(2 * BS) void k_attn_f32(AttnArgs a) {
     }
     const int qrel = 32 * w + l32;
     const int qrow = qb * BS + qrel;
-    float qf[64];
+    float qf[HD];
     {
-        const float* qp = (const float*)a.q + rid.q0 + (size_t)min(qrow, L - 1) * a.qs.rs + 64 * hh;
+        const float* qp = (const float*)a.q + rid.q0 + (size_t)min(qrow, L - 1) * a.qs.rs + HD * hh;
 #pragma unroll
-        for (int c = 0; c < 64; c += 4) {
+        for (int c = 0; c < HD; c += 4) {
             const float4 v = *reinterpret_cast<const float4*>(qp + c);
             qf[c] = v.x; qf[c + 1] = v.y; qf[c + 2] = v.z; qf[c + 3] = v.w;
         }
     }
-    f32x16_t o[4];
+    f32x16_t o[TDV];
 #pragma unroll
-    for (int T = 0; T < 4; ++T)
+    for (int T = 0; T < TDV; ++T)
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[T][r] = 0.0f;
     float m_run = -INFINITY, l_run = 0.0f;
@@ -645,7 +653,7 @@ __global__ __launch_bounds__(2 * BS) void k_attn_f32(AttnArgs a) {
         const int kb_ = SPARSE ? lst[(s_) / SPB] : (s_) / SPB;                                          \
         const int key0_ = kb_ * BS + ((s_) % SPB) * KT;                                              \
         _Pragma("unroll") for (int r = 0; r < KCH; ++r) {                                            \
-            const int e = tid + NT * r, key = e >> 5, d4 = e & 31;                                   \
+            const int e = tid + NT * r, key = e / D4, d4 = e % D4;                                   \
             kreg[r] = *reinterpret_cast<const f32x4_t*>(K + (size_t)min(key0_ + key, L - 1) * krs + 4 * d4); \
         }                                                                                            \
         _Pragma("unroll") for (int r = 0; r < VCH; ++r) {                                            \
@@ -655,7 +663,7 @@ __global__ __launch_bounds__(2 * BS) void k_attn_f32(AttnArgs a) {
     } else {                                                                                         \
         const int c0_ = ((s_) - nsub) * KT;                                                          \
         _Pragma("unroll") for (int r = 0; r < KCH; ++r) {                                            \
-            const int e = tid + NT * r, key = e >> 5, d4 = e & 31;                                   \
+            const int e = tid + NT * r, key = e / D4, d4 = e % D4;                                   \
             kreg[r] = *reinterpret_cast<const f32x4_t*>(KG + (size_t)(c0_ + key) * D + 4 * d4);      \
         }                                                                                            \
         _Pragma("unroll") for (int r = 0; r < VCH; ++r) {                                            \
@@ -668,7 +676,7 @@ __global__ __launch_bounds__(2 * BS) void k_attn_f32(AttnArgs a) {
         float* Ks_ = Ks0 + (buf_) * KT * KP;                                                         \
         float* Vs_ = Vs0 + (buf_) * D * VP;                                                          \
         _Pragma("unroll") for (int r = 0; r < KCH; ++r) {                                            \
-            const int e = tid + NT * r, key = e >> 5, d4 = e & 31;                                   \
+            const int e = tid + NT * r, key = e / D4, d4 = e % D4;                                   \
             *reinterpret_cast<f32x4_t*>(&Ks_[key * KP + 4 * d4]) = kreg[r];                           \
         }                                                                                            \
         _Pragma("unroll") for (int r = 0; r < VCH; ++r) {                                            \
@@ -693,9 +701,9 @@ __global__ __launch_bounds__(2 * BS) void k_attn_f32(AttnArgs a) {
         for (int t = 0; t < 2; ++t) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) st[t][r] = 0.0f;
-            const float* kr = &Ks[(32 * t + l32) * KP + 64 * hh];
+            const float* kr = &Ks[(32 * t + l32) * KP + HD * hh];
 #pragma unroll
-            for (int c = 0; c < 64; c += 4) {
+            for (int c = 0; c < HD; c += 4) {
                 const float4 kv = *reinterpret_cast<const float4*>(kr + c);
                 st[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(kv.x, qf[c], st[t], 0, 0, 0);
                 st[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(kv.y, qf[c + 1], st[t], 0, 0, 0);
@@ -725,7 +733,7 @@ __global__ __launch_bounds__(2 * BS) void k_attn_f32(AttnArgs a) {
             const float alpha = fast_exp2((m_run - m_new) * sl);
             l_run *= alpha;
 #pragma unroll
-            for (int T = 0; T < 4; ++T)
+            for (int T = 0; T < TDV; ++T)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) o[T][r] *= alpha;
             m_run = m_new;
@@ -741,7 +749,7 @@ __global__ __launch_bounds__(2 * BS) void k_attn_f32(AttnArgs a) {
             }
         l_run += ls;
 #pragma unroll
-        for (int T = 0; T < 4; ++T) {
+        for (int T = 0; T < TDV; ++T) {
             const float* vr = &Vs[(32 * T + l32) * VP + 4 * hh];
 #pragma unroll
             for (int t = 0; t < 2; ++t)
@@ -764,7 +772,7 @@ __global__ __launch_bounds__(2 * BS) void k_attn_f32(AttnArgs a) {
     if (qrow >= L) return;
     float* op = (float*)a.o + rid.q0 + (size_t)qrow * a.qs.rs;
 #pragma unroll
-    for (int T = 0; T < 4; ++T)
+    for (int T = 0; T < TDV; ++T)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int dv = 32 * T + 8 * i + 4 * hh;
@@ -783,10 +791,10 @@ __global__ __launch_bounds__(2 * BS) void k_attn_f32(AttnArgs a) {
 // With PERMUTE, key n of every 16-key chunk is stored at position
 // (n & ~12) | ((n & 4) << 1) | ((n & 8) >> 1): key groups [0-3, 8-11, 4-7, 12-15].
 // ---------------------------------------------------------------------------
-template <typename T, bool PERMUTE>
+template <typename T, bool PERMUTE, int D>
 __global__ __launch_bounds__(256) void k_transpose_v(const T* __restrict__ v, TokStride vs, int Hkv,
                                                      T* __restrict__ vt, int L, int NT) {
-    constexpr int D = kHeadDim, TK = 64, VEC = 16 / (int)sizeof(T);   // elements per 16-byte access
+    constexpr int TK = 64, VEC = 16 / (int)sizeof(T);   // elements per 16-byte access
     __shared__ __attribute__((aligned(16))) T tile[TK][D + VEC];
     const int head = blockIdx.y, n0 = blockIdx.x * TK, tid = threadIdx.x;
     const T* src = v + (size_t)(head / Hkv) * vs.bst + (size_t)(head % Hkv) * vs.hs;
@@ -840,19 +848,27 @@ hipError_t launch_head_order(const unsigned long long* total_blocks, int* hperm,
     return hipGetLastError();
 }
 
-hipError_t launch_transpose_v(const void* v, const TokStride& vs, void* vt, int dtype_bf16, int nseq, int Hkv,
-                              int L, int NT, hipStream_t st) {
+template <int D>
+static void launch_transpose_v_t(const void* v, const TokStride& vs, void* vt, int dtype_bf16, int nseq, int Hkv,
+                                 int L, int NT, hipStream_t st) {
     const dim3 g(NT / 64, nseq * Hkv);
     if (dtype_bf16)
-        hipLaunchKernelGGL((k_transpose_v<bf16_t, true>), g, dim3(256), 0, st, (const bf16_t*)v, vs, Hkv,
+        hipLaunchKernelGGL((k_transpose_v<bf16_t, true, D>), g, dim3(256), 0, st, (const bf16_t*)v, vs, Hkv,
                            (bf16_t*)vt, L, NT);
     else
-        hipLaunchKernelGGL((k_transpose_v<float, false>), g, dim3(256), 0, st, (const float*)v, vs, Hkv,
+        hipLaunchKernelGGL((k_transpose_v<float, false, D>), g, dim3(256), 0, st, (const float*)v, vs, Hkv,
                            (float*)vt, L, NT);
+}
+
+hipError_t launch_transpose_v(const void* v, const TokStride& vs, void* vt, int dtype_bf16, int d, int nseq, int Hkv,
+                              int L, int NT, hipStream_t st) {
+    if (d == 128) launch_transpose_v_t<128>(v, vs, vt, dtype_bf16, nseq, Hkv, L, NT, st);
+    else if (d == 64) launch_transpose_v_t<64>(v, vs, vt, dtype_bf16, nseq, Hkv, L, NT, st);
+    else return hipErrorInvalidValue;
     return hipGetLastError();
 }
 
-template <bool SPARSE, bool GATHER>
+template <bool SPARSE, bool GATHER, int D>
 static void launch_attention_t(const AttnArgs& a, hipStream_t st) {
     const unsigned items = (unsigned)a.items;
     if (a.dtype_bf16) {
@@ -860,30 +876,40 @@ static void launch_attention_t(const AttnArgs& a, hipStream_t st) {
         // per CU): 4-5 % faster than one row per workgroup there, while on the
         // sparse selections the pairs' list unions cost more than the shared
         // tile loads save.
-        if (a.BS == 128 && !SPARSE) hipLaunchKernelGGL((k_attn_bf16<128, false, false, true>), dim3(items), dim3(512), 0, st, a);
-        else if (a.BS == 128) hipLaunchKernelGGL((k_attn_bf16<128, SPARSE, GATHER>), dim3(items), dim3(256), 0, st, a);
-        else hipLaunchKernelGGL((k_attn_bf16<64, SPARSE, GATHER, true>), dim3(items), dim3(256), 0, st, a);
+        if (a.BS == 128 && !SPARSE)
+            hipLaunchKernelGGL((k_attn_bf16<128, false, false, true, D>), dim3(items), dim3(512), 0, st, a);
+        else if (a.BS == 128)
+            hipLaunchKernelGGL((k_attn_bf16<128, SPARSE, GATHER, false, D>), dim3(items), dim3(256), 0, st, a);
+        else
+            hipLaunchKernelGGL((k_attn_bf16<64, SPARSE, GATHER, true, D>), dim3(items), dim3(256), 0, st, a);
     } else {
-        const size_t lds = (size_t)2 * (kKT * (kHeadDim + 4) + kHeadDim * (kKT + 4)) * sizeof(float);
+        const size_t lds = (size_t)2 * (kKT * (D + 4) + D * (kKT + 4)) * sizeof(float);
         if (a.BS == 128) {
-            (void)hipFuncSetAttribute((const void*)k_attn_f32<128, SPARSE, GATHER>,
+            (void)hipFuncSetAttribute((const void*)k_attn_f32<128, SPARSE, GATHER, D>,
                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-            hipLaunchKernelGGL((k_attn_f32<128, SPARSE, GATHER>), dim3(items), dim3(256), lds, st, a);
+            hipLaunchKernelGGL((k_attn_f32<128, SPARSE, GATHER, D>), dim3(items), dim3(256), lds, st, a);
         } else {
-            (void)hipFuncSetAttribute((const void*)k_attn_f32<64, SPARSE, GATHER>,
+            (void)hipFuncSetAttribute((const void*)k_attn_f32<64, SPARSE, GATHER, D>,
                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-            hipLaunchKernelGGL((k_attn_f32<64, SPARSE, GATHER>), dim3(items), dim3(128), lds, st, a);
+            hipLaunchKernelGGL((k_attn_f32<64, SPARSE, GATHER, D>), dim3(items), dim3(128), lds, st, a);
         }
     }
+}
+
+template <int D>
+static void launch_attention_d(const AttnArgs& a, hipStream_t st) {
+    if (!a.lists) launch_attention_t<false, false, D>(a, st);
+    else if (a.colptr) launch_attention_t<true, true, D>(a, st);
+    else launch_attention_t<true, false, D>(a, st);
 }
 
 hipError_t launch_attention(const AttnArgs& a, hipStream_t st) {
     // bf16 at block 64, and bf16 dense rows, run query-block pairs; the work
     // items must have been counted that way
     if (a.dtype_bf16 && (a.BS == 64 || !a.lists) && !a.pair) return hipErrorInvalidValue;
-    if (!a.lists) launch_attention_t<false, false>(a, st);
-    else if (a.colptr) launch_attention_t<true, true>(a, st);
-    else launch_attention_t<true, false>(a, st);
+    if (a.d == 128) launch_attention_d<128>(a, st);
+    else if (a.d == 64) launch_attention_d<64>(a, st);
+    else return hipErrorInvalidValue;
     return hipGetLastError();
 }
 
@@ -894,12 +920,12 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t st) {
 // column of the 64-column tile.  grid (NT / 64, nseq * Hq); heads without
 // columns return at once.
 // ---------------------------------------------------------------------------
-template <typename T, bool PERMUTE>
+template <typename T, bool PERMUTE, int D>
 __global__ __launch_bounds__(256) void k_gather_cols(const T* __restrict__ k, const T* __restrict__ v, TokStride ks,
                                                      int Hq, int Hkv, int L, int nb, int NT,
                                                      const int* __restrict__ colptr, const int* __restrict__ colidx,
                                                      T* __restrict__ kg, T* __restrict__ vgt) {
-    constexpr int D = kHeadDim, TK = 64;
+    constexpr int TK = 64;
     __shared__ T tile[TK][D + 2];
     __shared__ int js[TK];
     const int bh = blockIdx.y, c0 = blockIdx.x * TK, tid = threadIdx.x;
@@ -925,16 +951,25 @@ __global__ __launch_bounds__(256) void k_gather_cols(const T* __restrict__ k, co
     }
 }
 
-hipError_t launch_gather_cols(const void* k, const void* v, const TokStride& ks, int dtype_bf16, int nseq, int Hq,
-                              int Hkv, int L, int nb, int NT, const int* colptr, const int* colidx, void* kg,
-                              void* vgt, hipStream_t st) {
+template <int D>
+static void launch_gather_cols_t(const void* k, const void* v, const TokStride& ks, int dtype_bf16, int nseq, int Hq,
+                                 int Hkv, int L, int nb, int NT, const int* colptr, const int* colidx, void* kg,
+                                 void* vgt, hipStream_t st) {
     const dim3 g(NT / 64, nseq * Hq);
     if (dtype_bf16)
-        hipLaunchKernelGGL((k_gather_cols<bf16_t, true>), g, dim3(256), 0, st, (const bf16_t*)k, (const bf16_t*)v,
+        hipLaunchKernelGGL((k_gather_cols<bf16_t, true, D>), g, dim3(256), 0, st, (const bf16_t*)k, (const bf16_t*)v,
                            ks, Hq, Hkv, L, nb, NT, colptr, colidx, (bf16_t*)kg, (bf16_t*)vgt);
     else
-        hipLaunchKernelGGL((k_gather_cols<float, false>), g, dim3(256), 0, st, (const float*)k, (const float*)v,
+        hipLaunchKernelGGL((k_gather_cols<float, false, D>), g, dim3(256), 0, st, (const float*)k, (const float*)v,
                            ks, Hq, Hkv, L, nb, NT, colptr, colidx, (float*)kg, (float*)vgt);
+}
+
+hipError_t launch_gather_cols(const void* k, const void* v, const TokStride& ks, int dtype_bf16, int d, int nseq,
+                              int Hq, int Hkv, int L, int nb, int NT, const int* colptr, const int* colidx, void* kg,
+                              void* vgt, hipStream_t st) {
+    if (d == 128) launch_gather_cols_t<128>(k, v, ks, dtype_bf16, nseq, Hq, Hkv, L, nb, NT, colptr, colidx, kg, vgt, st);
+    else if (d == 64) launch_gather_cols_t<64>(k, v, ks, dtype_bf16, nseq, Hq, Hkv, L, nb, NT, colptr, colidx, kg, vgt, st);
+    else return hipErrorInvalidValue;
     return hipGetLastError();
 }
 

@@ -84,7 +84,7 @@ fp_status hip_fail(hipError_t e, const char* what) {
 fp_status check_common(fp_dtype dtype, int Hq, int Hkv, int d, int block) {
     if (dtype != FP_BF16 && dtype != FP_FP32) return fail(FP_ERR_UNSUPPORTED, "unknown dtype %d", (int)dtype);
     if (Hq < 0 || Hkv < 0) return fail(FP_ERR_INVALID_ARG, "negative size");
-    if (d != kHeadDim) return fail(FP_ERR_UNSUPPORTED, "head dim %d (supported: %d)", d, kHeadDim);
+    if (d != 64 && d != 128) return fail(FP_ERR_UNSUPPORTED, "head dim %d (supported: 64, 128)", d);
     if (block != 64 && block != 128) return fail(FP_ERR_UNSUPPORTED, "block %d (supported: 64, 128)", block);
     if (Hkv == 0 && Hq != 0) return fail(FP_ERR_SHAPE, "Hkv = 0 with Hq = %d", Hq);
     if (Hkv > 0 && Hq % Hkv != 0) return fail(FP_ERR_SHAPE, "Hq %d not a multiple of Hkv %d", Hq, Hkv);
@@ -128,10 +128,10 @@ fp_status check_varlen(fp_dtype dtype, int nseq, const int* cu, int Hq, int Hkv,
 
 // Segments of a [B, H, N, d] problem (one) or of a packed problem (one per
 // non-empty sequence), with the token strides of Q/O and K/V.
-void build_segments(int layout, int B, int N, const int* cu, int Hq, int Hkv, int bs, std::vector<SegHost>& segs,
-                    TokStride& qs, TokStride& ks) {
+void build_segments(int layout, int B, int N, const int* cu, int Hq, int Hkv, int d, int bs,
+                    std::vector<SegHost>& segs, TokStride& qs, TokStride& ks) {
     segs.clear();
-    const long long D = kHeadDim;
+    const long long D = d;
     if (layout == FP_LAYOUT_BHND) {
         qs = TokStride{D, (long long)N * D, (long long)Hq * N * D};
         ks = TokStride{D, (long long)N * D, (long long)Hkv * N * D};
@@ -263,8 +263,8 @@ hipError_t lane_streams(hipStream_t* out) {
 bool attention_pairs(int bs, fp_dtype dtype, bool dense) { return dtype == FP_BF16 && (bs == 64 || dense); }
 
 // The attention segment table of a problem and the V^T workspace size.
-void attention_table(const std::vector<SegHost>& segs, int Hq, int Hkv, int bs, bool pair, std::vector<AttnSeg>& t,
-                     long long& items, size_t& vt_elems, size_t& g_elems) {
+void attention_table(const std::vector<SegHost>& segs, int Hq, int Hkv, int d, int bs, bool pair,
+                     std::vector<AttnSeg>& t, long long& items, size_t& vt_elems, size_t& g_elems) {
     t.clear();
     items = 0;
     long long vt = 0, loff = 0, coff = 0, goff = 0, cpoff = 0, cioff = 0;
@@ -288,10 +288,10 @@ void attention_table(const std::vector<SegHost>& segs, int Hq, int Hkv, int bs, 
         t.push_back(a);
         const long long nbh = (long long)g.nseq * Hq;
         items += nbh * a.npi;
-        vt += (long long)g.nseq * Hkv * kHeadDim * a.NT;
+        vt += (long long)g.nseq * Hkv * d * a.NT;
         loff += nbh * g.tri;
         coff += nbh * g.nb;
-        goff += nbh * kHeadDim * a.NT;
+        goff += nbh * d * a.NT;
         cpoff += nbh * (g.nb + 1);
         cioff += nbh * g.L;
     }
@@ -312,15 +312,16 @@ struct AttendWork {
 // segment table is the plan's or must fit there too), no events are created
 // and the profiling hooks are skipped.
 fp_status attend_common(const void* q, const void* k, const void* v, void* o, fp_dtype dtype, int Hq, int Hkv,
-                        int block, const std::vector<SegHost>& segs, const TokStride& qs, const TokStride& ks,
-                        const fp_plan* plan, hipStream_t st, void* scratch = nullptr, size_t scratch_bytes = 0) {
+                        int d, int block, const std::vector<SegHost>& segs, const TokStride& qs,
+                        const TokStride& ks, const fp_plan* plan, hipStream_t st, void* scratch = nullptr,
+                        size_t scratch_bytes = 0) {
     const size_t esz = dtype == FP_BF16 ? 2 : 4;
     std::vector<AttnSeg> table;
     long long items = 0;
     size_t vt_elems = 0, g_elems = 0;
     const bool gather = plan && plan->colptr;
     const bool pair = attention_pairs(block, dtype, plan == nullptr);
-    attention_table(segs, Hq, Hkv, block, pair, table, items, vt_elems, g_elems);
+    attention_table(segs, Hq, Hkv, d, block, pair, table, items, vt_elems, g_elems);
     if (items == 0) return FP_OK;
     AttendWork w;
     AttnSeg* dtab = plan ? plan->aseg : nullptr;
@@ -359,16 +360,17 @@ fp_status attend_common(const void* q, const void* k, const void* v, void* o, fp
         e = hipMemcpyAsync(dtab, table.data(), table.size() * sizeof(AttnSeg), hipMemcpyHostToDevice, st);
     for (size_t i = 0; gather && i < segs.size() && e == hipSuccess; ++i)
         e = launch_gather_cols((const unsigned char*)k + (size_t)segs[i].koff * esz,
-                               (const unsigned char*)v + (size_t)segs[i].koff * esz, ks, dtype == FP_BF16,
+                               (const unsigned char*)v + (size_t)segs[i].koff * esz, ks, dtype == FP_BF16, d,
                                segs[i].nseq, Hq, Hkv, segs[i].L, segs[i].nb, table[i].NT,
                                plan->colptr + table[i].cpoff, plan->colidx + table[i].cioff,
                                (unsigned char*)w.kg + (size_t)table[i].goff * esz,
                                (unsigned char*)w.vgt + (size_t)table[i].goff * esz, st);
     for (size_t i = 0; i < segs.size() && e == hipSuccess; ++i)
         e = launch_transpose_v((const unsigned char*)v + (size_t)segs[i].koff * esz, ks,
-                               (unsigned char*)w.vt + (size_t)table[i].vtoff * esz, dtype == FP_BF16, segs[i].nseq,
-                               Hkv, segs[i].L, table[i].NT, st);
+                               (unsigned char*)w.vt + (size_t)table[i].vtoff * esz, dtype == FP_BF16, d,
+                               segs[i].nseq, Hkv, segs[i].L, table[i].NT, st);
     AttnArgs a{};
+    a.d = d;
     a.q = q;
     a.k = k;
     a.vt = w.vt;
@@ -383,7 +385,7 @@ fp_status attend_common(const void* q, const void* k, const void* v, void* o, fp
     a.segs = dtab;
     a.nseg = (int)table.size();
     a.items = items;
-    a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)kHeadDim));
+    a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d));
     if (plan) {
         a.lists = plan->lists;
         a.counts = plan->counts;
@@ -454,7 +456,7 @@ fp_status make_plan(const void* q, const void* k, fp_dtype dtype, int layout, in
     }
     std::vector<SegHost> segs;
     TokStride qs, ks;
-    build_segments(layout, B, N, cu, Hq, Hkv, block, segs, qs, ks);
+    build_segments(layout, B, N, cu, Hq, Hkv, d, block, segs, qs, ks);
     if (!segs.empty() && (!q || !k)) return fail(FP_ERR_INVALID_ARG, "q or k is NULL");
 
     fp_plan* p = new (std::nothrow) fp_plan();
@@ -491,8 +493,8 @@ fp_status make_plan(const void* q, const void* k, fp_dtype dtype, int layout, in
         p->rows += nbh * g.nb;
         p->dense_blocks += nbh * g.tri;
         lists_n += nbh * g.tri;
-        n_qbar += (size_t)nbh * g.nb * kHeadDim;
-        n_kbar += (size_t)g.nseq * Hkv * g.nb * kHeadDim;
+        n_qbar += (size_t)nbh * g.nb * d;
+        n_kbar += (size_t)g.nseq * Hkv * g.nb * d;
         n_rowmax += (size_t)nbh * block;
         n_colsum += (size_t)nbh * g.L;
         n_atrue += (size_t)nbh * g.nb;
@@ -502,7 +504,7 @@ fp_status make_plan(const void* q, const void* k, fp_dtype dtype, int layout, in
         s2_max[ln] = std::max(s2_max[ln], (size_t)nbh * block * NS);
         pmax_max[ln] = std::max(pmax_max[ln], (size_t)nbh * (NS / 256) * block);
         rz_max[ln] = std::max(rz_max[ln], (size_t)nbh * block);
-        qt_max[ln] = std::max(qt_max[ln], (size_t)nbh * kHeadDim * block);
+        qt_max[ln] = std::max(qt_max[ln], (size_t)nbh * d * block);
     }
     p->n_qbar = n_qbar; p->n_kbar = n_kbar; p->n_rowmax = n_rowmax; p->n_colsum = n_colsum;
     p->n_atrue = n_atrue; p->n_ahat = n_ahat; p->n_counts = (size_t)p->rows; p->n_lists = (size_t)lists_n;
@@ -574,7 +576,7 @@ fp_status make_plan(const void* q, const void* k, fp_dtype dtype, int layout, in
     p->aseg = aseg;
     long long items = 0;
     size_t vt_elems = 0, g_elems = 0;
-    attention_table(segs, Hq, Hkv, block, attention_pairs(block, dtype, false), p->aseg_host, items, vt_elems,
+    attention_table(segs, Hq, Hkv, d, block, attention_pairs(block, dtype, false), p->aseg_host, items, vt_elems,
                     g_elems);
     hipStream_t st = p->stream;
     he = hipMemcpyAsync(aseg, p->aseg_host.data(), segs.size() * sizeof(AttnSeg), hipMemcpyHostToDevice, st);
@@ -628,8 +630,8 @@ fp_status make_plan(const void* q, const void* k, fp_dtype dtype, int layout, in
         }
         P.sel = sel + (size_t)2 * max_bh * (i % kPlanLanes);
         P.hist = hist + (size_t)2 * max_bh * kRadixBins * (i % kPlanLanes);
-        o_qbar += (size_t)nbh * g.nb * kHeadDim;
-        o_kbar += (size_t)g.nseq * Hkv * g.nb * kHeadDim;
+        o_qbar += (size_t)nbh * g.nb * d;
+        o_kbar += (size_t)g.nseq * Hkv * g.nb * d;
         o_rowmax += (size_t)nbh * block;
         o_colsum += (size_t)nbh * g.L;
         o_atrue += (size_t)nbh * g.nb;
@@ -669,6 +671,7 @@ fp_status make_plan(const void* q, const void* k, fp_dtype dtype, int layout, in
     for (size_t i = 0; i < segs.size() && he == hipSuccess; ++i) {
         const int ln = (int)(i % kPlanLanes);
         PlanArgs a{};
+        a.d = d;
         a.q = (const unsigned char*)q + (size_t)segs[i].qoff * esz;
         a.k = (const unsigned char*)k + (size_t)segs[i].koff * esz;
         a.qs = qs;
@@ -772,8 +775,8 @@ fp_status fp_prefill_attend(const fp_plan* plan, const void* q, const void* k, c
     if (!plan) return fail(FP_ERR_INVALID_ARG, "plan is NULL");
     if (plan->segs.empty()) return FP_OK;
     if (!q || !k || !v || !o) return fail(FP_ERR_INVALID_ARG, "q, k, v or o is NULL");
-    return attend_common(q, k, v, o, plan->dtype, plan->Hq, plan->Hkv, plan->bs, plan->segs, plan->qs, plan->ks,
-                         plan, (hipStream_t)stream);
+    return attend_common(q, k, v, o, plan->dtype, plan->Hq, plan->Hkv, plan->d, plan->bs, plan->segs, plan->qs,
+                         plan->ks, plan, (hipStream_t)stream);
 }
 
 fp_status fp_prefill_attend_noalloc(const fp_plan* plan, const void* q, const void* k, const void* v, void* o,
@@ -785,8 +788,8 @@ fp_status fp_prefill_attend_noalloc(const fp_plan* plan, const void* q, const vo
     size_t bytes = 0;
     const hipError_t e = noalloc_scratch(&scr, &bytes);
     if (e != hipSuccess) return hip_fail(e, "workspace address of the allocation-free call");
-    return attend_common(q, k, v, o, plan->dtype, plan->Hq, plan->Hkv, plan->bs, plan->segs, plan->qs, plan->ks,
-                         plan, (hipStream_t)stream, scr, bytes);
+    return attend_common(q, k, v, o, plan->dtype, plan->Hq, plan->Hkv, plan->d, plan->bs, plan->segs, plan->qs,
+                         plan->ks, plan, (hipStream_t)stream, scr, bytes);
 }
 
 fp_status fp_dense_attend(const void* q, const void* k, const void* v, void* o, fp_dtype dtype, int B, int Hq,
@@ -797,8 +800,8 @@ fp_status fp_dense_attend(const void* q, const void* k, const void* v, void* o, 
     if (!q || !k || !v || !o) return fail(FP_ERR_INVALID_ARG, "q, k, v or o is NULL");
     std::vector<SegHost> segs;
     TokStride qs, ks;
-    build_segments(FP_LAYOUT_BHND, B, N, nullptr, Hq, Hkv, block, segs, qs, ks);
-    return attend_common(q, k, v, o, dtype, Hq, Hkv, block, segs, qs, ks, nullptr, (hipStream_t)stream);
+    build_segments(FP_LAYOUT_BHND, B, N, nullptr, Hq, Hkv, d, block, segs, qs, ks);
+    return attend_common(q, k, v, o, dtype, Hq, Hkv, d, block, segs, qs, ks, nullptr, (hipStream_t)stream);
 }
 
 fp_status fp_dense_attend_varlen(const void* q, const void* k, const void* v, void* o, fp_dtype dtype, int nseq,
@@ -807,10 +810,10 @@ fp_status fp_dense_attend_varlen(const void* q, const void* k, const void* v, vo
     if (s != FP_OK) return s;
     std::vector<SegHost> segs;
     TokStride qs, ks;
-    build_segments(FP_LAYOUT_THD, nseq, 0, cu_seqlens, Hq, Hkv, block, segs, qs, ks);
+    build_segments(FP_LAYOUT_THD, nseq, 0, cu_seqlens, Hq, Hkv, d, block, segs, qs, ks);
     if (segs.empty()) return FP_OK;
     if (!q || !k || !v || !o) return fail(FP_ERR_INVALID_ARG, "q, k, v or o is NULL");
-    return attend_common(q, k, v, o, dtype, Hq, Hkv, block, segs, qs, ks, nullptr, (hipStream_t)stream);
+    return attend_common(q, k, v, o, dtype, Hq, Hkv, d, block, segs, qs, ks, nullptr, (hipStream_t)stream);
 }
 
 fp_status fp_plan_info_get(const fp_plan* plan, fp_plan_info* out) {
@@ -938,14 +941,14 @@ fp_status fp_profile_read(double* sparse_ms, long long* sparse_launches, double*
 
 fp_status fp_probe_exp2(const float* x, float* y, long long n, void* stream) {
     if (n < 0 || (n > 0 && (!x || !y))) return fail(FP_ERR_INVALID_ARG, "bad probe arguments");
-    hipError_t e = launch_probe_exp2(x, y, n, make_canon(kHeadDim), (hipStream_t)stream);
+    hipError_t e = launch_probe_exp2(x, y, n, make_canon(kMaxHeadDim), (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "probe exp2");
     return FP_OK;
 }
 
 fp_status fp_probe_ln(const double* x, double* y, long long n, void* stream) {
     if (n < 0 || (n > 0 && (!x || !y))) return fail(FP_ERR_INVALID_ARG, "bad probe arguments");
-    hipError_t e = launch_probe_ln(x, y, n, make_canon(kHeadDim), (hipStream_t)stream);
+    hipError_t e = launch_probe_ln(x, y, n, make_canon(kMaxHeadDim), (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "probe ln");
     return FP_OK;
 }

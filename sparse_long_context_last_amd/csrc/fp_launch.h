@@ -5,7 +5,7 @@
 
 namespace fp {
 
-constexpr int kHeadDim = 128;        // supported head dimension
+constexpr int kMaxHeadDim = 128;     // supported head dimensions: 64 and 128
 constexpr int kMaxBlock = 128;       // largest supported block size
 constexpr int kMaxBlocks = 4096;     // largest supported N / block
 constexpr int kScoreDSConst = 32;    // d-slice of the last-block score kernel
@@ -83,6 +83,7 @@ struct PlanDev {
 
 // Inputs and transient workspace of one segment's planning call.
 struct PlanArgs {
+    int d;            // head dimension (64 or 128)
     const void* q;    // the segment's first token of head 0 of its first sequence
     const void* k;
     TokStride qs, ks;
@@ -113,6 +114,7 @@ struct AttnSeg {
 };
 
 struct AttnArgs {
+    int d;               // head dimension (64 or 128)
     const void* q;
     const void* k;
     const void* vt;      // V transposed, per segment [nseq Hkv][d][NT], zero past L
@@ -139,7 +141,7 @@ hipError_t launch_fill_u32(unsigned int* p, unsigned int v, long long n, hipStre
 hipError_t launch_probe_exp2(const float* x, float* y, long long n, const Canon& K, hipStream_t st);
 hipError_t launch_probe_ln(const double* x, double* y, long long n, const Canon& K, hipStream_t st);
 hipError_t launch_probe_sqrt(const double* x, double* y, long long n, hipStream_t st);
-hipError_t launch_transpose_v(const void* v, const TokStride& vs, void* vt, int dtype_bf16, int nseq, int Hkv,
+hipError_t launch_transpose_v(const void* v, const TokStride& vs, void* vt, int dtype_bf16, int d, int nseq, int Hkv,
                               int L, int NT, hipStream_t st);
 hipError_t launch_attention(const AttnArgs& a, hipStream_t st);
 // Device address and size of the allocation-free call's workspace on the
@@ -147,8 +149,8 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t st);
 hipError_t noalloc_scratch(void** ptr, size_t* bytes);
 hipError_t launch_head_order(const unsigned long long* total_blocks, int* hperm, int nheads, int group,
                              hipStream_t st);
-hipError_t launch_gather_cols(const void* k, const void* v, const TokStride& ks, int dtype_bf16, int nseq, int Hq,
-                              int Hkv, int L, int nb, int NT, const int* colptr, const int* colidx, void* kg,
+hipError_t launch_gather_cols(const void* k, const void* v, const TokStride& ks, int dtype_bf16, int d, int nseq,
+                              int Hq, int Hkv, int L, int nb, int NT, const int* colptr, const int* colidx, void* kg,
                               void* vgt, hipStream_t st);
 
 }  // namespace fp

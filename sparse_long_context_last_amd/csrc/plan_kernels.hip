@@ -138,11 +138,12 @@ template <> __device__ __forceinline__ void load8_f32<float>(const float* p, flo
     v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
 }
 
-template <typename T>
+template <typename T, int D>
 __global__ __launch_bounds__(256) void k_pool(const T* __restrict__ x, TokStride xs, int H,
                                               float* __restrict__ out, int L, int bs) {
-    const int tid = threadIdx.x, cg = tid & 15;
-    const int kb = blockIdx.x * 16 + (tid >> 4), head = blockIdx.y;
+    constexpr int TPR = D / 8, RPW = 256 / TPR;   // threads per block row, block rows per workgroup
+    const int tid = threadIdx.x, cg = tid % TPR;
+    const int kb = blockIdx.x * RPW + tid / TPR, head = blockIdx.y;
     const int nb = (L + bs - 1) / bs;
     if (kb >= nb) return;
     const int rows = min(bs, L - kb * bs);
@@ -157,7 +158,7 @@ __global__ __launch_bounds__(256) void k_pool(const T* __restrict__ x, TokStride
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[e] = acc[e] + v[e];
     }
-    float* dst = out + ((size_t)head * nb + kb) * kHeadDim + 8 * cg;
+    float* dst = out + ((size_t)head * nb + kb) * D + 8 * cg;
     const float fr = (float)rows;
     float4 lo, hi;
     lo.x = acc[0] / fr; lo.y = acc[1] / fr; lo.z = acc[2] / fr; lo.w = acc[3] / fr;
@@ -183,10 +184,9 @@ constexpr int kScoreDS = kScoreDSConst;
 // The last block's queries, widened to fp32 and transposed once per call:
 // qt[bh][t][i] = q[L-BS+i][t] (0 for rows that do not exist), so that every
 // score workgroup stages its query slices with contiguous 16-byte loads.
-template <typename T, int BS>
+template <typename T, int BS, int D>
 __global__ __launch_bounds__(BS) void k_qt(const T* __restrict__ q, TokStride qs, float* __restrict__ qt, int L,
                                            int Hq) {
-    constexpr int D = kHeadDim;
     const int i = threadIdx.x, t0 = 8 * blockIdx.x, bh = blockIdx.y;
     const int b = bh / Hq, h = bh % Hq;
     const int pos = L - BS + i;
@@ -203,12 +203,13 @@ __global__ __launch_bounds__(BS) void k_qt(const T* __restrict__ q, TokStride qs
 
 // Built for three waves per SIMD (at most 168 registers), which measured
 // faster than two waves with more room.
-template <typename T, int BS>
+template <typename T, int BS, int D>
 __global__ __launch_bounds__(256, 3) void k_scores(const float* __restrict__ qt, const T* __restrict__ k,
                                                 TokStride ks, float* __restrict__ s2,
                                                 float* __restrict__ pmax, int L, int NS, int Hq, int group,
                                                 float C) {
-    constexpr int D = kHeadDim, TK = kScoreTK, DS = kScoreDS, MR = BS / 16;
+    constexpr int TK = kScoreTK, DS = kScoreDS, MR = BS / 16;
+    static_assert(D % DS == 0, "d slices");
     __shared__ __attribute__((aligned(16))) float Qs[DS][BS + 4];
     __shared__ __attribute__((aligned(16))) float Ks[DS][TK + 4];
     const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
@@ -321,13 +322,14 @@ __device__ __forceinline__ void lds_copy16(const void* base, unsigned voff, void
         (__attribute__((address_space(3))) void*)dst, 16, voff, 0, 0, 0);
 }
 
-template <int BS>
+template <int BS, int D>
 __global__ __launch_bounds__(256, 2) void k_scores_mfma(const float* __restrict__ qt, const bf16_t* __restrict__ k,
                                                         TokStride ks, float* __restrict__ s2,
                                                         float* __restrict__ pmax, int L, int NS, int Hq, int group,
                                                         float C) {
     typedef float f32x16_t __attribute__((ext_vector_type(16)));
-    constexpr int D = kHeadDim, TK = kScoreTK, QG = BS / 32, KG = 4 / QG;
+    constexpr int TK = kScoreTK, QG = BS / 32, KG = 4 / QG;
+    constexpr int RB = 2 * D, CH = D / 8, RPL = 1024 / RB;   // bytes, 16-byte chunks per key row; rows per 1 KB load
     constexpr int NQ = 4 / KG;                   // 32-key tiles per wave per step
     constexpr int KP = 32 * NQ * KG;             // keys per step (all waves): 128
     constexpr int SPC = TK / KP;                 // steps per 256-key chunk
@@ -357,20 +359,20 @@ __global__ __launch_bounds__(256, 2) void k_scores_mfma(const float* __restrict_
 #pragma unroll
         for (int t = 0; t < D / 2; ++t) qa[t] = qp[(size_t)(2 * t + par) * BS];
     }
-    // key tile loads: load j of wave w covers rows 4 (w + 4 j) + lane / 16; stored
-    // 16-byte chunk lane % 16 of a row holds chunk (lane % 16) ^ (row & 15).
+    // key tile loads: load j of wave w covers rows RPL (w + 4 j) + lane / CH; stored
+    // 16-byte chunk lane % CH of a row holds chunk (lane % CH) ^ (row % CH).
     // Rows past L read row L - 1 (finite; their scores are stored as 0).
 #define FP_KLOAD(st_, KD_)                                                                                 \
     {                                                                                                      \
         const int key0_ = (g + P * ((st_) / SPC)) * TK + ((st_) % SPC) * KP;                               \
         _Pragma("unroll") for (int j = 0; j < LOADS; ++j) {                                                \
-            const int r_ = 4 * (w + 4 * j) + (lane >> 4);                                                 \
+            const int r_ = RPL * (w + 4 * j) + lane / CH;                                                  \
             const int kr_ = min(key0_ + r_, L - 1);                                                        \
-            lds_copy16(kbase, (unsigned)((size_t)kr_ * krs + 16 * ((lane & 15) ^ (r_ & 15))),              \
+            lds_copy16(kbase, (unsigned)((size_t)kr_ * krs + 16 * ((lane % CH) ^ (r_ & (CH - 1)))),        \
                        &KD_[(w + 4 * j) * 1024]);                                                          \
         }                                                                                                  \
     }
-    // this lane's key row within the step: kg 128 + 32 q + l32; its 16-byte chunk c sits at c ^ (row & 15)
+    // this lane's key row within the step: kg 128 + 32 q + l32; its 16-byte chunk c sits at c ^ (row % CH)
     const int krow0 = kg * 32 * NQ + l32;
     // this lane's query of the transposed product S^T = K Q^T, and its position
     const int qi = qg * 32 + l32, qpos = L - BS + qi;
@@ -390,7 +392,7 @@ __global__ __launch_bounds__(256, 2) void k_scores_mfma(const float* __restrict_
             uint4 bv[NQ];                                                                                  \
             _Pragma("unroll") for (int q = 0; q < NQ; ++q) {                                               \
                 const int row = krow0 + 32 * q;                                                            \
-                bv[q] = *reinterpret_cast<const uint4*>(&KB_[row * 256 + 16 * (c ^ (row & 15))]);          \
+                bv[q] = *reinterpret_cast<const uint4*>(&KB_[row * RB + 16 * (c ^ (row & (CH - 1)))]);     \
             }                                                                                              \
             _Pragma("unroll") for (int u = 0; u < 4; ++u)                                                  \
             _Pragma("unroll") for (int q = 0; q < NQ; ++q) {                                               \
@@ -715,21 +717,21 @@ __global__ __launch_bounds__(256) void k_atrue(const float* __restrict__ colsum,
 // so every pooled key row it reads serves R dot products.
 // grid (ceil(nb / R), BH), dynamic LDS R * nb floats.
 // ---------------------------------------------------------------------------
-template <int R>
+template <int R, int D>
 __global__ __launch_bounds__(256) void k_estimate(const float* __restrict__ qbar, const float* __restrict__ kbar,
                                                   float* __restrict__ ahat, int nb, int Hq, int Hkv,
                                                   int group, Canon K) {
     extern __shared__ float sc[];              // [R][nb]
-    __shared__ __attribute__((aligned(16))) float qs[R][kHeadDim];
+    __shared__ __attribute__((aligned(16))) float qs[R][D];
     __shared__ float red[R][256];
     __shared__ float Mr[R], Zr[R];
     const int tid = threadIdx.x, bh = blockIdx.y;
     const int q0 = blockIdx.x * R;
     const int b = bh / Hq, h = bh % Hq;
     const size_t kvbh = (size_t)b * Hkv + h / group;
-    for (int e = tid; e < R * kHeadDim; e += 256) {
-        const int r = e / kHeadDim, t = e % kHeadDim;
-        qs[r][t] = (q0 + r < nb) ? qbar[((size_t)bh * nb + q0 + r) * kHeadDim + t] : 0.0f;
+    for (int e = tid; e < R * D; e += 256) {
+        const int r = e / D, t = e % D;
+        qs[r][t] = (q0 + r < nb) ? qbar[((size_t)bh * nb + q0 + r) * D + t] : 0.0f;
     }
     __syncthreads();
     const int qlast = min(q0 + R - 1, nb - 1);
@@ -737,12 +739,12 @@ __global__ __launch_bounds__(256) void k_estimate(const float* __restrict__ qbar
 #pragma unroll
     for (int r = 0; r < R; ++r) mx[r] = -INFINITY;
     for (int kb = tid; kb <= qlast; kb += 256) {
-        const float4* kr = reinterpret_cast<const float4*>(kbar + (kvbh * nb + kb) * kHeadDim);
+        const float4* kr = reinterpret_cast<const float4*>(kbar + (kvbh * nb + kb) * D);
         float acc[R];
 #pragma unroll
         for (int r = 0; r < R; ++r) acc[r] = 0.0f;
 #pragma unroll 4
-        for (int c = 0; c < kHeadDim / 4; ++c) {
+        for (int c = 0; c < D / 4; ++c) {
             const float4 v = kr[c];
 #pragma unroll
             for (int r = 0; r < R; ++r) {
@@ -1352,7 +1354,8 @@ __global__ __launch_bounds__(256) void k_probe_sqrt(const double* x, double* y, 
 // ---------------------------------------------------------------------------
 static inline unsigned grid1(long long n, int per = 256) { return (unsigned)((n + per - 1) / per); }
 
-hipError_t launch_plan(const PlanArgs& a, PlanDev& P, hipStream_t st) {
+template <int D>
+static hipError_t launch_plan_t(const PlanArgs& a, PlanDev& P, hipStream_t st) {
     const int BS = P.BS, nb = P.nb, L = P.L, NS = P.NS, BH = P.BH;
     const int bkv = a.nseq * a.Hkv;
     const int group = a.Hq / a.Hkv;
@@ -1374,22 +1377,22 @@ hipError_t launch_plan(const PlanArgs& a, PlanDev& P, hipStream_t st) {
         }
         ps = a.aux;
     }
-    const unsigned pg = (unsigned)((nb + 15) / 16);
+    const unsigned pg = (unsigned)((nb + 256 / (D / 8) - 1) / (256 / (D / 8)));
     if (a.dtype_bf16) {
-        hipLaunchKernelGGL(k_pool<bf16_t>, dim3(pg, BH), dim3(256), 0, ps, (const bf16_t*)a.q, a.qs, a.Hq, P.qbar, L, BS);
-        hipLaunchKernelGGL(k_pool<bf16_t>, dim3(pg, bkv), dim3(256), 0, ps, (const bf16_t*)a.k, a.ks, a.Hkv, P.kbar, L, BS);
+        hipLaunchKernelGGL((k_pool<bf16_t, D>), dim3(pg, BH), dim3(256), 0, ps, (const bf16_t*)a.q, a.qs, a.Hq, P.qbar, L, BS);
+        hipLaunchKernelGGL((k_pool<bf16_t, D>), dim3(pg, bkv), dim3(256), 0, ps, (const bf16_t*)a.k, a.ks, a.Hkv, P.kbar, L, BS);
     } else {
-        hipLaunchKernelGGL(k_pool<float>, dim3(pg, BH), dim3(256), 0, ps, (const float*)a.q, a.qs, a.Hq, P.qbar, L, BS);
-        hipLaunchKernelGGL(k_pool<float>, dim3(pg, bkv), dim3(256), 0, ps, (const float*)a.k, a.ks, a.Hkv, P.kbar, L, BS);
+        hipLaunchKernelGGL((k_pool<float, D>), dim3(pg, BH), dim3(256), 0, ps, (const float*)a.q, a.qs, a.Hq, P.qbar, L, BS);
+        hipLaunchKernelGGL((k_pool<float, D>), dim3(pg, bkv), dim3(256), 0, ps, (const float*)a.k, a.ks, a.Hkv, P.kbar, L, BS);
     }
     // K4: the estimated block map needs only the pooled vectors
     if (nb <= 1024) {
         const size_t lds = (size_t)8 * nb * sizeof(float);
-        hipLaunchKernelGGL(k_estimate<8>, dim3((nb + 7) / 8, BH), dim3(256), lds, ps, P.qbar, P.kbar, P.ahat, nb,
+        hipLaunchKernelGGL((k_estimate<8, D>), dim3((nb + 7) / 8, BH), dim3(256), lds, ps, P.qbar, P.kbar, P.ahat, nb,
                            a.Hq, a.Hkv, group, a.canon);
     } else {
         const size_t lds = (size_t)2 * nb * sizeof(float);
-        hipLaunchKernelGGL(k_estimate<2>, dim3((nb + 1) / 2, BH), dim3(256), lds, ps, P.qbar, P.kbar, P.ahat, nb,
+        hipLaunchKernelGGL((k_estimate<2, D>), dim3((nb + 1) / 2, BH), dim3(256), lds, ps, P.qbar, P.kbar, P.ahat, nb,
                            a.Hq, a.Hkv, group, a.canon);
     }
     if (a.aux) {
@@ -1404,13 +1407,13 @@ hipError_t launch_plan(const PlanArgs& a, PlanDev& P, hipStream_t st) {
     const dim3 gs(NS / kScoreTK, BH);
 #define FP_SCORES(T, B_)                                                                                   \
     do {                                                                                                   \
-        hipLaunchKernelGGL((k_qt<T, B_>), dim3(kHeadDim / 8, BH), dim3(B_), 0, st, (const T*)a.q, a.qs, a.qt, L, a.Hq); \
+        hipLaunchKernelGGL((k_qt<T, B_, D>), dim3(D / 8, BH), dim3(B_), 0, st, (const T*)a.q, a.qs, a.qt, L, a.Hq); \
         if constexpr (sizeof(T) == 2)                                                                      \
-            hipLaunchKernelGGL((k_scores_mfma<B_>), dim3(scores_mfma_groups(BH, NS / kScoreTK), BH), dim3(256), 0, \
+            hipLaunchKernelGGL((k_scores_mfma<B_, D>), dim3(scores_mfma_groups(BH, NS / kScoreTK), BH), dim3(256), 0, \
                                st, (const float*)a.qt, (const bf16_t*)a.k, a.ks, a.s2, a.pmax, L, NS, a.Hq, group, \
                                a.canon.C);                                                                 \
         else                                                                                               \
-            hipLaunchKernelGGL((k_scores<T, B_>), gs, dim3(256), 0, st, (const float*)a.qt, (const T*)a.k, a.ks, \
+            hipLaunchKernelGGL((k_scores<T, B_, D>), gs, dim3(256), 0, st, (const float*)a.qt, (const T*)a.k, a.ks, \
                                a.s2, a.pmax, L, NS, a.Hq, group, a.canon.C);                               \
     } while (0)
     if (a.dtype_bf16) {
@@ -1471,6 +1474,12 @@ hipError_t launch_plan(const PlanArgs& a, PlanDev& P, hipStream_t st) {
     hipLaunchKernelGGL(k_lists, dim3((nb + 3) / 4, BH), dim3(256), 0, st, P, P.sel);
     hipLaunchKernelGGL(k_head_totals, dim3(BH), dim3(256), 0, st, P.counts, P.total_blocks, nb);
     return hipGetLastError();
+}
+
+hipError_t launch_plan(const PlanArgs& a, PlanDev& P, hipStream_t st) {
+    if (a.d == 128) return launch_plan_t<128>(a, P, st);
+    if (a.d == 64) return launch_plan_t<64>(a, P, st);
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_fill_u32(unsigned int* p, unsigned int v, long long n, hipStream_t st) {

@@ -59,7 +59,7 @@ def _plan(lib, dtype=0, B=1, Hq=4, Hkv=4, N=1024, d=128, block=128, gamma=0.95, 
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(d=64), -2), (dict(d=256), -2), (dict(block=32), -2), (dict(dtype=7), -2),
+    (dict(d=96), -2), (dict(d=32), -2), (dict(d=256), -2), (dict(block=32), -2), (dict(dtype=7), -2),
     (dict(Hq=6, Hkv=4), -3), (dict(N=128 * 4097), -3), (dict(N=128 * 4096 + 1), -3), (dict(Hkv=0), -3),
     (dict(gamma=0.0), -1), (dict(gamma=1.5), -1), (dict(gamma=float("nan")), -1),
     (dict(tau=-0.1), -1), (dict(tau=float("inf")), -1), (dict(min_budget=-1), -1),
@@ -92,7 +92,7 @@ def test_empty_problems_need_no_device(lib):
 
 def test_attend_validation(lib):
     assert lib.fp_prefill_attend(None, 1, 1, 1, 1, None) == -1
-    assert lib.fp_dense_attend(1, 1, 1, 1, 0, 1, 4, 4, 1024, 64, 128, None) == -2
+    assert lib.fp_dense_attend(1, 1, 1, 1, 0, 1, 4, 4, 1024, 96, 128, None) == -2
     assert lib.fp_dense_attend(1, 1, 1, 1, 0, 1, 4, 3, 1024, 128, 128, None) == -3
     assert lib.fp_dense_attend(None, 1, 1, 1, 0, 1, 4, 4, 1024, 128, 128, None) == -1
     assert lib.fp_plan_copy_debug(None, 0, None, 0) == -1

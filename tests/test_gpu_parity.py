@@ -81,6 +81,12 @@ SMALL = {
                                                           explicit_types=("QA", "V", "S", "N")),
     # fp32 at block 64
     "bs64_fp32_1024": BY_NAME["tiny_fp32_4k"].with_(N=1024, block=64, min_budget=128),
+    # head dim 64: bf16 GQA 4:1 at block 128, bf16 block 64 with two batches, fp32 at both blocks
+    "d64_gqa_bf16_2k": BY_NAME["llama8b_32k"].with_(Hq=8, Hkv=2, N=2048, d=64, mix=(0.25, 0.25, 0.25, 0.25)),
+    "d64_bs64_bf16_1088_b2": BY_NAME["glm9b_64k_bs64"].with_(B=2, Hq=4, Hkv=2, N=1088, d=64, min_budget=256,
+                                                              explicit_types=("QA", "V", "S", "N")),
+    "d64_fp32_1024": BY_NAME["tiny_fp32_4k"].with_(N=1024, d=64),
+    "d64_bs64_fp32_704": BY_NAME["tiny_fp32_4k"].with_(N=704, d=64, block=64, min_budget=128),
 }
 
 

@@ -47,6 +47,10 @@ RAGGED = {
     "one_token_bf16": (BY_NAME["llama8b_32k"].with_(Hq=4, Hkv=1, explicit_types=("V", "S", "QA", "N")), 1),
     # fp32, block 64, 700 tokens
     "fp32_bs64_700": (BY_NAME["tiny_fp32_4k"].with_(block=64, min_budget=128), 700),
+    # head dim 64: bf16 at block 64 with two sequences, fp32 at block 128
+    "d64_bs64_bf16_1000_b2": (BY_NAME["glm9b_64k_bs64"].with_(B=2, Hq=4, Hkv=2, d=64, min_budget=256,
+                                                              explicit_types=("QA", "V", "S", "N")), 1000),
+    "d64_fp32_900": (BY_NAME["tiny_fp32_4k"].with_(d=64, min_budget=256), 900),
 }
 
 
@@ -100,6 +104,8 @@ VARLEN = {
     "bs64_bf16_mixed": (BY_NAME["glm9b_64k_bs64"].with_(Hq=4, Hkv=2, min_budget=256,
                                                         explicit_types=("QA", "V", "S", "N")), [1089, 130, 64]),
     "fp32_mixed": (BY_NAME["tiny_fp32_4k"].with_(min_budget=256), [300, 1024, 5]),
+    "d64_bf16_mixed": (BY_NAME["llama8b_32k"].with_(Hq=8, Hkv=2, d=64, mix=(0.25, 0.25, 0.25, 0.25)),
+                       [700, 0, 2048, 65]),
 }
 
 

@@ -78,6 +78,7 @@ SMALL = {
     "bs64_bf16_b2": (BY_NAME["glm9b_64k_bs64"].with_(B=2, Hq=4, Hkv=2, N=1088, min_budget=256,
                                                      explicit_types=("V", "V", "S", "QA")), 1088),
     "fp32_1024": (BY_NAME["tiny_fp32_4k"].with_(N=1024, explicit_types=("V", "V", "S", "QA")), 1024),
+    "d64_bf16_2k": (BY_NAME["llama8b_32k"].with_(Hq=8, Hkv=2, N=2048, d=64, mix=(0.5, 0.25, 0.25, 0.0)), 2048),
 }
 
 
