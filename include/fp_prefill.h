@@ -41,6 +41,10 @@
  *     the host unless its comment says "synchronizes".
  *   Ownership: the caller owns q, k, v, o and keeps them alive until the
  *     enqueued work completes.  The library owns every plan buffer.
+ *   Logging: with FP_LOG=1 in the environment every plan call synchronizes
+ *     its stream and prints one line for the plan and one per head (pattern,
+ *     square-root divergence, selected blocks and their share of the causal
+ *     blocks) on stderr.
  *   Errors: every call returns an fp_status; nothing aborts or throws across
  *     the ABI.  Arguments are validated on the host before any HIP call, so
  *     validation errors need no GPU.  fp_last_error() describes the most

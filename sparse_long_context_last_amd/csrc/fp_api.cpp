@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <cstdlib>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -187,18 +188,26 @@ std::vector<EvPair> g_prof_events;
 double g_prof_ms[2] = {0, 0};
 long long g_prof_n[2] = {0, 0};
 
+// Adds up the recorded kernel times and releases every event, also when one
+// of them cannot be read (that launch is then left out; the first failure is
+// returned).
 fp_status drain_profile_events() {
+    fp_status s = FP_OK;
     for (auto& e : g_prof_events) {
-        FP_HIP(hipEventSynchronize(e.b), "hipEventSynchronize");
         float ms = 0.f;
-        FP_HIP(hipEventElapsedTime(&ms, e.a, e.b), "hipEventElapsedTime");
-        g_prof_ms[e.dense ? 1 : 0] += ms;
-        g_prof_n[e.dense ? 1 : 0] += 1;
+        hipError_t he = hipEventSynchronize(e.b);
+        if (he == hipSuccess) he = hipEventElapsedTime(&ms, e.a, e.b);
+        if (he == hipSuccess) {
+            g_prof_ms[e.dense ? 1 : 0] += ms;
+            g_prof_n[e.dense ? 1 : 0] += 1;
+        } else if (s == FP_OK) {
+            s = hip_fail(he, "profiling events");
+        }
         (void)hipEventDestroy(e.a);
         (void)hipEventDestroy(e.b);
     }
     g_prof_events.clear();
-    return FP_OK;
+    return s;
 }
 
 void set_pool_threshold(int dev) {
@@ -432,6 +441,40 @@ fp_status attend_common(const void* q, const void* k, const void* v, void* o, fp
     return FP_OK;
 }
 
+// FP_LOG=1: one line per plan and one per head on stderr (pattern, divergence,
+// selected blocks and their share of the causal blocks).  Synchronizes the
+// plan's stream; a plan that cannot be read is reported as such.
+void log_plan(const fp_plan* p) {
+    const char* env = std::getenv("FP_LOG");
+    if (!env || std::strcmp(env, "1") != 0) return;
+    std::fprintf(stderr, "[fp_prefill] plan: %d sequence(s), Hq %d, Hkv %d, longest %d tokens, d %d, block %d, gamma %g, "
+                 "tau %g, min_budget %d, max_budget %d, %s, %s\n", p->B, p->Hq, p->Hkv, p->N, p->d, p->bs,
+                 (double)p->gamma, (double)p->tau, p->min_budget, p->max_budget,
+                 p->qa_selection == FP_QA_QUERYWISE ? "query-wise" : "flattened",
+                 p->vs_granularity == FP_VS_TOKEN ? "token columns" : "block columns");
+    if (p->segs.empty()) return;
+    const size_t BH = (size_t)p->B * p->Hq;
+    std::vector<unsigned char> pat(BH);
+    std::vector<double> djs(BH);
+    std::vector<unsigned long long> tot(BH);
+    hipError_t e = hipStreamSynchronize(p->stream);
+    if (e == hipSuccess) e = hipMemcpy(pat.data(), p->pattern, BH, hipMemcpyDeviceToHost);
+    if (e == hipSuccess) e = hipMemcpy(djs.data(), p->djs, BH * sizeof(double), hipMemcpyDeviceToHost);
+    if (e == hipSuccess) e = hipMemcpy(tot.data(), p->total_blocks, BH * sizeof(unsigned long long), hipMemcpyDeviceToHost);
+    if (e != hipSuccess) {
+        std::fprintf(stderr, "[fp_prefill] plan could not be read: %s\n", hipGetErrorString(e));
+        return;
+    }
+    for (size_t bh = 0; bh < BH; ++bh) {
+        const int b = (int)(bh / p->Hq), h = (int)(bh % p->Hq);
+        const long long nb = ((long long)p->seqlens[(size_t)b] + p->bs - 1) / p->bs;
+        const long long tri = nb * (nb + 1) / 2;
+        std::fprintf(stderr, "[fp_prefill]   seq %d head %d: %s D %.6f blocks %llu / %lld (%.4f)\n", b, h,
+                     pat[bh] == kPatternQueryAware ? "query-aware   " : "vertical-slash", djs[bh], tot[bh], tri,
+                     tri ? (double)tot[bh] / (double)tri : 0.0);
+    }
+}
+
 // Plan for every segment of a validated problem.
 fp_status make_plan(const void* q, const void* k, fp_dtype dtype, int layout, int B, int N, const int* cu, int Hq,
                     int Hkv, int d, int block, float gamma, float tau, int min_budget,
@@ -512,6 +555,7 @@ fp_status make_plan(const void* q, const void* k, fp_dtype dtype, int layout, in
     p->n_colptr = token ? n_cp : 0;
     if (segs.empty()) {
         p->device = -1;
+        log_plan(p);
         *out = p;
         return FP_OK;
     }
@@ -692,9 +736,15 @@ fp_status make_plan(const void* q, const void* k, fp_dtype dtype, int layout, in
     }
     if (lanes > 1) {
         // join: the caller's stream waits for every lane (also after a failure,
-        // so the workspace is not freed under running kernels)
+        // so the workspace is not freed under running kernels); a lane that
+        // cannot be joined that way is finished here, and the call fails
         for (int j = 0; j < lanes; ++j) {
-            if (ev[j] && hipEventRecord(ev[j], ls[j]) == hipSuccess) (void)hipStreamWaitEvent(st, ev[j], 0);
+            hipError_t je = ev[j] ? hipEventRecord(ev[j], ls[j]) : hipErrorInvalidValue;
+            if (je == hipSuccess) je = hipStreamWaitEvent(st, ev[j], 0);
+            if (je != hipSuccess) {
+                (void)hipStreamSynchronize(ls[j]);
+                if (he == hipSuccess) he = je;
+            }
         }
         for (int j = 0; j <= lanes; ++j)
             if (ev[j]) (void)hipEventDestroy(ev[j]);
@@ -711,6 +761,7 @@ fp_status make_plan(const void* q, const void* k, fp_dtype dtype, int layout, in
         free_plan(p);
         return hip_fail(he, "planning");
     }
+    log_plan(p);
     *out = p;
     return FP_OK;
 }

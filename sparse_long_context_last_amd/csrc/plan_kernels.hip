@@ -1399,6 +1399,8 @@ static hipError_t launch_plan_t(const PlanArgs& a, PlanDev& P, hipStream_t st) {
         he = hipEventRecord(join, ps);
         (void)hipEventDestroy(fork);
         if (he != hipSuccess) {
+            // the caller's stream cannot be made to wait: finish the pooling here
+            (void)hipStreamSynchronize(a.aux);
             (void)hipEventDestroy(join);
             return he;
         }
@@ -1446,7 +1448,10 @@ static hipError_t launch_plan_t(const PlanArgs& a, PlanDev& P, hipStream_t st) {
     if (a.aux) {
         he = hipStreamWaitEvent(st, join, 0);
         (void)hipEventDestroy(join);
-        if (he != hipSuccess) return he;
+        if (he != hipSuccess) {
+            (void)hipStreamSynchronize(a.aux);
+            return he;
+        }
     }
     hipLaunchKernelGGL(k_jsd, dim3(BH), dim3(256), 0, st, P.ahat, P.atrue, P.djs, P.pattern, nb, a.tau, a.canon);
     // K6

@@ -277,3 +277,26 @@ def test_wide_range_bf16_scores(F, block):
     k[:, :, ::5, :] = _wide_bf16(rng, k[:, :, ::5, :].shape, -75, -64)
     v = rng.standard_normal((1, cfg.Hkv, cfg.N, cfg.d)).astype(np.float32)
     run_and_compare(F, cfg, q, k, v, attention=False, dense=False)
+
+
+def test_plan_log_lines_match_the_plan(F, monkeypatch, capfd):
+    """FP_LOG=1: one line for the plan and one per head whose pattern,
+    divergence and block count agree with the plan's own copy."""
+    import re
+    cfg = SMALL["gqa_bf16_2k"]
+    q, k, _ = LayerGen(cfg).numpy_layer()
+    monkeypatch.setenv("FP_LOG", "1")
+    P = F.plan(to_dev(q, "bf16"), to_dev(k, "bf16"), block=cfg.block, gamma=cfg.gamma, tau=cfg.tau,
+               min_budget=cfg.min_budget)
+    monkeypatch.delenv("FP_LOG")
+    err = capfd.readouterr().err
+    pattern, djs, row_ptr, _ = P.copy_out()
+    lines = [l for l in err.splitlines() if l.startswith("[fp_prefill]   seq")]
+    assert len(lines) == cfg.Hq and "[fp_prefill] plan: 1 sequence(s), Hq 8, Hkv 2" in err
+    tri = cfg.nb * (cfg.nb + 1) // 2
+    for h, line in enumerate(lines):
+        m = re.search(r"head (\d+): (\S+)\s+D (\S+) blocks (\d+) / (\d+)", line)
+        assert int(m.group(1)) == h
+        assert m.group(2) == ("query-aware" if pattern[h] == O.QUERY_AWARE else "vertical-slash")
+        assert abs(float(m.group(3)) - djs[h]) <= 5e-7
+        assert int(m.group(4)) == row_ptr[(h + 1) * cfg.nb] - row_ptr[h * cfg.nb] and int(m.group(5)) == tri
