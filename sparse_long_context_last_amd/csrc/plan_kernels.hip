@@ -312,9 +312,14 @@ __global__ __launch_bounds__(256, 3) void k_scores(const float* __restrict__ qt,
 // Built for two waves per SIMD.  Used for bf16 inputs (fp32 ones keep
 // k_scores).
 // Same outputs as k_scores: s2 (0 past L) and the per-chunk causal row maxima.
-// Measured on the 128k layer: 1.54 ms against 1.9 ms for k_scores.  Storing a
-// step's scores during the next step's MFMAs, or two tiles per step at three
-// waves per SIMD, ran out of registers (spills) and measured slower.
+// The bf16 half of a key word is widened with one v_perm_b32 per MFMA, and
+// steps whose keys all precede the first query position skip the causal and
+// length tests: the vector ALU then issues about a third of the instructions
+// of shift/mask/select widening with the tests everywhere, and the kernel
+// takes 1.31-1.37 ms on the 128k layer (1.54 ms before; 1.9 ms for k_scores).
+// Storing a step's scores during the next step's MFMAs, or two tiles per
+// step at three waves per SIMD, ran out of registers (spills) and measured
+// slower.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ void lds_copy16(const void* base, unsigned voff, void* dst) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
@@ -374,6 +379,10 @@ __global__ __launch_bounds__(256, 2) void k_scores_mfma(const float* __restrict_
     }
     // this lane's key row within the step: kg 128 + 32 q + l32; its 16-byte chunk c sits at c ^ (row % CH)
     const int krow0 = kg * 32 * NQ + l32;
+    // byte selector of v_perm_b32 that widens this lane's bf16 half of a 32-bit
+    // word to fp32 (bits moved to the top, low half zero): the low half for
+    // contraction index 2 t, the high half for 2 t + 1
+    const unsigned bsel = par ? 0x03020c0cu : 0x01000c0cu;
     // this lane's query of the transposed product S^T = K Q^T, and its position
     const int qi = qg * 32 + l32, qpos = L - BS + qi;
     float* const srow = s2 + ((size_t)bh * BS + qi) * NS;
@@ -397,28 +406,45 @@ __global__ __launch_bounds__(256, 2) void k_scores_mfma(const float* __restrict_
             _Pragma("unroll") for (int u = 0; u < 4; ++u)                                                  \
             _Pragma("unroll") for (int q = 0; q < NQ; ++q) {                                               \
                 const unsigned wd = u == 0 ? bv[q].x : u == 1 ? bv[q].y : u == 2 ? bv[q].z : bv[q].w;      \
-                const float kb = __uint_as_float(par ? (wd & 0xffff0000u) : (wd << 16));                  \
+                const float kb = __uint_as_float(__builtin_amdgcn_perm(0u, wd, bsel));                     \
                 acc[q] = __builtin_amdgcn_mfma_f32_32x32x2f32(kb, qa[4 * c + u], acc[q], 0, 0, 0);         \
             }                                                                                              \
         }                                                                                                  \
-        /* lane: query qi, keys .. + 32 q + 8 (r / 4) + 4 par + r % 4: four consecutive per store */     \
-        _Pragma("unroll") for (int q = 0; q < NQ; ++q)                                                     \
-        _Pragma("unroll") for (int g4 = 0; g4 < 4; ++g4) {                                                 \
-            const int j = key0_ + kg * 32 * NQ + 32 * q + 8 * g4 + 4 * par;                                \
-            float4 v_;                                                                                     \
-            v_.x = acc[q][4 * g4] * C;                                                                     \
-            v_.y = acc[q][4 * g4 + 1] * C;                                                                 \
-            v_.z = acc[q][4 * g4 + 2] * C;                                                                 \
-            v_.w = acc[q][4 * g4 + 3] * C;                                                                 \
-            if (j <= qpos) mx = fmaxf(mx, v_.x);                                                           \
-            if (j + 1 <= qpos) mx = fmaxf(mx, v_.y);                                                       \
-            if (j + 2 <= qpos) mx = fmaxf(mx, v_.z);                                                       \
-            if (j + 3 <= qpos) mx = fmaxf(mx, v_.w);                                                       \
-            if (j >= L) v_.x = 0.0f;                                                                       \
-            if (j + 1 >= L) v_.y = 0.0f;                                                                   \
-            if (j + 2 >= L) v_.z = 0.0f;                                                                   \
-            if (j + 3 >= L) v_.w = 0.0f;                                                                   \
-            *reinterpret_cast<float4*>(srow + j) = v_;                                                     \
+        /* lane: query qi, keys .. + 32 q + 8 (r / 4) + 4 par + r % 4: four consecutive per store. */    \
+        /* A step whose keys all precede the first query position needs neither the causal */            \
+        /* nor the length test (uniform branch). */                                                      \
+        if (key0_ + KP <= L - BS + 1) {                                                                    \
+            _Pragma("unroll") for (int q = 0; q < NQ; ++q)                                                 \
+            _Pragma("unroll") for (int g4 = 0; g4 < 4; ++g4) {                                             \
+                const int j = key0_ + kg * 32 * NQ + 32 * q + 8 * g4 + 4 * par;                            \
+                float4 v_;                                                                                 \
+                v_.x = acc[q][4 * g4] * C;                                                                 \
+                v_.y = acc[q][4 * g4 + 1] * C;                                                             \
+                v_.z = acc[q][4 * g4 + 2] * C;                                                             \
+                v_.w = acc[q][4 * g4 + 3] * C;                                                             \
+                mx = fmaxf(fmaxf(mx, v_.x), v_.y);                                                         \
+                mx = fmaxf(fmaxf(mx, v_.z), v_.w);                                                         \
+                *reinterpret_cast<float4*>(srow + j) = v_;                                                 \
+            }                                                                                              \
+        } else {                                                                                           \
+            _Pragma("unroll") for (int q = 0; q < NQ; ++q)                                                 \
+            _Pragma("unroll") for (int g4 = 0; g4 < 4; ++g4) {                                             \
+                const int j = key0_ + kg * 32 * NQ + 32 * q + 8 * g4 + 4 * par;                            \
+                float4 v_;                                                                                 \
+                v_.x = acc[q][4 * g4] * C;                                                                 \
+                v_.y = acc[q][4 * g4 + 1] * C;                                                             \
+                v_.z = acc[q][4 * g4 + 2] * C;                                                             \
+                v_.w = acc[q][4 * g4 + 3] * C;                                                             \
+                if (j <= qpos) mx = fmaxf(mx, v_.x);                                                       \
+                if (j + 1 <= qpos) mx = fmaxf(mx, v_.y);                                                   \
+                if (j + 2 <= qpos) mx = fmaxf(mx, v_.z);                                                   \
+                if (j + 3 <= qpos) mx = fmaxf(mx, v_.w);                                                   \
+                if (j >= L) v_.x = 0.0f;                                                                   \
+                if (j + 1 >= L) v_.y = 0.0f;                                                               \
+                if (j + 2 >= L) v_.z = 0.0f;                                                               \
+                if (j + 3 >= L) v_.w = 0.0f;                                                               \
+                *reinterpret_cast<float4*>(srow + j) = v_;                                                 \
+            }                                                                                              \
         }                                                                                                  \
         if ((st_) % SPC == SPC - 1) {                                                                      \
             /* chunk done: its row maxima (the other half of the keys sits in lane ^ 32) */                \
@@ -514,18 +540,33 @@ __global__ __launch_bounds__(256) void k_rowexp(const float* __restrict__ s2, co
     float Z = 0.0f;
     int zn = 0;
     for (int seg0 = 0; seg0 < L; seg0 += SEG) {
+        if (seg0 + SEG - 1 <= pos) {
+            // every key of the segment is causal and inside the sequence
 #pragma unroll
-        for (int u = 0; u < NU; ++u) {
-            const int jl = u * 1024 + 4 * tid;      // 4 consecutive keys, coalesced
-            const int j = seg0 + jl;
-            float4 v = buf[u];
-            const bool in = j < L;
-            v.x = in && j <= pos ? exp2_c(v.x - M, K) : 0.0f;
-            v.y = in && j + 1 <= pos ? exp2_c(v.y - M, K) : 0.0f;
-            v.z = in && j + 2 <= pos ? exp2_c(v.z - M, K) : 0.0f;
-            v.w = in && j + 3 <= pos ? exp2_c(v.w - M, K) : 0.0f;
-            float* e = &es[jl / BS][jl % BS];
-            e[0] = v.x; e[1] = v.y; e[2] = v.z; e[3] = v.w;
+            for (int u = 0; u < NU; ++u) {
+                const int jl = u * 1024 + 4 * tid;      // 4 consecutive keys, coalesced
+                float4 v = buf[u];
+                v.x = exp2_c(v.x - M, K);
+                v.y = exp2_c(v.y - M, K);
+                v.z = exp2_c(v.z - M, K);
+                v.w = exp2_c(v.w - M, K);
+                float* e = &es[jl / BS][jl % BS];
+                e[0] = v.x; e[1] = v.y; e[2] = v.z; e[3] = v.w;
+            }
+        } else {
+#pragma unroll
+            for (int u = 0; u < NU; ++u) {
+                const int jl = u * 1024 + 4 * tid;
+                const int j = seg0 + jl;
+                float4 v = buf[u];
+                const bool in = j < L;
+                v.x = in && j <= pos ? exp2_c(v.x - M, K) : 0.0f;
+                v.y = in && j + 1 <= pos ? exp2_c(v.y - M, K) : 0.0f;
+                v.z = in && j + 2 <= pos ? exp2_c(v.z - M, K) : 0.0f;
+                v.w = in && j + 3 <= pos ? exp2_c(v.w - M, K) : 0.0f;
+                float* e = &es[jl / BS][jl % BS];
+                e[0] = v.x; e[1] = v.y; e[2] = v.z; e[3] = v.w;
+            }
         }
         if (tid == 0)
             for (int i = 0; i < zn; ++i) Z = Z + zs[i];
@@ -562,20 +603,25 @@ __global__ __launch_bounds__(256) void k_rowexp(const float* __restrict__ s2, co
 //   diagsum[o] = sum_{i: pos_i >= o} p[i][pos_i - o],  i ascending.
 // Workgroup x owns columns j0 .. j0+W-1 and the offsets o = L - BS - j0 - t,
 // t in [0, W): row i of such an offset reads column j0 + t + i, so one LDS
-// tile of W + BS columns per row serves both sums.  Rows are staged RC at a
-// time (8 at block 128: a 20 KB tile, several workgroups per CU; 16 at block
-// 64, where RC (W + BS) must stay a multiple of 1024 for the float4 tiling);
-// every thread keeps its sums in registers across the chunks.
+// tile of W + BS columns per row serves both sums (the BS extra columns are
+// also in the next workgroup's tile: BS / W of the exponentials are formed
+// twice).  W = 1024 where that still leaves at least 2048 workgroups, else
+// 512 (measured: 0.48 -> 0.45 ms on the 128k layer, but 0.14 -> 0.16 ms on
+// the 32k one, whose 1024 workgroups then fill the chip only once).  Rows
+// are staged RC at a time (8 at block 128; 16 at block 64, where RC (W + BS)
+// must stay a multiple of 1024 for the float4 tiling); every thread keeps its
+// sums in registers across the chunks.  The tile holds p = e * rz (the
+// product is rounded once whichever sum uses it).
 // Offsets above L - BS are done by k_diagtail.  grid (ceil(L / W), BH).
 // Rows that do not exist (L < BS) have M = rz = 0 and contribute zeros.
 // ---------------------------------------------------------------------------
-constexpr int kLineW = 512;
+inline int line_width(int L, int BH) { return (long long)((L + 1023) / 1024) * BH >= 2048 ? 1024 : 512; }
 
-template <int BS>
+template <int BS, int W>
 __global__ __launch_bounds__(256) void k_linesums(const float* __restrict__ s2, const float* __restrict__ rowmax,
                                                   const float* __restrict__ rz, float* __restrict__ colsum,
                                                   float* __restrict__ diagsum, int L, int NS, Canon K) {
-    constexpr int W = kLineW, RC = BS == 128 ? 8 : 16, TW = W + BS;
+    constexpr int RC = BS == 128 ? 8 : 16, TW = W + BS;
     __shared__ __attribute__((aligned(16))) float es[RC][TW];
     __shared__ float sM[BS], sR[BS];
     const int tid = threadIdx.x, bh = blockIdx.y;
@@ -604,34 +650,49 @@ __global__ __launch_bounds__(256) void k_linesums(const float* __restrict__ s2, 
     FP_LOAD_CHUNK(0);
     __syncthreads();
     for (int i0 = 0; i0 < BS; i0 += RC) {
+        if (j0 + TW - 1 <= L - BS) {
+            // every column of the tile is causal for every row and inside the sequence
 #pragma unroll
-        for (int n = 0; n < NL; ++n) {
-            const int e4 = tid + 256 * n;
-            const int ii = e4 / (TW / 4), cc = 4 * (e4 % (TW / 4));
-            const int i = i0 + ii, j = j0 + cc, pos = L - BS + i;
-            const float4 v = buf[n];
-            const float M = sM[i];
-            const bool in = j < L;
-            float4 x;
-            x.x = in && j <= pos ? exp2_c(v.x - M, K) : 0.0f;
-            x.y = in && j + 1 <= pos ? exp2_c(v.y - M, K) : 0.0f;
-            x.z = in && j + 2 <= pos ? exp2_c(v.z - M, K) : 0.0f;
-            x.w = in && j + 3 <= pos ? exp2_c(v.w - M, K) : 0.0f;
-            *reinterpret_cast<float4*>(&es[ii][cc]) = x;
+            for (int n = 0; n < NL; ++n) {
+                const int e4 = tid + 256 * n;
+                const int ii = e4 / (TW / 4), cc = 4 * (e4 % (TW / 4));
+                const int i = i0 + ii;
+                const float4 v = buf[n];
+                const float M = sM[i], r = sR[i];
+                float4 x;
+                x.x = exp2_c(v.x - M, K) * r;
+                x.y = exp2_c(v.y - M, K) * r;
+                x.z = exp2_c(v.z - M, K) * r;
+                x.w = exp2_c(v.w - M, K) * r;
+                *reinterpret_cast<float4*>(&es[ii][cc]) = x;
+            }
+        } else {
+#pragma unroll
+            for (int n = 0; n < NL; ++n) {
+                const int e4 = tid + 256 * n;
+                const int ii = e4 / (TW / 4), cc = 4 * (e4 % (TW / 4));
+                const int i = i0 + ii, j = j0 + cc, pos = L - BS + i;
+                const float4 v = buf[n];
+                const float M = sM[i], r = sR[i];
+                const bool in = j < L;
+                float4 x;
+                x.x = in && j <= pos ? exp2_c(v.x - M, K) * r : 0.0f;
+                x.y = in && j + 1 <= pos ? exp2_c(v.y - M, K) * r : 0.0f;
+                x.z = in && j + 2 <= pos ? exp2_c(v.z - M, K) * r : 0.0f;
+                x.w = in && j + 3 <= pos ? exp2_c(v.w - M, K) * r : 0.0f;
+                *reinterpret_cast<float4*>(&es[ii][cc]) = x;
+            }
         }
         __syncthreads();
         if (i0 + RC < BS) { FP_LOAD_CHUNK(i0 + RC); }
 #pragma unroll 4
         for (int ii = 0; ii < RC; ++ii) {
             const int i = i0 + ii;
-            const float r = sR[i];
 #pragma unroll
             for (int q = 0; q < W / 256; ++q) {
                 const int t = tid + 256 * q;
-                float p = es[ii][t] * r;
-                cacc[q] = cacc[q] + p;
-                p = es[ii][t + i] * r;
-                gacc[q] = gacc[q] + p;
+                cacc[q] = cacc[q] + es[ii][t];
+                gacc[q] = gacc[q] + es[ii][t + i];
             }
         }
         __syncthreads();
@@ -1385,10 +1446,13 @@ static hipError_t launch_plan_t(const PlanArgs& a, PlanDev& P, hipStream_t st) {
         hipLaunchKernelGGL((k_pool<float, D>), dim3(pg, BH), dim3(256), 0, ps, (const float*)a.q, a.qs, a.Hq, P.qbar, L, BS);
         hipLaunchKernelGGL((k_pool<float, D>), dim3(pg, bkv), dim3(256), 0, ps, (const float*)a.k, a.ks, a.Hkv, P.kbar, L, BS);
     }
-    // K4: the estimated block map needs only the pooled vectors
+    // K4: the estimated block map needs only the pooled vectors.  At most
+    // 22 KB of LDS per workgroup, so that one fits on a CU beside the two
+    // score workgroups (64 KB each) running on the other stream: the vector
+    // ALU work of the estimate then overlaps their matrix work.
     if (nb <= 1024) {
-        const size_t lds = (size_t)8 * nb * sizeof(float);
-        hipLaunchKernelGGL((k_estimate<8, D>), dim3((nb + 7) / 8, BH), dim3(256), lds, ps, P.qbar, P.kbar, P.ahat, nb,
+        const size_t lds = (size_t)4 * nb * sizeof(float);
+        hipLaunchKernelGGL((k_estimate<4, D>), dim3((nb + 3) / 4, BH), dim3(256), lds, ps, P.qbar, P.kbar, P.ahat, nb,
                            a.Hq, a.Hkv, group, a.canon);
     } else {
         const size_t lds = (size_t)2 * nb * sizeof(float);
@@ -1431,18 +1495,27 @@ static hipError_t launch_plan_t(const PlanArgs& a, PlanDev& P, hipStream_t st) {
     else
         hipLaunchKernelGGL(k_rowexp<64>, dim3(BS, BH), dim3(256), 0, st, a.s2, a.pmax, P.rowmax, P.rowsum, a.rz, L,
                            NS, a.canon);
-    const dim3 gl((L + kLineW - 1) / kLineW, BH);
+    const int lw = line_width(L, BH);
+    const dim3 gl((L + lw - 1) / lw, BH);
+#define FP_LINESUMS(B_)                                                                                    \
+    do {                                                                                                   \
+        if (lw == 1024)                                                                                    \
+            hipLaunchKernelGGL((k_linesums<B_, 1024>), gl, dim3(256), 0, st, a.s2, P.rowmax, a.rz, P.colsum,  \
+                               P.diagsum, L, NS, a.canon);                                                 \
+        else                                                                                               \
+            hipLaunchKernelGGL((k_linesums<B_, 512>), gl, dim3(256), 0, st, a.s2, P.rowmax, a.rz, P.colsum,   \
+                               P.diagsum, L, NS, a.canon);                                                 \
+    } while (0)
     if (BS == 128) {
-        hipLaunchKernelGGL(k_linesums<128>, gl, dim3(256), 0, st, a.s2, P.rowmax, a.rz, P.colsum, P.diagsum, L, NS,
-                           a.canon);
+        FP_LINESUMS(128);
         hipLaunchKernelGGL(k_diagtail<128>, dim3(BH), dim3(128), 0, st, a.s2, P.rowmax, a.rz, P.diagsum, L, NS,
                            a.canon);
     } else {
-        hipLaunchKernelGGL(k_linesums<64>, gl, dim3(256), 0, st, a.s2, P.rowmax, a.rz, P.colsum, P.diagsum, L, NS,
-                           a.canon);
+        FP_LINESUMS(64);
         hipLaunchKernelGGL(k_diagtail<64>, dim3(BH), dim3(64), 0, st, a.s2, P.rowmax, a.rz, P.diagsum, L, NS,
                            a.canon);
     }
+#undef FP_LINESUMS
     hipLaunchKernelGGL(k_atrue, dim3(BH), dim3(256), 0, st, P.colsum, P.atrue, L, BS);
     // K5
     if (a.aux) {
