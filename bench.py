@@ -37,6 +37,64 @@ ATTN_SOURCES = ("attn_kernels.hip",)
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "attention_counters_llama8b_128k.md")
 
 
+class PowerSampler:
+    """Socket power and graphics clock of the GPU sampled from the driver's
+    metrics table (amdsmi, read-only) every 10 ms while a timed region runs.
+    The chip holds its socket power at the cap under these kernels, so the
+    clock it settles at explains the attention kernel's fraction of the
+    2.4 GHz matrix peak.  Absent (None) where amdsmi is not available."""
+
+    def __init__(self):
+        self.ok = False
+        try:
+            import threading
+            import amdsmi
+            amdsmi.amdsmi_init()
+            self._smi = amdsmi
+            self._h = amdsmi.amdsmi_get_processor_handles()[0]
+            cap = amdsmi.amdsmi_get_power_cap_info(self._h).get("power_cap")
+            self.cap_w = round(cap / 1e6, 1) if isinstance(cap, (int, float)) else None
+            self._threading = threading
+            self.ok = True
+        except Exception:
+            pass
+
+    def _read(self):
+        m = self._smi.amdsmi_get_gpu_metrics_info(self._h)
+        pw, clk = m.get("current_socket_power"), m.get("current_gfxclk")
+        ok = lambda v: isinstance(v, (int, float)) and 0 < v < 65535
+        return (pw if ok(pw) else None), (clk if ok(clk) else None)
+
+    def start(self):
+        if not self.ok:
+            return
+        self._stop = False
+        self._samples = []
+
+        def run():
+            while not self._stop:
+                try:
+                    self._samples.append(self._read())
+                except Exception:
+                    pass
+                time.sleep(0.01)
+        self._t = self._threading.Thread(target=run, daemon=True)
+        self._t.start()
+
+    def stop(self):
+        if not self.ok:
+            return None
+        self._stop = True
+        self._t.join()
+        s = self._samples[len(self._samples) // 5:]     # the first fifth covers the ramp from idle
+        pw = sorted(x for x, _ in s if x is not None)
+        clk = sorted(y for _, y in s if y is not None)
+        if not pw or not clk:
+            return None
+        return {"source": "amdsmi gpu metrics", "samples": len(s), "socket_power_w_median": pw[len(pw) // 2],
+                "gfxclk_mhz_median": clk[len(clk) // 2], "power_cap_w": self.cap_w}
+
+
 def kernel_source_hash() -> str:
     """Hash of the attention kernel source without its // comments and blank
     lines (a comment edit does not change the kernel the counters measured)."""
@@ -226,6 +284,8 @@ def main() -> int:
            torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     plans = []
     torch.cuda.synchronize()
+    power = PowerSampler()
+    power.start()
     t_wall = time.perf_counter()
     for i in range(args.steps):
         ev[i][0].record(stream)
@@ -236,6 +296,7 @@ def main() -> int:
         plans.append(P)
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t_wall) * 1e3 / args.steps
+    power_steps = power.stop()
     plan_ms = float(np.median([a.elapsed_time(b) for a, b, _ in ev]))
     attend_ms = float(np.median([b.elapsed_time(c) for _, b, c in ev]))
     step_ms = float(np.mean([a.elapsed_time(c) for a, _, c in ev]))
@@ -261,6 +322,7 @@ def main() -> int:
     achieved = sparse_flop / (kern_avg_ms * 1e-3) / 1e12
 
     dense_ms = None
+    power_dense = None
     if not args.no_dense:
         F.profile_enable(True)
         F.profile_read(reset=True)
@@ -274,11 +336,14 @@ def main() -> int:
         torch.cuda.synchronize()
         F.profile_read(reset=True)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        pd = PowerSampler()
+        pd.start()
         e0.record(stream)
         for _ in range(args.dense_reps):
             dense()
         e1.record(stream)
         torch.cuda.synchronize()
+        power_dense = pd.stop()
         dense_ms = e0.elapsed_time(e1) / args.dense_reps
         _, _, dk_ms, dk_n = F.profile_read(reset=True)
         F.profile_enable(False)
@@ -343,6 +408,8 @@ def main() -> int:
         "mfma_frac_attention_kernel": round(achieved / peak, 4),
         "dense_eff_tflops": round(dense_flop / (dense_kernel_ms * 1e-3) / 1e12, 1) if dense_ms else None,
         "roofline": roof,
+        "power_timed_steps": power_steps,
+        "power_dense": power_dense,
         "cpu_baseline": cpu,
         "input_generation_s": round(gen_s, 1),
     }

@@ -328,8 +328,9 @@ __global__ __launch_bounds__(PAIR ? 2 * 2 * BS : 2 * BS, (PAIR && BS == 128) ? 1
         __syncthreads();
         if (w == 0) {
             // lane l: blocks 64 l .. 64 l + 63; exclusive scan of the union counts
-            const unsigned u0 = pbits[0][2 * lane] | pbits[1][2 * lane];
-            const unsigned u1 = pbits[0][2 * lane + 1] | pbits[1][2 * lane + 1];
+            const unsigned a0 = pbits[0][2 * lane], b0 = pbits[1][2 * lane];
+            const unsigned a1 = pbits[0][2 * lane + 1], b1 = pbits[1][2 * lane + 1];
+            const unsigned u0 = a0 | b0, u1 = a1 | b1;
             const int c = __popc(u0) + __popc(u1);
             int incl = c;
 #pragma unroll
@@ -338,8 +339,15 @@ __global__ __launch_bounds__(PAIR ? 2 * 2 * BS : 2 * BS, (PAIR && BS == 128) ? 1
                 if (lane >= o) incl += t;
             }
             int at = incl - c;
-            for (unsigned m = u0; m; m &= m - 1) ulist[at++] = (unsigned short)(64 * lane + __builtin_ctz(m));
-            for (unsigned m = u1; m; m &= m - 1) ulist[at++] = (unsigned short)(64 * lane + 32 + __builtin_ctz(m));
+            // entry: key block | in the list of block qb (bit 12) | of block qb - 1 (bit 13)
+            for (unsigned m = u0; m; m &= m - 1) {
+                const int t = __builtin_ctz(m);
+                ulist[at++] = (unsigned short)((64 * lane + t) | ((a0 >> t) & 1u) << 12 | ((b0 >> t) & 1u) << 13);
+            }
+            for (unsigned m = u1; m; m &= m - 1) {
+                const int t = __builtin_ctz(m);
+                ulist[at++] = (unsigned short)((64 * lane + 32 + t) | ((a1 >> t) & 1u) << 12 | ((b1 >> t) & 1u) << 13);
+            }
             if (lane == 63) ucnt[0] = incl;
         }
         __syncthreads();
@@ -348,11 +356,21 @@ __global__ __launch_bounds__(PAIR ? 2 * 2 * BS : 2 * BS, (PAIR && BS == 128) ? 1
     } else if constexpr (PAIR) {
         nsub = nstage = (rid.qb + 1) * SPB;
     }
-    // key block of stage s, and whether it is in this wave's own list
-#define FP_KB(s_) (UNION ? (int)__builtin_amdgcn_readfirstlane((int)ulist[(s_) / SPB])                    \
+    // Union walks keep the list entries of stages s, s + 1 and s + 2 in scalar
+    // registers (uwin) and read the entry of stage s + 3 from LDS during stage
+    // s, so no tile load waits on an LDS read for its address.
+    const int ulast = UNION ? (nsub > 0 ? nsub / SPB - 1 : 0) : 0;
+    int uwin[3] = {0, 0, 0};
+    if constexpr (UNION) {
+#pragma unroll
+        for (int i = 0; i < 3; ++i) uwin[i] = __builtin_amdgcn_readfirstlane((int)ulist[min(i / SPB, ulast)]);
+    }
+    // key block of stage s_ (for union walks s_ is s_cur, s_cur + 1 or
+    // s_cur + 2, s_cur being the stage in progress), and whether a block is in
+    // this wave's own list
+#define FP_KB(s_) (UNION ? (uwin[(s_) - s_cur] & 4095)                                                     \
                          : (PAIR ? (s_) / SPB : (SPARSE ? lst[(s_) / SPB] : (s_) / SPB)))
-#define FP_MINE(kb_) (!PAIR || (UNION ? ((__builtin_amdgcn_readfirstlane(pbits[prow][(kb_) >> 5]) >> ((kb_) & 31)) & 1u) != 0 \
-                                      : (kb_) <= qb))
+#define FP_MINE(kb_) (!PAIR || (kb_) <= qb)
     const unsigned char* KG = GATHER ? (const unsigned char*)a.kg + rid.g0 * 2 : nullptr;
     const unsigned char* VGT = GATHER ? (const unsigned char*)a.vgt + rid.g0 * 2 : nullptr;
     if (GATHER && !PAIR && ngs > 0) {
@@ -455,9 +473,13 @@ __global__ __launch_bounds__(PAIR ? 2 * 2 * BS : 2 * BS, (PAIR && BS == 128) ? 1
     // unit computes the scores of tile s + 1, then O^T += V^T P^T of tile s.
     // K tiles are fetched two stages ahead, V^T tiles one stage ahead.
     f32x16_t scA[NT], scB[NT];
-    FP_FETCH_K(0, Ks0);
-    FP_FETCH_V(0, Vs0);
-    if (nstage > 1) { FP_FETCH_K(1, Ks1); }
+    {
+        const int s_cur = 0;
+        (void)s_cur;
+        FP_FETCH_K(0, Ks0);
+        FP_FETCH_V(0, Vs0);
+        if (nstage > 1) { FP_FETCH_K(1, Ks1); }
+    }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
 #pragma unroll
@@ -471,14 +493,17 @@ __global__ __launch_bounds__(PAIR ? 2 * 2 * BS : 2 * BS, (PAIR && BS == 128) ? 1
     // keep that order, so each MFMA runs while the vector ALU works.
 #define FP_STAGE_BF16(s, KC_, VC_, KN_, VN_, SC_, SN_)                                                   \
     {                                                                                                    \
+        const int s_cur = (s);                                                                           \
+        (void)s_cur;                                                                                     \
         const bool gst = GATHER && (s) >= nsub;                                                          \
         const int kb = gst ? -1 : FP_KB(s);                                                              \
         const int sub = (s) % SPB;                                                                       \
+        const int uvn = UNION ? (int)ulist[min(((s) + 3) / SPB, ulast)] : 0;                             \
         if ((s) + 2 < nstage) { FP_FETCH_K((s) + 2, KN_); }                                              \
         if ((s) + 1 < nstage) { FP_FETCH_V((s) + 1, VN_); }                                              \
         /* PAIR: a tile outside the wave's own list gets scores and exponentials */                     \
         /* (cheap: the union exceeds each list by a few tiles) but no P V and no row sum */              \
-        const bool mS = gst || FP_MINE(kb);                                                              \
+        const bool mS = gst || (UNION ? ((uwin[0] >> (12 + prow)) & 1) != 0 : FP_MINE(kb));            \
         if (kb == qb) {                                                                                  \
             _Pragma("unroll") for (int t = 0; t < NT; ++t)                                               \
             _Pragma("unroll") for (int r = 0; r < 16; ++r) {                                             \
@@ -536,6 +561,11 @@ __global__ __launch_bounds__(PAIR ? 2 * 2 * BS : 2 * BS, (PAIR && BS == 128) ? 1
                 if (i + RING < NMV) fr[i % RING] = FP_VFRAG(VC_, (i + RING) % TDV, (i + RING) / TDV);    \
                 __builtin_amdgcn_sched_barrier(0);                                                       \
             }                                                                                            \
+        }                                                                                                \
+        if constexpr (UNION) {                                                                           \
+            uwin[0] = uwin[1];                                                                           \
+            uwin[1] = uwin[2];                                                                           \
+            uwin[2] = __builtin_amdgcn_readfirstlane(uvn);                                               \
         }                                                                                                \
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");                                                 \
         __syncthreads();                                                                                 \
