@@ -38,11 +38,14 @@ COUNTERS_FILE = os.path.join(ROOT, "profiles", "attention_counters_llama8b_128k.
 
 
 class PowerSampler:
-    """Socket power and graphics clock of the GPU sampled from the driver's
-    metrics table (amdsmi, read-only) every 10 ms while a timed region runs.
-    The chip holds its socket power at the cap under these kernels, so the
-    clock it settles at explains the attention kernel's fraction of the
-    2.4 GHz matrix peak.  Absent (None) where amdsmi is not available."""
+    """Socket power and graphics clock of the GPU, read from the driver's
+    metrics table (amdsmi, read-only) every 10 ms while a callable runs
+    back to back for a few seconds.  The table lags the load by a few hundred
+    milliseconds, so the first 40 % of the samples are dropped and a window
+    much shorter than a second reads stale values.  The chip holds its socket
+    power at the cap under these kernels, and the clock it settles at explains
+    the attention kernel's fraction of the 2.4 GHz matrix peak.  Returns None
+    where amdsmi is not available."""
 
     def __init__(self):
         self.ok = False
@@ -65,34 +68,39 @@ class PowerSampler:
         ok = lambda v: isinstance(v, (int, float)) and 0 < v < 65535
         return (pw if ok(pw) else None), (clk if ok(clk) else None)
 
-    def start(self):
+    def measure(self, fn, seconds: float, sync_every: int = 4):
         if not self.ok:
-            return
-        self._stop = False
-        self._samples = []
+            return None
+        import torch
+        stop, samples = [False], []
 
         def run():
-            while not self._stop:
+            while not stop[0]:
                 try:
-                    self._samples.append(self._read())
+                    samples.append(self._read())
                 except Exception:
                     pass
                 time.sleep(0.01)
-        self._t = self._threading.Thread(target=run, daemon=True)
-        self._t.start()
-
-    def stop(self):
-        if not self.ok:
-            return None
-        self._stop = True
-        self._t.join()
-        s = self._samples[len(self._samples) // 5:]     # the first fifth covers the ramp from idle
+        t = self._threading.Thread(target=run, daemon=True)
+        t.start()
+        t0, n = time.perf_counter(), 0
+        while time.perf_counter() - t0 < seconds:
+            fn()
+            n += 1
+            if n % sync_every == 0:
+                torch.cuda.synchronize()
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
+        stop[0] = True
+        t.join()
+        s = samples[int(len(samples) * 0.4):]
         pw = sorted(x for x, _ in s if x is not None)
         clk = sorted(y for _, y in s if y is not None)
         if not pw or not clk:
             return None
-        return {"source": "amdsmi gpu metrics", "samples": len(s), "socket_power_w_median": pw[len(pw) // 2],
-                "gfxclk_mhz_median": clk[len(clk) // 2], "power_cap_w": self.cap_w}
+        return {"source": "amdsmi gpu metrics", "window_s": round(elapsed, 2), "calls": n, "samples": len(s),
+                "socket_power_w_median": pw[len(pw) // 2], "gfxclk_mhz_median": clk[len(clk) // 2],
+                "power_cap_w": self.cap_w}
 
 
 def kernel_source_hash() -> str:
@@ -217,6 +225,9 @@ def main() -> int:
     ap.add_argument("--varlen", default="",
                     help="comma-separated sequence lengths: time a packed [T, H, d] batch of sequences of "
                          "these lengths (the --config head shape) instead of the batched layer")
+    ap.add_argument("--power-s", type=float, default=2.5,
+                    help="seconds of extra steps (and dense calls) over which socket power and clock are sampled "
+                         "after the timed region (0: skip)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -284,8 +295,6 @@ def main() -> int:
            torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     plans = []
     torch.cuda.synchronize()
-    power = PowerSampler()
-    power.start()
     t_wall = time.perf_counter()
     for i in range(args.steps):
         ev[i][0].record(stream)
@@ -296,12 +305,14 @@ def main() -> int:
         plans.append(P)
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t_wall) * 1e3 / args.steps
-    power_steps = power.stop()
     plan_ms = float(np.median([a.elapsed_time(b) for a, b, _ in ev]))
     attend_ms = float(np.median([b.elapsed_time(c) for _, b, c in ev]))
     step_ms = float(np.mean([a.elapsed_time(c) for a, _, c in ev]))
     kern_ms, kern_n, _, _ = F.profile_read(reset=True)
     F.profile_enable(False)
+    # socket power and clock over a few seconds of the same steps, after the timed ones
+    power = PowerSampler()
+    power_steps = power.measure(step, args.power_s) if args.power_s > 0 else None
     info = plans[-1].info()
     colptrs = ([c for c in plans[-1].debug_seqs("colptr") if c is not None]
                if args.vs_granularity == "token" else None)
@@ -336,17 +347,16 @@ def main() -> int:
         torch.cuda.synchronize()
         F.profile_read(reset=True)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        pd = PowerSampler()
-        pd.start()
         e0.record(stream)
         for _ in range(args.dense_reps):
             dense()
         e1.record(stream)
         torch.cuda.synchronize()
-        power_dense = pd.stop()
         dense_ms = e0.elapsed_time(e1) / args.dense_reps
         _, _, dk_ms, dk_n = F.profile_read(reset=True)
         F.profile_enable(False)
+        if args.power_s > 0:
+            power_dense = power.measure(dense, args.power_s, sync_every=1)
         dense_kernel_ms = dk_ms / max(dk_n, 1)
         del outd
 
@@ -408,7 +418,7 @@ def main() -> int:
         "mfma_frac_attention_kernel": round(achieved / peak, 4),
         "dense_eff_tflops": round(dense_flop / (dense_kernel_ms * 1e-3) / 1e12, 1) if dense_ms else None,
         "roofline": roof,
-        "power_timed_steps": power_steps,
+        "power_sparse_steps": power_steps,
         "power_dense": power_dense,
         "cpu_baseline": cpu,
         "input_generation_s": round(gen_s, 1),
