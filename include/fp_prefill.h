@@ -173,8 +173,9 @@ fp_status fp_prefill_plan_ex(const void* q, const void* k, fp_dtype dtype,
  *   each query block attending only to the key blocks its plan selected.
  *   q must be the tensor the plan was built from (the plan stores lists,
  *   not values); k and v of the plan's shape and layout.  Every token row
- *   of o is written.  Uses a stream-ordered workspace of V transposed, per
- *   sequence Hkv*d*nb*block elements.  `stream` may differ from the plan's
+ *   of o is written.  Uses a device workspace of V transposed, per
+ *   sequence Hkv*d*nb*block elements, taken from the library's memory cache
+ *   (see fp_workspace_trim).  `stream` may differ from the plan's
  *   stream: the call then waits for the planning kernels, and the plan's
  *   stream waits for this call's kernels (so fp_plan_destroy, ordered on the
  *   plan's stream, cannot free the lists under them).
@@ -283,6 +284,27 @@ fp_status fp_plan_copy_debug(const fp_plan* plan, int which, void* host_dst, siz
 /* Releases the plan's buffers, stream-ordered on the stream the plan was
  * created on; work using the plan on other streams must be complete. */
 void fp_plan_destroy(fp_plan* plan);
+
+/*
+ * Device memory.  Plans, attends and dense attends take their device memory
+ * (a plan's buffers, the score workspace of planning, the attention's V^T
+ * workspace) from a cache kept by the library, and give it back when their
+ * work is enqueued (a plan's buffers when it is destroyed).  A block given
+ * back carries an event recorded on the stream of its last use; a later call
+ * on any stream reuses it after making its stream wait on that event, so no
+ * call waits on the host for earlier GPU work (an allocation from the
+ * runtime's stream-ordered pool that reused memory freed earlier on a stream
+ * made the host wait until the stream reached the free).  The cache holds at
+ * most 16 GiB; beyond that its oldest blocks are freed once their last use
+ * has completed.  Thread-safe.
+ *
+ * fp_workspace_trim -- frees every cached block (on every device), waiting on
+ *   the host for the last use of each, and returns the runtime pool's unused
+ *   memory to the device.  Blocks held by calls in flight on other threads
+ *   and the buffers of live plans are not touched.  FP_ERR_HIP if a wait
+ *   failed (the remaining blocks are still freed).
+ */
+fp_status fp_workspace_trim(void);
 
 const char* fp_status_str(fp_status s);
 const char* fp_last_error(void);

@@ -298,6 +298,12 @@ def dense_attend_varlen(q, k, v, cu_seqlens, block: int = 128, out=None, stream=
     return out
 
 
+def workspace_trim() -> None:
+    """Free the device memory the library keeps cached for reuse (see
+    fp_workspace_trim); live plans keep their buffers."""
+    _lib.check(_lib.load().fp_workspace_trim(), "fp_workspace_trim")
+
+
 def profile_enable(on: bool = True) -> None:
     _lib.check(_lib.load().fp_profile_enable(1 if on else 0), "fp_profile_enable")
 

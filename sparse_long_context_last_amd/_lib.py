@@ -63,6 +63,7 @@ SIGNATURES = {
                                    C.c_void_p]),
     "fp_plan_copy_debug": (C.c_int, [C.c_void_p, C.c_int, C.c_void_p, C.c_size_t]),
     "fp_plan_destroy": (None, [C.c_void_p]),
+    "fp_workspace_trim": (C.c_int, []),
     "fp_status_str": (C.c_char_p, [C.c_int]),
     "fp_last_error": (C.c_char_p, []),
     "fp_profile_enable": (C.c_int, [C.c_int]),

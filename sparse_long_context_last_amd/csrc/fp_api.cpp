@@ -9,6 +9,7 @@
 #include <cstdio>
 #include <cstring>
 #include <algorithm>
+#include <deque>
 #include <mutex>
 #include <new>
 #include <vector>
@@ -56,7 +57,12 @@ struct fp_plan {
     hipStream_t stream;
     hipEvent_t ready;                // recorded on `stream` when planning is enqueued
     hipEvent_t used;                 // recorded after an attend on another stream
-    std::vector<void*> allocs;
+    struct {
+        void* p = nullptr;           // every device buffer of the plan, carved from one cached block
+        size_t bytes = 0;
+        int dev = -1;
+        hipEvent_t ev = nullptr;
+    } mem;
 };
 
 namespace {
@@ -224,19 +230,133 @@ void set_pool_threshold(int dev) {
     done.push_back(dev);
 }
 
-template <typename T>
-fp_status palloc(fp_plan* p, T** ptr, size_t count) {
-    void* q = nullptr;
-    const size_t bytes = count * sizeof(T) > 0 ? count * sizeof(T) : 16;
-    FP_HIP(hipMallocAsync(&q, bytes, p->stream), "hipMallocAsync (plan)");
-    p->allocs.push_back(q);
-    *ptr = (T*)q;
-    return FP_OK;
+// ---------------------------------------------------------------------------
+// Device memory cache.  On this runtime an allocation from the stream-ordered
+// pool that reuses memory freed earlier, while the stream has not yet reached
+// that free, makes the host wait until it has: a 256 MiB hipMallocAsync after
+// a hipFreeAsync of the same size waited out the 6 ms of work queued before
+// the free, and returned in 0.08 ms without the free.  A plan or an attend
+// that allocated and freed per call therefore held its caller until the GPU
+// drained, one call behind.  The library instead keeps the blocks it
+// releases: a released block carries an event recorded on the stream of its
+// last use, and a later call on any stream takes it after making its own
+// stream wait on that event (a stream dependency, no host wait).  The cache
+// holds at most kCacheLimit bytes (oldest blocks freed first, after their
+// last use is complete) and fp_workspace_trim returns it to the runtime.
+// ---------------------------------------------------------------------------
+struct WsBlock {
+    void* p = nullptr;
+    size_t bytes = 0;
+    int dev = -1;
+    hipEvent_t ev = nullptr;    // recorded when the block was last released
+};
+std::mutex g_ws_mu;
+std::deque<WsBlock> g_ws;       // released blocks, oldest first
+size_t g_ws_bytes = 0;
+constexpr size_t kCacheLimit = 16ull << 30;
+
+// A cached block serves a request it exceeds by at most half (2 MiB for
+// requests up to 1 MiB), so large blocks are not spent on small requests.
+bool ws_fits(size_t have, size_t need) {
+    return have >= need && (need <= (1u << 20) ? have <= (2u << 20) : have - need <= need / 2);
 }
 
+// Frees a block whose last use may still be queued: waits for that use on
+// the host first, so the free (on the null stream) has nothing to wait for.
+void ws_free_now(WsBlock& b) {
+    if (b.ev) {
+        (void)hipEventSynchronize(b.ev);
+        (void)hipEventDestroy(b.ev);
+    }
+    (void)hipFreeAsync(b.p, nullptr);
+    b = WsBlock{};
+}
+
+// A block of at least `bytes` on device `dev` for work enqueued on `st`.
+hipError_t ws_get(size_t bytes, int dev, hipStream_t st, WsBlock* out) {
+    bytes = bytes ? (bytes + 255) / 256 * 256 : 256;
+    WsBlock b;
+    {
+        std::lock_guard<std::mutex> g(g_ws_mu);
+        auto best = g_ws.end();
+        for (auto it = g_ws.begin(); it != g_ws.end(); ++it)
+            if (it->dev == dev && ws_fits(it->bytes, bytes) && (best == g_ws.end() || it->bytes < best->bytes))
+                best = it;
+        if (best != g_ws.end()) {
+            b = *best;
+            g_ws_bytes -= b.bytes;
+            g_ws.erase(best);
+        }
+    }
+    if (b.p) {
+        const hipError_t e = hipStreamWaitEvent(st, b.ev, 0);
+        if (e != hipSuccess) {
+            ws_free_now(b);
+            return e;
+        }
+        *out = b;
+        return hipSuccess;
+    }
+    b.bytes = bytes;
+    b.dev = dev;
+    const hipError_t e = hipMallocAsync(&b.p, bytes, st);
+    if (e != hipSuccess) return e;
+    *out = b;
+    return hipSuccess;
+}
+
+// Gives a block back once the work using it is enqueued on `st`.  When its
+// last use cannot be marked, it is freed in the order of `st` instead (and
+// the error returned); either way `b` is empty afterwards.
+hipError_t ws_put(WsBlock& b, hipStream_t st) {
+    if (!b.p) return hipSuccess;
+    hipError_t e = hipSuccess;
+    if (!b.ev) e = hipEventCreateWithFlags(&b.ev, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventRecord(b.ev, st);
+    if (e != hipSuccess) {
+        (void)hipFreeAsync(b.p, st);
+        if (b.ev) (void)hipEventDestroy(b.ev);
+        b = WsBlock{};
+        return e;
+    }
+    std::vector<WsBlock> evict;
+    {
+        std::lock_guard<std::mutex> g(g_ws_mu);
+        g_ws.push_back(b);
+        g_ws_bytes += b.bytes;
+        for (auto it = g_ws.begin(); g_ws_bytes > kCacheLimit && it != g_ws.end();) {
+            if (it->dev == b.dev && it->p != b.p) {
+                g_ws_bytes -= it->bytes;
+                evict.push_back(*it);
+                it = g_ws.erase(it);
+            } else {
+                ++it;
+            }
+        }
+    }
+    for (WsBlock& x : evict) ws_free_now(x);
+    b = WsBlock{};
+    return hipSuccess;
+}
+
+// Offsets of several buffers carved from one block (256-byte aligned).
+struct Layout {
+    std::vector<std::pair<void**, size_t>> items;
+    size_t total = 0;
+    template <typename T>
+    void add(T** ptr, size_t count) {
+        const size_t bytes = count * sizeof(T) > 0 ? count * sizeof(T) : 16;
+        items.push_back({reinterpret_cast<void**>(ptr), total});
+        total += (bytes + 255) / 256 * 256;
+    }
+    void assign(void* base) const {
+        for (const auto& it : items) *it.first = static_cast<unsigned char*>(base) + it.second;
+    }
+};
+
 void free_plan(fp_plan* p) {
-    for (void* q : p->allocs) (void)hipFreeAsync(q, p->stream);
-    p->allocs.clear();
+    WsBlock b{p->mem.p, p->mem.bytes, p->mem.dev, p->mem.ev};
+    (void)ws_put(b, p->stream);
     if (p->ready) (void)hipEventDestroy(p->ready);
     if (p->used) (void)hipEventDestroy(p->used);
     delete p;
@@ -333,6 +453,7 @@ fp_status attend_common(const void* q, const void* k, const void* v, void* o, fp
     attention_table(segs, Hq, Hkv, d, block, pair, table, items, vt_elems, g_elems);
     if (items == 0) return FP_OK;
     AttendWork w;
+    WsBlock wblk;
     AttnSeg* dtab = plan ? plan->aseg : nullptr;
     hipError_t e = hipSuccess;
     if (scratch) {
@@ -354,19 +475,24 @@ fp_status attend_common(const void* q, const void* k, const void* v, void* o, fp
         int dev = 0;
         FP_HIP(hipGetDevice(&dev), "hipGetDevice");
         set_pool_threshold(dev);
-        e = hipMallocAsync(&w.vt, vt_elems * esz, st);
-        if (e == hipSuccess && gather) e = hipMallocAsync(&w.kg, g_elems * esz, st);
-        if (e == hipSuccess && gather) e = hipMallocAsync(&w.vgt, g_elems * esz, st);
-        if (e == hipSuccess && !dtab) {
-            e = hipMallocAsync((void**)&w.dtab, table.size() * sizeof(AttnSeg), st);
-            dtab = w.dtab;
+        Layout wl;
+        wl.add(reinterpret_cast<unsigned char**>(&w.vt), vt_elems * esz);
+        if (gather) {
+            wl.add(reinterpret_cast<unsigned char**>(&w.kg), g_elems * esz);
+            wl.add(reinterpret_cast<unsigned char**>(&w.vgt), g_elems * esz);
+        }
+        if (!dtab) wl.add(&w.dtab, table.size());
+        e = ws_get(wl.total, dev, st, &wblk);
+        if (e == hipSuccess) {
+            wl.assign(wblk.p);
+            if (!dtab) dtab = w.dtab;
         }
     }
     // a plan made on another stream: wait for its kernels
     const bool cross = plan && plan->ready && st != plan->stream;
     if (e == hipSuccess && cross) e = hipStreamWaitEvent(st, plan->ready, 0);
     if (e == hipSuccess && dtab != (plan ? plan->aseg : nullptr))
-        e = hipMemcpyAsync(dtab, table.data(), table.size() * sizeof(AttnSeg), hipMemcpyHostToDevice, st);
+        e = launch_upload(dtab, table.data(), table.size() * sizeof(AttnSeg), st);
     for (size_t i = 0; gather && i < segs.size() && e == hipSuccess; ++i)
         e = launch_gather_cols((const unsigned char*)k + (size_t)segs[i].koff * esz,
                                (const unsigned char*)v + (size_t)segs[i].koff * esz, ks, dtype == FP_BF16, d,
@@ -432,10 +558,8 @@ fp_status attend_common(const void* q, const void* k, const void* v, void* o, fp
     if (e == hipSuccess && cross) e = hipEventRecord(plan->used, st);
     if (e == hipSuccess && cross) e = hipStreamWaitEvent(plan->stream, plan->used, 0);
     if (!scratch) {
-        if (w.vt) (void)hipFreeAsync(w.vt, st);
-        if (w.kg) (void)hipFreeAsync(w.kg, st);
-        if (w.vgt) (void)hipFreeAsync(w.vgt, st);
-        if (w.dtab) (void)hipFreeAsync(w.dtab, st);
+        const hipError_t re = ws_put(wblk, st);
+        if (e == hipSuccess) e = re;
     }
     if (e != hipSuccess) return hip_fail(e, "attention");
     return FP_OK;
@@ -570,14 +694,9 @@ fp_status make_plan(const void* q, const void* k, fp_dtype dtype, int layout, in
     const size_t BHall = (size_t)B * Hq;
     const bool cap = max_budget > 0;
 
-#define PALLOC(ptr, n)                          \
-    do {                                        \
-        fp_status s_ = palloc(p, &(ptr), (n));  \
-        if (s_ != FP_OK) {                      \
-            free_plan(p);                       \
-            return s_;                          \
-        }                                       \
-    } while (0)
+    // every device buffer of the plan, carved from one block of the cache
+    Layout lay;
+#define PALLOC(ptr, n) lay.add(&(ptr), (n))
     unsigned char *colblk, *diagA, *diagB, *diagT;
     float *colmass = nullptr, *diagmass = nullptr;
     int* colcount = nullptr;
@@ -617,17 +736,28 @@ fp_status make_plan(const void* q, const void* k, fp_dtype dtype, int layout, in
     PALLOC(hist, (size_t)2 * max_bh * kRadixBins * lanes);
     PALLOC(aseg, segs.size());
 #undef PALLOC
+    {
+        WsBlock blk;
+        const hipError_t ae = ws_get(lay.total, p->device, p->stream, &blk);
+        if (ae != hipSuccess) {
+            free_plan(p);
+            return hip_fail(ae, "device memory for the plan");
+        }
+        p->mem.p = blk.p;
+        p->mem.bytes = blk.bytes;
+        p->mem.dev = blk.dev;
+        p->mem.ev = blk.ev;
+        lay.assign(blk.p);
+    }
     p->aseg = aseg;
     long long items = 0;
     size_t vt_elems = 0, g_elems = 0;
     attention_table(segs, Hq, Hkv, d, block, attention_pairs(block, dtype, false), p->aseg_host, items, vt_elems,
                     g_elems);
     hipStream_t st = p->stream;
-    he = hipMemcpyAsync(aseg, p->aseg_host.data(), segs.size() * sizeof(AttnSeg), hipMemcpyHostToDevice, st);
     // heads of empty sequences keep pattern 0, divergence 0 and no blocks
-    if (he == hipSuccess) he = launch_fill_u32((unsigned int*)p->pattern, 0u, (long long)(BHall + 3) / 4, st);
-    if (he == hipSuccess) he = launch_fill_u32((unsigned int*)p->djs, 0u, 2LL * (long long)BHall, st);
-    if (he == hipSuccess) he = launch_fill_u32((unsigned int*)p->total_blocks, 0u, 2LL * (long long)BHall, st);
+    he = launch_zero3_u32((unsigned int*)p->pattern, (long long)(BHall + 3) / 4, (unsigned int*)p->djs,
+                          2LL * (long long)BHall, (unsigned int*)p->total_blocks, 2LL * (long long)BHall, st);
 
     // per-segment views
     size_t o_qbar = 0, o_kbar = 0, o_rowmax = 0, o_colsum = 0, o_atrue = 0, o_ahat = 0, o_rows = 0, o_cp = 0;
@@ -692,11 +822,17 @@ fp_status make_plan(const void* q, const void* k, fp_dtype dtype, int layout, in
         o_rz[j + 1] = o_rz[j] + rz_max[j];
         o_qt[j + 1] = o_qt[j] + qt_max[j];
     }
-    void *s2 = nullptr, *pmax = nullptr, *rz = nullptr, *qt = nullptr;
-    if (he == hipSuccess) he = hipMallocAsync(&s2, o_s2[lanes] * sizeof(float), st);
-    if (he == hipSuccess) he = hipMallocAsync(&pmax, o_pm[lanes] * sizeof(float), st);
-    if (he == hipSuccess) he = hipMallocAsync(&rz, o_rz[lanes] * sizeof(float), st);
-    if (he == hipSuccess) he = hipMallocAsync(&qt, o_qt[lanes] * sizeof(float), st);
+    float *s2 = nullptr, *pmax = nullptr, *rz = nullptr, *qt = nullptr;
+    WsBlock tmp;
+    {
+        Layout tl;
+        tl.add(&s2, o_s2[lanes]);
+        tl.add(&pmax, o_pm[lanes]);
+        tl.add(&rz, o_rz[lanes]);
+        tl.add(&qt, o_qt[lanes]);
+        if (he == hipSuccess) he = ws_get(tl.total, p->device, st, &tmp);
+        if (he == hipSuccess) tl.assign(tmp.p);
+    }
     hipStream_t ls[kPlanLanes];
     hipEvent_t ev[kPlanLanes + 1] = {};
     hipStream_t pool_streams[kPlanLanes];
@@ -727,10 +863,10 @@ fp_status make_plan(const void* q, const void* k, fp_dtype dtype, int layout, in
         a.tau = (double)tau;
         a.G = G;
         a.canon = canon;
-        a.s2 = (float*)s2 + o_s2[ln];
-        a.pmax = (float*)pmax + o_pm[ln];
-        a.rz = (float*)rz + o_rz[ln];
-        a.qt = (float*)qt + o_qt[ln];
+        a.s2 = s2 + o_s2[ln];
+        a.pmax = pmax + o_pm[ln];
+        a.rz = rz + o_rz[ln];
+        a.qt = qt + o_qt[ln];
         a.aux = aux;
         he = launch_plan(a, p->dev[i], ls[ln]);
     }
@@ -750,13 +886,16 @@ fp_status make_plan(const void* q, const void* k, fp_dtype dtype, int layout, in
             if (ev[j]) (void)hipEventDestroy(ev[j]);
     }
     if (he == hipSuccess) he = launch_head_order(p->total_blocks, p->hperm, (int)BHall, Hq / Hkv, st);
+    // the attention's segment table (only attend reads it), after the plan's kernels
+    if (he == hipSuccess) he = launch_upload(aseg, p->aseg_host.data(), segs.size() * sizeof(AttnSeg), st);
     if (he == hipSuccess) he = hipEventCreateWithFlags(&p->ready, hipEventDisableTiming);
     if (he == hipSuccess) he = hipEventCreateWithFlags(&p->used, hipEventDisableTiming);
     if (he == hipSuccess) he = hipEventRecord(p->ready, st);
-    if (s2) (void)hipFreeAsync(s2, st);
-    if (pmax) (void)hipFreeAsync(pmax, st);
-    if (rz) (void)hipFreeAsync(rz, st);
-    if (qt) (void)hipFreeAsync(qt, st);
+    {
+        // the score workspace goes back to the cache after the plan's kernels
+        const hipError_t re = ws_put(tmp, st);
+        if (he == hipSuccess) he = re;
+    }
     if (he != hipSuccess) {
         free_plan(p);
         return hip_fail(he, "planning");
@@ -966,6 +1105,32 @@ fp_status fp_plan_copy_debug(const fp_plan* plan, int which, void* host_dst, siz
 
 void fp_plan_destroy(fp_plan* plan) {
     if (plan) free_plan(plan);
+}
+
+fp_status fp_workspace_trim(void) {
+    std::deque<WsBlock> blocks;
+    {
+        std::lock_guard<std::mutex> g(g_ws_mu);
+        blocks.swap(g_ws);
+        g_ws_bytes = 0;
+    }
+    hipError_t first = hipSuccess;
+    std::vector<int> devs;
+    for (WsBlock& b : blocks) {
+        if (b.ev) {
+            const hipError_t e = hipEventSynchronize(b.ev);
+            if (e != hipSuccess && first == hipSuccess) first = e;
+            (void)hipEventDestroy(b.ev);
+        }
+        (void)hipFreeAsync(b.p, nullptr);
+        if (std::find(devs.begin(), devs.end(), b.dev) == devs.end()) devs.push_back(b.dev);
+    }
+    for (int dev : devs) {
+        hipMemPool_t pool;
+        if (hipDeviceGetDefaultMemPool(&pool, dev) == hipSuccess) (void)hipMemPoolTrimTo(pool, 0);
+    }
+    if (first != hipSuccess) return hip_fail(first, "waiting for the last use of a cached block");
+    return FP_OK;
 }
 
 fp_status fp_profile_enable(int on) {

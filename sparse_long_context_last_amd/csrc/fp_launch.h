@@ -113,6 +113,8 @@ struct AttnSeg {
     int npi;              // work items per head: nb, or (nb + 1) / 2 with two query blocks per item
 };
 
+static_assert(sizeof(AttnSeg) % 4 == 0, "segment tables are uploaded as 32-bit words");
+
 struct AttnArgs {
     int d;               // head dimension (64 or 128)
     const void* q;
@@ -138,6 +140,10 @@ struct AttnArgs {
 
 hipError_t launch_plan(const PlanArgs& a, PlanDev& P, hipStream_t st);
 hipError_t launch_fill_u32(unsigned int* p, unsigned int v, long long n, hipStream_t st);
+// Copies a host table (bytes a multiple of 4) to device memory in stream order.
+hipError_t launch_upload(void* dst, const void* src, size_t bytes, hipStream_t st);
+hipError_t launch_zero3_u32(unsigned int* a, long long na, unsigned int* b, long long nb, unsigned int* c,
+                           long long nc, hipStream_t st);
 hipError_t launch_probe_exp2(const float* x, float* y, long long n, const Canon& K, hipStream_t st);
 hipError_t launch_probe_ln(const double* x, double* y, long long n, const Canon& K, hipStream_t st);
 hipError_t launch_probe_sqrt(const double* x, double* y, long long n, hipStream_t st);

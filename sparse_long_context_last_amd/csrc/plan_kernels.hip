@@ -11,6 +11,8 @@
 // are therefore bit-reproducible across runs and launch geometries.
 #pragma clang fp contract(off)
 
+#include <cstring>
+
 #include "fp_common.h"
 #include "fp_launch.h"
 
@@ -709,19 +711,35 @@ __global__ __launch_bounds__(256) void k_linesums(const float* __restrict__ s2, 
 }
 
 // Offsets o = L - BS + 1 + t (t < BS - 1, o >= 0): only rows i > t reach
-// them, at column i - t - 1.  grid (BH), BS threads.
+// them, at column i - t - 1.  grid (BH), BS threads.  The row statistics are
+// staged in LDS and the scattered scores are loaded eight at a time ahead of
+// the (sequential, i ascending) sum.
 template <int BS>
 __global__ __launch_bounds__(BS) void k_diagtail(const float* __restrict__ s2, const float* __restrict__ rowmax,
                                                  const float* __restrict__ rz, float* __restrict__ diagsum,
                                                  int L, int NS, Canon K) {
+    __shared__ float sM[BS], sR[BS];
     const int t = threadIdx.x, bh = blockIdx.x;
+    sM[t] = rowmax[(size_t)bh * BS + t];
+    sR[t] = rz[(size_t)bh * BS + t];
+    __syncthreads();
     const int o = L - BS + 1 + t;
     if (t >= BS - 1 || o < 0) return;
     const float* S = s2 + (size_t)bh * BS * NS;
     float g = 0.0f;
-    for (int i = t + 1; i < BS; ++i) {
-        const float e = exp2_c(S[(size_t)i * NS + (i - t - 1)] - rowmax[(size_t)bh * BS + i], K);
-        const float p = e * rz[(size_t)bh * BS + i];
+    int i = t + 1;
+    for (; i + 8 <= BS; i += 8) {
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = S[(size_t)(i + u) * NS + (i + u - t - 1)];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const float p = exp2_c(v[u] - sM[i + u], K) * sR[i + u];
+            g = g + p;
+        }
+    }
+    for (; i < BS; ++i) {
+        const float p = exp2_c(S[(size_t)i * NS + (i - t - 1)] - sM[i], K) * sR[i];
         g = g + p;
     }
     diagsum[(size_t)bh * L + o] = g;
@@ -1396,6 +1414,25 @@ __global__ __launch_bounds__(256) void k_fill_u32(unsigned int* __restrict__ p, 
     for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < n; i += (long long)gridDim.x * 256) p[i] = v;
 }
 
+// Small host tables (the attention segment table) copied to the device by
+// value through kernel arguments, 2 KB per launch: a copy from pageable host
+// memory may be serialized with the host by the runtime.
+struct UploadChunk {
+    unsigned int w[512];
+};
+__global__ __launch_bounds__(256) void k_upload(unsigned int* __restrict__ dst, UploadChunk c, int n) {
+    for (int i = threadIdx.x; i < n; i += 256) dst[i] = c.w[i];
+}
+
+// Three buffers zeroed by one launch (blockIdx.y picks the buffer).
+__global__ __launch_bounds__(256) void k_zero3_u32(unsigned int* __restrict__ a, long long na,
+                                                   unsigned int* __restrict__ b, long long nb,
+                                                   unsigned int* __restrict__ c, long long nc) {
+    unsigned int* p = blockIdx.y == 0 ? a : blockIdx.y == 1 ? b : c;
+    const long long n = blockIdx.y == 0 ? na : blockIdx.y == 1 ? nb : nc;
+    for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < n; i += (long long)gridDim.x * 256) p[i] = 0u;
+}
+
 // probes of the canonical functions
 __global__ __launch_bounds__(256) void k_probe_exp2(const float* x, float* y, long long n, Canon K) {
     const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
@@ -1564,6 +1601,32 @@ hipError_t launch_fill_u32(unsigned int* p, unsigned int v, long long n, hipStre
     if (n > 0) {
         const long long g = (n + 255) / 256;
         hipLaunchKernelGGL(k_fill_u32, dim3((unsigned)(g < 65535 ? g : 65535)), dim3(256), 0, st, p, v, n);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_upload(void* dst, const void* src, size_t bytes, hipStream_t st) {
+    if (bytes % 4 != 0) return hipErrorInvalidValue;
+    const unsigned char* s = static_cast<const unsigned char*>(src);
+    for (size_t off = 0; off < bytes; off += sizeof(UploadChunk)) {
+        UploadChunk c;
+        const size_t n = bytes - off < sizeof c ? bytes - off : sizeof c;
+        memcpy(c.w, s + off, n);
+        hipLaunchKernelGGL(k_upload, dim3(1), dim3(256), 0, st,
+                           reinterpret_cast<unsigned int*>(static_cast<unsigned char*>(dst) + off), c, (int)(n / 4));
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+hipError_t launch_zero3_u32(unsigned int* a, long long na, unsigned int* b, long long nb, unsigned int* c,
+                           long long nc, hipStream_t st) {
+    const long long n = na > nb ? (na > nc ? na : nc) : (nb > nc ? nb : nc);
+    if (n > 0) {
+        const long long g = (n + 255) / 256;
+        hipLaunchKernelGGL(k_zero3_u32, dim3((unsigned)(g < 65535 ? g : 65535), 3), dim3(256), 0, st, a, na, b, nb, c,
+                           nc);
     }
     return hipGetLastError();
 }

@@ -8,8 +8,8 @@
 // library handles counts as one fallible call; stub_fail_call(n) makes the
 // n-th fallible call from now on fail (allocations with
 // hipErrorOutOfMemory, everything else with hipErrorLaunchFailure).  Release
-// calls (hipFreeAsync, hipEventDestroy) never fail, and refuse pointers they
-// did not hand out.
+// calls (hipFree, hipFreeAsync, hipEventDestroy) never fail, and refuse
+// pointers they did not hand out.
 #include <hip/hip_runtime.h>
 
 #include <cstdio>
@@ -28,9 +28,12 @@ std::set<void*>& g_mem = *new std::set<void*>;
 std::set<void*>& g_events = *new std::set<void*>;
 std::set<void*>& g_streams = *new std::set<void*>;
 long long g_calls = 0, g_fail_at = 0, g_bad_release = 0;
+bool g_paused = false;
 
-// One fallible call: true if it is the one chosen to fail.
+// One fallible call: true if it is the one chosen to fail.  While paused,
+// calls are neither counted nor failed.
 bool fail_now() {
+    if (g_paused) return false;
     ++g_calls;
     return g_fail_at > 0 && g_calls == g_fail_at;
 }
@@ -43,6 +46,11 @@ void stub_fail_call(long long n) {
     g_fail_at = n > 0 ? g_calls + n : 0;
 }
 long long stub_calls() { return g_calls; }
+// Stop (1) or resume (0) counting and failing calls.
+void stub_pause(int on) {
+    std::lock_guard<std::mutex> l(g_mu);
+    g_paused = on != 0;
+}
 long long stub_live_memory() { return (long long)g_mem.size(); }
 long long stub_live_events() { return (long long)g_events.size(); }
 long long stub_live_streams() { return (long long)g_streams.size(); }
@@ -90,6 +98,19 @@ hipError_t hipFreeAsync(void* p, hipStream_t) {
     std::free(p);
     return hipSuccess;
 }
+
+hipError_t hipFree(void* p) {
+    std::lock_guard<std::mutex> l(g_mu);
+    if (!p) return hipSuccess;
+    if (!g_mem.erase(p)) {
+        ++g_bad_release;
+        return hipErrorInvalidValue;
+    }
+    std::free(p);
+    return hipSuccess;
+}
+
+hipError_t hipMemPoolTrimTo(hipMemPool_t, size_t) { return hipSuccess; }
 
 hipError_t hipStreamCreateWithFlags(hipStream_t* s, unsigned int) {
     std::lock_guard<std::mutex> l(g_mu);
@@ -179,6 +200,14 @@ static hipError_t launch() {
 
 hipError_t launch_plan(const PlanArgs&, PlanDev&, hipStream_t) { return launch(); }
 hipError_t launch_fill_u32(unsigned int*, unsigned int, long long, hipStream_t) { return launch(); }
+hipError_t launch_upload(void* dst, const void* src, size_t bytes, hipStream_t) {
+    const hipError_t e = launch();
+    if (e == hipSuccess && bytes) std::memcpy(dst, src, bytes);
+    return e;
+}
+hipError_t launch_zero3_u32(unsigned int*, long long, unsigned int*, long long, unsigned int*, long long, hipStream_t) {
+    return launch();
+}
 hipError_t launch_probe_exp2(const float*, float*, long long, const Canon&, hipStream_t) { return launch(); }
 hipError_t launch_probe_ln(const double*, double*, long long, const Canon&, hipStream_t) { return launch(); }
 hipError_t launch_probe_sqrt(const double*, double*, long long, hipStream_t) { return launch(); }

@@ -3,10 +3,13 @@
 // CPU.  Test infrastructure only.
 //
 // Every scenario runs once as is (it must succeed and leave no stub memory,
-// events or streams behind) and then once with each of its fallible runtime
-// calls failing in turn: the entry point must return FP_ERR_OOM (allocation
-// failures) or FP_ERR_HIP, set a message, hand out no plan, and again leave
-// nothing behind.  Host leaks are LeakSanitizer's to report at exit.
+// events or streams behind once the library's memory cache is trimmed) and
+// then once with each of its fallible runtime calls failing in turn: the
+// entry point must return FP_ERR_OOM (allocation failures) or FP_ERR_HIP, set
+// a message, hand out no plan, and again leave nothing behind.  Destroying a
+// plan cannot fail; its runtime calls are failed in turn separately, and must
+// leave nothing behind either.  Host leaks are LeakSanitizer's to report at
+// exit.
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
@@ -17,6 +20,7 @@
 
 extern "C" {
 void stub_fail_call(long long n);
+void stub_pause(int on);
 long long stub_calls();
 long long stub_live_memory();
 long long stub_live_events();
@@ -51,10 +55,12 @@ Live live() { return {stub_live_memory(), stub_live_events(), stub_live_streams(
 // The last `best_effort` calls may fail without failing the scenario (they
 // only serve logging), but must still leave nothing behind.
 void sweep(const char* name, const std::function<fp_status()>& body, long long best_effort = 0) {
+    EXPECT(fp_workspace_trim() == FP_OK, "%s: trim", name);
     const Live before = live();
     const long long c0 = stub_calls();
     const fp_status s = body();
     const long long n = stub_calls() - c0;
+    EXPECT(fp_workspace_trim() == FP_OK, "%s: trim", name);
     EXPECT(s == FP_OK, "%s: status %s (%s)", name, fp_status_str(s), fp_last_error());
     EXPECT(live() == before, "%s: resources left after a successful run", name);
     EXPECT(n > 0, "%s: no fallible call", name);
@@ -62,6 +68,7 @@ void sweep(const char* name, const std::function<fp_status()>& body, long long b
         stub_fail_call(k);
         const fp_status f = body();
         stub_fail_call(0);
+        (void)fp_workspace_trim();
         const bool tail = k > n - best_effort;
         EXPECT(f == FP_ERR_OOM || f == FP_ERR_HIP || (tail && f == FP_OK), "%s: call %lld of %lld failing gave %s",
                name, k, n, fp_status_str(f));
@@ -74,7 +81,8 @@ void sweep(const char* name, const std::function<fp_status()>& body, long long b
     std::printf("%-28s %3lld fallible calls, each failing cleanly\n", name, n);
 }
 
-// A plan call: on failure no plan is handed out; on success the plan is released.
+// A plan call: on failure no plan is handed out; on success the plan is
+// released, outside the swept calls (the stub neither counts nor fails them).
 fp_status plan_and_release(const std::function<fp_status(fp_plan**)>& make) {
     fp_plan* p = reinterpret_cast<fp_plan*>(0x1);
     const fp_status s = make(&p);
@@ -82,7 +90,9 @@ fp_status plan_and_release(const std::function<fp_status(fp_plan**)>& make) {
         EXPECT(p == nullptr, "a failed plan call handed out a plan");
         return s;
     }
+    stub_pause(1);
     fp_plan_destroy(p);
+    stub_pause(0);
     return s;
 }
 
@@ -142,6 +152,35 @@ int main() {
         return st;
     }, 4);   // the log's stream synchronization and three reads
 
+    // destroying a plan with each of its runtime calls failing (giving the
+    // plan's block back to the cache): nothing is left behind
+    {
+        auto make = [&](fp_plan** p) {
+            return fp_prefill_plan(q, k, FP_BF16, 2, 8, 2, 1000, 128, 128, 0.95f, 0.1f, 1024, nullptr, p);
+        };
+        EXPECT(fp_workspace_trim() == FP_OK, "trim");
+        const Live before = live();
+        fp_plan* d = nullptr;
+        EXPECT(make(&d) == FP_OK, "plan for destroy: %s", fp_last_error());
+        const long long c0 = stub_calls();
+        fp_plan_destroy(d);
+        const long long n = stub_calls() - c0;
+        EXPECT(fp_workspace_trim() == FP_OK, "trim");
+        EXPECT(live() == before, "destroy: resources left");
+        for (long long kk = 1; kk <= n; ++kk) {
+            d = nullptr;
+            EXPECT(make(&d) == FP_OK, "plan for destroy: %s", fp_last_error());
+            stub_fail_call(kk);
+            fp_plan_destroy(d);
+            stub_fail_call(0);
+            (void)fp_workspace_trim();
+            const Live after = live();
+            EXPECT(after == before, "destroy: call %lld failing left memory %lld events %lld", kk, after.mem,
+                   after.ev);
+        }
+        std::printf("%-28s %3lld fallible calls, each failing cleanly\n", "plan destroy", n);
+    }
+
     // calls on an existing plan
     fp_plan* P = nullptr;
     EXPECT(fp_prefill_plan(q, k, FP_BF16, 2, 8, 2, 1000, 128, 128, 0.95f, 0.1f, 1024, nullptr, &P) == FP_OK, "plan");
@@ -160,6 +199,21 @@ int main() {
     sweep("attend token columns", [&] { return fp_prefill_attend(PT, q, k, v, o, nullptr); });
     sweep("attend packed batch", [&] { return fp_prefill_attend(PV, q, k, v, o, nullptr); });
     sweep("attend allocation-free", [&] { return fp_prefill_attend_noalloc(PT, q, k, v, o, other); });
+    // the second call takes the first one's block from the cache (its stream
+    // waits on the block's release event); here on another stream
+    sweep("attend twice (cache reuse)", [&] {
+        const fp_status s = fp_prefill_attend(P, q, k, v, o, nullptr);
+        return s != FP_OK ? s : fp_prefill_attend(P, q, k, v, o, other);
+    });
+    sweep("plan twice (cache reuse)", [&] {
+        const fp_status s = plan_and_release([&](fp_plan** p) {
+            return fp_prefill_plan(q, k, FP_BF16, 2, 8, 2, 1000, 128, 128, 0.95f, 0.1f, 1024, nullptr, p);
+        });
+        if (s != FP_OK) return s;
+        return plan_and_release([&](fp_plan** p) {
+            return fp_prefill_plan(q, k, FP_BF16, 2, 8, 2, 1000, 128, 128, 0.95f, 0.1f, 1024, nullptr, p);
+        });
+    });
     sweep("attend profiled", [&] {
         fp_profile_enable(1);
         fp_status s = fp_prefill_attend(P, q, k, v, o, nullptr);
@@ -234,6 +288,7 @@ int main() {
     fp_plan_destroy(P);
     fp_plan_destroy(PT);
     fp_plan_destroy(PV);
+    EXPECT(fp_workspace_trim() == FP_OK, "final trim");
     EXPECT(stub_live_memory() == 0, "plan memory left: %lld", stub_live_memory());
     EXPECT(stub_live_events() == 0, "events left: %lld", stub_live_events());
     EXPECT(stub_bad_releases() == 0, "releases of unknown pointers: %lld", stub_bad_releases());
