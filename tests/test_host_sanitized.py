@@ -1,4 +1,4 @@
-"""The host library (fp_api.cpp: validation, plan bookkeeping, stream and
+"""The host library (fp_api.cpp: validation, plan bookkeeping, memory cache, stream and
 event handling, every error path) built for the host alone with address and
 undefined-behaviour sanitizers, against a stub HIP runtime in which any one
 runtime call can be made to fail (tests/host/hip_stub.cpp), and driven by
@@ -53,3 +53,24 @@ def test_host_library_error_paths_under_sanitizers(tmp_path):
     print(r.stdout[-4000:])
     assert r.returncode == 0, r.stdout[-8000:]
     assert "check(s) failed" in r.stdout and " 0 check(s) failed" in r.stdout
+
+
+def test_host_library_threads_under_thread_sanitizer(tmp_path):
+    """Six threads plan, attend, read back and destroy plans at once while a
+    seventh trims the memory cache and toggles the measurement hooks; the
+    thread sanitizer must report no data race and every call must succeed."""
+    hipcc, clang = _tools()
+    common = ["-std=c++17", "-O1", "-g", "-fno-omit-frame-pointer", "-I", CSRC, "-I", INC]
+    tsan_host = ["-Xarch_host", "-fsanitize=thread"]
+    for src, obj in ((os.path.join(CSRC, "fp_api.cpp"), "fp_api.o"), (os.path.join(HOST, "hip_stub.cpp"), "stub.o")):
+        _run([hipcc, "-x", "hip", "--offload-host-only", *common, *tsan_host, "-c", src, "-o", obj], tmp_path)
+    tsan = ["-fsanitize=thread"]
+    _run([clang, *common, *tsan, "-c", os.path.join(HOST, "threads_driver.cpp"), "-o", "driver.o"], tmp_path)
+    _run([clang, *tsan, "fp_api.o", "stub.o", "driver.o", "-lpthread", "-o", "driver"], tmp_path)
+    env = dict(os.environ, TSAN_OPTIONS="halt_on_error=1 second_deadlock_stack=1")
+    r = subprocess.run([str(tmp_path / "driver")], cwd=tmp_path, env=env, stdout=subprocess.PIPE,
+                       stderr=subprocess.STDOUT, text=True, timeout=300)
+    print(r.stdout[-4000:])
+    assert r.returncode == 0, r.stdout[-8000:]
+    assert "ThreadSanitizer" not in r.stdout
+    assert " 0 failure(s)" in r.stdout
