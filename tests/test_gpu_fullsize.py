@@ -84,7 +84,24 @@ def gpu_plan_arrays(P, cfg):
 
 @pytest.mark.parametrize("name", FULL)
 def test_full_size_layer(F, pool, name):
-    cfg = BY_NAME[name]
+    run_layer(F, pool, name, BY_NAME[name])
+
+
+# Head dimension 64 at sizes well past the small parity layers: every head
+# bit-exact, as above (block 128 with GQA 4:1; block 64 with 16 query heads
+# per key/value head).
+D64 = {
+    "llama8b_d64_16k": BY_NAME["llama8b_32k"].with_(N=16384, d=64),
+    "glm9b_d64_16k_bs64": BY_NAME["glm9b_64k_bs64"].with_(N=16384, d=64, min_budget=1024),
+}
+
+
+@pytest.mark.parametrize("name", list(D64))
+def test_full_head_parity_d64(F, pool, name):
+    run_layer(F, pool, name, D64[name])
+
+
+def run_layer(F, pool, name, cfg):
     gen = LayerGen(cfg)
     reps = representatives(gen)
     dense = name == "llama8b_32k"
