@@ -1115,6 +1115,8 @@ fp_status fp_workspace_trim(void) {
         g_ws_bytes = 0;
     }
     hipError_t first = hipSuccess;
+    int cur = -1;
+    (void)hipGetDevice(&cur);
     std::vector<int> devs;
     for (WsBlock& b : blocks) {
         if (b.ev) {
@@ -1122,7 +1124,10 @@ fp_status fp_workspace_trim(void) {
             if (e != hipSuccess && first == hipSuccess) first = e;
             (void)hipEventDestroy(b.ev);
         }
+        // freed on the null stream of the block's own device
+        if (b.dev != cur) (void)hipSetDevice(b.dev);
         (void)hipFreeAsync(b.p, nullptr);
+        if (b.dev != cur && cur >= 0) (void)hipSetDevice(cur);
         if (std::find(devs.begin(), devs.end(), b.dev) == devs.end()) devs.push_back(b.dev);
     }
     for (int dev : devs) {

@@ -112,6 +112,9 @@ hipError_t hipFree(void* p) {
 
 hipError_t hipMemPoolTrimTo(hipMemPool_t, size_t) { return hipSuccess; }
 
+// One device (0): switching to it always succeeds.
+hipError_t hipSetDevice(int) { return hipSuccess; }
+
 hipError_t hipStreamCreateWithFlags(hipStream_t* s, unsigned int) {
     std::lock_guard<std::mutex> l(g_mu);
     if (fail_now()) return hipErrorOutOfMemory;
