@@ -702,7 +702,7 @@ fp_status make_plan(const void* q, const void* k, fp_dtype dtype, int layout, in
     int* colcount = nullptr;
     p->colptr = nullptr;
     p->colidx = nullptr;
-    SelState* sel;
+    SelState *sel, *selk;
     unsigned long long* hist;
     AttnSeg* aseg;
     PALLOC(p->pattern, (BHall + 3) / 4 * 4);
@@ -733,7 +733,8 @@ fp_status make_plan(const void* q, const void* k, fp_dtype dtype, int layout, in
         PALLOC(p->colidx, n_colsum);
     }
     PALLOC(sel, (size_t)2 * max_bh * lanes);
-    PALLOC(hist, (size_t)2 * max_bh * kRadixBins * lanes);
+    PALLOC(selk, (size_t)kSelMaxPasses * 2 * max_bh * lanes);
+    PALLOC(hist, (size_t)kSelMaxPasses * 2 * max_bh * kRadixBins * lanes);
     PALLOC(aseg, segs.size());
 #undef PALLOC
     {
@@ -803,7 +804,8 @@ fp_status make_plan(const void* q, const void* k, fp_dtype dtype, int layout, in
             P.colidx = p->colidx + o_colsum;
         }
         P.sel = sel + (size_t)2 * max_bh * (i % kPlanLanes);
-        P.hist = hist + (size_t)2 * max_bh * kRadixBins * (i % kPlanLanes);
+        P.selk = selk + (size_t)kSelMaxPasses * 2 * max_bh * (i % kPlanLanes);
+        P.hist = hist + (size_t)kSelMaxPasses * 2 * max_bh * kRadixBins * (i % kPlanLanes);
         o_qbar += (size_t)nbh * g.nb * d;
         o_kbar += (size_t)g.nseq * Hkv * g.nb * d;
         o_rowmax += (size_t)nbh * block;

@@ -11,7 +11,9 @@ constexpr int kMaxBlocks = 4096;     // largest supported N / block
 constexpr int kScoreDSConst = 32;    // d-slice of the last-block score kernel
 constexpr int kRadixBits = 11;       // bits resolved per selection pass
 constexpr int kRadixBins = 1 << kRadixBits;
-constexpr int kSelChunk = 4096;      // list elements per selection workgroup
+constexpr int kSelChunk = 4096;      // list elements per selection workgroup (twice that for long lists)
+constexpr long long kSelLongList = 262144;
+constexpr int kSelMaxPasses = 5;     // radix passes over 31 value bits + at most 24 index bits
 constexpr int kGammaShift = 24;      // G = rint(gamma * 2^24)
 constexpr unsigned char kPatternQueryAware = 1;
 constexpr size_t kNoAllocScratchBytes = 64ull << 20;   // device workspace of fp_prefill_attend_noalloc
@@ -63,10 +65,11 @@ struct PlanDev {
     float* rowsum;               // [BH][BS]
     float* colsum;               // [BH][L]
     float* diagsum;              // [BH][L]
-    float* atrue;                // [BH][nb]
+    float* atrue;                // [BH][nb]  (block sums of colsum until the divergence kernel normalises them)
     float* ahat;                 // [BH][tri]
-    SelState* sel;               // [2 BH]
-    unsigned long long* hist;    // [2 BH][kRadixBins]
+    SelState* sel;               // [2 BH]  final selection state per list
+    SelState* selk;              // [kSelMaxPasses][2 BH]  state before each radix pass
+    unsigned long long* hist;    // [kSelMaxPasses][2 BH][kRadixBins]  mass histogram of each pass
     unsigned char* colblk;       // [BH][nb]
     unsigned char* diagA;        // [BH][nb]
     unsigned char* diagB;        // [BH][nb]
