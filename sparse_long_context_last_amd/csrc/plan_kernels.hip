@@ -490,17 +490,17 @@ inline int scores_mfma_groups(int BH, int nchunks) {
 // K3a: per last-block row: M = max, e = exp2_c(s - M) (0 for j > pos);
 // zpart[kb] = sum over the block's keys ascending; Z = sum of zpart
 // over kb ascending; rz = 1 / Z.  One workgroup per (bh, row); the row is
-// walked in segments of 32 key blocks staged through LDS (17 KB, so several
-// rows share a CU and one row's loads overlap another's arithmetic), where
-// one thread per key block forms its sequential sum.  A row that does not exist
+// walked in segments of 4096 keys (32 blocks of 128, 64 of 64) staged
+// through LDS (17 KB, so several rows share a CU and one row's loads overlap
+// another's arithmetic), where one thread per key block forms its sequential
+// sum.  A row that does not exist
 // (pos < 0) gets M = Z = rz = 0, so it adds exact zeros downstream.
 // ---------------------------------------------------------------------------
-constexpr int kRowSeg = 32;
-
 template <int BS>
 __global__ __launch_bounds__(256) void k_rowexp(const float* __restrict__ s2, const float* __restrict__ pmax,
                                                 float* __restrict__ rowmax, float* __restrict__ rowsum,
                                                 float* __restrict__ rz, int L, int NS, Canon K) {
+    constexpr int kRowSeg = 4096 / BS;      // blocks per segment: 4096 keys at either block size
     constexpr int SEG = kRowSeg * BS;
     __shared__ float es[kRowSeg][BS + 1];
     __shared__ float zs[kRowSeg];
@@ -610,9 +610,9 @@ __global__ __launch_bounds__(256) void k_rowexp(const float* __restrict__ s2, co
 // twice).  W = 1024 where that still leaves at least 2048 workgroups, else
 // 512 (measured: 0.48 -> 0.45 ms on the 128k layer, but 0.14 -> 0.16 ms on
 // the 32k one, whose 1024 workgroups then fill the chip only once).  Rows
-// are staged RC at a time (8 at block 128; 16 at block 64, where RC (W + BS)
-// must stay a multiple of 1024 for the float4 tiling); every thread keeps its
-// sums in registers across the chunks.  The tile holds p = e * rz (the
+// are staged 8 at a time (at block 64 a chunk is not a whole number of
+// float4 per thread: the last load covers only the first waves); every
+// thread keeps its sums in registers across the chunks.  The tile holds p = e * rz (the
 // product is rounded once whichever sum uses it).
 // Once its columns are summed, a workgroup also forms the block sums
 // t[kb] = sum of colsum over key block kb (j ascending) of the blocks its
@@ -656,7 +656,7 @@ __global__ __launch_bounds__(256) void k_linesums(const float* __restrict__ s2, 
                                                   const float* __restrict__ rz, float* __restrict__ colsum,
                                                   float* __restrict__ diagsum, float* __restrict__ blocksum,
                                                   int L, int NS, Canon K) {
-    constexpr int RC = BS == 128 ? 8 : 16, TW = W + BS;
+    constexpr int RC = 8, TW = W + BS;
     static_assert(W % BS == 0 && RC * TW >= W, "block sums are staged in the row tile");
     __shared__ __attribute__((aligned(16))) float es[RC][TW];
     __shared__ float sM[BS], sR[BS];
@@ -679,12 +679,16 @@ __global__ __launch_bounds__(256) void k_linesums(const float* __restrict__ s2, 
     // Each thread loads NL float4 of a chunk; the next chunk's loads are in
     // flight while the current one is summed.  Columns at or past L read
     // column 0 of their row and count as 0.
-    constexpr int NL = RC * TW / 4 / 256;
-    static_assert(NL * 256 * 4 == RC * TW, "chunk tiling");
+    constexpr int N4 = RC * TW / 4;                 // float4 per chunk
+    constexpr int NL = (N4 + 255) / 256;
+    static_assert(N4 * 4 == RC * TW && (N4 % 256) % 64 == 0, "chunk tiling: whole waves per load");
     float4 buf[NL];
+    // the last load of a chunk may cover only its first waves (wave-uniform)
+#define FP_IN_CHUNK(n_) (N4 % 256 == 0 || (n_) < NL - 1 || tid < N4 % 256)
 #define FP_LOAD_CHUNK(i0_)                                                                                 \
     _Pragma("unroll") for (int n = 0; n < NL; ++n) {                                                     \
         const int e4 = tid + 256 * n;                                                                    \
+        if (!FP_IN_CHUNK(n)) continue;                                                                   \
         const int ii = e4 / (TW / 4), cc = 4 * (e4 % (TW / 4));                                          \
         const int j = j0 + cc;                                                                           \
         buf[n] = *reinterpret_cast<const float4*>(S + (size_t)((i0_) + ii) * NS + (j < L ? j : 0));       \
@@ -697,6 +701,7 @@ __global__ __launch_bounds__(256) void k_linesums(const float* __restrict__ s2, 
 #pragma unroll
             for (int n = 0; n < NL; ++n) {
                 const int e4 = tid + 256 * n;
+                if (!FP_IN_CHUNK(n)) continue;
                 const int ii = e4 / (TW / 4), cc = 4 * (e4 % (TW / 4));
                 const int i = i0 + ii;
                 const float4 v = buf[n];
@@ -712,6 +717,7 @@ __global__ __launch_bounds__(256) void k_linesums(const float* __restrict__ s2, 
 #pragma unroll
             for (int n = 0; n < NL; ++n) {
                 const int e4 = tid + 256 * n;
+                if (!FP_IN_CHUNK(n)) continue;
                 const int ii = e4 / (TW / 4), cc = 4 * (e4 % (TW / 4));
                 const int i = i0 + ii, j = j0 + cc, pos = L - BS + i;
                 const float4 v = buf[n];
@@ -740,6 +746,7 @@ __global__ __launch_bounds__(256) void k_linesums(const float* __restrict__ s2, 
         __syncthreads();
     }
 #undef FP_LOAD_CHUNK
+#undef FP_IN_CHUNK
     float* cs = &es[0][0];      // free after the last chunk's barrier
 #pragma unroll
     for (int q = 0; q < W / 256; ++q) {
