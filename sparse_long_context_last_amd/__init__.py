@@ -22,7 +22,7 @@ from . import _lib
 from ._lib import FpError, PlanInfo  # noqa: F401
 
 __all__ = ["Plan", "plan", "plan_varlen", "attend", "dense_attend", "dense_attend_varlen",
-           "profile_enable", "profile_read", "canonical_constants", "FpError"]
+           "profile_enable", "profile_read", "canonical_constants", "workspace_trim", "FpError"]
 
 
 def _torch():
@@ -70,8 +70,9 @@ class Plan:
     """Device-resident FlexPrefill plan (pattern per head, block lists)."""
 
     def __init__(self, handle: C.c_void_p, Hq, Hkv, d, block, seqlens, layout: int, dtype_code: int, stream,
-                 N: Optional[int] = None):
+                 N: Optional[int] = None, params: Optional[dict] = None):
         self._h = handle
+        self.params = dict(params or {})      # gamma, tau, min_budget, max_budget, qa_selection, vs_granularity
         self.Hq, self.Hkv, self.d, self.block = Hq, Hkv, d, block
         self.seqlens = [int(x) for x in seqlens]
         self.layout = layout
@@ -162,6 +163,24 @@ class Plan:
             return np.zeros((0,) + shape[1:], dt)
         return np.concatenate(parts, axis=0)
 
+    def export(self, path, intermediates: bool = True) -> None:
+        """Write the plan's host copy to an .npz file (plan_io format): the
+        pattern, D and block lists of every head, the shapes and parameters
+        it was made with and, with `intermediates`, every selection
+        intermediate, so that it can be replayed against another
+        implementation later (plan_io.read)."""
+        from . import plan_io
+        pattern, djs, row_ptr, col_idx = self.copy_out()
+        meta = dict(Hq=self.Hq, Hkv=self.Hkv, d=self.d, block=self.block, seqlens=self.seqlens,
+                    layout="bhnd" if self.layout == _lib.FP_LAYOUT_BHND else "thd",
+                    dtype="bf16" if self.dtype_code == _lib.FP_BF16 else "fp32", **self.params)
+        inter = None
+        if intermediates:
+            items = [it for it in plan_io.ITEMS
+                     if it not in ("colptr", "colidx") or self.params.get("vs_granularity") == "token"]
+            inter = {it: self.debug_seqs(it) for it in items}
+        plan_io.write(path, meta, pattern, djs, row_ptr, col_idx, inter)
+
     def destroy(self) -> None:
         if self._h is not None:
             _lib.load().fp_plan_destroy(self._h)
@@ -181,6 +200,11 @@ def _options(max_budget: int, qa_selection: str, vs_granularity: str):
         raise ValueError(f"vs_granularity must be one of {sorted(_lib.VS_GRANULARITY)}")
     return _lib.PlanOptions(int(max_budget), _lib.QA_SELECTION[qa_selection],
                             _lib.VS_GRANULARITY[vs_granularity])
+
+
+def _params(gamma, tau, min_budget, max_budget, qa_selection, vs_granularity) -> dict:
+    return dict(gamma=float(gamma), tau=float(tau), min_budget=int(min_budget), max_budget=int(max_budget),
+                qa_selection=str(qa_selection), vs_granularity=str(vs_granularity))
 
 
 def plan(q, k, block: int = 128, gamma: float = 0.95, tau: float = 0.1,
@@ -204,7 +228,8 @@ def plan(q, k, block: int = 128, gamma: float = 0.95, tau: float = 0.1,
     _lib.check(_lib.load().fp_prefill_plan_ex(q.data_ptr(), k.data_ptr(), dt, B, Hq, Hkv, N, d, block,
                                               float(gamma), float(tau), int(min_budget), C.byref(opts),
                                               _stream_ptr(stream), C.byref(h)), "fp_prefill_plan_ex")
-    return Plan(h, Hq, Hkv, d, block, [N] * B, _lib.FP_LAYOUT_BHND, dt, stream, N=N)
+    return Plan(h, Hq, Hkv, d, block, [N] * B, _lib.FP_LAYOUT_BHND, dt, stream, N=N,
+                params=_params(gamma, tau, min_budget, max_budget, qa_selection, vs_granularity))
 
 
 def plan_varlen(q, k, cu_seqlens, block: int = 128, gamma: float = 0.95, tau: float = 0.1,
@@ -228,7 +253,8 @@ def plan_varlen(q, k, cu_seqlens, block: int = 128, gamma: float = 0.95, tau: fl
                                                   Hq, Hkv, d, block, float(gamma), float(tau), int(min_budget),
                                                   C.byref(opts), _stream_ptr(stream), C.byref(h)),
                "fp_prefill_plan_varlen")
-    return Plan(h, Hq, Hkv, d, block, np.diff(cu).tolist(), _lib.FP_LAYOUT_THD, dt, stream)
+    return Plan(h, Hq, Hkv, d, block, np.diff(cu).tolist(), _lib.FP_LAYOUT_THD, dt, stream,
+                params=_params(gamma, tau, min_budget, max_budget, qa_selection, vs_granularity))
 
 
 def attend(p: Plan, q, k, v, out=None, stream=None, noalloc: bool = False):
