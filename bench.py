@@ -13,7 +13,7 @@ blocks, the attention kernel's roofline (time from HIP events recorded by
 the library around that kernel), and the CPU oracle timed on a bounded
 sample (cpu_baseline).
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME] [--seed S]
 """
 from __future__ import annotations
 
@@ -211,6 +211,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--config", default="llama8b_128k")
+    ap.add_argument("--seed", type=int, default=None,
+                    help="seed of the synthetic inputs (default: the configuration's own)")
     ap.add_argument("--dense-reps", type=int, default=3)
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -246,6 +248,8 @@ def main() -> int:
         print(json.dumps({"error": "no GPU"}))
         return 1
     cfg = BY_NAME[args.config]
+    if args.seed is not None:
+        cfg = cfg.with_(seed=args.seed)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     t0 = time.perf_counter()
@@ -400,7 +404,7 @@ def main() -> int:
                    "d": cfg.d, "block": cfg.block, "gamma": cfg.gamma, "tau": cfg.tau,
                    "min_budget": cfg.min_budget, "max_budget": args.max_budget,
                    "qa_selection": args.qa_selection, "vs_granularity": args.vs_granularity,
-                   "parallelism": "single GPU"},
+                   "seed": cfg.seed, "parallelism": "single GPU"},
         "plan_ms": round(plan_ms, 3),
         "attend_ms": round(attend_ms, 3),
         "attention_kernel_ms": round(kern_avg_ms, 3),
