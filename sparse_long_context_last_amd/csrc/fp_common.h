@@ -36,7 +36,7 @@ __device__ __forceinline__ bf16_t f32_to_bf16(float f) {
 }
 
 // Number of bits needed to write every index in [0, n).
-__host__ __device__ inline int index_bits(long long n) {
+__host__ __device__ constexpr int index_bits(long long n) {
     int b = 1;
     while ((1LL << b) < n) ++b;
     return b;

@@ -15,6 +15,9 @@ constexpr int kSelChunk = 4096;      // list elements per selection workgroup (t
 constexpr long long kSelLongList = 262144;
 constexpr int kSelMaxPasses = 5;     // radix passes over 31 value bits + at most 24 index bits
 constexpr int kGammaShift = 24;      // G = rint(gamma * 2^24)
+// the longest selection list (the causal triangle of kMaxBlocks rows) fits the pass buffers
+static_assert(31 + index_bits((long long)kMaxBlocks * (kMaxBlocks + 1) / 2) <= kRadixBits * kSelMaxPasses,
+              "selection passes");
 constexpr unsigned char kPatternQueryAware = 1;
 constexpr size_t kNoAllocScratchBytes = 64ull << 20;   // device workspace of fp_prefill_attend_noalloc
 
