@@ -124,9 +124,10 @@ typedef struct fp_plan_options {
  *     min(row + 1, max(1, ceil(min_budget / block))) blocks, the missing ones
  *     filled nearest-first from the diagonal (pages: 1024 default, 2048).
  *   On FP_OK *out receives a new plan (released with fp_plan_destroy).  The
- *   plan's buffers are allocated stream-ordered on `stream`; a transient
- *   workspace of B*Hq*block*ceil(N/256)*256*4 bytes is used and released
- *   within the call.
+ *   plan's buffers are one block of the library's device memory cache (see
+ *   "Device memory" below), held until fp_plan_destroy; a transient
+ *   workspace of B*Hq*block*ceil(N/256)*256*4 bytes is taken from the cache
+ *   and given back within the call.
  */
 fp_status fp_prefill_plan(const void* q, const void* k, fp_dtype dtype,
                           int B, int Hq, int Hkv, int N, int d, int block,
@@ -208,9 +209,10 @@ fp_status fp_prefill_attend_noalloc(const fp_plan* plan, const void* q, const vo
  *   T = cu_seqlens[nseq].  cu_seqlens is a HOST array of nseq + 1 ints,
  *   cu_seqlens[0] = 0, non-decreasing (a zero-length sequence has no rows;
  *   its heads report pattern 0 and divergence 0).  Every sequence is planned
- *   exactly as fp_prefill_plan_ex would plan it alone; the call reuses one
- *   transient workspace of Hq*block*ceil(L/256)*256*4 bytes for the longest
- *   sequence L.  The plan records the layout: fp_prefill_attend then takes
+ *   exactly as fp_prefill_plan_ex would plan it alone, up to four sequences
+ *   at once on streams of the library (forked from and joined back to
+ *   `stream`); each of those streams takes one transient workspace of
+ *   Hq*block*ceil(L/256)*256*4 bytes for the longest sequence L it plans.  The plan records the layout: fp_prefill_attend then takes
  *   packed q, k, v and o.
  *   FP_ERR_INVALID_ARG for a NULL or malformed cu_seqlens; FP_ERR_SHAPE for a
  *   sequence of more than 4096 blocks.
@@ -281,8 +283,10 @@ enum {
 };
 fp_status fp_plan_copy_debug(const fp_plan* plan, int which, void* host_dst, size_t bytes);
 
-/* Releases the plan's buffers, stream-ordered on the stream the plan was
- * created on; work using the plan on other streams must be complete. */
+/* Gives the plan's buffers back to the library's device memory cache without
+ * waiting: they are reused only behind the plan's stream, which already
+ * waits for every attend enqueued with the plan on another stream.  Work
+ * using the plan must have been enqueued before this call. */
 void fp_plan_destroy(fp_plan* plan);
 
 /*
