@@ -38,7 +38,7 @@ COUNTERS_FILE = os.path.join(ROOT, "profiles", "attention_counters_llama8b_128k.
 
 
 class PowerSampler:
-    """Socket power and graphics clock of the GPU, read from the driver's
+    """Socket power and graphics clock of the GPU, read from the kernel GPU driver's
     metrics table (amdsmi, read-only) every 10 ms while a callable runs
     back to back for a few seconds.  The table lags the load by a few hundred
     milliseconds, so the first 40 % of the samples are dropped and a window
