@@ -101,6 +101,20 @@ def test_full_head_parity_d64(F, pool, name):
     run_layer(F, pool, name, D64[name])
 
 
+# fp32 inputs (vector-ALU last-block scores, fp32-MFMA attention) well past the
+# small layers: a 16k layer with GQA 4:1 at block 128 and a 16k layer at block
+# 64, every head bit-exact as above, sampled rows within 1e-4.
+FP32 = {
+    "fp32_gqa_16k": BY_NAME["tiny_fp32_4k"].with_(N=16384, Hq=8, Hkv=2, explicit_types=("V", "S", "QA", "N") * 2),
+    "fp32_bs64_16k": BY_NAME["tiny_fp32_4k"].with_(N=16384, block=64, min_budget=512),
+}
+
+
+@pytest.mark.parametrize("name", list(FP32))
+def test_full_head_parity_fp32(F, pool, name):
+    run_layer(F, pool, name, FP32[name])
+
+
 def run_layer(F, pool, name, cfg):
     gen = LayerGen(cfg)
     reps = representatives(gen)
