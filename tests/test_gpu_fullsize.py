@@ -115,6 +115,56 @@ def test_full_head_parity_fp32(F, pool, name):
     run_layer(F, pool, name, FP32[name])
 
 
+# A packed batch of sequences of different lengths (ragged tails, an empty
+# sequence) at sizes well past the small ragged layers: every head of every
+# sequence bit-exact, sampled rows within tolerance.
+PACKED_CFG = BY_NAME["llama8b_32k"].with_(Hq=8, Hkv=2, mix=(0.25, 0.25, 0.25, 0.25))
+PACKED_LENS = [16384, 5003, 0, 777, 9000, 200]
+
+
+def test_full_size_packed_batch(F, pool):
+    from tests.test_gpu_ragged import packed
+    cfg, lens = PACKED_CFG, PACKED_LENS
+    gens = [cfg.with_(B=1, N=max(128, -(-max(L, 1) // 128) * 128), seed=cfg.seed + 7 * b) for b, L in enumerate(lens)]
+    jobs = {}
+    for b, L in enumerate(lens):
+        if L == 0:
+            continue
+        nbL = -(-L // cfg.block)
+        for h in range(cfg.Hq):
+            rng = np.random.default_rng([37, b, h])
+            rows = sorted({nbL - 1, int(rng.integers(0, nbL))})
+            jobs[b, h] = pool.submit(oracle_head, gens[b], h, rows, None, (), L)
+    seqs, (qc, kc, vc), cu = packed(cfg, lens)
+    dt = torch.bfloat16
+    qd, kd, vd = (torch.from_numpy(np.ascontiguousarray(x)).to("cuda", dt) for x in (qc, kc, vc))
+    P = F.plan_varlen(qd, kd, cu, block=cfg.block, gamma=cfg.gamma, tau=cfg.tau, min_budget=cfg.min_budget)
+    out = F.attend(P, qd, kd, vd).float().cpu().numpy()
+    pattern, djs, row_ptr, col_idx = P.copy_out()
+    dbg = {x: P.debug_seqs(x) for x in ("qbar", "kbar", "rowmax", "rowsum", "colsum", "diagsum", "atrue", "ahat")}
+    r0 = 0
+    nchecked = 0
+    for b, L in enumerate(lens):
+        nbL = -(-L // cfg.block)
+        rows_b = cfg.Hq * nbL
+        if L == 0:
+            assert not pattern[b * cfg.Hq:(b + 1) * cfg.Hq].any()
+            continue
+        rp = row_ptr[r0: r0 + rows_b + 1] - row_ptr[r0]
+        ci = col_idx[row_ptr[r0]: row_ptr[r0 + rows_b]]
+        gpu = dict(pattern=pattern[b * cfg.Hq:(b + 1) * cfg.Hq], djs=djs[b * cfg.Hq:(b + 1) * cfg.Hq],
+                   row_ptr=rp, col_idx=ci, kvof=lambda h: h // cfg.group, **{x: dbg[x][b] for x in dbg})
+        for h in range(cfg.Hq):
+            ref = jobs[b, h].result()
+            compare_full_head(f"packed seq {b} (L={L})", ref, gpu, h)
+            for r, want in ref["ref"].items():
+                sl = slice(cu[b] + r * cfg.block, cu[b] + min(L, (r + 1) * cfg.block))
+                check_attention(out[sl, h], want, cfg.dtype, f"packed seq {b} h{h} row {r}")
+            nchecked += 1
+        r0 += rows_b
+    print(f"[packed] {nchecked} heads of {sum(1 for L in lens if L)} sequences bit-exact", flush=True)
+
+
 def run_layer(F, pool, name, cfg):
     gen = LayerGen(cfg)
     reps = representatives(gen)
