@@ -29,8 +29,9 @@ def make_pool(max_workers: int | None = None) -> ProcessPoolExecutor:
     return ProcessPoolExecutor(max_workers=n, mp_context=mp.get_context("spawn"), initializer=_init_worker)
 
 
-def oracle_head(cfg, h: int, rows, plan_kw: dict | None = None, dense_rows=(), L: int | None = None) -> dict:
-    """The oracle's plan of query head h (batch 0) of layer ``cfg`` and its
+def oracle_head(cfg, h: int, rows, plan_kw: dict | None = None, dense_rows=(), L: int | None = None,
+                b: int = 0) -> dict:
+    """The oracle's plan of query head h of sequence b of layer ``cfg`` and its
     float64 attention on the query-block rows ``rows`` (and dense causal
     attention on ``dense_rows``); with ``L`` the head's first L tokens only
     (a sequence of a packed batch).  Lists come back flattened with per-row
@@ -40,7 +41,7 @@ def oracle_head(cfg, h: int, rows, plan_kw: dict | None = None, dense_rows=(), L
 
     gen = LayerGen(cfg)
     kv = h // cfg.group
-    qh, kh, vh = gen.q_head(0, h), gen.k_head(0, kv), gen.v_head(0, kv)
+    qh, kh, vh = gen.q_head(b, h), gen.k_head(b, kv), gen.v_head(b, kv)
     if L is not None:
         qh, kh, vh = qh[:L], kh[:L], vh[:L]
     hp = O.plan_head(qh, kh, cfg.block, cfg.gamma, cfg.tau, cfg.min_budget, **(plan_kw or {}))
