@@ -335,7 +335,9 @@ def profile_enable(on: bool = True) -> None:
 
 
 def profile_read(reset: bool = True):
-    """(sparse_ms, sparse_launches, dense_ms, dense_launches) of the attention kernel."""
+    """(sparse_ms, sparse_launches, dense_ms, dense_launches): the attention
+    kernel's summed time in ms and its number of launches since the last
+    reset (divide for the average launch)."""
     sm, dm = C.c_double(), C.c_double()
     sn, dn = C.c_longlong(), C.c_longlong()
     _lib.check(_lib.load().fp_profile_read(C.byref(sm), C.byref(sn), C.byref(dm), C.byref(dn),
