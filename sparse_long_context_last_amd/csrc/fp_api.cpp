@@ -734,7 +734,7 @@ fp_status make_plan(const void* q, const void* k, fp_dtype dtype, int layout, in
     }
     PALLOC(sel, (size_t)2 * max_bh * lanes);
     PALLOC(selk, (size_t)kSelMaxPasses * 2 * max_bh * lanes);
-    PALLOC(hist, (size_t)kSelMaxPasses * 2 * max_bh * kRadixBins * lanes);
+    PALLOC(hist, (size_t)kSelHistBufs * 2 * max_bh * kRadixBins * lanes);
     PALLOC(aseg, segs.size());
 #undef PALLOC
     {
@@ -805,7 +805,7 @@ fp_status make_plan(const void* q, const void* k, fp_dtype dtype, int layout, in
         }
         P.sel = sel + (size_t)2 * max_bh * (i % kPlanLanes);
         P.selk = selk + (size_t)kSelMaxPasses * 2 * max_bh * (i % kPlanLanes);
-        P.hist = hist + (size_t)kSelMaxPasses * 2 * max_bh * kRadixBins * (i % kPlanLanes);
+        P.hist = hist + (size_t)kSelHistBufs * 2 * max_bh * kRadixBins * (i % kPlanLanes);
         o_qbar += (size_t)nbh * g.nb * d;
         o_kbar += (size_t)g.nseq * Hkv * g.nb * d;
         o_rowmax += (size_t)nbh * block;

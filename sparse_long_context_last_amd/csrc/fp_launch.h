@@ -14,6 +14,7 @@ constexpr int kRadixBins = 1 << kRadixBits;
 constexpr int kSelChunk = 4096;      // list elements per selection workgroup (twice that for long lists)
 constexpr long long kSelLongList = 262144;
 constexpr int kSelMaxPasses = 5;     // radix passes over 31 value bits + at most 24 index bits
+constexpr int kSelHistBufs = 3;      // histogram buffers the passes rotate through
 constexpr int kGammaShift = 24;      // G = rint(gamma * 2^24)
 // the longest selection list (the causal triangle of kMaxBlocks rows) fits the pass buffers
 static_assert(31 + index_bits((long long)kMaxBlocks * (kMaxBlocks + 1) / 2) <= kRadixBits * kSelMaxPasses,
@@ -72,7 +73,7 @@ struct PlanDev {
     float* ahat;                 // [BH][tri]
     SelState* sel;               // [2 BH]  final selection state per list
     SelState* selk;              // [kSelMaxPasses][2 BH]  state before each radix pass
-    unsigned long long* hist;    // [kSelMaxPasses][2 BH][kRadixBins]  mass histogram of each pass
+    unsigned long long* hist;    // [kSelHistBufs][2 BH][kRadixBins]  mass histograms, rotating over the passes
     unsigned char* colblk;       // [BH][nb]
     unsigned char* diagA;        // [BH][nb]
     unsigned char* diagB;        // [BH][nb]

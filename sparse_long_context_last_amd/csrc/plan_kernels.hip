@@ -963,15 +963,15 @@ __device__ __forceinline__ ListRef list_of(const PlanDev& P, int list) {
 }
 
 // Clears the lists' states (their totals are summed into them) and the
-// histograms of the first `passes` passes.
+// histogram buffer of the first pass.
 __global__ __launch_bounds__(256) void k_sel_reset(SelState* __restrict__ st, unsigned long long* __restrict__ hist,
-                                                   int nlists, int passes) {
+                                                   int nlists) {
     const int i = blockIdx.x * 256 + threadIdx.x;
     if (i < nlists) {
         SelState s = {};
         st[i] = s;
     }
-    const long long n = (long long)passes * nlists * kRadixBins;
+    const long long n = (long long)nlists * kRadixBins;
     for (long long t = i; t < n; t += (long long)gridDim.x * 256) hist[t] = 0ull;
 }
 
@@ -1079,7 +1079,10 @@ __device__ SelState sel_advance(const SelState s, const unsigned long long* __re
 // list's total; later passes: the previous state advanced by the previous
 // pass's histogram, by every workgroup of the list alike; workgroup 0
 // stores it), then the mass histogram of the next digit over the elements
-// whose key matches the resolved prefix.  grid (chunks of `chunk` elements, lists).
+// whose key matches the resolved prefix.  The histograms rotate through
+// kSelHistBufs buffers: pass k reads buffer k - 1, fills buffer k and (its
+// workgroup 0) clears buffer k + 1, which pass k - 1 was the last to read and
+// pass k + 1 fills.  grid (chunks of `chunk` elements, lists).
 __global__ __launch_bounds__(256) void k_sel_pass(PlanDev P, int k, int nlists, unsigned long long G, int chunk) {
     __shared__ unsigned long long hist[kRadixBins];
     const int list = blockIdx.y, tid = threadIdx.x;
@@ -1090,8 +1093,12 @@ __global__ __launch_bounds__(256) void k_sel_pass(PlanDev P, int k, int nlists, 
     if (blockIdx.x > 0 && base >= L.len) return;
     const SelState s = k == 0 ? sel_first_state(P.sel[list].U, L.len, G)
                               : sel_advance(P.selk[(size_t)(k - 1) * nlists + list],
-                                            P.hist + ((size_t)(k - 1) * nlists + list) * kRadixBins);
-    if (blockIdx.x == 0 && tid == 0) P.selk[(size_t)k * nlists + list] = s;
+                                            P.hist + ((size_t)((k - 1) % kSelHistBufs) * nlists + list) * kRadixBins);
+    if (blockIdx.x == 0) {
+        if (tid == 0) P.selk[(size_t)k * nlists + list] = s;
+        unsigned long long* nx = P.hist + ((size_t)((k + 1) % kSelHistBufs) * nlists + list) * kRadixBins;
+        for (int i = tid; i < kRadixBins; i += 256) nx[i] = 0ull;
+    }
     if (!s.active || base >= L.len) return;
     for (int i = tid; i < kRadixBins; i += 256) hist[i] = 0ull;
     __syncthreads();
@@ -1108,7 +1115,7 @@ __global__ __launch_bounds__(256) void k_sel_pass(PlanDev P, int k, int nlists, 
         }
     }
     __syncthreads();
-    unsigned long long* gh = P.hist + ((size_t)k * nlists + list) * kRadixBins;
+    unsigned long long* gh = P.hist + ((size_t)(k % kSelHistBufs) * nlists + list) * kRadixBins;
     for (int i = tid; i < kRadixBins; i += 256)
         if (hist[i]) atomicAdd(&gh[i], hist[i]);
 }
@@ -1118,7 +1125,7 @@ __global__ __launch_bounds__(256) void k_sel_pass(PlanDev P, int k, int nlists, 
 __global__ __launch_bounds__(256) void k_sel_final(PlanDev P, int passes, int nlists) {
     const int list = blockIdx.x;
     const SelState s = sel_advance(P.selk[(size_t)(passes - 1) * nlists + list],
-                                   P.hist + ((size_t)(passes - 1) * nlists + list) * kRadixBins);
+                                   P.hist + ((size_t)((passes - 1) % kSelHistBufs) * nlists + list) * kRadixBins);
     if (threadIdx.x == 0) P.sel[list] = s;
 }
 
@@ -1608,7 +1615,7 @@ static hipError_t launch_plan_t(const PlanArgs& a, PlanDev& P, hipStream_t st) {
         const int passes = (kbits + kRadixBits - 1) / kRadixBits;
         if (passes > kSelMaxPasses) return hipErrorInvalidValue;
         hipLaunchKernelGGL(k_sel_reset, dim3(grid1((long long)nlists * kRadixBins)), dim3(256), 0, st, P.sel, P.hist,
-                           nlists, passes);
+                           nlists);
         // list elements per workgroup: every workgroup of a pass first derives
         // the list's state from the previous pass's histogram, so long lists
         // take larger chunks (measured: 4096 at 32k, 8192 at 128k)
