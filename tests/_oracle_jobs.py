@@ -45,11 +45,12 @@ def oracle_head(cfg, h: int, rows, plan_kw: dict | None = None, dense_rows=(), L
     if L is not None:
         qh, kh, vh = qh[:L], kh[:L], vh[:L]
     hp = O.plan_head(qh, kh, cfg.block, cfg.gamma, cfg.tau, cfg.min_budget, **(plan_kw or {}))
-    ref = O.attend_rows(qh, kh, vh, hp.mask, cfg.block, list(rows)) if len(rows) else {}
+    ref = O.attend_rows(qh, kh, vh, hp.mask, cfg.block, list(rows), hp.cols) if len(rows) else {}
     refd = O.attend_rows(qh, kh, vh, O.dense_mask(cfg.nb), cfg.block, list(dense_rows)) if len(dense_rows) else {}
     counts = np.array([len(x) for x in hp.lists], dtype=np.int64)
     flat = np.concatenate(hp.lists).astype(np.int32) if len(hp.lists) else np.zeros(0, np.int32)
     return dict(h=h, type=gen.types[h], pattern=hp.pattern, D=hp.D, qbar=hp.qbar, kbar=hp.kbar,
                 M=hp.stats.M, Z=hp.stats.Z, c=hp.stats.c, g=hp.stats.g, a_true=hp.stats.a_true,
                 ahat=O.tri_values(hp.A), counts=counts, flat=flat, ref=ref, refd=refd,
-                blocks=int(counts.sum()))
+                blocks=int(counts.sum()),
+                cols=(np.nonzero(hp.cols)[0].astype(np.int32) if hp.cols is not None else np.zeros(0, np.int32)))

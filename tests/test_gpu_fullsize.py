@@ -270,6 +270,7 @@ def test_size_limits(F, name):
 
 
 @pytest.mark.parametrize("name,max_budget,qa_selection", [("llama8b_32k", 4096, "flattened"),
+                                                          ("llama8b_128k", 8192, "flattened"),
                                                           ("glm9b_64k_bs64", 8192, "flattened"),
                                                           ("llama8b_128k", 0, "querywise"),
                                                           ("glm9b_64k_bs64", 0, "querywise")])
@@ -302,3 +303,37 @@ def test_full_size_plan_options(F, pool, name, max_budget, qa_selection):
     print(f"[{name} cap {max_budget} {qa_selection}] all {cfg.Hq} heads bit-exact", flush=True)
     del q, k, v, out, P
     torch.cuda.empty_cache()
+
+
+def test_full_size_token_mode_every_head(F, pool):
+    """The 128k layer with token-granular vertical lines: every head's block
+    lists, pattern, divergence and selected columns (colptr, colidx)
+    bit-exact with the oracle's token-mode plan, two sampled rows of
+    attention per head within tolerance."""
+    cfg = BY_NAME["llama8b_128k"]
+    kw = dict(vs_granularity="token")
+    jobs = [pool.submit(oracle_head, cfg, h, row_sample(cfg, h, False), kw) for h in range(cfg.Hq)]
+    q, k, v = LayerGen(cfg).torch_layer("cuda")
+    P = F.plan(q, k, block=cfg.block, gamma=cfg.gamma, tau=cfg.tau, min_budget=cfg.min_budget, **kw)
+    out = F.attend(P, q, k, v)
+    torch.cuda.synchronize()
+    pattern, djs, row_ptr, col_idx = P.copy_out()
+    colptr, colidx = P.debug("colptr"), P.debug("colidx")
+    nb, bs = cfg.nb, cfg.block
+    with_cols = 0
+    for fut in jobs:
+        ref = fut.result()
+        h = ref["h"]
+        where = f"token 128k head {h} ({ref['type']})"
+        assert int(pattern[h]) == ref["pattern"] and djs[h] == ref["D"], where
+        np.testing.assert_array_equal(np.diff(row_ptr[h * nb: (h + 1) * nb + 1]), ref["counts"], err_msg=where)
+        np.testing.assert_array_equal(col_idx[row_ptr[h * nb]: row_ptr[(h + 1) * nb]], ref["flat"], err_msg=where)
+        cols = ref["cols"]
+        ptr = np.searchsorted(cols, np.arange(nb + 1) * bs).astype(np.int32)
+        np.testing.assert_array_equal(colptr[h], ptr, err_msg=where + ": colptr")
+        np.testing.assert_array_equal(colidx[h][: ptr[-1]], cols, err_msg=where + ": colidx")
+        with_cols += int(cols.size > 0)
+        for r, want in ref["ref"].items():
+            sl = slice(r * bs, (r + 1) * bs)
+            check_attention(out[0, h, sl].float().cpu().numpy(), want, cfg.dtype, f"{where} row {r}")
+    print(f"[token 128k] all {cfg.Hq} heads bit-exact, {with_cols} with token columns", flush=True)
