@@ -142,13 +142,18 @@ def test_full_size_two_sequences(F, pool):
 # A packed batch of sequences of different lengths (ragged tails, an empty
 # sequence) at sizes well past the small ragged layers: every head of every
 # sequence bit-exact, sampled rows within tolerance.
-PACKED_CFG = BY_NAME["llama8b_32k"].with_(Hq=8, Hkv=2, mix=(0.25, 0.25, 0.25, 0.25))
-PACKED_LENS = [16384, 5003, 0, 777, 9000, 200]
+PACKED = {
+    "gqa_6seq": (BY_NAME["llama8b_32k"].with_(Hq=8, Hkv=2, mix=(0.25, 0.25, 0.25, 0.25)),
+                 [16384, 5003, 0, 777, 9000, 200]),
+    # the packed batch bench.py --varlen times (128713 tokens, 32 query heads)
+    "bench_varlen_7seq": (BY_NAME["llama8b_128k"], [65536, 33000, 16500, 8300, 4200, 1100, 77]),
+}
 
 
-def test_full_size_packed_batch(F, pool):
+@pytest.mark.parametrize("name", list(PACKED))
+def test_full_size_packed_batch(F, pool, name):
     from tests.test_gpu_ragged import packed
-    cfg, lens = PACKED_CFG, PACKED_LENS
+    cfg, lens = PACKED[name]
     gens = [cfg.with_(B=1, N=max(128, -(-max(L, 1) // 128) * 128), seed=cfg.seed + 7 * b) for b, L in enumerate(lens)]
     jobs = {}
     for b, L in enumerate(lens):
@@ -176,17 +181,23 @@ def test_full_size_packed_batch(F, pool):
             continue
         rp = row_ptr[r0: r0 + rows_b + 1] - row_ptr[r0]
         ci = col_idx[row_ptr[r0]: row_ptr[r0 + rows_b]]
+        seq_dbg = {x: dbg[x][b] for x in dbg}
+        if L < cfg.block:
+            # the plan keeps `block` representative rows; the first ones do not exist and hold 0
+            for x in ("rowmax", "rowsum"):
+                assert not seq_dbg[x][:, : cfg.block - L].any()
+                seq_dbg[x] = seq_dbg[x][:, cfg.block - L:]
         gpu = dict(pattern=pattern[b * cfg.Hq:(b + 1) * cfg.Hq], djs=djs[b * cfg.Hq:(b + 1) * cfg.Hq],
-                   row_ptr=rp, col_idx=ci, kvof=lambda h: h // cfg.group, **{x: dbg[x][b] for x in dbg})
+                   row_ptr=rp, col_idx=ci, kvof=lambda h: h // cfg.group, **seq_dbg)
         for h in range(cfg.Hq):
             ref = jobs[b, h].result()
-            compare_full_head(f"packed seq {b} (L={L})", ref, gpu, h)
+            compare_full_head(f"{name} seq {b} (L={L})", ref, gpu, h)
             for r, want in ref["ref"].items():
                 sl = slice(cu[b] + r * cfg.block, cu[b] + min(L, (r + 1) * cfg.block))
                 check_attention(out[sl, h], want, cfg.dtype, f"packed seq {b} h{h} row {r}")
             nchecked += 1
         r0 += rows_b
-    print(f"[packed] {nchecked} heads of {sum(1 for L in lens if L)} sequences bit-exact", flush=True)
+    print(f"[packed {name}] {nchecked} heads of {sum(1 for L in lens if L)} sequences bit-exact", flush=True)
 
 
 def run_layer(F, pool, name, cfg):
