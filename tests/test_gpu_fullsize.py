@@ -316,12 +316,13 @@ def test_full_size_plan_options(F, pool, name, max_budget, qa_selection):
     torch.cuda.empty_cache()
 
 
-def test_full_size_token_mode_every_head(F, pool):
-    """The 128k layer with token-granular vertical lines: every head's block
-    lists, pattern, divergence and selected columns (colptr, colidx)
+@pytest.mark.parametrize("name", ["llama8b_128k", "glm9b_64k_bs64"])
+def test_full_size_token_mode_every_head(F, pool, name):
+    """A full-size layer with token-granular vertical lines: every head's
+    block lists, pattern, divergence and selected columns (colptr, colidx)
     bit-exact with the oracle's token-mode plan, two sampled rows of
     attention per head within tolerance."""
-    cfg = BY_NAME["llama8b_128k"]
+    cfg = BY_NAME[name]
     kw = dict(vs_granularity="token")
     jobs = [pool.submit(oracle_head, cfg, h, row_sample(cfg, h, False), kw) for h in range(cfg.Hq)]
     q, k, v = LayerGen(cfg).torch_layer("cuda")
@@ -335,7 +336,7 @@ def test_full_size_token_mode_every_head(F, pool):
     for fut in jobs:
         ref = fut.result()
         h = ref["h"]
-        where = f"token 128k head {h} ({ref['type']})"
+        where = f"token {name} head {h} ({ref['type']})"
         assert int(pattern[h]) == ref["pattern"] and djs[h] == ref["D"], where
         np.testing.assert_array_equal(np.diff(row_ptr[h * nb: (h + 1) * nb + 1]), ref["counts"], err_msg=where)
         np.testing.assert_array_equal(col_idx[row_ptr[h * nb]: row_ptr[(h + 1) * nb]], ref["flat"], err_msg=where)
@@ -347,4 +348,4 @@ def test_full_size_token_mode_every_head(F, pool):
         for r, want in ref["ref"].items():
             sl = slice(r * bs, (r + 1) * bs)
             check_attention(out[0, h, sl].float().cpu().numpy(), want, cfg.dtype, f"{where} row {r}")
-    print(f"[token 128k] all {cfg.Hq} heads bit-exact, {with_cols} with token columns", flush=True)
+    print(f"[token {name}] all {cfg.Hq} heads bit-exact, {with_cols} with token columns", flush=True)
