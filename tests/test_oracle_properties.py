@@ -80,3 +80,33 @@ def test_block_conversion_is_the_token_level_cover(case):
             if cols[j] or diags[i - j]:
                 want[i // bs, j // bs] = True
     np.testing.assert_array_equal(O.vs_block_mask(cols, diags, bs), want)
+
+
+@st.composite
+def _masks(draw):
+    nb = draw(st.integers(min_value=1, max_value=12))
+    bs = draw(st.sampled_from([64, 128]))
+    bits = draw(st.lists(st.booleans(), min_size=nb * nb, max_size=nb * nb))
+    mask = np.tril(np.array(bits, bool).reshape(nb, nb))
+    min_budget = draw(st.integers(min_value=0, max_value=14 * bs))
+    return mask, bs, min_budget
+
+
+@SETTINGS
+@given(case=_masks())
+def test_floor_adds_the_nearest_missing_blocks(case):
+    mask, bs, min_budget = case
+    nb = mask.shape[0]
+    out = O.apply_floor(mask, min_budget, bs)
+    f = max(1, -(-min_budget // bs))
+    for qb in range(nb):
+        want = mask[qb].copy()
+        need = min(qb + 1, f) - int(want.sum())
+        for kb in range(qb, -1, -1):          # nearest the diagonal first
+            if need <= 0:
+                break
+            if not want[kb]:
+                want[kb] = True
+                need -= 1
+        np.testing.assert_array_equal(out[qb], want, err_msg=f"row {qb}")
+    assert not np.triu(out, 1).any()
