@@ -1,4 +1,4 @@
-"""GPU parity on seeded random small shapes: batch, query / key-value heads
+"""GPU parity on seeded random small shapes (and packed batches of them): batch, query / key-value heads
 (grouped 1:1 up to 6:1, three key-value heads), head dim, block, dtype,
 sequence length (ragged tails, lengths below one block), gamma, tau and
 minimum budget drawn at collection from a fixed seed.  Every head is
@@ -8,7 +8,7 @@ import numpy as np
 import pytest
 
 from synth import BY_NAME
-from tests.test_gpu_ragged import check_layer
+from tests.test_gpu_ragged import check_layer, check_packed
 
 pytestmark = pytest.mark.gpu
 
@@ -54,3 +54,26 @@ def F():
 def test_random_shape_parity(F, name):
     cfg, N = CASES[name]
     check_layer(F, cfg, N, name)
+
+
+def _packed_cases(n=12, seed=2027):
+    rng = np.random.default_rng(seed)
+    out = {}
+    for i, (cfg, _) in enumerate(_cases(n, seed).values()):
+        nseq = int(rng.integers(1, 6))
+        lens = [int(rng.choice([0, int(rng.integers(1, cfg.block)), int(rng.integers(cfg.block, 1500))]))
+                for _ in range(nseq)]
+        if not any(lens):
+            lens[0] = int(rng.integers(1, 700))
+        out[f"packed{i}_H{cfg.Hq}x{cfg.Hkv}_d{cfg.d}_bs{cfg.block}_{cfg.dtype}_" + "-".join(map(str, lens))] = \
+            (cfg.with_(B=1), lens)
+    return out
+
+
+PACKED_CASES = _packed_cases()
+
+
+@pytest.mark.parametrize("name", list(PACKED_CASES))
+def test_random_packed_parity(F, name):
+    cfg, lens = PACKED_CASES[name]
+    check_packed(F, cfg, lens, name)
